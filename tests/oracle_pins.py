@@ -1,0 +1,479 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle (the ``oracle`` module,
+possibly running a planted-mistake build through ``oracle.variant``) disagrees with
+something the pages or the mathematics fix:
+
+* decode tables against torch's independent fp8 / bf16 casts and the OCP spec values
+  (golden files),
+* Eq. (1) against an exact rational brute force (``fractions.Fraction``, decoding through
+  torch / the golden e2m1 table, one correct RNE rounding to fp32),
+* special cases that reduce Eq. (1) to a numpy matrix product,
+* invariants (key / head permutation, linearity in w, power-of-two scale homogeneity,
+  non-negativity, masking),
+* top-k against the worked example in the golden file and against numpy's lexsort,
+* the equivalences between the three ways of naming keys (paged vs contiguous,
+  candidate blocks vs dense-masked).
+
+Sizes are tiny so that the whole list runs in seconds.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ----------------------------------------------------------------------------- helpers
+
+
+def _golden_lines(name):
+    for line in (GOLDEN / name).read_text().splitlines():
+        line = line.strip()
+        if line and not line.startswith("#"):
+            yield line.split()
+
+
+def e2m1_golden() -> dict[int, float]:
+    return {int(a): float(b) for a, b in _golden_lines("ocp_e2m1.txt")}
+
+
+def torch_fp8(codes) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def torch_bf16(bits) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def frac_to_f32(x: Fraction) -> np.float32:
+    """Exact rational -> float32 with one round-to-nearest-even (normal and subnormal)."""
+    if x == 0:
+        return np.float32(0.0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum = max(e, -126) - 23
+    m = a / Fraction(2) ** quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return np.float32(sign * float(Fraction(n) * Fraction(2) ** quantum))
+
+
+def near_f32_tie(x: Fraction) -> bool:
+    """True when x lies within 2^-40 (relative) of a float32 rounding midpoint, where an
+    fp64 evaluation may legitimately round to either neighbour."""
+    if x == 0:
+        return False
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    frac = (a / quantum) % 1
+    return abs(frac - Fraction(1, 2)) * quantum < a * Fraction(1, 2 ** 40)
+
+
+def exact_scores(qv, wv, kv):
+    """Eq. (1) in exact rationals: qv [H][D], wv [H], kv [N][D] of Fractions -> [N]."""
+    out = []
+    for key in kv:
+        acc = Fraction(0)
+        for j in range(len(qv)):
+            dot = sum((a * b for a, b in zip(qv[j], key)), Fraction(0))
+            acc += wv[j] * (dot if dot > 0 else Fraction(0))
+        out.append(acc)
+    return out
+
+
+def _fr(arr):
+    return [[Fraction(float(v)) for v in row] for row in np.asarray(arr, dtype=np.float64)]
+
+
+def _dense_one(q, qd, w, k, sc, kd, n):
+    return O.logits_dense(q[None], qd, w[None], k, sc, kd, np.array([0], np.int32),
+                          np.array([n], np.int32))[0]
+
+
+def _check_exact(got, exact, what):
+    for i, (g, x) in enumerate(zip(got, exact)):
+        want = frac_to_f32(x)
+        if not (g == want or near_f32_tie(x)):
+            raise AssertionError(f"{what}: key {i}: oracle {g!r} exact {want!r} ({float(x)!r})")
+
+
+# ----------------------------------------------------------------------------- decoding
+
+
+def pin_fp8_table_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours, ref = O.decode_fp8(codes), torch_fp8(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)), "fp8 NaN codes differ from torch"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok]), "fp8 values differ from torch"
+    assert np.array_equal(np.signbit(ours[ok]), np.signbit(ref[ok])), "fp8 zero signs differ"
+
+
+def pin_fp8_spec_values():
+    for code, val in _golden_lines("ocp_fp8_e4m3fn_special.txt"):
+        got = float(O.decode_fp8([int(code, 16)])[0])
+        want = float(val)
+        if np.isnan(want):
+            assert np.isnan(got), f"fp8 {code} should be NaN"
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), f"fp8 {code}: {got} != {want}"
+
+
+def pin_e2m1_spec_table():
+    table = e2m1_golden()
+    got = O.decode_e2m1(np.arange(16))
+    for c in range(16):
+        assert got[c] == table[c] and np.signbit(got[c]) == np.signbit(table[c]), f"e2m1 code {c}"
+
+
+def pin_ue8m0_closed_form():
+    got = O.decode_ue8m0(np.arange(256))
+    for e in range(255):
+        assert got[e] == float(Fraction(2) ** (e - 127)), f"ue8m0 {e}"
+    assert np.isnan(got[255]), "ue8m0 255 must be NaN"
+
+
+def pin_bf16_vs_torch():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 16, size=2000, dtype=np.uint32).astype(np.uint16)
+    ours, ref = O.decode_bf16(bits), torch_bf16(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+# ----------------------------------------------------------------------------- Eq. (1) exact
+
+
+def pin_bruteforce_fp8():
+    rng = np.random.default_rng(11)
+    for heads, dim, n in [(1, 4, 9), (2, 4, 9), (4, 32, 7), (64, 128, 4)]:
+        q = synth.to_fp8_e4m3fn(rng.standard_normal((heads, dim)).astype(np.float32) * 2)
+        k = synth.to_fp8_e4m3fn(rng.standard_normal((n, dim)).astype(np.float32) * 2)
+        sc = rng.uniform(0.5, 2.0, n).astype(np.float32)
+        w = (rng.standard_normal(heads) / 8).astype(np.float32)
+        got = _dense_one(q, "fp8", w, k, sc, "fp8", n)
+        kv = [[Fraction(float(v)) * Fraction(float(sc[i])) for v in row]
+              for i, row in enumerate(torch_fp8(k))]
+        exact = exact_scores(_fr(torch_fp8(q)), [Fraction(float(x)) for x in w], kv)
+        _check_exact(got, exact, f"fp8 H={heads} D={dim}")
+
+
+def pin_bruteforce_bf16():
+    rng = np.random.default_rng(12)
+    for heads, dim, n in [(1, 4, 9), (2, 4, 9), (64, 128, 3)]:
+        q = synth.to_bf16_bits(rng.standard_normal((heads, dim)).astype(np.float32) / 11)
+        k = synth.to_bf16_bits(rng.standard_normal((n, dim)).astype(np.float32) / 11)
+        w = (rng.standard_normal(heads) / 8).astype(np.float32)
+        got = _dense_one(q, "bf16", w, k, None, "bf16", n)
+        exact = exact_scores(_fr(torch_bf16(q)), [Fraction(float(x)) for x in w],
+                             _fr(torch_bf16(k)))
+        _check_exact(got, exact, f"bf16 H={heads} D={dim}")
+
+
+def _mx_decode_golden(codes, scales, dim):
+    table = e2m1_golden()
+    out = []
+    for row_c, row_s in zip(codes, scales):
+        vals = []
+        for i in range(dim):
+            byte = int(row_c[i // 2])
+            nib = byte & 0xF if i % 2 == 0 else byte >> 4
+            vals.append(Fraction(table[nib]) * Fraction(2) ** (int(row_s[i // 32]) - 127))
+        out.append(vals)
+    return out
+
+
+def pin_bruteforce_mxfp4():
+    rng = np.random.default_rng(13)
+    for heads, dim, n in [(1, 32, 9), (2, 64, 7), (64, 128, 4)]:
+        q = synth.to_fp8_e4m3fn(rng.standard_normal((heads, dim)).astype(np.float32) * 2)
+        codes, scales = synth.to_mxfp4(rng.standard_normal((n, dim)) * rng.uniform(0.1, 10, (n, 1)))
+        w = (rng.standard_normal(heads) / 8).astype(np.float32)
+        got = _dense_one(q, "fp8", w, codes, scales, "mxfp4", n)
+        exact = exact_scores(_fr(torch_fp8(q)), [Fraction(float(x)) for x in w],
+                             _mx_decode_golden(codes, scales, dim))
+        _check_exact(got, exact, f"mxfp4 H={heads} D={dim}")
+
+
+# ----------------------------------------------------------------------------- special cases
+
+
+def pin_single_head_is_relu_matmul():
+    """H = 1, w = 1: I = ReLU(q . k), i.e. np.maximum(K @ q, 0)."""
+    rng = np.random.default_rng(21)
+    n = 300
+    q = synth.to_fp8_e4m3fn(rng.standard_normal((1, 128)).astype(np.float32))
+    k = synth.to_fp8_e4m3fn(rng.standard_normal((n, 128)).astype(np.float32))
+    sc = rng.uniform(0.5, 2.0, n).astype(np.float32)
+    got = _dense_one(q, "fp8", np.ones(1, np.float32), k, sc, "fp8", n)
+    ref = np.maximum((torch_fp8(k) * sc[:, None].astype(np.float64)) @ torch_fp8(q)[0], 0.0)
+    assert np.allclose(got, ref, rtol=2e-7, atol=0), "H=1 ReLU(q.k) mismatch"
+    assert (got == 0).sum() > n // 4, "expected many ReLU zeros"
+
+
+def pin_positive_inputs_are_matvec():
+    """All-positive q and keys, w = 1: ReLU is inactive and I = (sum_j q_j) . k."""
+    rng = np.random.default_rng(22)
+    n, heads = 200, 64
+    q = synth.to_fp8_e4m3fn(np.abs(rng.standard_normal((heads, 128))).astype(np.float32))
+    k = synth.to_fp8_e4m3fn(np.abs(rng.standard_normal((n, 128))).astype(np.float32))
+    got = _dense_one(q, "fp8", np.ones(heads, np.float32), k, np.ones(n, np.float32), "fp8", n)
+    ref = torch_fp8(k) @ torch_fp8(q).sum(axis=0)
+    assert np.allclose(got, ref, rtol=2e-7, atol=0), "positive matvec mismatch"
+
+
+def pin_zero_weights():
+    """w = 0 gives I = 0 everywhere, so the top-k is the first k keys (lower index wins)."""
+    case = synth.batched_decode(seed=31, rows=2, n=300, topk=17)
+    case.w = np.zeros_like(case.w)
+    idx, val = O.select_case(case)
+    assert np.all(val == 0)
+    assert np.array_equal(idx, np.tile(np.arange(17, dtype=np.int32), (2, 1)))
+
+
+def pin_nonnegative_for_nonnegative_w():
+    case = synth.batched_decode(seed=32, rows=3, n=400, topk=8)
+    case.w = np.abs(case.w)
+    lg = O.logits_dense(case.q, case.q_dtype, case.w, case.k, case.k_scale, case.k_dtype,
+                        case.row_ks, case.row_ke)
+    assert np.all(lg >= 0) and np.any(lg > 0)
+
+
+# ----------------------------------------------------------------------------- invariants
+
+
+def pin_key_permutation():
+    """Permuting the keys permutes the logits and maps the selected indices through the
+    permutation (the selection must use the actual indices, not the first k)."""
+    rng = np.random.default_rng(41)
+    case = synth.batched_decode(seed=41, rows=1, n=500, topk=20)
+    perm = rng.permutation(500)
+    base = O.logits_dense(case.q, "fp8", case.w, case.k, case.k_scale, "fp8", case.row_ks, case.row_ke)
+    pl = O.logits_dense(case.q, "fp8", case.w, case.k[perm], case.k_scale[perm], "fp8",
+                        case.row_ks, case.row_ke)
+    assert np.array_equal(pl[0], base[0][perm]), "logits not permutation-equivariant"
+    i0, _ = O.topk(base, 20)
+    i1, _ = O.topk(pl, 20)
+    assert np.unique(base[0]).size == 500
+    assert np.array_equal(perm[i1[0]], i0[0]), "top-k not permutation-equivariant"
+
+
+def pin_head_permutation():
+    rng = np.random.default_rng(42)
+    case = synth.batched_decode(seed=42, rows=2, n=300, topk=8)
+    perm = rng.permutation(64)
+    a = O.logits_dense(case.q, "fp8", case.w, case.k, case.k_scale, "fp8", case.row_ks, case.row_ke)
+    b = O.logits_dense(case.q[:, perm], "fp8", case.w[:, perm], case.k, case.k_scale, "fp8",
+                       case.row_ks, case.row_ke)
+    assert np.allclose(a, b, rtol=1.2e-7, atol=0), "head order changed the score"
+
+
+def pin_linear_in_w():
+    case = synth.batched_decode(seed=43, rows=2, n=300, topk=8)
+    args = (case.k, case.k_scale, "fp8", case.row_ks, case.row_ke)
+    a = O.logits_dense(case.q, "fp8", case.w, *args)
+    b = O.logits_dense(case.q, "fp8", case.w * 2, *args)
+    assert np.array_equal(b, a * 2), "scaling w by 2 must scale I by 2 exactly"
+    w2 = np.random.default_rng(43).standard_normal(case.w.shape).astype(np.float32) / 8
+    c = O.logits_dense(case.q, "fp8", w2, *args)
+    d = O.logits_dense(case.q, "fp8", case.w + w2, *args)
+    assert np.allclose(d, a.astype(np.float64) + c, rtol=1e-5, atol=1e-5), "I not additive in w"
+
+
+def pin_scale_homogeneity():
+    """Multiplying a token's fp8 scale by 4 (or its UE8M0 exponents by +2) multiplies
+    its score by 4 exactly."""
+    case = synth.batched_decode(seed=44, rows=2, n=300, topk=8)
+    a = O.logits_dense(case.q, "fp8", case.w, case.k, case.k_scale, "fp8", case.row_ks, case.row_ke)
+    b = O.logits_dense(case.q, "fp8", case.w, case.k, case.k_scale * 4, "fp8", case.row_ks, case.row_ke)
+    assert np.array_equal(b, a * 4)
+    sp = synth.sparse_blocks(seed=45, rows=2, ctx=1024, n_blocks=3, block=128, topk=8,
+                             poison_noncand=False)
+    args = (sp.row_ks, sp.row_ke, sp.cand, sp.n_cols, sp.block)
+    a = O.logits_sparse(sp.q, "fp8", sp.w, sp.k, sp.k_scale, "mxfp4", *args)
+    b = O.logits_sparse(sp.q, "fp8", sp.w, sp.k, sp.k_scale + 2, "mxfp4", *args)
+    fin = np.isfinite(a)
+    assert np.array_equal(b[fin], a[fin] * 4)
+
+
+def pin_scale_per_group():
+    """Each UE8M0 byte scales only its own 32 elements: raising group g's exponent by one
+    equals doubling q's dims 32g..32g+31 (fp8 doubling is exact away from the top binade)."""
+    sp = synth.sparse_blocks(seed=46, rows=2, ctx=512, n_blocks=2, block=128, topk=8,
+                             poison_noncand=False)
+    args = (sp.row_ks, sp.row_ke, sp.cand, sp.n_cols, sp.block)
+    qf = torch_fp8(sp.q)
+    for g in range(4):
+        sc = sp.k_scale.copy()
+        sc[:, g] += 1
+        a = O.logits_sparse(sp.q, "fp8", sp.w, sp.k, sc, "mxfp4", *args)
+        q2f = qf.copy()
+        q2f[:, :, 32 * g:32 * g + 32] *= 2
+        q2 = synth.to_fp8_e4m3fn(q2f.astype(np.float32))
+        assert np.array_equal(torch_fp8(q2), q2f), "doubling must stay exact"
+        b = O.logits_sparse(q2, "fp8", sp.w, sp.k, sp.k_scale, "mxfp4", *args)
+        assert np.array_equal(a, b), f"group {g} scale does not match its 32 dims"
+
+
+def pin_masking():
+    """Keys outside a row's range are never read: poisoned (NaN) neighbours do not leak,
+    and columns past the row's length are -inf."""
+    case = synth.batched_decode(seed=47, rows=4, n=200, topk=8, ragged=True, gap=37)
+    lg = O.logits_dense(case.q, "fp8", case.w, case.k, case.k_scale, "fp8", case.row_ks,
+                        case.row_ke, ld=260)
+    for r in range(4):
+        L = int(case.row_ke[r] - case.row_ks[r])
+        assert np.all(np.isfinite(lg[r, :L])), "poison leaked into a valid key"
+        assert np.all(lg[r, L:] == -np.inf)
+
+
+# ----------------------------------------------------------------------------- top-k
+
+
+def pin_topk_worked_example():
+    lines = {ln[0]: ln[1:] for ln in _golden_lines("topk_worked_example.txt")}
+    scores = np.array([[float(x) for x in lines["scores"]]], np.float32)
+    k = int(lines["k"][0])
+    want = np.array([[int(x) for x in lines["selected"]]], np.int32)
+    idx, val = O.topk(scores, k)
+    assert np.array_equal(idx, want), f"worked example: {idx} != {want}"
+    assert np.array_equal(val, scores[0][want[0]][None])
+
+
+def pin_topk_vs_lexsort():
+    """top-k = prefix of the full (value desc, index asc) order, over rows with many ties,
+    signed zeros and absent (-inf / NaN) entries."""
+    rng = np.random.default_rng(51)
+    rows, n, k = 6, 700, 50
+    lg = rng.integers(-20, 20, size=(rows, n)).astype(np.float32) / 4
+    lg[rng.random((rows, n)) < 0.05] = -0.0
+    lg[rng.random((rows, n)) < 0.1] = -np.inf
+    lg[rng.random((rows, n)) < 0.02] = np.nan
+    lg[2] = np.where(rng.random(n) < 0.5, 0.0, -0.0)
+    lg[3, :] = -np.inf
+    lg[3, :10] = 1.0
+    lens = np.array([n, n - 1, 333, n, 17, 0], np.int32)
+    idx, val = O.topk(lg, k, lens)
+    for r in range(rows):
+        cols = np.arange(lens[r])
+        v = lg[r, :lens[r]].astype(np.float64)
+        ok = np.isfinite(v) | (v == np.inf)
+        cols, v = cols[ok], v[ok]
+        v = np.where(v == 0, 0.0, v)
+        order = cols[np.lexsort((cols, -v))][:k]
+        want = np.full(k, -1, np.int32)
+        want[:order.size] = order
+        assert np.array_equal(idx[r], want), f"row {r}: top-k is not the sort prefix"
+        assert np.array_equal(val[r][:order.size], lg[r][order])
+        assert np.all(val[r][order.size:] == -np.inf)
+
+
+def pin_topk_all_equal():
+    lg = np.full((2, 100), 3.5, np.float32)
+    idx, _ = O.topk(lg, 30)
+    assert np.array_equal(idx, np.tile(np.arange(30, dtype=np.int32), (2, 1)))
+
+
+def pin_topk_pads_short_rows():
+    lg = np.array([[1.0, 5.0, -np.inf, 2.0]], np.float32)
+    idx, val = O.topk(lg, 6)
+    assert idx.tolist() == [[1, 3, 0, -1, -1, -1]]
+    assert val[0, :3].tolist() == [5.0, 2.0, 1.0] and np.all(val[0, 3:] == -np.inf)
+
+
+# ----------------------------------------------------------------------------- key sources
+
+
+def _paged_from_dense(case, page, perm_pages, rng):
+    n = int(case.row_ke[0] - case.row_ks[0])
+    rows = case.rows
+    npg = (n + page - 1) // page
+    P = rows * npg
+    kp = np.full((P, page, 128), synth.FP8_NAN, np.uint8)
+    sp = np.full((P, page), np.nan, np.float32)
+    phys = rng.permutation(P) if perm_pages else np.arange(P)
+    bt = np.full((rows, npg + 2), -1, np.int32)
+    for r in range(rows):
+        for p in range(npg):
+            pid = int(phys[r * npg + p])
+            bt[r, p] = pid
+            lo = int(case.row_ks[r]) + p * page
+            hi = min(lo + page, int(case.row_ke[r]))
+            kp[pid, :hi - lo] = case.k[lo:hi]
+            sp[pid, :hi - lo] = case.k_scale[lo:hi]
+    return kp, sp, bt
+
+
+def pin_paged_equals_contiguous():
+    rng = np.random.default_rng(61)
+    case = synth.batched_decode(seed=61, rows=3, n=333, topk=16)
+    dense = O.logits_dense(case.q, "fp8", case.w, case.k, case.k_scale, "fp8", case.row_ks,
+                           case.row_ke, ld=64 * 8)
+    for perm in (False, True):
+        kp, sp, bt = _paged_from_dense(case, 64, perm, rng)
+        lens = (case.row_ke - case.row_ks).astype(np.int32)
+        pg = O.logits_paged(case.q, "fp8", case.w, kp, sp, "fp8", bt, lens, ld=64 * 8)
+        assert np.array_equal(pg, dense), f"paged (permuted={perm}) != contiguous"
+    rr = np.array([2, 0, 1], np.int32)
+    kp, sp, bt = _paged_from_dense(case, 64, True, rng)
+    pg = O.logits_paged(case.q, "fp8", case.w, kp, sp, "fp8", bt[rr], lens, row_req=np.argsort(rr).astype(np.int32), ld=64 * 8)
+    assert np.array_equal(pg, dense), "row -> request map not honoured"
+
+
+def pin_sparse_equals_dense_masked():
+    """Scoring only the candidate blocks and selecting over their columns gives exactly the
+    selection of the dense route that scores every token and masks non-candidates."""
+    for kd, seed in (("mxfp4", 71), ("fp8", 72)):
+        sp = synth.sparse_blocks(seed=seed, rows=4, ctx=2048, n_blocks=5, block=128, topk=100,
+                                 kdtype=kd, ragged=True, poison_noncand=False)
+        idx_sparse, val_sparse = O.select_case(sp)
+        dense = O.logits_dense(sp.q, "fp8", sp.w, sp.k, sp.k_scale, kd, sp.row_ks, sp.row_ke)
+        mask = np.zeros_like(dense, dtype=bool)
+        for r in range(sp.rows):
+            for c in range(int(sp.n_cols[r])):
+                tok = int(sp.cand[r, c // 128]) * 128 + c % 128
+                if tok < dense.shape[1]:
+                    mask[r, tok] = True
+        masked = np.where(mask, dense, -np.inf).astype(np.float32)
+        idx_dense, val_dense = O.topk(masked, 100)
+        assert np.array_equal(idx_sparse, idx_dense), f"{kd}: sparse != dense-masked"
+        assert np.array_equal(val_sparse, val_dense)
+
+
+def pin_sparse_columns():
+    sp = synth.sparse_blocks(seed=73, rows=3, ctx=1000, n_blocks=4, block=128, topk=10,
+                             kdtype="fp8", ragged=True, poison_noncand=False)
+    lg = O.logits_sparse(sp.q, "fp8", sp.w, sp.k, sp.k_scale, "fp8", sp.row_ks, sp.row_ke,
+                         sp.cand, sp.n_cols, sp.block)
+    dense = O.logits_dense(sp.q, "fp8", sp.w, sp.k, sp.k_scale, "fp8", sp.row_ks, sp.row_ke,
+                           ld=1024)
+    for r in range(3):
+        for c in range(lg.shape[1]):
+            tok = int(sp.cand[r, c // 128]) * 128 + c % 128
+            valid = c < sp.n_cols[r] and tok < sp.row_ke[r] - sp.row_ks[r]
+            if valid:
+                assert lg[r, c] == dense[r, tok], f"row {r} col {c}"
+            else:
+                assert lg[r, c] == -np.inf, f"row {r} col {c} should be masked"
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,71 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that at least
+one pin fails for each: the pins are strong enough to notice a dropped term, a wrong
+sign, bias or index, or a transposed operand."""
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+SRC = Path(oracle.__file__).resolve().parent / "ref.c"
+
+MUTANTS = {
+    "relu_dropped": ("double relu = dot > 0.0 ? dot : 0.0;", "double relu = dot;"),
+    "weight_index": ("acc += (double)w[j] * relu;", "acc += (double)w[0] * relu;"),
+    "weight_sign": ("acc += (double)w[j] * relu;", "acc -= (double)w[j] * relu;"),
+    "head_index": ("dot += qd[(int64_t)j * dim + i] * kd[i];", "dot += qd[i] * kd[i];"),
+    "q_transposed": ("dot += qd[(int64_t)j * dim + i] * kd[i];",
+                     "dot += qd[(int64_t)(i % heads) * dim + (j + i) % dim] * kd[i];"),
+    "fp8_bias": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);", "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "fp8_subnormal": ("mag = ldexp((double)m / 8.0, 1 - 7);", "mag = ldexp((double)m / 8.0, -7);"),
+    "fp8_mantissa": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);", "mag = ldexp(1.0 + (double)m / 16.0, e - 7);"),
+    "fp8_nan": ("if (e == 15 && m == 7)\n        return NAN;", "if (e == 15 && m == 7 && sign)\n        return NAN;"),
+    "nibble_order": ("(i % 2 == 0) ? (byte & 0xF) : (byte >> 4)", "(i % 2 == 1) ? (byte & 0xF) : (byte >> 4)"),
+    "e2m1_bias": ("mag = ldexp(1.0 + (double)m / 2.0, e - 1);", "mag = ldexp(1.0 + (double)m / 2.0, e - 2);"),
+    "ue8m0_bias": ("return ldexp(1.0, (int)e - 127);", "return ldexp(1.0, (int)e - 128);"),
+    "scale_group": ("ref_decode_ue8m0(((const uint8_t*)sc)[i / 32])", "ref_decode_ue8m0(((const uint8_t*)sc)[(i / 32) ^ 1])"),
+    "scale_ignored": ("out[i] = ref_decode_fp8_e4m3fn(k[i]) * (double)*(const float*)sc;",
+                      "out[i] = ref_decode_fp8_e4m3fn(k[i]);"),
+    "bf16_shift": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+    "double_rounding": ("return (float)acc;", "return (float)(double)(float)(acc * (1.0 + 1e-7));"),
+    "dense_range_start": ("int64_t s = row_ks[r] + c;", "int64_t s = c;"),
+    "dense_length": ("int64_t len = (int64_t)row_ke[r] - row_ks[r];\n        for (int64_t c = 0; c < ld; c++) {\n            if (c >= len) {\n                logits[r * ld + c] = -INFINITY;",
+                     "int64_t len = (int64_t)row_ke[r] - row_ks[r] + 1;\n        for (int64_t c = 0; c < ld; c++) {\n            if (c >= len) {\n                logits[r * ld + c] = -INFINITY;"),
+    "paged_slot": ("int64_t slot = page * page_size + s % page_size;", "int64_t slot = page * page_size + (s + 1) % page_size;"),
+    "paged_req": ("int64_t req = row_req ? row_req[r] : r;", "int64_t req = r;"),
+    "sparse_token": ("(int64_t)cand[r * cand_ld + b] * block + c % block", "(int64_t)cand[r * cand_ld + b] * block + (c + 1) % block"),
+    "sparse_end": ("if (c >= n_cols[r] || b >= cand_ld", "if (c > n_cols[r] || b >= cand_ld"),
+    "tie_break": ("return (a->idx > b->idx) - (a->idx < b->idx);", "return (a->idx < b->idx) - (a->idx > b->idx);"),
+    "ascending": ("if (a->v > b->v)\n        return -1;\n    if (a->v < b->v)\n        return 1;",
+                  "if (a->v < b->v)\n        return -1;\n    if (a->v > b->v)\n        return 1;"),
+    "neg_inf_selected": ("if (isnan(v) || v == -INFINITY)", "if (isnan(v))"),
+    "topk_len": ("int64_t n = lens ? lens[r] : ncols;", "int64_t n = ncols;"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, mutant_dir, oracle_lib):
+    old, new = MUTANTS[name]
+    src = SRC.read_text()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mut = mutant_dir / f"{name}.c"
+    mut.write_text(src.replace(old, new, 1))
+    so = mutant_dir / f"lib{name}.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC",
+                    "-shared", str(mut), "-o", str(so), "-lm"], check=True)
+    failed = []
+    with oracle.variant(so):
+        for pin in pins.ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                failed.append(pin.__name__)
+                break
+    assert failed, f"no pin caught the planted mistake {name}"
