@@ -1,0 +1,298 @@
+"""dsaidx: the DeepSeek Sparse Attention lightning indexer (scores + exact top-k) on
+AMD Instinct MI355X (gfx950).
+
+This module is a thin ctypes binding over the C ABI declared in ``include/dsaidx.h``
+and implemented by ``libdsaidx.so`` (hand-written HIP kernels). It only marshals
+arguments: torch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's kernels. The functions carry the C names.
+
+The library is loaded on first use; if it has not been built, the call raises
+``RuntimeError`` (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes as C
+from pathlib import Path
+
+_LIB_PATH = Path(__file__).resolve().parent / "libdsaidx.so"
+
+IDX_OK, IDX_ERR_ARG, IDX_ERR_UNSUPPORTED, IDX_ERR_WORKSPACE, IDX_ERR_HIP = 0, 1, 2, 3, 4
+IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
+IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS = 1, 2, 3
+IDX_TOPK_UNSORTED = 1
+IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK = 1, 2, 4
+IDX_HEADS, IDX_DIM, IDX_MAX_K = 64, 128, 2048
+
+KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
+
+# Every symbol include/dsaidx.h declares.
+EXPORTS = ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
+           "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
+           "idx_last_error", "idx_version", "idx_device_errors")
+
+
+class IdxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_STATUS_NAMES = {0: "IDX_OK", 1: "IDX_ERR_ARG", 2: "IDX_ERR_UNSUPPORTED",
+                 3: "IDX_ERR_WORKSPACE", 4: "IDX_ERR_HIP"}
+
+
+class idx_problem(C.Structure):
+    """Mirror of ``struct idx_problem`` (include/dsaidx.h)."""
+    _fields_ = [
+        ("mode", C.c_int32), ("rows", C.c_int32),
+        ("q", C.c_void_p), ("q_dtype", C.c_int32), ("k_dtype", C.c_int32),
+        ("w", C.c_void_p), ("k", C.c_void_p), ("k_scale", C.c_void_p),
+        ("n_keys", C.c_int64),
+        ("row_ks", C.c_void_p), ("row_ke", C.c_void_p),
+        ("max_cols", C.c_int64),
+        ("page_size", C.c_int32), ("block_size", C.c_int32),
+        ("block_table", C.c_void_p), ("bt_rows", C.c_int64), ("bt_ld", C.c_int64),
+        ("seq_lens", C.c_void_p), ("row_req", C.c_void_p),
+        ("cand_blocks", C.c_void_p), ("cand_ld", C.c_int64), ("n_cols", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def lib() -> C.CDLL:
+    """The loaded libdsaidx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not _LIB_PATH.exists():
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+                               "python -m dsa_lightning_indexer_idx_amd.build")
+        L = C.CDLL(str(_LIB_PATH))
+        P, I, I64, U32, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_uint32, C.c_size_t
+        L.idx_logits.argtypes = [P, I, P, P, P, I, I64, P, P, I, P, I64, P]
+        L.idx_logits_paged.argtypes = [P, I, P, P, P, I, I64, I, P, I64, I64, P, P, I, P, I64, P]
+        L.idx_logits_sparse_blocks.argtypes = [P, I, P, P, P, I, I64, P, P, P, I64, P, I, I, P, I64, P]
+        L.idx_topk.argtypes = [P, I64, P, I64, I, I, P, P, I64, U32, P, SZ, P]
+        L.idx_topk_workspace.argtypes = [I, I64, I]
+        L.idx_topk_workspace.restype = SZ
+        L.idx_select.argtypes = [C.POINTER(idx_problem), I, P, P, I64, U32, P, SZ, P]
+        L.idx_select_workspace.argtypes = [C.POINTER(idx_problem), I]
+        L.idx_select_workspace.restype = SZ
+        L.idx_status_string.argtypes = [I]
+        L.idx_status_string.restype = C.c_char_p
+        L.idx_last_error.argtypes = []
+        L.idx_last_error.restype = C.c_char_p
+        L.idx_version.restype = I
+        L.idx_device_errors.argtypes = [P]
+        L.idx_device_errors.restype = I
+        for name in ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
+                     "idx_select"):
+            getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != IDX_OK:
+        raise IdxError(status, lib().idx_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _need(t, name):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _q_dtype(k_dtype: str) -> int:
+    return IDX_BF16 if k_dtype == "bf16" else IDX_FP8_E4M3
+
+
+# ----------------------------------------------------------------------------- scores
+
+
+def idx_logits(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, ld: int | None = None,
+               out=None, stream=None):
+    """Scores of rows over contiguous key ranges (C: idx_logits). Returns fp32 [rows, ld]."""
+    import torch
+    for t, n in ((q, "q"), (w, "w"), (k, "k"), (k_scale, "k_scale"), (row_ks, "row_ks"),
+                 (row_ke, "row_ke")):
+        _need(t, n)
+    rows = q.shape[0]
+    if out is None:
+        if ld is None:
+            raise ValueError("give ld or out")
+        out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
+    ld = out.shape[1] if out.dim() == 2 else ld
+    _check(lib().idx_logits(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k), _ptr(k_scale),
+                            KDTYPES[k_dtype], k.shape[0], _ptr(row_ks), _ptr(row_ke), rows,
+                            _ptr(_need(out, "out")), ld, _stream(stream)))
+    return out
+
+
+def idx_logits_paged(q, w, k_pages, k_scale_pages, block_table, seq_lens, *, k_dtype: str,
+                     row_req=None, ld: int | None = None, out=None, stream=None):
+    """Scores of rows over a paged key cache (C: idx_logits_paged)."""
+    import torch
+    for t, n in ((q, "q"), (w, "w"), (k_pages, "k_pages"), (k_scale_pages, "k_scale_pages"),
+                 (block_table, "block_table"), (seq_lens, "seq_lens"), (row_req, "row_req")):
+        _need(t, n)
+    rows = q.shape[0]
+    page = k_pages.shape[1]
+    bt_rows, bt_ld = block_table.shape
+    if out is None:
+        ld = bt_ld * page if ld is None else ld
+        out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
+    _check(lib().idx_logits_paged(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k_pages),
+                                  _ptr(k_scale_pages), KDTYPES[k_dtype], k_pages.shape[0], page,
+                                  _ptr(block_table), bt_rows, bt_ld, _ptr(seq_lens),
+                                  _ptr(row_req), rows, _ptr(_need(out, "out")), out.shape[1],
+                                  _stream(stream)))
+    return out
+
+
+def idx_logits_sparse_blocks(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, *,
+                             k_dtype: str, block_size: int = 128, ld: int | None = None,
+                             out=None, stream=None):
+    """Scores of two-level rows over their candidate blocks (C: idx_logits_sparse_blocks)."""
+    import torch
+    for t, n in ((q, "q"), (w, "w"), (k, "k"), (k_scale, "k_scale"), (row_ks, "row_ks"),
+                 (row_ke, "row_ke"), (cand_blocks, "cand_blocks"), (n_cols, "n_cols")):
+        _need(t, n)
+    rows = q.shape[0]
+    cand_ld = cand_blocks.shape[1]
+    if out is None:
+        ld = cand_ld * block_size if ld is None else ld
+        out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
+    _check(lib().idx_logits_sparse_blocks(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k),
+                                          _ptr(k_scale), KDTYPES[k_dtype], k.shape[0],
+                                          _ptr(row_ks), _ptr(row_ke), _ptr(cand_blocks), cand_ld,
+                                          _ptr(n_cols), block_size, rows, _ptr(_need(out, "out")),
+                                          out.shape[1], _stream(stream)))
+    return out
+
+
+# ----------------------------------------------------------------------------- selection
+
+
+def idx_topk_workspace(rows: int, n_cols: int, k: int) -> int:
+    return int(lib().idx_topk_workspace(rows, n_cols, k))
+
+
+def idx_topk(logits, k: int, *, lens=None, n_cols: int | None = None, sorted: bool = True,
+             values: bool = True, out_idx=None, out_val=None, workspace=None, stream=None):
+    """Exact top-k per row (C: idx_topk). Returns (idx int32 [rows, k], val fp32 or None)."""
+    import torch
+    _need(logits, "logits")
+    _need(lens, "lens")
+    rows, ld = logits.shape
+    n_cols = ld if n_cols is None else n_cols
+    if out_idx is None:
+        out_idx = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    if values and out_val is None:
+        out_val = torch.empty((rows, k), dtype=torch.float32, device=logits.device)
+    need = idx_topk_workspace(rows, n_cols, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().idx_topk(_ptr(logits), ld, _ptr(lens), n_cols, rows, k, _ptr(out_idx),
+                          _ptr(out_val), out_idx.shape[1], 0 if sorted else IDX_TOPK_UNSORTED,
+                          _ptr(workspace), wsb, _stream(stream)))
+    return out_idx, out_val
+
+
+class Problem:
+    """An ``idx_problem`` plus references that keep its tensors alive."""
+
+    def __init__(self, st: idx_problem, tensors):
+        self.st = st
+        self._keep = tensors
+
+    @property
+    def rows(self) -> int:
+        return self.st.rows
+
+
+def dense_problem(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, max_cols: int) -> Problem:
+    st = idx_problem(mode=IDX_MODE_DENSE, rows=q.shape[0], q=q.data_ptr(),
+                     q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
+                     k=k.data_ptr(), k_scale=None if k_scale is None else k_scale.data_ptr(),
+                     n_keys=k.shape[0], row_ks=row_ks.data_ptr(), row_ke=row_ke.data_ptr(),
+                     max_cols=max_cols)
+    return Problem(st, (q, w, k, k_scale, row_ks, row_ke))
+
+
+def paged_problem(q, w, k_pages, k_scale_pages, block_table, seq_lens, *, k_dtype: str,
+                  row_req=None) -> Problem:
+    st = idx_problem(mode=IDX_MODE_PAGED, rows=q.shape[0], q=q.data_ptr(),
+                     q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
+                     k=k_pages.data_ptr(), k_scale=k_scale_pages.data_ptr(),
+                     n_keys=k_pages.shape[0], page_size=k_pages.shape[1],
+                     block_table=block_table.data_ptr(), bt_rows=block_table.shape[0],
+                     bt_ld=block_table.shape[1], seq_lens=seq_lens.data_ptr(),
+                     row_req=None if row_req is None else row_req.data_ptr())
+    return Problem(st, (q, w, k_pages, k_scale_pages, block_table, seq_lens, row_req))
+
+
+def sparse_problem(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, *, k_dtype: str,
+                   block_size: int = 128) -> Problem:
+    st = idx_problem(mode=IDX_MODE_SPARSE_BLOCKS, rows=q.shape[0], q=q.data_ptr(),
+                     q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
+                     k=k.data_ptr(), k_scale=k_scale.data_ptr(), n_keys=k.shape[0],
+                     row_ks=row_ks.data_ptr(), row_ke=row_ke.data_ptr(),
+                     cand_blocks=cand_blocks.data_ptr(), cand_ld=cand_blocks.shape[1],
+                     n_cols=n_cols.data_ptr(), block_size=block_size)
+    return Problem(st, (q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols))
+
+
+def idx_select_workspace(problem: Problem, k: int) -> int:
+    return int(lib().idx_select_workspace(C.byref(problem.st), k))
+
+
+def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = True,
+               out_idx=None, out_val=None, workspace=None, stream=None):
+    """Scores + exact top-k in one call (C: idx_select). Returns (idx, val or None)."""
+    import torch
+    dev = problem._keep[0].device
+    rows = problem.rows
+    if out_idx is None:
+        out_idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if values and out_val is None:
+        out_val = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(idx_select_workspace(problem, k), 1), dtype=torch.uint8,
+                                device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().idx_select(C.byref(problem.st), k, _ptr(out_idx), _ptr(out_val),
+                            out_idx.shape[1], 0 if sorted else IDX_TOPK_UNSORTED,
+                            _ptr(workspace), wsb, _stream(stream)))
+    return out_idx, out_val
+
+
+# ----------------------------------------------------------------------------- misc
+
+
+def idx_version() -> int:
+    return int(lib().idx_version())
+
+
+def idx_device_errors(stream=None) -> int:
+    v = int(lib().idx_device_errors(_stream(stream)))
+    if v < 0:
+        raise IdxError(IDX_ERR_HIP, lib().idx_last_error().decode())
+    return v

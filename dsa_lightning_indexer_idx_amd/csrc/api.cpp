@@ -1,0 +1,386 @@
+// C-ABI entry points of dsaidx: argument checks, workspace sizing and dispatch to
+// the kernels. Nothing here touches the device before every host-checkable
+// argument has passed.
+#include "dsaidx.h"
+#include "launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+using namespace dsaidx;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+idx_status fail(idx_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+idx_status ok() {
+  g_last_error.clear();
+  return IDX_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxCols = 0x7FFFFFFF;
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+// Format of the keys, given the dtype pair; -1 if the pair is not supported.
+int key_format(int q_dtype, int k_dtype) {
+  if (q_dtype == IDX_BF16 && k_dtype == IDX_BF16) return FMT_BF16;
+  if (q_dtype == IDX_FP8_E4M3 && k_dtype == IDX_FP8_E4M3) return FMT_FP8;
+  if (q_dtype == IDX_FP8_E4M3 && k_dtype == IDX_MXFP4) return FMT_MXFP4;
+  return -1;
+}
+
+idx_status check_common(const char* fn, const void* q, int q_dtype, const float* w, const void* k,
+                        const void* k_scale, int k_dtype, int rows, const float* logits, int64_t ld,
+                        int* fmt) {
+  REQUIRE(rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, rows);
+  *fmt = key_format(q_dtype, k_dtype);
+  REQUIRE(*fmt > 0, IDX_ERR_UNSUPPORTED,
+          "%s: q_dtype %d with k_dtype %d is not supported (bf16/bf16, fp8/fp8 or fp8/mxfp4)", fn,
+          q_dtype, k_dtype);
+  if (rows == 0) return IDX_OK;
+  REQUIRE(q && w && k && logits, IDX_ERR_ARG, "%s: q, w, k and logits must be non-null", fn);
+  REQUIRE(*fmt == FMT_BF16 || k_scale, IDX_ERR_ARG, "%s: k_scale is required for fp8 and mxfp4 keys", fn);
+  REQUIRE(aligned(q, 16) && aligned(k, 16), IDX_ERR_ARG, "%s: q and k must be 16-byte aligned", fn);
+  REQUIRE(aligned(w, 4) && aligned(logits, 4), IDX_ERR_ARG, "%s: w and logits must be 4-byte aligned", fn);
+  REQUIRE(*fmt != FMT_FP8 || aligned(k_scale, 4), IDX_ERR_ARG, "%s: fp8 k_scale must be 4-byte aligned", fn);
+  REQUIRE(ld >= 1 && ld <= kMaxCols, IDX_ERR_ARG, "%s: ld = %lld out of range [1, 2^31)", fn, (long long)ld);
+  return IDX_OK;
+}
+
+idx_status check_ints(const char* fn, std::initializer_list<const int32_t*> ps) {
+  for (const int32_t* p : ps) REQUIRE(p == nullptr || aligned(p, 4), IDX_ERR_ARG, "%s: int32 arrays must be 4-byte aligned", fn);
+  return IDX_OK;
+}
+
+idx_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(IDX_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+// Checks of a problem for both the score calls and idx_select; fills ``c`` (minus
+// the output pointers).
+idx_status check_problem(const char* fn, const idx_problem* p, ScoreCall* c, const float* logits,
+                         int64_t ld, bool need_out) {
+  REQUIRE(p, IDX_ERR_ARG, "%s: problem is null", fn);
+  *c = ScoreCall{};
+  int fmt = 0;
+  idx_status s = check_common(fn, p->q, p->q_dtype, p->w, p->k, p->k_scale, p->k_dtype, p->rows,
+                              need_out ? logits : (const float*)p->w, need_out ? ld : 1, &fmt);
+  if (s != IDX_OK) return s;
+  c->fmt = fmt;
+  c->rows = p->rows;
+  c->q = (const uint8_t*)p->q;
+  c->w = p->w;
+  c->k = (const uint8_t*)p->k;
+  c->k_scale = p->k_scale;
+  c->n_keys = p->n_keys;
+  c->logits = (float*)logits;
+  c->ld = ld;
+  if (p->mode == IDX_MODE_DENSE) {
+    c->source = SRC_DENSE;
+    if (p->rows == 0) return IDX_OK;
+    REQUIRE(p->n_keys >= 0, IDX_ERR_ARG, "%s: n_keys is negative", fn);
+    REQUIRE(p->row_ks && p->row_ke, IDX_ERR_ARG, "%s: row_ks and row_ke must be non-null", fn);
+    c->row_ks = p->row_ks;
+    c->row_ke = p->row_ke;
+    return check_ints(fn, {p->row_ks, p->row_ke});
+  }
+  if (p->mode == IDX_MODE_PAGED) {
+    c->source = SRC_PAGED;
+    REQUIRE(fmt != FMT_BF16, IDX_ERR_UNSUPPORTED, "%s: paged keys must be fp8 or mxfp4", fn);
+    REQUIRE(p->page_size >= 64 && p->page_size % 64 == 0, IDX_ERR_UNSUPPORTED,
+            "%s: page_size = %d must be a positive multiple of 64", fn, p->page_size);
+    if (p->rows == 0) return IDX_OK;
+    REQUIRE(p->n_keys >= 1, IDX_ERR_ARG, "%s: n_pages must be >= 1", fn);
+    REQUIRE(p->block_table && p->seq_lens, IDX_ERR_ARG, "%s: block_table and seq_lens must be non-null", fn);
+    REQUIRE(p->bt_ld >= 1 && p->bt_ld * p->page_size <= kMaxCols, IDX_ERR_ARG,
+            "%s: bt_ld = %lld out of range", fn, (long long)p->bt_ld);
+    c->page_size = p->page_size;
+    c->block_table = p->block_table;
+    c->bt_ld = p->bt_ld;
+    c->seq_lens = p->seq_lens;
+    c->row_req = p->row_req;
+    return check_ints(fn, {p->block_table, p->seq_lens, p->row_req});
+  }
+  if (p->mode == IDX_MODE_SPARSE_BLOCKS) {
+    c->source = SRC_SPARSE;
+    REQUIRE(fmt != FMT_BF16, IDX_ERR_UNSUPPORTED, "%s: candidate-block keys must be fp8 or mxfp4", fn);
+    REQUIRE(p->block_size >= 64 && p->block_size % 64 == 0, IDX_ERR_UNSUPPORTED,
+            "%s: block_size = %d must be a positive multiple of 64", fn, p->block_size);
+    if (p->rows == 0) return IDX_OK;
+    REQUIRE(p->n_keys >= 0, IDX_ERR_ARG, "%s: n_keys is negative", fn);
+    REQUIRE(p->row_ks && p->row_ke && p->cand_blocks && p->n_cols, IDX_ERR_ARG,
+            "%s: row_ks, row_ke, cand_blocks and n_cols must be non-null", fn);
+    REQUIRE(p->cand_ld >= 1 && p->cand_ld * p->block_size <= kMaxCols, IDX_ERR_ARG,
+            "%s: cand_ld = %lld out of range", fn, (long long)p->cand_ld);
+    c->row_ks = p->row_ks;
+    c->row_ke = p->row_ke;
+    c->cand = p->cand_blocks;
+    c->cand_ld = p->cand_ld;
+    c->n_cols = p->n_cols;
+    c->block = p->block_size;
+    return check_ints(fn, {p->row_ks, p->row_ke, p->cand_blocks, p->n_cols});
+  }
+  return fail(IDX_ERR_ARG, "%s: unknown mode %d", fn, p->mode);
+}
+
+// Width of the score matrix idx_select builds for a problem.
+int64_t select_width(const idx_problem* p) {
+  switch (p->mode) {
+    case IDX_MODE_DENSE: return p->max_cols;
+    case IDX_MODE_PAGED: return p->bt_ld * p->page_size;
+    case IDX_MODE_SPARSE_BLOCKS: return p->cand_ld * p->block_size;
+  }
+  return 0;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+extern "C" {
+
+idx_status idx_logits(const void* q, int q_dtype, const float* w, const void* k, const void* k_scale,
+                      int k_dtype, int64_t n_keys, const int32_t* row_ks, const int32_t* row_ke,
+                      int rows, float* logits, int64_t ld, idx_stream_t stream) {
+  idx_problem p{};
+  p.mode = IDX_MODE_DENSE;
+  p.rows = rows;
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_dtype = k_dtype;
+  p.w = w;
+  p.k = k;
+  p.k_scale = k_scale;
+  p.n_keys = n_keys;
+  p.row_ks = row_ks;
+  p.row_ke = row_ke;
+  ScoreCall c;
+  idx_status s = check_problem("idx_logits", &p, &c, logits, ld, true);
+  if (s != IDX_OK) return s;
+  if (rows == 0) return ok();
+  c.err = device_error_word();
+  return launched("idx_logits", launch_score(c, (hipStream_t)stream));
+}
+
+idx_status idx_logits_paged(const void* q, int q_dtype, const float* w, const void* k_pages,
+                            const void* k_scale_pages, int k_dtype, int64_t n_pages, int page_size,
+                            const int32_t* block_table, int64_t bt_rows, int64_t bt_ld,
+                            const int32_t* seq_lens, const int32_t* row_req, int rows, float* logits,
+                            int64_t ld, idx_stream_t stream) {
+  idx_problem p{};
+  p.mode = IDX_MODE_PAGED;
+  p.rows = rows;
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_dtype = k_dtype;
+  p.w = w;
+  p.k = k_pages;
+  p.k_scale = k_scale_pages;
+  p.n_keys = n_pages;
+  p.page_size = page_size;
+  p.block_table = block_table;
+  p.bt_rows = bt_rows;
+  p.bt_ld = bt_ld;
+  p.seq_lens = seq_lens;
+  p.row_req = row_req;
+  ScoreCall c;
+  idx_status s = check_problem("idx_logits_paged", &p, &c, logits, ld, true);
+  if (s != IDX_OK) return s;
+  if (rows == 0) return ok();
+  REQUIRE(bt_rows >= 1 && (row_req || bt_rows >= rows), IDX_ERR_ARG,
+          "idx_logits_paged: bt_rows = %lld too small", (long long)bt_rows);
+  c.bt_rows = bt_rows;
+  c.err = device_error_word();
+  return launched("idx_logits_paged", launch_score(c, (hipStream_t)stream));
+}
+
+idx_status idx_logits_sparse_blocks(const void* q, int q_dtype, const float* w, const void* k,
+                                    const void* k_scale, int k_dtype, int64_t n_keys,
+                                    const int32_t* row_ks, const int32_t* row_ke,
+                                    const int32_t* cand_blocks, int64_t cand_ld, const int32_t* n_cols,
+                                    int block_size, int rows, float* logits, int64_t ld,
+                                    idx_stream_t stream) {
+  idx_problem p{};
+  p.mode = IDX_MODE_SPARSE_BLOCKS;
+  p.rows = rows;
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_dtype = k_dtype;
+  p.w = w;
+  p.k = k;
+  p.k_scale = k_scale;
+  p.n_keys = n_keys;
+  p.row_ks = row_ks;
+  p.row_ke = row_ke;
+  p.cand_blocks = cand_blocks;
+  p.cand_ld = cand_ld;
+  p.n_cols = n_cols;
+  p.block_size = block_size;
+  ScoreCall c;
+  idx_status s = check_problem("idx_logits_sparse_blocks", &p, &c, logits, ld, true);
+  if (s != IDX_OK) return s;
+  if (rows == 0) return ok();
+  REQUIRE(ld >= cand_ld * block_size, IDX_ERR_ARG,
+          "idx_logits_sparse_blocks: ld = %lld < cand_ld * block_size = %lld", (long long)ld,
+          (long long)(cand_ld * block_size));
+  c.err = device_error_word();
+  return launched("idx_logits_sparse_blocks", launch_score(c, (hipStream_t)stream));
+}
+
+size_t idx_topk_workspace(int, int64_t, int) { return 0; }
+
+idx_status idx_topk(const float* logits, int64_t ld, const int32_t* lens, int64_t n_cols, int rows,
+                    int k, int32_t* out_idx, float* out_val, int64_t out_ld, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, idx_stream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const char* fn = "idx_topk";
+  REQUIRE(rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, rows);
+  REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
+  REQUIRE((flags & ~IDX_TOPK_UNSORTED) == 0, IDX_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
+  if (rows == 0) return ok();
+  REQUIRE(logits && out_idx, IDX_ERR_ARG, "%s: logits and out_idx must be non-null", fn);
+  REQUIRE(n_cols >= 0 && n_cols <= kMaxCols, IDX_ERR_ARG, "%s: n_cols = %lld out of range", fn, (long long)n_cols);
+  REQUIRE(ld >= n_cols && ld >= 1, IDX_ERR_ARG, "%s: ld = %lld < n_cols = %lld", fn, (long long)ld, (long long)n_cols);
+  REQUIRE(out_ld >= k, IDX_ERR_ARG, "%s: out_ld = %lld < k = %d", fn, (long long)out_ld, k);
+  REQUIRE(aligned(logits, 4) && aligned(out_idx, 4) && (!out_val || aligned(out_val, 4)), IDX_ERR_ARG,
+          "%s: arrays must be 4-byte aligned", fn);
+  idx_status s = check_ints(fn, {lens});
+  if (s != IDX_OK) return s;
+  TopkCall c{};
+  c.logits = logits;
+  c.ld = ld;
+  c.n_cols = n_cols;
+  c.lens = lens;
+  c.rows = rows;
+  c.k = k;
+  c.out_idx = out_idx;
+  c.out_val = out_val;
+  c.out_ld = out_ld;
+  c.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
+  return launched(fn, launch_topk(c, (hipStream_t)stream));
+}
+
+size_t idx_select_workspace(const idx_problem* p, int k) {
+  (void)k;
+  if (!p || p->rows <= 0) return 0;
+  int64_t width = select_width(p);
+  if (width <= 0) return 0;
+  return (size_t)p->rows * (size_t)round_up(width, 64) * sizeof(float) + 256;
+}
+
+idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_val, int64_t out_ld,
+                      uint32_t flags, void* workspace, size_t workspace_bytes, idx_stream_t stream) {
+  const char* fn = "idx_select";
+  REQUIRE(p, IDX_ERR_ARG, "%s: problem is null", fn);
+  REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
+  REQUIRE((flags & ~IDX_TOPK_UNSORTED) == 0, IDX_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
+  REQUIRE(p->rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, p->rows);
+  const int64_t width = select_width(p);
+  ScoreCall c;
+  {
+    // validate the problem with a stand-in output so the score checks run
+    idx_status s = check_problem(fn, p, &c, (const float*)p->w, 1, false);
+    if (s != IDX_OK) return s;
+  }
+  if (p->rows == 0) return ok();
+  REQUIRE(width >= 1 && width <= kMaxCols, IDX_ERR_ARG,
+          "%s: score width %lld out of range (dense problems need max_cols >= 1)", fn, (long long)width);
+  REQUIRE(out_idx && out_ld >= k, IDX_ERR_ARG, "%s: out_idx must be non-null and out_ld >= k", fn);
+  REQUIRE(aligned(out_idx, 4) && (!out_val || aligned(out_val, 4)), IDX_ERR_ARG,
+          "%s: outputs must be 4-byte aligned", fn);
+  if (p->mode == IDX_MODE_PAGED)
+    REQUIRE(p->bt_rows >= 1 && (p->row_req || p->bt_rows >= p->rows), IDX_ERR_ARG,
+            "%s: bt_rows = %lld too small", fn, (long long)p->bt_rows);
+  const size_t need = idx_select_workspace(p, k);
+  REQUIRE(workspace && workspace_bytes >= need, IDX_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(aligned(workspace, 256), IDX_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
+
+  const int64_t ldw = round_up(width, 64);
+  float* scores = (float*)workspace;
+  c.logits = scores;
+  c.ld = ldw;
+  c.bt_rows = p->bt_rows;
+  c.err = device_error_word();
+  hipError_t e = launch_score(c, (hipStream_t)stream);
+  if (e != hipSuccess) return launched(fn, e);
+
+  TopkCall t{};
+  t.logits = scores;
+  t.ld = ldw;
+  t.n_cols = width;
+  t.rows = p->rows;
+  t.k = k;
+  t.out_idx = out_idx;
+  t.out_val = out_val;
+  t.out_ld = out_ld;
+  t.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
+  if (p->mode == IDX_MODE_DENSE) {
+    t.len_ks = p->row_ks;
+    t.len_ke = p->row_ke;
+  } else if (p->mode == IDX_MODE_PAGED) {
+    t.lens = p->seq_lens;
+  } else {
+    t.lens = p->n_cols;
+    t.cand = p->cand_blocks;
+    t.cand_ld = p->cand_ld;
+    t.block = p->block_size;
+  }
+  return launched(fn, launch_topk(t, (hipStream_t)stream));
+}
+
+const char* idx_status_string(idx_status s) {
+  switch (s) {
+    case IDX_OK: return "IDX_OK";
+    case IDX_ERR_ARG: return "IDX_ERR_ARG";
+    case IDX_ERR_UNSUPPORTED: return "IDX_ERR_UNSUPPORTED";
+    case IDX_ERR_WORKSPACE: return "IDX_ERR_WORKSPACE";
+    case IDX_ERR_HIP: return "IDX_ERR_HIP";
+  }
+  return "IDX_ERR_UNKNOWN";
+}
+
+const char* idx_last_error(void) { return g_last_error.c_str(); }
+
+int idx_version(void) { return 100; }
+
+int idx_device_errors(idx_stream_t stream) {
+  unsigned* p = device_error_word();
+  if (!p) {
+    fail(IDX_ERR_HIP, "idx_device_errors: no device error word");
+    return -1;
+  }
+  unsigned v = 0;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess) e = hipMemcpy(&v, p, sizeof v, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(p, 0, sizeof v);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    fail(IDX_ERR_HIP, "idx_device_errors: %s", hipGetErrorString(e));
+    return -1;
+  }
+  return (int)v;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Host-side launch descriptions shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+enum SourceKind { SRC_DENSE = 1, SRC_PAGED = 2, SRC_SPARSE = 3 };
+enum KeyFmt { FMT_BF16 = 1, FMT_FP8 = 2, FMT_MXFP4 = 3 };
+
+// One scoring call, validated by the C-ABI layer.
+struct ScoreCall {
+  int source;  // SourceKind
+  int fmt;     // KeyFmt
+  int rows;
+  const uint8_t* q;
+  const float* w;
+  const uint8_t* k;       // dense / sparse: key rows; paged: pages
+  const void* k_scale;
+  int64_t n_keys;         // dense / sparse: key rows; paged: pages
+  const int32_t* row_ks;  // dense / sparse
+  const int32_t* row_ke;
+  int page_size;          // paged
+  const int32_t* block_table;
+  int64_t bt_rows;
+  int64_t bt_ld;
+  const int32_t* seq_lens;
+  const int32_t* row_req;
+  const int32_t* cand;    // sparse
+  int64_t cand_ld;
+  const int32_t* n_cols;
+  int block;
+  float* logits;
+  int64_t ld;
+  unsigned* err;          // device error word (may be null)
+};
+
+// One top-k call.
+struct TopkCall {
+  const float* logits;
+  int64_t ld;
+  int64_t n_cols;
+  const int32_t* lens;    // optional: row length
+  const int32_t* len_ks;  // optional: row length = len_ke - len_ks
+  const int32_t* len_ke;
+  int rows;
+  int k;
+  int32_t* out_idx;
+  float* out_val;
+  int64_t out_ld;
+  int sorted;
+  const int32_t* cand;    // optional column -> token map
+  int64_t cand_ld;
+  int block;
+};
+
+hipError_t launch_score(const ScoreCall& c, hipStream_t stream);
+hipError_t launch_topk(const TopkCall& c, hipStream_t stream);
+
+// Per-device error word (device address) and compute-unit count.
+unsigned* device_error_word();
+int device_cu_count();
+
+}  // namespace dsaidx

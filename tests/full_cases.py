@@ -1,0 +1,15 @@
+"""The five workloads at their stated sizes, generated once per test session and kept on the
+GPU (shared by the score, top-k and select tests)."""
+import synth
+from gpu_util import Uploaded, say
+
+_CACHE = {}
+
+
+def full_case(cfg: int):
+    if cfg not in _CACHE:
+        _CACHE.clear()  # keep at most one full-size workload resident
+        say(f"[full] generating workload {cfg}")
+        case = synth.full_size(cfg)
+        _CACHE[cfg] = (case, Uploaded(case))
+    return _CACHE[cfg]

@@ -1,0 +1,129 @@
+"""GPU idx_select: bit-identical to idx_topk over the library's own scores (and the
+column -> token map for candidate blocks), and end-to-end against the oracle under the
+overlap / tie-gap rule; sparse-block selection equals the dense-masked selection."""
+import numpy as np
+import pytest
+
+import dsa_lightning_indexer_idx_amd as D
+import oracle as O
+import synth
+from full_cases import full_case
+from gpu_util import Uploaded, assert_selection_matches, dev, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_dense": lambda: synth.tiny_dense(),
+    "dense_fp8_ragged": lambda: synth.batched_decode(seed=131, rows=5, n=6000, ragged=True, gap=33),
+    "dense_mxfp4": lambda: synth.batched_decode(seed=132, rows=3, n=4000, kdtype="mxfp4"),
+    "paged_fp8": lambda: synth.paged_decode(seed=133, rows=5, min_len=100, max_len=9000,
+                                            row_req=True),
+    "paged_mxfp4": lambda: synth.paged_decode(seed=134, rows=4, min_len=3000, max_len=6000,
+                                              kdtype="mxfp4"),
+    "sparse_mxfp4": lambda: synth.sparse_blocks(seed=135, rows=5, ctx=16384, n_blocks=24,
+                                                ragged=True),
+    "sparse_fp8": lambda: synth.sparse_blocks(seed=136, rows=3, ctx=8192, n_blocks=20,
+                                              kdtype="fp8"),
+    "prefill": lambda: synth.prefill_chunk(seed=137, q_tokens=96, prior=3000),
+}
+
+
+def _self_consistent(up, k):
+    """idx_select == idx_topk(idx_logits*) bit for bit."""
+    case = up.case
+    s_idx, s_val = up.select(k)
+    lg = up.logits()
+    if up.kind == "Dense":
+        lens = up.ke - up.ks
+    elif up.kind == "Paged":
+        lens = up.sl
+    else:
+        lens = up.nc
+    t_idx, t_val = D.idx_topk(lg, k, lens=lens.contiguous(), n_cols=lg.shape[1])
+    t_idx, t_val = host(t_idx), host(t_val)
+    if up.kind == "Sparse":
+        t_idx = O.columns_to_tokens(t_idx, case.cand, case.block)
+    s_idx, s_val = host(s_idx), host(s_val)
+    assert np.array_equal(s_idx, t_idx), "select != topk(logits)"
+    assert np.array_equal(s_val, t_val)
+    return s_idx, s_val
+
+
+def _ref_scores_fn(case, ref_lg):
+    if type(case).__name__ != "Sparse":
+        return lambda r, idx: ref_lg[r][idx]
+    # sparse: selected values are tokens; find their columns
+    def f(r, toks):
+        cols = []
+        for t in toks:
+            b = np.searchsorted(case.cand[r], t // case.block)
+            cols.append(b * case.block + t % case.block)
+        return ref_lg[r][np.array(cols)]
+    return f
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_select_small(name):
+    require_gpu()
+    case = SMALL[name]()
+    up = Uploaded(case)
+    k = min(case.topk, 2048)
+    s_idx, _ = _self_consistent(up, k)
+    r_idx, r_val, r_lg = O.select_case(case, k=k, with_logits=True)
+    kth = np.array([r_val[r][max(0, int((r_idx[r] >= 0).sum()) - 1)] for r in range(case.rows)])
+    inter, total = assert_selection_matches(s_idx, r_idx, _ref_scores_fn(case, r_lg), kth, name)
+    say(f"[select] {name}: overlap {inter}/{total}")
+
+
+def test_sparse_equals_dense_masked_on_gpu():
+    """The candidate-block route and the dense route with non-candidate tokens masked pick
+    the same tokens (scores agree within tolerance, so compare under the overlap rule)."""
+    require_gpu()
+    sp = synth.sparse_blocks(seed=138, rows=4, ctx=4096, n_blocks=10, ragged=True,
+                             poison_noncand=False)
+    g_idx, _ = Uploaded(sp).select(300)
+    dense = synth.Dense("dense_view", sp.q, "fp8", sp.w, sp.k, sp.k_scale, sp.k_dtype, sp.row_ks,
+                        sp.row_ke, 300)
+    d_lg = host(Uploaded(dense).logits(ld=4096))
+    mask = np.zeros_like(d_lg, dtype=bool)
+    for r in range(sp.rows):
+        cols = np.arange(int(sp.n_cols[r]))
+        toks = sp.cand[r][cols // 128] * 128 + cols % 128
+        toks = toks[toks < sp.row_ke[r] - sp.row_ks[r]]
+        mask[r, toks] = True
+    masked = np.where(mask, d_lg, -np.inf).astype(np.float32)
+    m_idx, _ = D.idx_topk(dev(masked), 300)
+    assert np.array_equal(host(g_idx), host(m_idx))
+
+
+def test_unsorted_select_same_set():
+    require_gpu()
+    case = synth.paged_decode(seed=139, rows=3, min_len=5000, max_len=9000)
+    up = Uploaded(case)
+    a, _ = up.select(1024)
+    b, _ = up.select(1024, sorted=False)
+    a, b = host(a), host(b)
+    for r in range(3):
+        assert sorted(a[r].tolist()) == sorted(b[r].tolist())
+
+
+FULL = {2: [0, 31], 3: [0, 63], 4: [0, 4095], 5: [0, 63]}
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_select(cfg):
+    """The workloads at full size through idx_select (the benchmark's call); the oracle
+    checks sampled rows end to end, and every row is checked against idx_topk."""
+    require_gpu()
+    case, up = full_case(cfg)
+    ks = [2048, 1024, 512] if cfg == 3 else [case.topk]
+    for k in ks:
+        say(f"[select] full workload {cfg} k={k}")
+        s_idx, _ = _self_consistent(up, k)
+        rows = FULL[cfg]
+        sub = O.subset_rows(case, rows)
+        r_idx, r_val, r_lg = O.select_case(sub, k=k, with_logits=True)
+        kth = np.array([r_val[i][max(0, int((r_idx[i] >= 0).sum()) - 1)] for i in range(len(rows))])
+        inter, total = assert_selection_matches(s_idx[rows], r_idx, _ref_scores_fn(sub, r_lg), kth,
+                                                f"workload {cfg} k={k}")
+        say(f"[select] full workload {cfg} k={k}: sampled overlap {inter}/{total}")
