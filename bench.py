@@ -1,0 +1,216 @@
+"""Benchmark of the DSA lightning-indexer hot path on one MI355X.
+
+A step is one idx_select call (scores of every cached key by Eq. (1) + exact top-k) over
+the long-context paged decode workload: 64 rows with valid lengths uniform in
+[65536, 131072], fp8 e4m3 keys with a per-token fp32 scale in 64-token pages behind a
+randomly permuted block table, 64 heads x 128, k = 2048 (also timed at k = 1024, 512).
+Inputs are generated once (seeded) and resident in HBM before timing.
+
+Prints one JSON line: tokens scored per second (value), top-k rows per second, the
+roofline of the dominant kernel (the key-cache scan, timed alone with HIP events on its
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "indexer tokens scored/s + top-k rows/s at 128K ctx; % of HBM roofline"
+HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
+PROFILES = ROOT / "profiles"
+SCAN_SOURCES = [ROOT / "dsa_lightning_indexer_idx_amd" / "csrc" / f for f in
+                ("scan.hip", "device.h", "launch.h")]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def scan_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in SCAN_SOURCES:
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def scan_bytes(case) -> int:
+    """Algorithmic HBM bytes of one paged scan launch: per valid token its 128-byte fp8 key,
+    4-byte scale and 4-byte score; per page one 4-byte block-table entry; per row q (8 KiB),
+    w (256 B) and the -inf fill of the unscored tail of its score row."""
+    import numpy as np
+    L = case.seq_lens.astype(np.int64)
+    pages = (L + case.page_size - 1) // case.page_size
+    width = case.block_table.shape[1] * case.page_size
+    return int(L.sum() * (128 + 4 + 4) + pages.sum() * 4 + case.rows * (64 * 128 + 64 * 4)
+               + (width - L).sum() * 4)
+
+
+def step_bytes(case, k: int) -> int:
+    """Algorithmic HBM bytes of one fused step (keys, scales, table, q, w, k indices out)."""
+    import numpy as np
+    L = case.seq_lens.astype(np.int64)
+    pages = (L + case.page_size - 1) // case.page_size
+    return int(L.sum() * 132 + pages.sum() * 4 + case.rows * (64 * 128 + 64 * 4 + 4 * k))
+
+
+def stored_traffic():
+    """HBM traffic per scan launch from the committed counter summary, if it was taken on
+    the current scan source; else None."""
+    f = PROFILES / "scan_paged_fp8_128k_counters.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("scan_source_sha") != scan_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_loop(fn, steps: int, warmup: int, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
+
+
+def cpu_baseline(case, k: int, budget_s: float = 15.0):
+    """The oracle (scores + top-k) on whole rows of the same workload. The oracle spreads
+    rows over its OpenMP threads, so each batch holds one row per thread; batches run
+    until about ``budget_s`` seconds have been spent (at least one batch)."""
+    import oracle
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    batch = max(1, min(threads, case.rows))
+    done, tokens, spent = 0, 0, 0.0
+    while done < case.rows and spent < budget_s:
+        rows = list(range(done, min(done + batch, case.rows)))
+        sub = oracle.subset_rows(case, rows)
+        t0 = time.perf_counter()
+        oracle.select_case(sub, k=k)
+        spent += time.perf_counter() - t0
+        done += len(rows)
+        tokens += int(sub.seq_lens.sum())
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": batch, "kind": "oracle",
+            "sample": f"rows 0..{done - 1} of {case.rows} ({tokens} keys), scores + top-k "
+                      f"k={k}, {spent:.1f} s wall, one row per OpenMP thread",
+            "rows_per_s": done / spent}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "scan", "select"], default="all",
+                    help="run one timed loop only (for profiler counter runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the indexer's rows shard "
+              "across GPUs without any exchange, so per-GPU throughput is the figure.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dsa_lightning_indexer_idx_amd as D
+    import synth
+
+    D.lib()
+    torch.cuda.set_device(0)
+    log("generating the 128K paged decode workload")
+    case = synth.paged_decode(poison=False)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    q, w, kp, sp = dev(case.q), dev(case.w), dev(case.k_pages), dev(case.k_scale_pages)
+    bt, sl = dev(case.block_table), dev(case.seq_lens)
+    tokens = int(case.tokens)
+    rows = case.rows
+    stream = torch.cuda.current_stream()
+    prob = D.paged_problem(q, w, kp, sp, bt, sl, k_dtype="fp8")
+    ws = torch.empty(D.idx_select_workspace(prob, 2048), dtype=torch.uint8, device="cuda")
+    outs = {k: torch.empty((rows, k), dtype=torch.int32, device="cuda") for k in (2048, 1024, 512)}
+    width = case.block_table.shape[1] * case.page_size
+    scores = torch.empty((rows, width), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def select(k):
+        return lambda: D.idx_select(prob, k, values=False, out_idx=outs[k], workspace=ws)
+
+    def scan():
+        D.idx_logits_paged(q, w, kp, sp, bt, sl, k_dtype="fp8", out=scores)
+
+    res = {}
+    if args.only in ("all", "select"):
+        ms, wall_ms = time_loop(select(2048), args.steps, args.warmup, stream)
+        res["select"] = (ms, wall_ms)
+        log(f"idx_select k=2048: {ms:.3f} ms/step (wall {wall_ms:.3f})")
+        if args.only == "all":
+            for k in (1024, 512):
+                kk, _ = time_loop(select(k), max(5, args.steps // 2), 2, stream)
+                res[f"select_k{k}"] = kk
+                log(f"idx_select k={k}: {kk:.3f} ms/step")
+    if args.only in ("all", "scan"):
+        ms_scan, _ = time_loop(scan, args.steps, args.warmup, stream)
+        res["scan"] = ms_scan
+        log(f"scan kernel alone: {ms_scan:.3f} ms/launch")
+    if args.only != "all":
+        return 0
+
+    ms = res["select"][0]
+    sb = scan_bytes(case)
+    achieved = sb / (res["scan"] * 1e-3)
+    step_b = step_bytes(case, 2048)
+    cpu = None if args.no_cpu else cpu_baseline(case, 2048)
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "paged_decode_128k", "rows": rows, "valid_len": "U[65536,131072]",
+                   "tokens": tokens, "page_size": 64, "key": "fp8 e4m3 + fp32 per-token scale",
+                   "heads": 64, "dim": 128, "k": 2048, "seed": 3},
+        "rows_per_s": rows / (ms * 1e-3),
+        "step_hbm_frac": step_b / (ms * 1e-3) / HBM_PEAK,
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": stored_traffic(),
+                     "kernel": "scan_kernel<fp8, paged>", "ms_per_launch": res["scan"],
+                     "bytes_per_launch": sb},
+        "cpu_baseline": cpu,
+        "extra": {"ms_per_step_k1024": res["select_k1024"], "ms_per_step_k512": res["select_k512"],
+                  "tokens_per_s_k1024": tokens / (res["select_k1024"] * 1e-3),
+                  "tokens_per_s_k512": tokens / (res["select_k512"] * 1e-3),
+                  "wall_ms_per_step": res["select"][1], "scan_source_sha": scan_source_hash()},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -18,6 +18,8 @@ reproducible array by array. Poison fill (fp8 code 0x7F = NaN, scale NaN, UE8M0
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -92,13 +94,26 @@ def _normal(rng, shape, scale=1.0, chunk=1 << 26) -> np.ndarray:
     return out.reshape(shape)
 
 
-def _fp8_normal(rng, shape, chunk=1 << 26) -> np.ndarray:
-    """N(0,1) draws cast to e4m3fn codes, in chunks to bound host memory."""
+_CHUNK = 1 << 24
+
+
+def _fp8_normal(rng, shape) -> np.ndarray:
+    """N(0,1) draws cast to e4m3fn codes. Fixed 16M-element chunks each draw from their
+    own stream seeded from ``rng`` and fill in parallel threads, so the result depends
+    only on the seed, never on the thread count."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint8)
-    for s in range(0, n, chunk):
-        m = min(chunk, n - s)
-        out[s:s + m] = to_fp8_e4m3fn(rng.standard_normal(m, dtype=np.float32))
+    starts = list(range(0, n, _CHUNK))
+    seeds = rng.integers(0, 2 ** 63, size=len(starts))
+
+    def fill(i):
+        s = starts[i]
+        m = min(_CHUNK, n - s)
+        g = np.random.Generator(np.random.PCG64(int(seeds[i])))
+        out[s:s + m] = to_fp8_e4m3fn(g.standard_normal(m, dtype=np.float32))
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(len(starts))))
     return out.reshape(shape)
 
 
@@ -113,10 +128,18 @@ def _keys(rng, n: int, kdtype: str, scale_rng):
     if kdtype == "mxfp4":
         codes = np.empty((n, DIM // 2), np.uint8)
         scales = np.empty((n, DIM // 32), np.uint8)
-        step = 1 << 18
-        for s in range(0, n, step):
+        step = _CHUNK // DIM
+        starts = list(range(0, n, step))
+        seeds = rng.integers(0, 2 ** 63, size=len(starts))
+
+        def fill(i):
+            s = starts[i]
             m = min(step, n - s)
-            codes[s:s + m], scales[s:s + m] = to_mxfp4(_normal(rng, (m, DIM)))
+            g = np.random.Generator(np.random.PCG64(int(seeds[i])))
+            codes[s:s + m], scales[s:s + m] = to_mxfp4(g.standard_normal((m, DIM), dtype=np.float32))
+
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(len(starts))))
         return codes, scales
     raise ValueError(kdtype)
 
@@ -354,7 +377,7 @@ def sparse_blocks(seed: int = 5, rows: int = 64, ctx: int = 131072, n_blocks: in
             codes = np.full((n_keys, DIM), FP8_NAN, np.uint8)
             sc = np.full(n_keys, np.nan, np.float32)
         else:
-            codes = r["poison"].integers(0, 256, size=(n_keys, DIM // 2), dtype=np.uint8)
+            codes = np.zeros((n_keys, DIM // 2), np.uint8)
             sc = np.full((n_keys, DIM // 32), UE8M0_NAN, np.uint8)
         toks = (np.arange(rows)[:, None, None] * ctx + cand[:, :, None] * block
                 + np.arange(block)[None, None, :]).reshape(-1)
