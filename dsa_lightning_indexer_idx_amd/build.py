@@ -21,9 +21,12 @@ OBJ = PKG / "_build"
 SOURCES = ["api.cpp", "scan.hip", "prefill.hip", "topk.hip"]
 
 # Device code never uses packed-fp32 instructions (the flag is a device-target
-# feature; the host pass only warns that it does not know it).
+# feature; the host pass only warns that it does not know it). MFMA results stay in
+# VGPRs: the epilogue reads every accumulator, and AGPR results would each cost a
+# v_accvgpr_read.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -247,13 +247,11 @@ idx_status idx_logits_sparse_blocks(const void* q, int q_dtype, const float* w, 
   return launched("idx_logits_sparse_blocks", launch_score(c, (hipStream_t)stream));
 }
 
-size_t idx_topk_workspace(int, int64_t, int) { return 0; }
+size_t idx_topk_workspace(int rows, int64_t n_cols, int) { return topk_workspace_bytes(rows, n_cols); }
 
 idx_status idx_topk(const float* logits, int64_t ld, const int32_t* lens, int64_t n_cols, int rows,
                     int k, int32_t* out_idx, float* out_val, int64_t out_ld, uint32_t flags,
                     void* workspace, size_t workspace_bytes, idx_stream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   const char* fn = "idx_topk";
   REQUIRE(rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, rows);
   REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
@@ -267,6 +265,10 @@ idx_status idx_topk(const float* logits, int64_t ld, const int32_t* lens, int64_
           "%s: arrays must be 4-byte aligned", fn);
   idx_status s = check_ints(fn, {lens});
   if (s != IDX_OK) return s;
+  const size_t need = topk_workspace_bytes(rows, n_cols);
+  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), IDX_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(need == 0 || aligned(workspace, 256), IDX_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
   TopkCall c{};
   c.logits = logits;
   c.ld = ld;
@@ -278,7 +280,13 @@ idx_status idx_topk(const float* logits, int64_t ld, const int32_t* lens, int64_
   c.out_val = out_val;
   c.out_ld = out_ld;
   c.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
-  return launched(fn, launch_topk(c, (hipStream_t)stream));
+  return launched(fn, launch_topk(c, workspace, (hipStream_t)stream));
+}
+
+// idx_select workspace: the score matrix [rows, round_up(width, 64)] fp32, then the
+// top-k workspace at the next 256-byte boundary.
+size_t select_scores_bytes(const idx_problem* p) {
+  return (size_t)round_up((int64_t)p->rows * round_up(select_width(p), 64) * (int64_t)sizeof(float), 256);
 }
 
 size_t idx_select_workspace(const idx_problem* p, int k) {
@@ -286,7 +294,7 @@ size_t idx_select_workspace(const idx_problem* p, int k) {
   if (!p || p->rows <= 0) return 0;
   int64_t width = select_width(p);
   if (width <= 0) return 0;
-  return (size_t)p->rows * (size_t)round_up(width, 64) * sizeof(float) + 256;
+  return select_scores_bytes(p) + topk_workspace_bytes(p->rows, width);
 }
 
 idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_val, int64_t out_ld,
@@ -347,7 +355,7 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
     t.cand_ld = p->cand_ld;
     t.block = p->block_size;
   }
-  return launched(fn, launch_topk(t, (hipStream_t)stream));
+  return launched(fn, launch_topk(t, (uint8_t*)workspace + select_scores_bytes(p), (hipStream_t)stream));
 }
 
 const char* idx_status_string(idx_status s) {

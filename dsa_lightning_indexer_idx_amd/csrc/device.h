@@ -52,6 +52,12 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ReLU as one integer max: a float with its sign bit set is a negative int, so
+// max(bits, 0) keeps positive values and turns negatives and -0.0 into +0.0.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ---------------------------------------------------------------- cross-lane sums
 //
 // Lane l holds four partial sums p[j], one per 16-token tile j, each covering the

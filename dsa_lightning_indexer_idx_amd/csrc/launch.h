@@ -56,7 +56,8 @@ struct TopkCall {
 };
 
 hipError_t launch_score(const ScoreCall& c, hipStream_t stream);
-hipError_t launch_topk(const TopkCall& c, hipStream_t stream);
+size_t topk_workspace_bytes(int rows, int64_t n_cols);
+hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
 
 // Per-device error word (device address) and compute-unit count.
 unsigned* device_error_word();

@@ -34,6 +34,16 @@ struct ScanCommon {
 };
 
 // ------------------------------------------------------------------ key sources
+//
+// Pages and candidate blocks hold a multiple of 64 keys and steps start at multiples
+// of 64 positions, so the 64 positions of a step name 64 consecutive key rows. A
+// source describes step s of a row by its first key row and by how many leading
+// positions of the step are scored (its valid prefix, <= 0 when none is).
+
+struct StepDesc {
+  int64_t kidx0;
+  int32_t vlim;
+};
 
 // Contiguous range [row_ks, row_ke) of a flat key array.
 struct DenseSrc {
@@ -52,10 +62,8 @@ struct DenseSrc {
     return {s2, len};
   }
   __device__ int64_t bound(const Row& R) const { return R.len; }
-  __device__ bool key(const Row& R, int64_t pos, int64_t& kidx, unsigned*) const {
-    bool v = pos < R.len;
-    kidx = R.base + (v ? pos : R.len - 1);
-    return v;
+  __device__ StepDesc step(const Row& R, int64_t pos0, unsigned*) const {
+    return {R.base + pos0, (int32_t)min(R.len - pos0, (int64_t)kTileTokens)};
   }
 };
 
@@ -80,16 +88,14 @@ struct PagedSrc {
     return {bt + req2 * bt_ld, L2};
   }
   __device__ int64_t bound(const Row& R) const { return R.len; }
-  __device__ bool key(const Row& R, int64_t pos, int64_t& kidx, unsigned* err) const {
-    bool v = pos < R.len;
-    int64_t p = v ? pos : R.len - 1;
-    int64_t pg = R.bt_row[p / page];
+  __device__ StepDesc step(const Row& R, int64_t pos0, unsigned* err) const {
+    if (pos0 >= R.len) return {0, 0};
+    int64_t pg = R.bt_row[pos0 / page];
     if (pg < 0 || pg >= n_pages) {
-      if (v) flag_error(err, kErrPage);
+      flag_error(err, kErrPage);
       pg = min(max(pg, (int64_t)0), n_pages - 1);
     }
-    kidx = pg * page + p % page;
-    return v;
+    return {pg * page + pos0 % page, (int32_t)min(R.len - pos0, (int64_t)kTileTokens)};
   }
 };
 
@@ -119,14 +125,16 @@ struct SparseSrc {
     return {s2, e2 - s2, cand + (int64_t)r * cand_ld, nc2};
   }
   __device__ int64_t bound(const Row& R) const { return R.ncols; }
-  __device__ bool key(const Row& R, int64_t pos, int64_t& kidx, unsigned* err) const {
-    bool in = pos < R.ncols;
-    int64_t cb = in ? (int64_t)R.cand_row[pos / block] : 0;
-    int64_t tok = cb * block + pos % block;
-    bool v = in && cb >= 0 && tok < R.len;
-    if (in && cb < 0) flag_error(err, kErrBlock);
-    kidx = R.base + (v ? tok : 0);
-    return v;
+  __device__ StepDesc step(const Row& R, int64_t pos0, unsigned* err) const {
+    if (pos0 >= R.ncols) return {0, 0};
+    const int64_t cb = R.cand_row[pos0 / block];
+    if (cb < 0) {
+      flag_error(err, kErrBlock);
+      return {0, 0};
+    }
+    const int64_t tok0 = cb * block + pos0 % block;
+    const int64_t v = min(min(R.ncols - pos0, R.len - tok0), (int64_t)kTileTokens);
+    return {R.base + (v > 0 ? tok0 : 0), (int32_t)v};
   }
 };
 
@@ -231,11 +239,47 @@ struct KOps<FMT_BF16> {
 
 // ------------------------------------------------------------------ kernel
 
+// Loads the key operands of one step (lane: column c16 of tile j, K-block g) and the
+// scale of the key whose score this lane stores (position lane of the step).
+template <int F>
+__device__ __forceinline__ void load_step(KOps<F> (&ko)[4], float& sc, const ScanCommon& a, int64_t kidx0,
+                                          int32_t vlim, int lane) {
+  const int g = lane >> 4, c16 = lane & 15;
+  const int last = vlim - 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ko[j].load(a.k, a.k_scale, kidx0 + min(16 * j + c16, last), g);
+  if constexpr (F == FMT_FP8) sc = ((const float*)a.k_scale)[kidx0 + min(lane, last)];
+}
+
+template <int F>
+__device__ __forceinline__ float score_step(const KOps<F> (&ko)[4], float sc, const QOps<F>& qo,
+                                           const float (&wr)[4][4]) {
+  float p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p[j] = 0.f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const v4f s = ko[j].mma(qo, h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[j] = fmaf(wr[h][i], relu(s[i]), p[j]);
+    }
+  }
+  float v = sum_lane_groups(p[0], p[1], p[2], p[3]);
+  if constexpr (F == FMT_FP8) v *= sc;
+  return v;
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 template <int F, class Src>
 __global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
   const int lane = lane_id();
   const int g = lane >> 4;
-  const int c16 = lane & 15;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
   const int64_t chunk = (int64_t)a.chunk_tiles * kTileTokens;
@@ -246,13 +290,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
     const int64_t c0 = (item / a.rows) * chunk;
     if (c0 >= a.ld) continue;
     const int64_t c1 = min(c0 + chunk, a.ld);
+    const int nsteps = (int)((c1 - c0 + kTileTokens - 1) / kTileTokens);
     float* out = a.logits + (int64_t)r * a.ld;
     const auto R = src.row(r, a.ld, a.err, c0 == 0);
-    const int64_t bound = src.bound(R);
-    if (c0 >= bound) {
+    if (c0 >= src.bound(R)) {
       for (int64_t p = c0 + lane; p < c1; p += kWave) out[p] = NEG_INF;
       continue;
     }
+    // lane s describes step s of this item
+    StepDesc mine{0, 0};
+    if (lane < nsteps) mine = src.step(R, c0 + (int64_t)kTileTokens * lane, a.err);
     QOps<F> qo;
     qo.load(a.q, r, lane);
     float wr[4][4];
@@ -264,39 +311,29 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
       wr[h][2] = wv.z;
       wr[h][3] = wv.w;
     }
-    for (int64_t base = c0; base < c1; base += kTileTokens) {
-      const int64_t pst = base + lane;
-      if (base >= bound) {
-        if (pst < c1) out[pst] = NEG_INF;
-        continue;
+    // two register sets, A and B: the keys of step s + 1 load while step s computes
+    KOps<F> ka[4], kb[4];
+    float sa = 1.f, sb = 1.f;
+    int32_t va = __builtin_amdgcn_readlane(mine.vlim, 0);
+    if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, 0), va, lane);
+    for (int s = 0; s < nsteps; s += 2) {
+      int32_t vb = 0;
+      if (s + 1 < nsteps) {
+        vb = __builtin_amdgcn_readlane(mine.vlim, s + 1);
+        if (vb > 0) load_step<F>(kb, sb, a, readlane64(mine.kidx0, s + 1), vb, lane);
       }
-      KOps<F> ko[4];
-      int64_t kidx_st = 0;
-      bool valid_st = false;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int64_t kidx;
-        const bool v = src.key(R, base + 16 * j + c16, kidx, a.err);
-        ko[j].load(a.k, a.k_scale, kidx, g);
-        if (j == g) {
-          kidx_st = kidx;
-          valid_st = v;
-        }
+      int64_t pst = c0 + (int64_t)kTileTokens * s + lane;
+      float v = va > 0 ? score_step<F>(ka, sa, qo, wr) : NEG_INF;
+      if (pst < c1) out[pst] = lane < va ? v : NEG_INF;
+      if (s + 1 >= nsteps) break;
+      va = 0;
+      if (s + 2 < nsteps) {
+        va = __builtin_amdgcn_readlane(mine.vlim, s + 2);
+        if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, s + 2), va, lane);
       }
-      float p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = 0.f;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const v4f s = ko[j].mma(qo, h);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[j] = fmaf(wr[h][i], fmaxf(s[i], 0.f), p[j]);
-        }
-      }
-      float v = sum_lane_groups(p[0], p[1], p[2], p[3]);
-      if constexpr (F == FMT_FP8) v *= ((const float*)a.k_scale)[kidx_st];
-      if (pst < c1) out[pst] = valid_st ? v : NEG_INF;
+      pst += kTileTokens;
+      v = vb > 0 ? score_step<F>(kb, sb, qo, wr) : NEG_INF;
+      if (pst < c1) out[pst] = lane < vb ? v : NEG_INF;
     }
   }
 }

@@ -61,7 +61,8 @@ def test_misc_entry_points(L):
     assert L.idx_version() == 100
     assert L.idx_status_string(0) == b"IDX_OK"
     assert L.idx_status_string(3) == b"IDX_ERR_WORKSPACE"
-    assert L.idx_topk_workspace(64, 131072, 2048) == 0
+    assert L.idx_topk_workspace(4096, 8192, 2048) == 0       # short rows: no workspace
+    assert L.idx_topk_workspace(64, 131072, 2048) > 0        # long rows: histogram + lists
 
 
 def _dense(L, **kw):
@@ -142,6 +143,9 @@ CASES = [
     ("topk null out", _topk, dict(oi=None), ARG),
     ("topk misaligned lens", _topk, dict(lens=KS + 1), ARG),
     ("topk bad flags", _topk, dict(flags=6), ARG),
+    ("topk long rows without workspace", _topk, dict(ld=131072, ncols=131072), WSP),
+    ("topk long rows small workspace", _topk, dict(ld=131072, ncols=131072, ws=WS, wsb=4096), WSP),
+    ("topk long rows misaligned workspace", _topk, dict(ld=131072, ncols=131072, ws=WS + 8, wsb=1 << 30), ARG),
     ("topk negative rows", _topk, dict(rows=-2), ARG),
 ]
 
@@ -167,14 +171,15 @@ def _problem(**kw):
 
 
 def test_select_workspace_sizes(L):
-    p = _problem()
-    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 4096 * 4 + 256
+    # the score matrix (rows padded to 64 columns, 256-byte aligned) plus the top-k workspace
+    p = _problem(max_cols=4000)
+    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 4032 * 4
     p = _problem(mode=D.IDX_MODE_PAGED, page_size=64, block_table=BT, bt_rows=4, bt_ld=2048,
                  seq_lens=SL)
-    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 131072 * 4 + 256
+    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 131072 * 4 + L.idx_topk_workspace(4, 131072, 2048)
     p = _problem(mode=D.IDX_MODE_SPARSE_BLOCKS, k_dtype=D.IDX_MXFP4, cand_blocks=CAND, cand_ld=64,
                  n_cols=NC, block_size=128)
-    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 8192 * 4 + 256
+    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 8192 * 4
 
 
 SELECT_CASES = [

@@ -44,7 +44,10 @@ def adversarial_rows(n: int, seed: int) -> np.ndarray:
 @pytest.mark.parametrize("k", [1, 7, 256, 512, 1024, 2048])
 def test_adversarial_rows(k):
     require_gpu()
-    for n in (5, 2047, 2048, 2049, 9000):
+    # widths up to 16384 take the one-kernel path; wider rows the histogram / filter /
+    # finish path, whose candidate list overflows (falling back to a full-row select) on
+    # the all-equal and few-level rows
+    for n in (5, 2047, 2048, 2049, 9000, 16384, 16385, 40000):
         lg = adversarial_rows(n, seed=n + k)
         _check(lg, k, what=f"adversarial n={n} k={k}")
         lens = np.random.default_rng(n).integers(0, n + 1, lg.shape[0]).astype(np.int32)
