@@ -115,6 +115,80 @@ def cpu_baseline(case, k: int, budget_s: float = 15.0):
             "rows_per_s": done / spent}
 
 
+FP8_PEAK = 5.0e15  # MI355X dense fp8 MFMA, FLOP/s
+
+
+def other_workloads(D, np, torch, stream, args):
+    """Rates of the other workloads (reported next to the headline): the prefill chunk's
+    score kernel against the fp8 MFMA peak, and idx_select on batched decode and on the
+    two-level candidate blocks. Inputs that would fit in the 256 MB Infinity Cache are
+    rotated over several copies at distinct addresses, and the short two-level step is
+    timed as a captured HIP graph of one call per copy."""
+    import synth
+    out = {}
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    steps = max(5, args.steps // 2)
+    # prefill chunk: 4096 queries x 8192 keys, causal
+    c4 = synth.prefill_chunk()
+    q, w, k, sc, ks, ke = map(dev, (c4.q, c4.w, c4.k, c4.k_scale, c4.row_ks, c4.row_ke))
+    lg = torch.empty((c4.rows, c4.max_cols), dtype=torch.float32, device="cuda")
+    ms, _ = time_loop(lambda: D.idx_logits(q, w, k, sc, ks, ke, k_dtype="fp8", out=lg), steps, 3, stream)
+    flop = float((c4.row_ke.astype(np.int64) - c4.row_ks).sum()) * 64 * 128 * 2
+    out["prefill_logits_ms"] = ms
+    out["prefill_mfma_frac"] = flop / (ms * 1e-3) / FP8_PEAK
+    p4 = D.dense_problem(q, w, k, sc, ks, ke, k_dtype="fp8", max_cols=c4.max_cols)
+    ws4 = torch.empty(D.idx_select_workspace(p4, 2048), dtype=torch.uint8, device="cuda")
+    oi4 = torch.empty((c4.rows, 2048), dtype=torch.int32, device="cuda")
+    ms, _ = time_loop(lambda: D.idx_select(p4, 2048, values=False, out_idx=oi4, workspace=ws4), steps, 3, stream)
+    out["prefill_select_ms"] = ms
+    out["prefill_select_rows_per_s"] = c4.rows / (ms * 1e-3)
+    log(f"prefill: logits {out['prefill_logits_ms']*1e3:.1f} us ({100*out['prefill_mfma_frac']:.1f}% fp8 MFMA), "
+        f"select {ms*1e3:.1f} us")
+    del q, w, k, sc, ks, ke, lg, p4, ws4, oi4
+    # batched decode: 32 rows x 32768 fp8 keys (132.5 MiB: rotate 4 copies)
+    c2 = synth.batched_decode()
+    base = [dev(a) for a in (c2.q, c2.w, c2.k, c2.k_scale, c2.row_ks, c2.row_ke)]
+    copies = [base] + [[t.clone() for t in base] for _ in range(3)]
+    probs = [D.dense_problem(*cp, k_dtype="fp8", max_cols=c2.max_cols) for cp in copies]
+    ws2 = torch.empty(D.idx_select_workspace(probs[0], 2048), dtype=torch.uint8, device="cuda")
+    oi2 = torch.empty((c2.rows, 2048), dtype=torch.int32, device="cuda")
+    it = [0]
+
+    def sel2():
+        D.idx_select(probs[it[0] % 4], 2048, values=False, out_idx=oi2, workspace=ws2)
+        it[0] += 1
+    ms, _ = time_loop(sel2, 4 * steps, 4, stream)
+    out["batched_decode_select_ms"] = ms
+    out["batched_decode_tokens_per_s"] = c2.tokens / (ms * 1e-3)
+    log(f"batched decode: select {ms*1e3:.1f} us ({c2.tokens/(ms*1e-3)/1e9:.2f} G keys/s)")
+    del base, copies, probs, ws2, oi2
+    # two-level candidate blocks: 64 rows x 8192 candidate keys of 131072, MXFP4 (rotate 8
+    # copies of the candidate data, as a graph)
+    c5 = synth.sparse_blocks()
+    base = [dev(a) for a in (c5.q, c5.w, c5.k, c5.k_scale, c5.row_ks, c5.row_ke, c5.cand, c5.n_cols)]
+    copies = [base] + [[t.clone() for t in base] for _ in range(7)]
+    probs = [D.sparse_problem(*cp, k_dtype="mxfp4", block_size=128) for cp in copies]
+    ws5 = torch.empty(D.idx_select_workspace(probs[0], 2048), dtype=torch.uint8, device="cuda")
+    oi5 = torch.empty((c5.rows, 2048), dtype=torch.int32, device="cuda")
+    for p in probs:
+        D.idx_select(p, 2048, values=False, out_idx=oi5, workspace=ws5)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        g.capture_begin()
+        for p in probs:
+            D.idx_select(p, 2048, values=False, out_idx=oi5, workspace=ws5)
+        g.capture_end()
+    torch.cuda.synchronize()
+    ms, _ = time_loop(g.replay, steps, 2, stream)
+    ms /= len(probs)
+    out["two_level_select_ms"] = ms
+    out["two_level_tokens_per_s"] = c5.tokens / (ms * 1e-3)
+    log(f"two-level: select {ms*1e3:.1f} us per call ({c5.tokens/(ms*1e-3)/1e9:.2f} G keys/s, graph of {len(probs)})")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +249,8 @@ def main() -> int:
     if args.only != "all":
         return 0
 
+    extra = other_workloads(D, np, torch, stream, args)
+
     ms = res["select"][0]
     sb = scan_bytes(case)
     achieved = sb / (res["scan"] * 1e-3)
@@ -203,7 +279,8 @@ def main() -> int:
                      "kernel": "scan_kernel<fp8, paged>", "ms_per_launch": res["scan"],
                      "bytes_per_launch": sb},
         "cpu_baseline": cpu,
-        "extra": {"ms_per_step_k1024": res["select_k1024"], "ms_per_step_k512": res["select_k512"],
+        "extra": {**extra,
+                  "ms_per_step_k1024": res["select_k1024"], "ms_per_step_k512": res["select_k512"],
                   "tokens_per_s_k1024": tokens / (res["select_k1024"] * 1e-3),
                   "tokens_per_s_k512": tokens / (res["select_k512"] * 1e-3),
                   "wall_ms_per_step": res["select"][1], "scan_source_sha": scan_source_hash()},

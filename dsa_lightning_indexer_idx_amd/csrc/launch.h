@@ -56,6 +56,12 @@ struct TopkCall {
 };
 
 hipError_t launch_score(const ScoreCall& c, hipStream_t stream);
+
+// Dense fp8 calls with at least this many rows are taken as prefill chunks (rows that
+// share their keys) and run the tiled prefill kernel; fewer rows run the decode scan.
+constexpr int kPrefillMinRows = 256;
+bool prefill_applies(const ScoreCall& c);
+hipError_t launch_prefill(const ScoreCall& c, hipStream_t stream);
 size_t topk_workspace_bytes(int rows, int64_t n_cols);
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
 

@@ -340,17 +340,38 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
 
 // ------------------------------------------------------------------ launcher
 
+// Launch shape: the grid holds exactly the workgroups that are resident at once (from
+// the occupancy of each kernel instance), so no workgroup starts late and becomes a
+// tail; items are at most kMaxSteps 64-key steps (at most 64: one step per lane).
+#ifndef DSAIDX_SCAN_MAX_STEPS
+#define DSAIDX_SCAN_MAX_STEPS 32
+#endif
 static constexpr int kBlock = 256;
-static constexpr int kWavesPerCU = 16;
+static constexpr int kMaxSteps = DSAIDX_SCAN_MAX_STEPS;
+static_assert(kMaxSteps >= 1 && kMaxSteps <= kWave, "an item describes one step per lane");
+
+template <int F, class Src>
+static int resident_blocks_per_cu() {
+  static std::once_flag once;
+  static int n = 1;
+  std::call_once(once, [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)scan_kernel<F, Src>, kBlock, 0) ==
+            hipSuccess &&
+        b > 0)
+      n = b;
+  });
+  return n;
+}
 
 template <int F, class Src>
 static hipError_t run(const ScoreCall& c, const Src& src, hipStream_t stream) {
   const int cus = device_cu_count();
-  const int64_t waves_total = (int64_t)cus * kWavesPerCU;
+  const int64_t waves_total = (int64_t)cus * resident_blocks_per_cu<F, Src>() * (kBlock / kWave);
   const int64_t tiles_per_row = (c.ld + kTileTokens - 1) / kTileTokens;
   const int64_t tiles = tiles_per_row * c.rows;
   int64_t ct = tiles / (2 * waves_total);
-  ct = ct < 1 ? 1 : (ct > 32 ? 32 : ct);
+  ct = ct < 1 ? 1 : (ct > kMaxSteps ? kMaxSteps : ct);
   const int64_t chunks = (tiles_per_row + ct - 1) / ct;
   ScanCommon a;
   a.q = c.q;
@@ -383,6 +404,7 @@ hipError_t launch_score(const ScoreCall& c, hipStream_t stream) {
   if (c.rows <= 0 || c.ld <= 0) return hipSuccess;
   switch (c.source) {
     case SRC_DENSE: {
+      if (prefill_applies(c)) return launch_prefill(c, stream);
       DenseSrc s{c.row_ks, c.row_ke, c.n_keys};
       if (c.fmt == FMT_BF16) return run<FMT_BF16>(c, s, stream);
       return run_fmt(c, s, stream);

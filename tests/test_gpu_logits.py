@@ -42,6 +42,10 @@ SMALL = {
     "sparse_fp8_ragged": lambda: synth.sparse_blocks(seed=109, rows=4, ctx=3000, n_blocks=5,
                                                      kdtype="fp8", ragged=True),
     "prefill_q300_prior700": lambda: synth.prefill_chunk(seed=110, q_tokens=300, prior=700),
+    # 300 rows take the tiled prefill kernel even though their ranges are disjoint and ragged
+    "dense_many_rows_disjoint": lambda: synth.batched_decode(seed=116, rows=300, n=700, ragged=True,
+                                                             gap=9),
+    "prefill_q1030_prior64": lambda: synth.prefill_chunk(seed=117, q_tokens=1030, prior=64),
 }
 
 
