@@ -2,20 +2,26 @@
 // query rows that share one key array (a prefill chunk against its context, causal
 // mask carried by row_ke).
 //
-// Unlike the decode scan, rows here read the same keys, so keys are staged once per
-// workgroup and reused by every query of the workgroup:
-//   * a workgroup owns kQB consecutive queries (two per wave) and walks the union of
-//     their key ranges in 64-key tiles; query blocks run longest range first;
-//   * each tile (8 KiB of fp8 keys + 256 B of scales) is loaded by all 256 threads with
-//     full-line 16-byte loads and stored to LDS with the 16-byte chunks of every key
-//     rotated by XOR with (key % 8), so the MFMA-layout reads that follow (16 keys of
-//     one 16-byte chunk column per instruction) hit distinct banks;
-//   * the next tile's global loads are in flight while the current tile computes;
-//   * per query and tile: 16 MFMAs (4 head tiles x 4 key tiles, K = 128 in one
-//     instruction), ReLU and head weights in registers, three lane swaps for the head
-//     sum, the key's fp8 scale, one 256-byte store;
-//   * tiles past a query's range are masked; a query block stops at its longest
-//     range, so tiles above the causal diagonal of the whole block are never loaded.
+//   * A workgroup owns kQB consecutive queries (two per wave) and walks the union of
+//     their key ranges in 64-key tiles; query blocks run longest range first.
+//   * Tiles are staged in LDS, three slots deep: all 256 threads load tile t + 2 (one
+//     16-byte chunk each per load) while tile t computes, and store it chunk-major
+//     (chunk c of key k at c * 1 KiB + k * 16) so the stores and the MFMA-layout reads
+//     (16 keys of one chunk per 16 lanes) touch contiguous LDS. One barrier per tile.
+//   * Because tile t + 1 is already visible while tile t computes, a wave reads the B
+//     operands of the next 16 keys (crossing into tile t + 1) while the current 16
+//     compute, and no LDS read waits on a barrier.
+//   * The ReLU-weighted head sum uses sum_j w_j ReLU(s_j) = (L + A) / 2 with the linear
+//     part L = sum_j w_j s_j = (sum_j w_j q_j) . k and A = sum_j w_j |s_j|. A costs one
+//     FMA per head (|s| is a free source modifier) instead of a max and an FMA. L is one
+//     more MFMA row per piece: q' = sum_j w_j q_j (fp32) is split into five fp8 pieces
+//     with power-of-two weights (each piece is the fp8 rounding of the scaled residual of
+//     the previous ones, so the split is exact to 2^-20 of max |q'|), and the pieces of a
+//     wave's two queries fill rows 0..9 of one extra 16-row MFMA tile.
+//   * Per 16 keys and wave: 9 MFMAs (2 queries x 4 head tiles + the pieces; K = 128 in
+//     one instruction), 20 FMAs per query and lane, three lane swaps for the head sum,
+//     the key's fp8 scale and one 256-byte store per query (non-temporal: scores are
+//     not re-read here and must not push the keys out of L2).
 #include "device.h"
 #include "launch.h"
 
@@ -23,10 +29,17 @@
 
 namespace dsaidx {
 
-constexpr int kQB = 8;               // queries per workgroup
-constexpr int kPThreads = 256;       // 4 waves, 2 queries each
+#ifndef DSAIDX_PREFILL_QW
+#define DSAIDX_PREFILL_QW 2
+#endif
+#ifndef DSAIDX_PREFILL_WAVES_PER_SIMD
+#define DSAIDX_PREFILL_WAVES_PER_SIMD 2
+#endif
+constexpr int kQW = DSAIDX_PREFILL_QW;  // queries per wave
+constexpr int kPThreads = 256;          // 4 waves
+constexpr int kQB = 4 * kQW;            // queries per workgroup
+constexpr int kSlots = 3;        // LDS tile slots
 constexpr int kTileBytes = kTileTokens * kDim;
-
 struct PrefillArgs {
   const uint8_t* q;
   const float* w;
@@ -41,12 +54,23 @@ struct PrefillArgs {
   unsigned* err;
 };
 
-// LDS byte offset of 16-byte chunk c (0..7) of key t (0..63) in a tile.
-__device__ __forceinline__ int tile_off(int t, int c) { return t * kDim + ((c ^ (t & 7)) << 4); }
+constexpr int kPieces = 5;  // fp8 pieces of q' per query
 
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTileBytes];
-  __shared__ float tscale[2][kTileTokens];
+// fp8 e4m3fn byte of x (RNE; |x| <= 448) and its value.
+__device__ __forceinline__ uint32_t to_fp8(float x) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xFFu;
+}
+__device__ __forceinline__ float from_fp8(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
+// LDS byte offset of 16-byte chunk c (0..7) of key k (0..63) in a tile slot.
+__device__ __forceinline__ int tile_off(int k, int c) { return c * (kTileTokens * 16) + (k << 4); }
+
+__global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kSlots][kTileBytes];
+  __shared__ float tscale[kSlots][kTileTokens];
+  __shared__ __attribute__((aligned(16))) float qlin[kPThreads / kWave][2][kDim];
+  __shared__ int qexp[kPThreads / kWave][2];
+  static_assert(kQW == 1 || kQW == 2, "one or two queries per wave");
   __shared__ int64_t s_lo, s_hi;
 
   const int tid = threadIdx.x;
@@ -59,11 +83,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   // key range of each of this wave's two queries, and of the whole block
   int64_t qs[2], qe[2];
-  bool qv[2];
+  bool qv[2] = {false, false};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int r = q0 + 2 * wave + u;
-    qv[u] = r < a.rows;
+    const int r = q0 + kQW * wave + u;
+    qv[u] = u < kQW && r < a.rows;
     int64_t s = 0, e = 0;
     if (qv[u]) {
       const int64_t s0 = a.ks[r], e0 = a.ke[r];
@@ -88,16 +112,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         atomicMax((unsigned long long*)&s_hi, (unsigned long long)qe[u]);
       }
   }
-  __syncthreads();
-  const int64_t lo = s_lo, hi = s_hi;
-  const int ntiles = hi > lo ? (int)((hi - lo + kTileTokens - 1) / kTileTokens) : 0;
 
   // query operands and head weights of the two queries
   v8i qa[2][4];
   float wr[2][4][4];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int r = qv[u] ? q0 + 2 * wave + u : 0;
+    const int r = qv[u] ? q0 + kQW * wave + u : 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const v4i* p = (const v4i*)(a.q + ((int64_t)r * kHeads + 16 * h + c16) * kDim + 32 * g);
@@ -111,20 +132,95 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // cooperative tile load: thread t moves chunks t and t + 256 (key = chunk / 8)
+  // q' = sum_j w_j q_j of the two queries: lane l sums dims 4 (l % 32) .. + 3 of query
+  // l / 32 over the 64 heads, in head order
+  {
+    const int uu = lane >> 5, d0 = 4 * (lane & 31);
+    const int r = qv[uu] ? q0 + kQW * wave + uu : 0;
+    const uint8_t* qrow = a.q + (int64_t)r * kHeads * kDim + d0;
+    const float* wrow = a.w + (int64_t)r * kHeads;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int j = 0; j < kHeads; ++j) {
+      const float wj = wrow[j];
+      const int codes = *(const int*)(qrow + j * kDim);
+      acc[0] = fmaf(wj, __builtin_amdgcn_cvt_f32_fp8(codes, 0), acc[0]);
+      acc[1] = fmaf(wj, __builtin_amdgcn_cvt_f32_fp8(codes, 1), acc[1]);
+      acc[2] = fmaf(wj, __builtin_amdgcn_cvt_f32_fp8(codes, 2), acc[2]);
+      acc[3] = fmaf(wj, __builtin_amdgcn_cvt_f32_fp8(codes, 3), acc[3]);
+    }
+    *(float4*)(&qlin[wave][uu][d0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    float mx = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    // scale so the largest |q'| lands in [128, 256): e0 = 8 - E for mx = m 2^E, m in [0.5, 1)
+    int E = 0;
+    frexpf(mx, &E);
+    if ((lane & 31) == 0) qexp[wave][uu] = mx > 0.f ? 8 - E : 0;
+  }
+  __syncthreads();
+  const int64_t lo = s_lo, hi = s_hi;
+  const int ntiles = hi > lo ? (int)((hi - lo + kTileTokens - 1) / kTileTokens) : 0;
+
+  // A operand of the pieces tile: row rho = l % 16 < 10 holds piece rho % 5 of query
+  // rho / 5 (dims 32g .. 32g+31, the same K order as the keys); coefficient of the
+  // lane's accumulator rows 4g + i for each query
+  v8i apiece = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  float coef[2][4];
+  {
+    const int rho = c16;
+    if (rho < kQW * kPieces) {
+      const int u = rho / kPieces, m = rho % kPieces;
+      const int e0 = qexp[wave][u];
+      uint32_t words[8];
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float y = ldexpf(qlin[wave][u][32 * g + 4 * wd + b], e0);
+          for (int mm = 0; mm < m; ++mm) y = (y - from_fp8(to_fp8(y))) * 16.f;
+          word |= to_fp8(y) << (8 * b);
+        }
+        words[wd] = word;
+      }
+      apiece = v8i{(int)words[0], (int)words[1], (int)words[2], (int)words[3],
+                   (int)words[4], (int)words[5], (int)words[6], (int)words[7]};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool mine = u < kQW && row < kQW * kPieces && row / kPieces == u;
+        coef[u][i] = mine ? ldexpf(1.f, -(qexp[wave][u] + 4 * (row % kPieces))) : 0.f;
+      }
+    }
+  }
+
+  // cooperative tile load: thread t moves chunks t / 64 and t / 64 + 4 of key t % 64
   const int64_t last_key = a.n_keys - 1;
+  const int lkey = tid & (kTileTokens - 1), lchunk = tid >> 6;
   auto fetch = [&](int t, v4i& x0, v4i& x1, float& sc) {
     const int64_t base = lo + (int64_t)t * kTileTokens;
-    const int64_t k0 = min(base + (tid >> 3), last_key);
-    const int64_t k1 = min(base + 32 + (tid >> 3), last_key);
-    x0 = *(const v4i*)(a.k + k0 * kDim + ((tid & 7) << 4));
-    x1 = *(const v4i*)(a.k + k1 * kDim + ((tid & 7) << 4));
+    const uint8_t* src = a.k + min(base + lkey, last_key) * kDim + (lchunk << 4);
+    x0 = *(const v4i*)src;
+    x1 = *(const v4i*)(src + 64);
     sc = tid < kTileTokens ? a.k_scale[min(base + tid, last_key)] : 0.f;
   };
-  auto stash = [&](int slot, const v4i& x0, const v4i& x1, float sc) {
-    *(v4i*)(&tile[slot][tile_off(tid >> 3, tid & 7)]) = x0;
-    *(v4i*)(&tile[slot][tile_off(32 + (tid >> 3), tid & 7)]) = x1;
+  auto stash = [&](int t, const v4i& x0, const v4i& x1, float sc) {
+    const int slot = t % kSlots;
+    *(v4i*)(&tile[slot][tile_off(lkey, lchunk)]) = x0;
+    *(v4i*)(&tile[slot][tile_off(lkey, lchunk + 4)]) = x1;
     if (tid < kTileTokens) tscale[slot][tid] = sc;
+  };
+  // B operand of 16-key group j of tile t: key 16j + c16, chunks 2g and 2g + 1
+  auto read_b = [&](int t, int j) -> v8i {
+    const int slot = t % kSlots;
+    const int key = 16 * j + c16;
+    const v4i y0 = *(const v4i*)(&tile[slot][tile_off(key, 2 * g)]);
+    const v4i y1 = *(const v4i*)(&tile[slot][tile_off(key, 2 * g + 1)]);
+    return v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
   };
 
   v4i x0, x1;
@@ -133,42 +229,72 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     fetch(0, x0, x1, xs);
     stash(0, x0, x1, xs);
   }
+  if (ntiles > 1) {
+    fetch(1, x0, x1, xs);
+    stash(1, x0, x1, xs);
+  }
   __syncthreads();
+  // Per tile, the four 16-key groups are software-pipelined in source order: the 9
+  // MFMAs of group j are written before the FMAs of group j - 1, so the FMAs can
+  // consume results that are already complete while the matrix core works.
+  v4f ra[9], rb[9];
+  auto mfmas = [&](v4f (&r)[9], const v8i& kb) {
+    r[0] = mfma_fp8_fp8(apiece, kb, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int h = 0; h < 4; ++h) r[1 + h] = mfma_fp8_fp8(qa[0][h], kb, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int h = 0; h < 4; ++h) r[5 + h] = mfma_fp8_fp8(qa[kQW - 1][h], kb, v4f{0.f, 0.f, 0.f, 0.f});
+  };
+  auto epilogue = [&](const v4f (&r)[9], float& p0, float& p1) {
+    p0 = 0.f;
+    p1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p0 = fmaf(coef[0][i], r[0][i], p0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p1 = fmaf(coef[1][i], r[0][i], p1);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p0 = fmaf(wr[0][h][i], fabsf(r[1 + h][i]), p0);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p1 = fmaf(wr[kQW - 1][h][i], fabsf(r[5 + h][i]), p1);
+  };
+  v8i kb_next = read_b(0, 0);
   for (int t = 0; t < ntiles; ++t) {
-    const int slot = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1, x0, x1, xs);
-    // B operands of the four 16-key tiles: key 16j + c16, chunks 2g and 2g + 1
-    v8i kb[4];
+    if (t + 2 < ntiles) fetch(t + 2, x0, x1, xs);
+    const int64_t t0 = lo + (int64_t)t * kTileTokens;
+    const bool act0 = qv[0] && t0 < qe[0] && t0 + kTileTokens > qs[0];
+    const bool act1 = qv[1] && t0 < qe[1] && t0 + kTileTokens > qs[1];
+    const float sc = 0.5f * tscale[t % kSlots][lane];
+    float p[2][4];
+    v8i kb = kb_next;
+    kb_next = read_b(t, 1);
+    mfmas(ra, kb);
+    kb = kb_next;
+    kb_next = read_b(t, 2);
+    mfmas(rb, kb);
+    epilogue(ra, p[0][0], p[1][0]);
+    kb = kb_next;
+    kb_next = read_b(t, 3);
+    mfmas(ra, kb);
+    epilogue(rb, p[0][1], p[1][1]);
+    kb = kb_next;
+    // the first 16 keys of tile t + 1 (already visible)
+    if (t + 1 < ntiles) kb_next = read_b(t + 1, 0);
+    mfmas(rb, kb);
+    epilogue(ra, p[0][2], p[1][2]);
+    epilogue(rb, p[0][3], p[1][3]);
+    const int64_t key = t0 + lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = 16 * j + c16;
-      const v4i y0 = *(const v4i*)(&tile[slot][tile_off(key, 2 * g)]);
-      const v4i y1 = *(const v4i*)(&tile[slot][tile_off(key, 2 * g + 1)]);
-      kb[j] = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    for (int u = 0; u < kQW; ++u) {
+      const float v = sum_lane_groups(p[u][0], p[u][1], p[u][2], p[u][3]) * sc;
+      if ((u == 0 ? act0 : act1) && key >= qs[u] && key < qe[u])
+        __builtin_nontemporal_store(v, &a.logits[(int64_t)(q0 + kQW * wave + u) * a.ld + (key - qs[u])]);
     }
-    const float sc = tscale[slot][lane];
-    const int64_t key = lo + (int64_t)t * kTileTokens + lane;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!qv[u]) continue;
-      if (lo + (int64_t)t * kTileTokens >= qe[u] || lo + (int64_t)(t + 1) * kTileTokens <= qs[u]) continue;
-      float p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = 0.f;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const v4f s = mfma_fp8_fp8(qa[u][h], kb[j], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[j] = fmaf(wr[u][h][i], relu(s[i]), p[j]);
-        }
-      }
-      const float v = sum_lane_groups(p[0], p[1], p[2], p[3]) * sc;
-      const int r = q0 + 2 * wave + u;
-      if (key >= qs[u] && key < qe[u]) a.logits[(int64_t)r * a.ld + (key - qs[u])] = v;
-    }
-    // slot ^ 1 was last read in iteration t - 1, before the barrier that ended it
-    if (t + 1 < ntiles) stash(slot ^ 1, x0, x1, xs);
+    // slot (t + 2) % 3 last held tile t - 1, whose reads all finished in iteration t - 1
+    if (t + 2 < ntiles) stash(t + 2, x0, x1, xs);
     __syncthreads();
   }
 
@@ -176,9 +302,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (!qv[u]) continue;
-    const int r = q0 + 2 * wave + u;
-    float* out = a.logits + (int64_t)r * a.ld;
-    for (int64_t c = (qe[u] - qs[u]) + lane; c < a.ld; c += kWave) out[c] = -__builtin_inff();
+    float* out = a.logits + (int64_t)(q0 + kQW * wave + u) * a.ld;
+    for (int64_t c = (qe[u] - qs[u]) + lane; c < a.ld; c += kWave) __builtin_nontemporal_store(-__builtin_inff(), &out[c]);
   }
 }
 
