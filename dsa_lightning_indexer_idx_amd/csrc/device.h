@@ -94,14 +94,19 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Wave-wide inclusive prefix sum (lane order).
+// Wave-wide inclusive prefix sum (lane order): a scan inside each 16-lane row with
+// DPP row shifts (lanes without a source add 0), then the row totals, read from lanes
+// 15, 31 and 47, added to the rows above them.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = lane_id() >> 4;
+  v += (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
   return v;
 }
 

@@ -4,27 +4,28 @@
 // Selection key. Every entry gets a 64-bit key: the order-preserving image of its
 // fp32 score in the high word and the bitwise complement of its column in the low
 // word, so "larger key" means "higher score, then lower column" and no two entries
-// tie. The k winners are exactly the keys >= the k-th largest key T, found by
-// MSB-first radix select with 8-bit digits (LDS histograms); the passes over the
-// column word run only when score ties straddle the cut. The winners are then
-// bitonic-sorted into selection order.
+// tie. The k winners are exactly the keys >= the k-th largest key.
+//
+// Both paths first build a 12-bit histogram of the value keys, which fixes the bin
+// that holds the k-th largest entry (the "cut" bin): every entry above it is a
+// winner, entries below it are not, and only the entries in the cut bin (the
+// candidates) need a closer look. The missing winners are found among the candidates
+// by MSB-first radix select with 8-bit digits, starting below the 12 bits the bin
+// already fixes; ties between equal scores are settled by the column word. This is
+// the sampled-filtering idea of the persistent top-k on the pages with an exact
+// histogram instead of a sample, so the cut estimate is never wrong.
 //
 // Short rows (n_cols <= kShortRow) take one workgroup per row with the row's value
-// keys cached in LDS, so the row is read from memory once.
+// keys cached in LDS, so the row is read from memory once. Long rows use the whole
+// chip: segments of every row add into a global row histogram (hist), then every
+// segment streams out its winners and candidates (filter), then one workgroup per
+// row selects among the candidates and writes the row (finish). A cut bin with more
+// candidates than the lists hold (e.g. a row of equal scores) is resolved by radix
+// passes over the whole row instead.
 //
-// Long rows use the whole chip. The cutoff is estimated from the scores themselves
-// (the sampled-filtering idea of the persistent top-k on the pages, here with an
-// exact histogram instead of a sample, so the estimate is never wrong):
-//   1. hist:   segments of every row build 12-bit histograms of their value keys
-//              in LDS and add the non-empty bins into the row's histogram;
-//   2. filter: every segment reads the row histogram, finds the bin holding the
-//              k-th largest value, and streams out the entries above that bin
-//              (certain winners) and the entries in it (candidates), with one
-//              atomic per wave for each list;
-//   3. finish: one workgroup per row loads the candidates into LDS, radix-selects
-//              the missing winners among them, sorts and writes the row. If the
-//              cut bin held more candidates than the workspace keeps (e.g. a row
-//              of equal scores) the row is selected from memory instead.
+// Sorted output is ordered by a bitonic network over registers: strides inside a
+// thread compare registers, strides inside a wave exchange through DPP and
+// permlane moves, and only strides across waves go through LDS.
 #include "device.h"
 #include "launch.h"
 
@@ -35,9 +36,12 @@ namespace dsaidx {
 
 constexpr int kMaxK = 2048;
 constexpr int kShortRow = 16384;       // rows up to this width take the one-kernel path
-constexpr int kHistBits = 12;          // bins of the long-row histogram
+constexpr int kHistBits = 12;          // bins of the value histogram
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kCandCap = 8192;         // candidates kept per row in the workspace
+constexpr int kBinShift = 32 - kHistBits;  // bin of a 32-bit value key
+constexpr int kKeyBinShift = 64 - kHistBits;  // bin of a 64-bit selection key
+constexpr int kCandCap = 8192;         // long rows: candidates kept per row in the workspace
+constexpr int kShortCandCap = 2 * kHistBins;  // short rows: candidate columns (u16) over the histogram
 constexpr int kSegThreads = 256;
 constexpr int kFinishThreads = 1024;
 constexpr int kShortThreads = 512;
@@ -58,22 +62,58 @@ __device__ __forceinline__ int64_t row_len(const TopkCall& a, int r) {
   return n;
 }
 
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Appends item[j] for every take[j] of every lane (U entries per lane) to an LDS list
+// with one LDS atomic per wave; entries past cap are dropped (callers size the lists
+// or detect the overflow from the count). Every lane of the wave must call it.
+template <int U, class T>
+__device__ __forceinline__ void wave_append(const bool (&take)[U], const T (&item)[U], T* list, uint32_t* count,
+                                            uint32_t cap) {
+  uint64_t m[U];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    m[j] = __ballot(take[j]);
+    tot += (uint32_t)__popcll(m[j]);
+  }
+  if (tot == 0) return;
+  uint32_t base = 0;
+  if (lane_id() == 0) base = atomicAdd(count, tot);
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    if (take[j]) {
+      const uint32_t slot = base + lanes_below(m[j]);
+      if (slot < cap) list[slot] = item[j];
+    }
+    base += (uint32_t)__popcll(m[j]);
+  }
+}
+
+// ------------------------------------------------------------------ radix select
+
 struct RadixShared {
   uint32_t hist[256];
   uint64_t prefix;
   uint32_t krem, stop, total;
 };
 
-// Block-wide: the smallest threshold T such that exactly ``want`` of the (unique,
-// non-zero) keys produced by get(i), i < n, are >= T. Needs 1 <= want <= number of
-// non-zero keys. Every thread of the block must call it.
+// Block-wide: among the non-zero keys get(i), i < n, whose bits at and above `top`
+// equal those of `prefix`, the smallest key T such that exactly `want` of them are
+// >= T. Keys are unique; needs 1 <= want <= the number of such keys. Every thread of
+// the block must call it.
 template <int NT, class Get>
-__device__ uint64_t radix_threshold(const Get& get, int64_t n, uint32_t want, RadixShared& sh) {
+__device__ uint64_t radix_threshold(const Get& get, int64_t n, uint32_t want, RadixShared& sh, uint64_t prefix = 0,
+                                    int top = 64) {
   const int tid = threadIdx.x;
-  uint64_t prefix = 0, mask = 0;
+  uint64_t mask = top >= 64 ? 0ull : ~0ull << top;
+  prefix &= mask;
   uint32_t krem = want;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
+  while (top > 0) {
+    const int shift = top > 8 ? top - 8 : 0;  // the last digit may overlap fixed bits
     for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
     if (tid == 0) sh.stop = 0;
     __syncthreads();
@@ -109,7 +149,8 @@ __device__ uint64_t radix_threshold(const Get& get, int64_t n, uint32_t want, Ra
     prefix = sh.prefix;
     krem = sh.krem;
     const uint32_t stop = sh.stop;
-    mask |= (uint64_t)255u << shift;
+    mask = ~0ull << shift;
+    top = shift;
     __syncthreads();  // all threads have read the decision before the next pass resets it
     if (stop) break;
   }
@@ -131,34 +172,200 @@ __device__ uint32_t count_present(const Get& get, int64_t n, RadixShared& sh) {
   return t;
 }
 
-// Block-wide descending bitonic sort of sel[0, cnt) (cnt <= kMaxK).
-template <int NT>
-__device__ void sort_desc(uint64_t* sel, int cnt) {
-  int P = 1;
-  while (P < cnt) P <<= 1;
-  if (cnt <= 1) return;
-  for (int i = cnt + threadIdx.x; i < P; i += NT) sel[i] = 0ull;
+// Block-wide: appends item(i) to list (LDS, at *count) for every i < n whose key get(i)
+// is non-zero and >= thr.
+template <int NT, class T, class Get, class Item>
+__device__ void gather_at_least(const Get& get, const Item& item, int64_t n, uint64_t thr, T* list, uint32_t* count,
+                                uint32_t cap) {
+  for (int64_t b = 0; b < n; b += NT) {
+    const int64_t i = b + threadIdx.x;
+    const uint64_t key = i < n ? get(i) : 0ull;
+    const bool take[1] = {key != 0 && key >= thr};
+    const T it[1] = {take[0] ? item(i) : T(0)};
+    wave_append<1>(take, it, list, count, cap);
+  }
   __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < (P >> 1); t += NT) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t x = sel[lo], y = sel[hi];
-        if ((x < y) == desc) {
-          sel[lo] = y;
-          sel[hi] = x;
-        }
+}
+
+// ------------------------------------------------------------------ cut bin
+
+struct CutInfo {
+  int bin;          // bin of the k-th largest entry; -1: at most k entries, all selected
+  uint32_t above;   // entries in higher bins
+  uint32_t count;   // entries in the cut bin
+  uint32_t total;   // present entries
+  uint32_t sums[16];
+};
+
+// Block-wide, over a kHistBins-bin histogram h (LDS or global memory).
+template <int NT>
+__device__ void find_cut(const uint32_t* h, int k, CutInfo& ci) {
+  constexpr int per = kHistBins / NT;
+  constexpr int waves = NT / kWave;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  // thread t owns bins kHistBins-1-per*t down to kHistBins-per*(t+1), highest first
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) c += h[kHistBins - 1 - per * tid - j];
+  uint32_t incl = wave_inclusive_sum(c);
+  if (lane_id() == kWave - 1) ci.sums[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < waves; ++w) {
+    const uint32_t s = ci.sums[w];
+    off += w < wave ? s : 0u;
+    total += s;
+  }
+  incl += off;
+  const uint32_t excl = incl - c;
+  if (tid == 0) {
+    ci.total = total;
+    if (total <= (uint32_t)k) {
+      ci.bin = -1;
+      ci.above = total;
+      ci.count = 0;
+    }
+  }
+  if (total > (uint32_t)k && excl < (uint32_t)k && (uint32_t)k <= incl) {
+    uint32_t cum = excl;
+    for (int j = 0; j < per; ++j) {
+      const int b = kHistBins - 1 - per * tid - j;
+      const uint32_t hb = h[b];
+      if (cum + hb >= (uint32_t)k) {
+        ci.bin = b;
+        ci.above = cum;
+        ci.count = hb;
+        break;
       }
-      __syncthreads();
+      cum += hb;
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ sorting
+
+// x from lane (lane ^ (1 << lb)), lb = 0..5, through DPP / permlane moves (no LDS).
+// The swaps return, for both operands equal to x, the even (first) and odd (second)
+// 16-lane rows or 32-lane halves duplicated, so the partner's value is the one of the
+// other parity.
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lb) {
+  switch (lb) {
+    case 0:  // quad_perm [1,0,3,2]
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+    case 1:  // quad_perm [2,3,0,1]
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+    case 2: {  // row_half_mirror (l ^ 7), then quad_perm [3,2,1,0] (l ^ 3)
+      const int y = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, false);
+    }
+    case 3: {  // row_mirror (l ^ 15), then row_half_mirror (l ^ 7)
+      const int y = __builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, false);
+    }
+    case 4: {
+      const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      return (lane_id() & 16) ? s[0] : s[1];
+    }
+    default: {
+      const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      return (lane_id() & 32) ? s[0] : s[1];
     }
   }
 }
 
-// Block-wide: write row r's output from sel[0, cnt) (k slots, -1 / -inf padding).
-template <int NT>
-__device__ void write_row(const TopkCall& a, int r, const uint64_t* sel, int cnt) {
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t x, int lb) {
+  const uint32_t lo = xor_lane((uint32_t)x, lb), hi = xor_lane((uint32_t)(x >> 32), lb);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// Block-wide descending bitonic sort of the NT * E keys x[e] of element tid * E + e.
+// xch: LDS exchange buffer of NT * E keys (used only when NT > kWave); the first use
+// is preceded by a barrier, so it may alias LDS the block was reading before the call.
+template <int NT, int E>
+__device__ void sort_desc(uint64_t (&x)[E], uint64_t* xch) {
+  constexpr int LE = ilog2(E);
+  constexpr int LP = ilog2(NT * E);
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m = 1; m <= LP; ++m) {  // merges of 2^m elements
+#pragma unroll
+    for (int b = m - 1; b >= 0; --b) {  // compare elements 2^b apart
+      if (b < LE) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & (1 << b)) continue;
+          const int f = e | (1 << b);
+          const bool desc = m < LE ? !((e >> m) & 1) : !((tid >> (m - LE)) & 1);
+          const uint64_t hi = x[e] > x[f] ? x[e] : x[f];
+          const uint64_t lo = x[e] > x[f] ? x[f] : x[e];
+          x[e] = desc ? hi : lo;
+          x[f] = desc ? lo : hi;
+        }
+      } else {
+        const int tb = b - LE;  // the stride as a thread-index bit
+        const bool take_max = (((tid >> tb) & 1) != 0) != !((tid >> (m - LE)) & 1);
+        uint64_t y[E];
+        if (tb < 6) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) y[e] = xor_lane64(x[e], tb);
+        } else {
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) xch[tid * E + e] = x[e];
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) y[e] = xch[(tid ^ (1 << tb)) * E + e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = (x[e] > y[e]) == take_max ? x[e] : y[e];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ output
+
+__device__ __forceinline__ int32_t out_index(const TopkCall& a, const int32_t* cand_row, int64_t col) {
+  if (!cand_row) return (int32_t)col;
+  return (int32_t)((int64_t)cand_row[col / a.block] * a.block + col % a.block);
+}
+
+// Block-wide: positions tid * E + e of row r from sorted keys (key 0: padding), and
+// -1 / -inf for the positions past NT * E.
+template <int NT, int E>
+__device__ void write_sorted(const TopkCall& a, int r, const uint64_t (&x)[E]) {
+  int32_t* oi = a.out_idx + (int64_t)r * a.out_ld;
+  float* ov = a.out_val ? a.out_val + (int64_t)r * a.out_ld : nullptr;
+  const int32_t* cand_row = a.cand ? a.cand + (int64_t)r * a.cand_ld : nullptr;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = threadIdx.x * E + e;
+    if (i < a.k) {
+      int32_t idx = -1;
+      float val = -__builtin_inff();
+      if (x[e]) {
+        idx = out_index(a, cand_row, key_col(x[e]));
+        val = key_value((uint32_t)(x[e] >> 32));
+      }
+      oi[i] = idx;
+      if (ov) ov[i] = val;
+    }
+  }
+  for (int i = NT * E + threadIdx.x; i < a.k; i += NT) {
+    oi[i] = -1;
+    if (ov) ov[i] = -__builtin_inff();
+  }
+}
+
+// Block-wide: row r from the selection key(i), i < cnt, in list order (k slots, -1 / -inf
+// padding).
+template <int NT, class Key>
+__device__ void write_list(const TopkCall& a, int r, const Key& key, int cnt) {
   int32_t* oi = a.out_idx + (int64_t)r * a.out_ld;
   float* ov = a.out_val ? a.out_val + (int64_t)r * a.out_ld : nullptr;
   const int32_t* cand_row = a.cand ? a.cand + (int64_t)r * a.cand_ld : nullptr;
@@ -166,87 +373,343 @@ __device__ void write_row(const TopkCall& a, int r, const uint64_t* sel, int cnt
     int32_t idx = -1;
     float val = -__builtin_inff();
     if (i < cnt) {
-      const uint64_t key = sel[i];
-      const int64_t col = key_col(key);
-      val = key_value((uint32_t)(key >> 32));
-      idx = (int32_t)col;
-      if (cand_row) idx = (int32_t)((int64_t)cand_row[col / a.block] * a.block + col % a.block);
+      const uint64_t kk = key(i);
+      idx = out_index(a, cand_row, key_col(kk));
+      val = key_value((uint32_t)(kk >> 32));
     }
     oi[i] = idx;
     if (ov) ov[i] = val;
   }
 }
 
-// Block-wide: append every key >= thr produced by get(i), i < n, to sel starting at
-// *count (an LDS counter).
-template <int NT, class Get>
-__device__ void gather_at_least(const Get& get, int64_t n, uint64_t thr, uint64_t* sel, uint32_t* count) {
-  for (int64_t i = threadIdx.x; i < n; i += NT) {
-    const uint64_t key = get(i);
-    if (key != 0 && key >= thr) {
-      const uint32_t slot = atomicAdd(count, 1u);
-      if (slot < (uint32_t)kMaxK) sel[slot] = key;
-    }
+template <int NT, int E, class Key>
+__device__ void sort_write_e(const TopkCall& a, int r, const Key& key, int cnt, uint64_t* xch) {
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = threadIdx.x * E + e;
+    x[e] = i < cnt ? key(i) : 0ull;
   }
-  __syncthreads();
+  sort_desc<NT, E>(x, xch);
+  write_sorted<NT, E>(a, r, x);
 }
 
-// Full selection of one row read from memory (the short-row kernel without its LDS
-// cache, and the long-row fallback).
-template <int NT, class Get>
-__device__ int select_row(const Get& get, int64_t n, int k, uint64_t* sel, RadixShared& sh, uint32_t* count) {
-  const uint32_t total = count_present<NT>(get, n, sh);
-  const uint32_t keff = min((uint32_t)k, total);
-  const uint64_t thr = keff == 0 ? ~0ull : (keff == total ? 1ull : radix_threshold<NT>(get, n, keff, sh));
-  if (threadIdx.x == 0) *count = 0;
-  __syncthreads();
-  gather_at_least<NT>(get, n, thr, sel, count);
-  return (int)keff;
+// Block-wide: sorts the cnt (<= kMaxK) selected keys key(i) and writes row r; xch
+// holds kMaxK keys.
+template <int NT, class Key>
+__device__ void sort_and_write(const TopkCall& a, int r, const Key& key, int cnt, uint64_t* xch) {
+  static_assert(NT * 4 >= kMaxK, "sort_and_write: at most four keys per thread");
+  if (cnt <= NT) {
+    sort_write_e<NT, 1>(a, r, key, cnt, xch);
+  } else if constexpr (NT * 2 >= kMaxK) {
+    sort_write_e<NT, 2>(a, r, key, cnt, xch);
+  } else {
+    if (cnt <= 2 * NT)
+      sort_write_e<NT, 2>(a, r, key, cnt, xch);
+    else
+      sort_write_e<NT, 4>(a, r, key, cnt, xch);
+  }
+}
+
+// Entries one bucket of the bucket sort may hold; a row with a fuller bucket (many
+// equal or tightly clustered scores) is bitonic-sorted instead.
+constexpr int kBucketCap = 64;
+constexpr int kBuckets = kHistBins;
+
+struct SortShared {
+  unsigned long long kmax, kmin;
+  uint32_t big;
+  uint32_t sums[16];
+};
+
+// Block-wide: writes the cnt (<= kMaxK) selected keys key(i) of row r in selection
+// order. The keys are spread over kBuckets buckets linear in the score between the
+// smallest and the largest selected score (a monotone map, so the buckets are in
+// order); an entry's position is the number of entries in higher buckets plus the
+// number of larger keys in its own bucket. counts: kBuckets words of LDS (kMaxK
+// keys), 16-byte aligned; tmp: kMaxK keys of LDS. Neither may overlap what key(i)
+// reads.
+template <int NT, class Key>
+__device__ void bucket_sort_write(const TopkCall& a, int r, const Key& key, int cnt, uint32_t* counts, uint64_t* tmp,
+                                  SortShared& ss) {
+  constexpr int E = kMaxK / NT;
+  constexpr int per = kBuckets / NT;
+  constexpr int waves = NT / kWave;
+  const int tid = threadIdx.x;
+  if (cnt > 0) {
+    uint64_t x[E];
+    uint64_t mx = 0, mn = ~0ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = e * NT + tid;
+      x[e] = i < cnt ? key(i) : 0ull;
+      if (x[e]) {
+        mx = max(mx, x[e]);
+        mn = min(mn, x[e]);
+      }
+    }
+#pragma unroll
+    for (int lb = 0; lb < 6; ++lb) {
+      mx = max(mx, xor_lane64(mx, lb));
+      mn = min(mn, xor_lane64(mn, lb));
+    }
+    if (tid == 0) {
+      ss.kmax = 0;
+      ss.kmin = ~0ull;
+      ss.big = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < kBuckets; i += NT) counts[i] = 0;
+    if (lane_id() == 0) {
+      atomicMax(&ss.kmax, (unsigned long long)mx);
+      atomicMin(&ss.kmin, (unsigned long long)mn);
+    }
+    __syncthreads();
+    // bucket of a score: (v - lo) * scale, clamped; NaN (only 0 * inf) goes to 0
+    const float lo = key_value((uint32_t)(ss.kmin >> 32));
+    const float d = key_value((uint32_t)(ss.kmax >> 32)) - lo;
+    const float scale = (d > 0.f && d <= 3.0e38f) ? (float)(kBuckets - 0.01) / d : 0.f;
+    int ib[E];
+    uint32_t slot[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      ib[e] = -1;
+      if (x[e]) {
+        const float f = (key_value((uint32_t)(x[e] >> 32)) - lo) * scale;
+        const int b = f >= 1.f ? min((int)f, kBuckets - 1) : 0;
+        ib[e] = kBuckets - 1 - b;  // highest bucket first
+        slot[e] = atomicAdd(&counts[ib[e]], 1u);
+        if (slot[e] >= (uint32_t)kBucketCap) ss.big = 1;
+      }
+    }
+    __syncthreads();
+    if (ss.big) {
+      sort_and_write<NT>(a, r, key, cnt, tmp);
+      return;
+    }
+    // exclusive scan of the bucket counts, in place
+    static_assert(per % 4 == 0, "bucket counts are read four at a time");
+    uint32_t c[per], sum = 0;
+#pragma unroll
+    for (int j = 0; j < per; j += 4) {
+      const uint4 q = ((const uint4*)counts)[per / 4 * tid + j / 4];
+      c[j] = q.x;
+      c[j + 1] = q.y;
+      c[j + 2] = q.z;
+      c[j + 3] = q.w;
+    }
+#pragma unroll
+    for (int j = 0; j < per; ++j) sum += c[j];
+    uint32_t incl = wave_inclusive_sum(sum);
+    if (lane_id() == kWave - 1) ss.sums[tid / kWave] = incl;
+    __syncthreads();
+    uint32_t off = incl - sum;
+#pragma unroll
+    for (int w = 0; w < waves; ++w) off += w < tid / kWave ? ss.sums[w] : 0u;
+#pragma unroll
+    for (int j = 0; j < per; j += 4) {
+      uint4 q;
+      q.x = off;
+      q.y = q.x + c[j];
+      q.z = q.y + c[j + 1];
+      q.w = q.z + c[j + 2];
+      off = q.w + c[j + 3];
+      ((uint4*)counts)[per / 4 * tid + j / 4] = q;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (ib[e] >= 0) tmp[counts[ib[e]] + slot[e]] = x[e];
+    __syncthreads();
+    // rank inside the bucket; the loads of all E entries are issued together
+    uint32_t st[E], len[E], pos[E], most = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      st[e] = ib[e] >= 0 ? counts[ib[e]] : 0u;
+      const uint32_t end = ib[e] < 0 ? 0u : (ib[e] == kBuckets - 1 ? (uint32_t)cnt : counts[ib[e] + 1]);
+      len[e] = ib[e] >= 0 ? end - st[e] : 0u;
+      pos[e] = st[e];
+      most = max(most, len[e]);
+    }
+    for (uint32_t j = 0; j < most; j += 4) {
+      uint64_t v[E][4];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[e][q] = tmp[st[e] + min(j + q, len[e] ? len[e] - 1 : 0u)];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pos[e] += (j + q < len[e]) & (v[e][q] > x[e]);
+    }
+    // the keys in order into LDS (over the counts, read above), then a coalesced row
+    uint64_t* sorted = (uint64_t*)counts;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (ib[e] >= 0) sorted[pos[e]] = x[e];
+    __syncthreads();
+    write_list<NT>(a, r, [&](int i) { return sorted[i]; }, cnt);
+    return;
+  }
+  write_list<NT>(a, r, [&](int i) { return 0ull; }, 0);
+}
+
+// ------------------------------------------------------------------ loads
+
+// Four row entries starting at i (a multiple of 4) of a row of n entries: one 16-byte
+// load when all four exist and the row is 16-byte aligned, -inf past the end. LAST:
+// the last read of the data (a non-temporal load).
+template <bool V4, bool LAST>
+__device__ __forceinline__ float4 load4(const float* row, int64_t i, int64_t n) {
+  if (V4 && i + 4 <= n) {
+    const v4f* p = (const v4f*)(row + i);
+    const v4f x = LAST ? __builtin_nontemporal_load(p) : *p;
+    return make_float4(x[0], x[1], x[2], x[3]);
+  }
+  float4 v;
+  v.x = i < n ? row[i] : -__builtin_inff();
+  v.y = i + 1 < n ? row[i + 1] : -__builtin_inff();
+  v.z = i + 2 < n ? row[i + 2] : -__builtin_inff();
+  v.w = i + 3 < n ? row[i + 3] : -__builtin_inff();
+  return v;
 }
 
 // ------------------------------------------------------------------ short rows
 
+template <bool V4>
 __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkCall a) {
-  extern __shared__ uint32_t vkeys[];  // n_cols value keys
-  __shared__ uint64_t sel[kMaxK];
+  constexpr int NT = kShortThreads;
+  extern __shared__ uint4 dyn[];                 // the row's value keys (n_cols rounded up to 4, at
+                                                 // least kMaxK keys' worth), then the sorted keys
+  uint32_t* vkeys = (uint32_t*)dyn;
+  __shared__ __align__(16) union {
+    uint32_t hist[kHistBins];                    // value histogram, then
+    uint16_t cand[kShortCandCap];                // the cut bin's columns, then the bucket counts
+  } u;
+  __shared__ uint16_t sel[kMaxK];                // selected columns
   __shared__ RadixShared sh;
-  __shared__ uint32_t count;
+  __shared__ CutInfo ci;
+  __shared__ SortShared ss;
+  __shared__ uint32_t n_sel, n_cand;
+  const int tid = threadIdx.x;
   const int r = blockIdx.x;
   const int64_t n = row_len(a, r);
-  const float* row = a.logits + (int64_t)r * a.ld;
-  for (int64_t i = threadIdx.x; i < n; i += kShortThreads) vkeys[i] = order_key(row[i]);
+  for (int i = tid; i < kHistBins; i += NT) u.hist[i] = 0;
+  if (tid == 0) {
+    n_sel = 0;
+    n_cand = 0;
+  }
   __syncthreads();
-  auto get = [&](int64_t i) -> uint64_t {
-    const uint32_t v = vkeys[i];
-    return v ? sel_key(v, i) : 0ull;
+
+  // 1. value keys into LDS and the histogram
+  const float* row = a.logits + (int64_t)r * a.ld;
+  constexpr int U = 4;  // four-entry groups per thread per pass
+  for (int64_t b = 0; b < n; b += (int64_t)NT * 4 * U) {
+    float4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) v[j] = load4<V4, true>(row, b + ((int64_t)j * NT + tid) * 4, n);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t i = b + ((int64_t)j * NT + tid) * 4;
+      if (i < n) {
+        uint4 kk;
+        kk.x = order_key(v[j].x);
+        kk.y = order_key(v[j].y);
+        kk.z = order_key(v[j].z);
+        kk.w = order_key(v[j].w);
+        dyn[i / 4] = kk;
+        if (kk.x) atomicAdd(&u.hist[kk.x >> kBinShift], 1u);
+        if (kk.y) atomicAdd(&u.hist[kk.y >> kBinShift], 1u);
+        if (kk.z) atomicAdd(&u.hist[kk.z >> kBinShift], 1u);
+        if (kk.w) atomicAdd(&u.hist[kk.w >> kBinShift], 1u);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. the cut bin
+  find_cut<NT>(u.hist, a.k, ci);
+  const int cut = ci.bin;
+  const bool compact = ci.count <= (uint32_t)kShortCandCap;
+  const uint32_t keff = min((uint32_t)a.k, ci.total);
+
+  // 3. winners above the cut, candidates in it
+  constexpr int U2 = 8;
+  for (int64_t b = 0; b < n; b += (int64_t)NT * U2) {
+    bool tw[U2], tc[U2];
+    uint16_t col[U2];
+#pragma unroll
+    for (int j = 0; j < U2; ++j) {
+      const int64_t i = b + (int64_t)j * NT + tid;
+      const uint32_t v = i < n ? vkeys[i] : 0u;
+      const int bin = v ? (int)(v >> kBinShift) : -2;
+      tw[j] = bin > cut;
+      tc[j] = compact && bin == cut;
+      col[j] = (uint16_t)i;
+    }
+    wave_append<U2>(tw, col, sel, &n_sel, (uint32_t)kMaxK);
+    wave_append<U2>(tc, col, u.cand, &n_cand, (uint32_t)kShortCandCap);
+  }
+  __syncthreads();
+
+  // 4. the rest of the winners from the cut bin
+  const uint32_t have = n_sel;
+  const uint32_t need = keff - have;
+  if (need > 0) {
+    const uint64_t pre = (uint64_t)cut << kKeyBinShift;
+    if (compact) {
+      const uint32_t nc = n_cand;
+      auto get = [&](int64_t i) -> uint64_t {
+        const uint32_t c = u.cand[i];
+        return sel_key(vkeys[c], c);
+      };
+      const uint64_t thr = need == nc ? 1ull : radix_threshold<NT>(get, nc, need, sh, pre, kKeyBinShift);
+      gather_at_least<NT, uint16_t>(get, [&](int64_t i) { return u.cand[i]; }, nc, thr, sel, &n_sel,
+                                    (uint32_t)kMaxK);
+    } else {
+      auto get = [&](int64_t i) -> uint64_t {
+        const uint32_t v = vkeys[i];
+        return (int)(v >> kBinShift) == cut ? sel_key(v, i) : 0ull;
+      };
+      const uint64_t thr = radix_threshold<NT>(get, n, need, sh, pre, kKeyBinShift);
+      gather_at_least<NT, uint16_t>(get, [&](int64_t i) { return (uint16_t)i; }, n, thr, sel, &n_sel,
+                                    (uint32_t)kMaxK);
+    }
+  }
+  __syncthreads();
+
+  // 5. the row
+  auto key = [&](int i) -> uint64_t {
+    const uint32_t c = sel[i];
+    return sel_key(vkeys[c], c);
   };
-  const int cnt = select_row<kShortThreads>(get, n, a.k, sel, sh, &count);
-  if (a.sorted) sort_desc<kShortThreads>(sel, cnt);
-  write_row<kShortThreads>(a, r, sel, cnt);
+  if (a.sorted)
+    bucket_sort_write<NT>(a, r, key, (int)keff, u.hist, (uint64_t*)dyn, ss);
+  else
+    write_list<NT>(a, r, key, (int)keff);
 }
 
 // ------------------------------------------------------------------ long rows
 
 struct LongWs {
   uint32_t* hist;    // [rows, kHistBins]
-  uint32_t* counts;  // [rows, 2]: certain winners, candidates
+  uint32_t* counts;  // [rows, 2]: winners above the cut, candidates
   uint64_t* win;     // [rows, kMaxK]
   uint64_t* cand;    // [rows, kCandCap]
 };
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
 
 __global__ __launch_bounds__(kSegThreads) void topk_zero_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kSegThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kSegThreads)
     p[i] = 0u;
 }
 
-// Values per thread per pass of the segment loops: independent loads issued together
-// so the loop is not bound by one memory latency per element.
-constexpr int kUnroll = 16;
+// Four-entry groups per thread per pass of the segment loops: independent loads issued
+// together so the loop is not bound by one memory latency per load.
+constexpr int kSegGroups = 4;
+constexpr int kSegStep = kSegThreads * 4 * kSegGroups;
 
+template <bool V4>
 __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(TopkCall a, LongWs ws, int64_t seg, int segs) {
   __shared__ uint32_t hist[kHistBins];
   const int r = (int)(blockIdx.x / (unsigned)segs);
@@ -257,17 +720,18 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(TopkCall a, Long
   for (int i = threadIdx.x; i < kHistBins; i += kSegThreads) hist[i] = 0;
   __syncthreads();
   const float* row = a.logits + (int64_t)r * a.ld;
-  for (int64_t b = s0; b < s1; b += kSegThreads * kUnroll) {
-    float x[kUnroll];
+  for (int64_t b = s0; b < s1; b += kSegStep) {
+    float4 v[kSegGroups];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t i = b + j * kSegThreads + threadIdx.x;
-      x[j] = i < s1 ? row[i] : -__builtin_inff();
-    }
+    for (int j = 0; j < kSegGroups; ++j) v[j] = load4<V4, false>(row, b + ((int64_t)j * kSegThreads + threadIdx.x) * 4, s1);
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const uint32_t v = order_key(x[j]);
-      if (v) atomicAdd(&hist[v >> (32 - kHistBits)], 1u);
+    for (int j = 0; j < kSegGroups; ++j) {
+      const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t key = order_key(e[c]);
+        if (key) atomicAdd(&hist[key >> kBinShift], 1u);
+      }
     }
   }
   __syncthreads();
@@ -276,69 +740,13 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(TopkCall a, Long
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
-// The bin holding the k-th largest value of row r and the number of entries above it;
-// bin -1 means "take every entry".
-__device__ void find_cut(const uint32_t* ghist, int k, int* s_bin, uint32_t* s_above, uint32_t* sums) {
-  constexpr int per = kHistBins / kSegThreads;
-  const int tid = threadIdx.x;
-  // thread t owns bins from the top: kHistBins-1-per*t .. kHistBins-per*(t+1)
-  uint32_t c = 0;
-  for (int j = 0; j < per; ++j) c += ghist[kHistBins - 1 - per * tid - j];
-  // block inclusive scan in thread order (highest bins first)
-  uint32_t incl = wave_inclusive_sum(c);
-  const int wave = tid / kWave;
-  if (lane_id() == kWave - 1) sums[wave] = incl;
-  __syncthreads();
-  uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += sums[w];
-  incl += off;
-  const uint32_t excl = incl - c;
-  uint32_t total = 0;
-  for (int w = 0; w < kSegThreads / kWave; ++w) total += sums[w];
-  if (tid == 0 && total <= (uint32_t)k) {
-    *s_bin = -1;
-    *s_above = 0;
-  }
-  if (total > (uint32_t)k && excl < (uint32_t)k && (uint32_t)k <= incl) {
-    uint32_t cum = excl;
-    for (int j = 0; j < per; ++j) {
-      const int b = kHistBins - 1 - per * tid - j;
-      const uint32_t h = ghist[b];
-      if (cum + h >= (uint32_t)k) {
-        *s_bin = b;
-        *s_above = cum;
-        break;
-      }
-      cum += h;
-    }
-  }
-  __syncthreads();
-}
-
 // Candidates one filter workgroup stages in LDS; a segment with more forces its row
-// onto the full-row fallback (the candidate count is pushed past kCandCap).
+// onto the full-row path (the candidate count is pushed past kCandCap).
 constexpr int kSegCandCap = 4096;
 
-// Appends key to an LDS list through one LDS atomic per wave; returns nothing, drops
-// entries past cap (the caller detects the overflow from the final count).
-__device__ __forceinline__ void wave_append(bool take, uint64_t key, uint64_t* list, uint32_t* count,
-                                            uint32_t cap) {
-  const uint64_t m = __ballot(take);
-  if (!m) return;
-  const int leader = __builtin_ctzll(m);
-  uint32_t base = 0;
-  if (lane_id() == leader) base = atomicAdd(count, (uint32_t)__popcll(m));
-  base = __shfl(base, leader, kWave);
-  if (take) {
-    const uint32_t slot = base + lanes_below(m);
-    if (slot < cap) list[slot] = key;
-  }
-}
-
+template <bool V4>
 __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, LongWs ws, int64_t seg, int segs) {
-  __shared__ uint32_t sums[kSegThreads / kWave];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_above;
+  __shared__ CutInfo ci;
   __shared__ uint64_t lwin[kMaxK];
   __shared__ uint64_t lcand[kSegCandCap];
   __shared__ uint32_t n_lwin, n_lcand, base_win, base_cand;
@@ -351,26 +759,33 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, Lo
     n_lwin = 0;
     n_lcand = 0;
   }
-  find_cut(ws.hist + (int64_t)r * kHistBins, a.k, &s_bin, &s_above, sums);
-  const int cut = s_bin;
+  find_cut<kSegThreads>(ws.hist + (int64_t)r * kHistBins, a.k, ci);
+  const int cut = ci.bin;
+  // a cut bin too large for the workspace is resolved from the row itself
+  const bool keep_cand = ci.count <= (uint32_t)kCandCap;
   const float* row = a.logits + (int64_t)r * a.ld;
   // every thread runs the same number of iterations so whole waves vote together
-  for (int64_t b = s0; b < s1; b += kSegThreads * kUnroll) {
-    float x[kUnroll];
+  for (int64_t b = s0; b < s1; b += kSegStep) {
+    float4 v[kSegGroups];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t i = b + j * kSegThreads + threadIdx.x;
-      x[j] = i < s1 ? row[i] : -__builtin_inff();
-    }
+    for (int j = 0; j < kSegGroups; ++j) v[j] = load4<V4, true>(row, b + ((int64_t)j * kSegThreads + threadIdx.x) * 4, s1);
+    bool tw[4 * kSegGroups], tc[4 * kSegGroups];
+    uint64_t key[4 * kSegGroups];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t i = b + j * kSegThreads + threadIdx.x;
-      const uint32_t v = order_key(x[j]);
-      const int bin = v ? (int)(v >> (32 - kHistBits)) : -2;
-      const uint64_t key = sel_key(v, i);
-      wave_append(v && bin > cut, key, lwin, &n_lwin, kMaxK);
-      wave_append(v && bin == cut, key, lcand, &n_lcand, kSegCandCap);
+    for (int j = 0; j < kSegGroups; ++j) {
+      const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      const int64_t i0 = b + ((int64_t)j * kSegThreads + threadIdx.x) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t vk = order_key(e[c]);
+        const int bin = vk ? (int)(vk >> kBinShift) : -2;
+        tw[4 * j + c] = bin > cut;
+        tc[4 * j + c] = keep_cand && bin == cut;
+        key[4 * j + c] = sel_key(vk, i0 + c);
+      }
     }
+    wave_append<4 * kSegGroups>(tw, key, lwin, &n_lwin, (uint32_t)kMaxK);
+    wave_append<4 * kSegGroups>(tc, key, lcand, &n_lcand, (uint32_t)kSegCandCap);
   }
   __syncthreads();
   uint32_t* cnt = ws.counts + 2 * (int64_t)r;
@@ -378,23 +793,27 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, Lo
   const uint32_t nc = n_lcand;
   if (threadIdx.x == 0) {
     base_win = nw ? atomicAdd(&cnt[0], nw) : 0u;
-    // an overflowing segment pushes the row's count past the cap: full-row fallback
-    base_cand = nc ? atomicAdd(&cnt[1], nc > (uint32_t)kSegCandCap ? (uint32_t)kCandCap + 1u : nc) : 0u;
+    // an overflowing segment, or a cut bin too large to keep, pushes the row's count
+    // past the cap: the finish kernel then works from the row itself
+    const bool over = !keep_cand || nc > (uint32_t)kSegCandCap;
+    base_cand = over ? atomicAdd(&cnt[1], (uint32_t)kCandCap + 1u) : (nc ? atomicAdd(&cnt[1], nc) : 0u);
   }
   __syncthreads();
   uint64_t* win = ws.win + (int64_t)r * kMaxK;
   uint64_t* cand = ws.cand + (int64_t)r * kCandCap;
   for (uint32_t i = threadIdx.x; i < nw; i += kSegThreads)
     if (base_win + i < (uint32_t)kMaxK) win[base_win + i] = lwin[i];
-  if (nc <= (uint32_t)kSegCandCap)
+  if (keep_cand && nc <= (uint32_t)kSegCandCap)
     for (uint32_t i = threadIdx.x; i < nc; i += kSegThreads)
       if (base_cand + i < (uint32_t)kCandCap) cand[base_cand + i] = lcand[i];
 }
 
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(TopkCall a, LongWs ws) {
+  constexpr int NT = kFinishThreads;
   __shared__ uint64_t sel[kMaxK];
-  __shared__ uint64_t cand[kCandCap];
+  __shared__ __align__(16) uint64_t cand[kCandCap];  // then the sort's bucket counts and keys
   __shared__ RadixShared sh;
+  __shared__ SortShared ss;
   __shared__ uint32_t count;
   const int r = blockIdx.x;
   const int64_t n = row_len(a, r);
@@ -404,29 +823,42 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(TopkCall a,
   if (n_cand <= (uint32_t)kCandCap) {
     const uint64_t* gw = ws.win + (int64_t)r * kMaxK;
     const uint64_t* gc = ws.cand + (int64_t)r * kCandCap;
-    for (uint32_t i = threadIdx.x; i < n_win; i += kFinishThreads) sel[i] = gw[i];
-    for (uint32_t i = threadIdx.x; i < n_cand; i += kFinishThreads) cand[i] = gc[i];
+    for (uint32_t i = threadIdx.x; i < n_win; i += NT) sel[i] = gw[i];
+    for (uint32_t i = threadIdx.x; i < n_cand; i += NT) cand[i] = gc[i];
     if (threadIdx.x == 0) count = n_win;
     __syncthreads();
     // every present entry is a winner or a candidate, so the winners still missing are
-    // min(k, total) - n_win and they all come from the candidates
+    // min(k, total) - n_win and they all come from the candidates, which share the bits
+    // of the cut bin
     const uint32_t need = min((uint32_t)a.k - n_win, n_cand);
     auto get = [&](int64_t i) -> uint64_t { return cand[i]; };
     if (need > 0) {
-      const uint64_t thr = need == n_cand ? 1ull : radix_threshold<kFinishThreads>(get, n_cand, need, sh);
-      gather_at_least<kFinishThreads>(get, n_cand, thr, sel, &count);
+      const uint64_t pre = cand[0];
+      const uint64_t thr = need == n_cand ? 1ull : radix_threshold<NT>(get, n_cand, need, sh, pre, kKeyBinShift);
+      gather_at_least<NT, uint64_t>(get, get, n_cand, thr, sel, &count, (uint32_t)kMaxK);
     }
     cnt = (int)(n_win + need);
   } else {
+    // the cut bin did not fit the lists: select from the row itself
     const float* row = a.logits + (int64_t)r * a.ld;
     auto get = [&](int64_t i) -> uint64_t {
       const uint32_t v = order_key(row[i]);
       return v ? sel_key(v, i) : 0ull;
     };
-    cnt = select_row<kFinishThreads>(get, n, a.k, sel, sh, &count);
+    const uint32_t total = count_present<NT>(get, n, sh);
+    const uint32_t keff = min((uint32_t)a.k, total);
+    const uint64_t thr = keff == 0 ? ~0ull : (keff == total ? 1ull : radix_threshold<NT>(get, n, keff, sh));
+    if (threadIdx.x == 0) count = 0;
+    __syncthreads();
+    gather_at_least<NT, uint64_t>(get, get, n, thr, sel, &count, (uint32_t)kMaxK);
+    cnt = (int)keff;
   }
-  if (a.sorted) sort_desc<kFinishThreads>(sel, cnt);
-  write_row<kFinishThreads>(a, r, sel, cnt);
+  __syncthreads();
+  auto key = [&](int i) -> uint64_t { return sel[i]; };
+  if (a.sorted)
+    bucket_sort_write<NT>(a, r, key, cnt, (uint32_t*)cand, cand + kBuckets / 2, ss);
+  else
+    write_list<NT>(a, r, key, cnt);
 }
 
 // ------------------------------------------------------------------ host side
@@ -440,20 +872,32 @@ size_t topk_workspace_bytes(int rows, int64_t n_cols) {
                   R * kCandCap * 8);
 }
 
+template <bool V4>
+static hipError_t launch_short(const TopkCall& c, hipStream_t stream) {
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute((const void*)topk_short_kernel<V4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kShortRow * (int)sizeof(uint32_t));
+  });
+  if (attr != hipSuccess) return attr;
+  const size_t lds = (size_t)std::max<int64_t>(round_up(c.n_cols, 4) * 4, kMaxK * 8);
+  hipLaunchKernelGGL(topk_short_kernel<V4>, dim3((unsigned)c.rows), dim3(kShortThreads), lds, stream, c);
+  return hipGetLastError();
+}
+
+template <bool V4>
+static void launch_long(const TopkCall& c, const LongWs& ws, int64_t seg, int64_t segs, hipStream_t stream) {
+  dim3 grid((unsigned)(segs * c.rows));
+  hipLaunchKernelGGL(topk_hist_kernel<V4>, grid, dim3(kSegThreads), 0, stream, c, ws, seg, (int)segs);
+  hipLaunchKernelGGL(topk_filter_kernel<V4>, grid, dim3(kSegThreads), 0, stream, c, ws, seg, (int)segs);
+}
+
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   if (c.rows <= 0) return hipSuccess;
-  if (c.n_cols <= kShortRow) {
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    std::call_once(once, [] {
-      attr = hipFuncSetAttribute((const void*)topk_short_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 kShortRow * (int)sizeof(uint32_t));
-    });
-    if (attr != hipSuccess) return attr;
-    const size_t lds = (size_t)(c.n_cols > 0 ? c.n_cols : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL(topk_short_kernel, dim3((unsigned)c.rows), dim3(kShortThreads), lds, stream, c);
-    return hipGetLastError();
-  }
+  // rows start on 16-byte boundaries: whole groups of four are read with one load
+  const bool v4 = ((uintptr_t)c.logits % 16 == 0) && (c.ld % 4 == 0);
+  if (c.n_cols <= kShortRow) return v4 ? launch_short<true>(c, stream) : launch_short<false>(c, stream);
   const int64_t R = c.rows;
   uint8_t* p = (uint8_t*)workspace;
   LongWs ws;
@@ -468,14 +912,16 @@ hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   const int64_t nz = (int64_t)((uint8_t*)ws.win - (uint8_t*)workspace) / 4;
   hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)std::min<int64_t>((nz + kSegThreads - 1) / kSegThreads, 1024)),
                      dim3(kSegThreads), 0, stream, (uint32_t*)workspace, nz);
-  // about four segment workgroups per compute unit over all rows
+  // about four segment workgroups per compute unit over all rows; segments are whole
+  // passes of the segment loop
   const int cus = device_cu_count();
   int64_t segs = (4 * (int64_t)cus + R - 1) / R;
-  int64_t seg = round_up((c.n_cols + segs - 1) / segs, 1024);
+  const int64_t seg = round_up((c.n_cols + segs - 1) / segs, kSegStep);
   segs = (c.n_cols + seg - 1) / seg;
-  dim3 grid((unsigned)(segs * R));
-  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kSegThreads), 0, stream, c, ws, seg, (int)segs);
-  hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kSegThreads), 0, stream, c, ws, seg, (int)segs);
+  if (v4)
+    launch_long<true>(c, ws, seg, segs, stream);
+  else
+    launch_long<false>(c, ws, seg, segs, stream);
   hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)R), dim3(kFinishThreads), 0, stream, c, ws);
   return hipGetLastError();
 }
