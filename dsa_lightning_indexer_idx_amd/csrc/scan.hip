@@ -3,16 +3,20 @@
 //
 // Work split: an item is (row, chunk of positions); waves take items in a
 // grid-stride loop. A wave scores 64 positions per step:
-//   * each lane loads the 32 K-elements of block (lane / 16) for the token at
-//     column lane % 16 of each of the four 16-token tiles (coalesced 16-byte loads;
-//     the four lane groups together read each 128-byte fp8 key row once),
+//   * each lane loads 32 K-elements of block (lane / 16) for the token at column
+//     lane % 16 of each of the four 16-token tiles (16-byte loads; the four lane
+//     groups together read each key row once, each load instruction whole 64-byte
+//     halves of 16 rows),
 //   * 16 MFMAs (4 head tiles x 4 token tiles) give S[head, token] = q_head . k,
 //   * each lane applies ReLU and its 16 head weights in registers, three lane
 //     swaps finish the 64-head sum, and lane l holds the score of position l,
 //   * the fp8 per-token scale multiplies after the head sum (scales are >= 0, so
 //     ReLU(scale * x) = scale * ReLU(x)); MXFP4 group scales enter the MFMA itself,
-//   * one 256-byte store per step writes 64 scores (-inf where the position is
-//     not scored).
+//   * the 64 scores (-inf where the position is not scored) go to the wave's LDS
+//     slice; the item's scores leave in 1 KiB stores once it is done, so score
+//     stores do not interleave with the key stream.
+// The keys of step s + 1 load while step s computes (two register sets), and every
+// item first touches all of its pages so their address translations arrive together.
 #include "device.h"
 #include "launch.h"
 
@@ -145,28 +149,15 @@ struct QOps;
 template <int F>
 struct KOps;
 
-// fp8 q against fp8 keys: head tile h, lane l -> q[16h + l%16][32g .. 32g+31] (the
-// keys use the same K order, so the pairing is right whatever the hardware order).
-template <>
-struct QOps<FMT_FP8> {
-  v8i a[4];
-  __device__ void load(const uint8_t* q, int r, int lane) {
-    const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const v4i* p = (const v4i*)(q + ((int64_t)r * kHeads + 16 * h + c) * kDim + 32 * g);
-      v4i lo = p[0], hi = p[1];
-      a[h] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-  }
-};
-// fp8 q against MXFP4 keys. Here the K order matters: the fp4 operand of lane
-// group g holds elements 32g .. 32g+31 (one UE8M0 group) while the 8-bit operand of
-// lane group g holds K = 16g .. 16g+15 in its low 16 bytes and K = 64+16g .. 64+16g+15
-// in its high 16 bytes (measured on gfx950 with one-hot inputs). So q dims are
-// loaded in that order.
-template <>
-struct QOps<FMT_MXFP4> {
+// fp8 q, head tile h, lane l: row 16h + l%16, dims 16g .. 16g+15 and 64+16g ..
+// 64+16g+15 (g = l / 16), which is the 8-bit operand's own K order (measured on gfx950
+// with one-hot inputs). Against fp8 keys any K order shared by both operands would
+// do; this one lets each key load instruction read whole 64-byte halves of the key
+// rows. Against MXFP4 keys it is required: the fp4 operand of lane group g holds
+// dims 32g .. 32g+31 (one UE8M0 group) in hardware order.
+template <int F>
+struct QOps {
+  static_assert(F == FMT_FP8 || F == FMT_MXFP4, "8-bit q operand");
   v8i a[4];
   __device__ void load(const uint8_t* q, int r, int lane) {
     const int g = lane >> 4, c = lane & 15;
@@ -179,7 +170,8 @@ struct QOps<FMT_MXFP4> {
   }
 };
 
-// bf16 q: head tile h, K-step s, lane l -> q[16h + l%16][32g + 8s .. +7].
+// bf16 q: head tile h, K-step s, lane l -> q[16h + l%16][32s + 8g .. +7]; the keys use
+// the same order (each key load instruction then reads 64 contiguous bytes per key).
 template <>
 struct QOps<FMT_BF16> {
   v8bf a[4][4];
@@ -187,19 +179,20 @@ struct QOps<FMT_BF16> {
     const int g = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const v8bf* p = (const v8bf*)(q + (((int64_t)r * kHeads + 16 * h + c) * kDim + 32 * g) * 2);
+      const v8bf* p = (const v8bf*)(q + (((int64_t)r * kHeads + 16 * h + c) * kDim + 8 * g) * 2);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[h][s] = p[s];
+      for (int s = 0; s < 4; ++s) a[h][s] = p[4 * s];
     }
   }
 };
 
 template <>
 struct KOps<FMT_FP8> {
+  static constexpr int kRowBytes = kDim;
   v8i b;
   __device__ void load(const uint8_t* k, const void*, int64_t kidx, int g) {
-    const v4i* p = (const v4i*)(k + kidx * kDim + 32 * g);
-    v4i lo = p[0], hi = p[1];
+    const uint8_t* row = k + kidx * kDim;
+    v4i lo = *(const v4i*)(row + 16 * g), hi = *(const v4i*)(row + 64 + 16 * g);
     b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ v4f mma(const QOps<FMT_FP8>& qo, int h) const {
@@ -209,6 +202,7 @@ struct KOps<FMT_FP8> {
 
 template <>
 struct KOps<FMT_MXFP4> {
+  static constexpr int kRowBytes = kDim / 2;
   v4i b;
   int sc;
   __device__ void load(const uint8_t* k, const void* scale, int64_t kidx, int g) {
@@ -223,11 +217,12 @@ struct KOps<FMT_MXFP4> {
 
 template <>
 struct KOps<FMT_BF16> {
+  static constexpr int kRowBytes = 2 * kDim;
   v8bf b[4];
   __device__ void load(const uint8_t* k, const void*, int64_t kidx, int g) {
-    const v8bf* p = (const v8bf*)(k + (kidx * kDim + 32 * g) * 2);
+    const v8bf* p = (const v8bf*)(k + (kidx * kDim + 8 * g) * 2);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = p[s];
+    for (int s = 0; s < 4; ++s) b[s] = p[4 * s];
   }
   __device__ v4f mma(const QOps<FMT_BF16>& qo, int h) const {
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -276,14 +271,29 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
   return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
+#ifndef DSAIDX_SCAN_MAX_STEPS
+#define DSAIDX_SCAN_MAX_STEPS 32
+#endif
+#ifndef DSAIDX_SCAN_LDS_OUT
+#define DSAIDX_SCAN_LDS_OUT 1
+#endif
+static constexpr int kBlock = 256;
+static constexpr int kMaxSteps = DSAIDX_SCAN_MAX_STEPS;
+static_assert(kMaxSteps >= 1 && kMaxSteps <= kWave, "an item describes one step per lane");
+
 template <int F, class Src>
-__global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
+__global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
   const int lane = lane_id();
   const int g = lane >> 4;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
   const int64_t chunk = (int64_t)a.chunk_tiles * kTileTokens;
   const float NEG_INF = -__builtin_inff();
+#if DSAIDX_SCAN_LDS_OUT
+  // the item's scores collect in this wave's LDS slice and leave in 1 KiB bursts
+  __shared__ __align__(16) float sbuf[kBlock / kWave][kMaxSteps * kTileTokens];
+  float* sb = sbuf[threadIdx.x / kWave];
+#endif
 
   for (int64_t item = wave; item < a.n_items; item += nwaves) {
     const int r = (int)(item % a.rows);
@@ -300,6 +310,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
     // lane s describes step s of this item
     StepDesc mine{0, 0};
     if (lane < nsteps) mine = src.step(R, c0 + (int64_t)kTileTokens * lane, a.err);
+    // touch the first key of every step now: the address translations of all the
+    // item's pages are then fetched together instead of one step at a time
+    int touch = 0;
+    if (mine.vlim > 0) touch = *(const int*)(a.k + mine.kidx0 * KOps<F>::kRowBytes);
     QOps<F> qo;
     qo.load(a.q, r, lane);
     float wr[4][4];
@@ -311,30 +325,56 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
       wr[h][2] = wv.z;
       wr[h][3] = wv.w;
     }
+#if DSAIDX_SCAN_LDS_OUT
+    auto put = [&](int s, int32_t vlim, float v) { sb[s * kTileTokens + lane] = lane < vlim ? v : NEG_INF; };
+#else
+    auto put = [&](int s, int32_t vlim, float v) {
+      const int64_t p = c0 + (int64_t)kTileTokens * s + lane;
+      if (p < c1) out[p] = lane < vlim ? v : NEG_INF;
+    };
+#endif
     // two register sets, A and B: the keys of step s + 1 load while step s computes
     KOps<F> ka[4], kb[4];
-    float sa = 1.f, sb = 1.f;
+    float sa = 1.f, sb_ = 1.f;
     int32_t va = __builtin_amdgcn_readlane(mine.vlim, 0);
     if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, 0), va, lane);
     for (int s = 0; s < nsteps; s += 2) {
       int32_t vb = 0;
       if (s + 1 < nsteps) {
         vb = __builtin_amdgcn_readlane(mine.vlim, s + 1);
-        if (vb > 0) load_step<F>(kb, sb, a, readlane64(mine.kidx0, s + 1), vb, lane);
+        if (vb > 0) load_step<F>(kb, sb_, a, readlane64(mine.kidx0, s + 1), vb, lane);
       }
-      int64_t pst = c0 + (int64_t)kTileTokens * s + lane;
-      float v = va > 0 ? score_step<F>(ka, sa, qo, wr) : NEG_INF;
-      if (pst < c1) out[pst] = lane < va ? v : NEG_INF;
+      put(s, va, va > 0 ? score_step<F>(ka, sa, qo, wr) : NEG_INF);
       if (s + 1 >= nsteps) break;
       va = 0;
       if (s + 2 < nsteps) {
         va = __builtin_amdgcn_readlane(mine.vlim, s + 2);
         if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, s + 2), va, lane);
       }
-      pst += kTileTokens;
-      v = vb > 0 ? score_step<F>(kb, sb, qo, wr) : NEG_INF;
-      if (pst < c1) out[pst] = lane < vb ? v : NEG_INF;
+      put(s + 1, vb, vb > 0 ? score_step<F>(kb, sb_, qo, wr) : NEG_INF);
     }
+#if DSAIDX_SCAN_LDS_OUT
+    // LDS operations of one wave complete in order, so the lanes read what the wave
+    // wrote; the row slice is written four scores per lane per instruction
+    __builtin_amdgcn_wave_barrier();
+    const int64_t cnt = c1 - c0;
+    float* o = out + c0;
+    const bool vec = ((uintptr_t)o & 15) == 0;
+    for (int64_t i = 4 * lane; i < cnt; i += 4 * kWave) {
+      const float4 v = *(const float4*)(sb + i);
+      if (vec && i + 4 <= cnt) {
+        *(float4*)(o + i) = v;
+      } else {
+        o[i] = v.x;
+        if (i + 1 < cnt) o[i + 1] = v.y;
+        if (i + 2 < cnt) o[i + 2] = v.z;
+        if (i + 3 < cnt) o[i + 3] = v.w;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // the next item's scores wait for these reads
+#endif
+    if (touch == 0x7F800001 && a.ld < 0) out[0] = 0.f;  // never true (ld > 0): keeps the touch load
+
   }
 }
 
@@ -343,13 +383,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanCommon a, Src src) {
 // Launch shape: the grid holds exactly the workgroups that are resident at once (from
 // the occupancy of each kernel instance), so no workgroup starts late and becomes a
 // tail; items are at most kMaxSteps 64-key steps (at most 64: one step per lane).
-#ifndef DSAIDX_SCAN_MAX_STEPS
-#define DSAIDX_SCAN_MAX_STEPS 32
-#endif
-static constexpr int kBlock = 256;
-static constexpr int kMaxSteps = DSAIDX_SCAN_MAX_STEPS;
-static_assert(kMaxSteps >= 1 && kMaxSteps <= kWave, "an item describes one step per lane");
-
 template <int F, class Src>
 static int resident_blocks_per_cu() {
   static std::once_flag once;
