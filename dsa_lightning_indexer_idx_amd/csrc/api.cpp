@@ -331,6 +331,7 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
   c.ld = ldw;
   c.bt_rows = p->bt_rows;
   c.err = device_error_word();
+  c.skip_tail = 1;  // the top-k below reads each row only up to its length
   hipError_t e = launch_score(c, (hipStream_t)stream);
   if (e != hipSuccess) return launched(fn, e);
 

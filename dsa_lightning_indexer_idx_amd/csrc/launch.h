@@ -34,6 +34,8 @@ struct ScoreCall {
   float* logits;
   int64_t ld;
   unsigned* err;          // device error word (may be null)
+  int skip_tail;          // 1: columns past a row's scored length stay unwritten (their
+                          // reader knows the lengths); 0: they are set to -inf
 };
 
 // One top-k call.

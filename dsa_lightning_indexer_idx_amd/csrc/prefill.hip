@@ -52,6 +52,7 @@ struct PrefillArgs {
   float* logits;
   int64_t ld;
   unsigned* err;
+  int skip_tail;  // 1: columns past a query's length stay unwritten
 };
 
 constexpr int kPieces = 5;  // fp8 pieces of q' per query
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
   // columns past each query's length
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (!qv[u]) continue;
+    if (!qv[u] || a.skip_tail) continue;
     float* out = a.logits + (int64_t)(q0 + kQW * wave + u) * a.ld;
     for (int64_t c = (qe[u] - qs[u]) + lane; c < a.ld; c += kWave) __builtin_nontemporal_store(-__builtin_inff(), &out[c]);
   }
@@ -324,6 +325,7 @@ hipError_t launch_prefill(const ScoreCall& c, hipStream_t stream) {
   a.logits = c.logits;
   a.ld = c.ld;
   a.err = c.err;
+  a.skip_tail = c.skip_tail;
   const int nblocks = (c.rows + kQB - 1) / kQB;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)nblocks), dim3(kPThreads), 0, stream, a);
   return hipGetLastError();

@@ -32,9 +32,10 @@ struct ScanCommon {
   float* logits;
   int64_t ld;
   int rows;
-  int chunk_tiles;
+  int chunk_tiles;  // item schedule: steps per item
   int64_t n_items;
   unsigned* err;
+  int skip_tail;    // columns past a row's scored steps stay unwritten
 };
 
 // ------------------------------------------------------------------ key sources
@@ -274,107 +275,200 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
 #ifndef DSAIDX_SCAN_MAX_STEPS
 #define DSAIDX_SCAN_MAX_STEPS 32
 #endif
-#ifndef DSAIDX_SCAN_LDS_OUT
-#define DSAIDX_SCAN_LDS_OUT 1
+#ifndef DSAIDX_SCAN_DEPTH
+#define DSAIDX_SCAN_DEPTH 2
 #endif
 static constexpr int kBlock = 256;
 static constexpr int kMaxSteps = DSAIDX_SCAN_MAX_STEPS;
-static_assert(kMaxSteps >= 1 && kMaxSteps <= kWave, "an item describes one step per lane");
+static_assert(kMaxSteps >= 1 && kMaxSteps <= kWave, "a segment describes one step per lane");
+// Row counts up to this take the balanced schedule (every wave reads all row lengths).
+static constexpr int kBalancedMaxRows = 512;
 
+// Scores steps [s0, s0 + nsteps) of row r (nsteps <= kMaxSteps) and writes their
+// columns, clipped to ld. sb: the wave's LDS slice of kMaxSteps * 64 floats.
 template <int F, class Src>
-__global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
+__device__ __forceinline__ void scan_segment(const ScanCommon& a, const Src& src, int r, int64_t s0, int nsteps,
+                                             float* sb) {
   const int lane = lane_id();
   const int g = lane >> 4;
+  const float NEG_INF = -__builtin_inff();
+  const int64_t c0 = s0 * kTileTokens;
+  const int64_t c1 = min(c0 + (int64_t)nsteps * kTileTokens, a.ld);
+  float* out = a.logits + (int64_t)r * a.ld;
+  const auto R = src.row(r, a.ld, a.err, false);
+  // lane s describes step s of the segment
+  StepDesc mine{0, 0};
+  if (lane < nsteps) mine = src.step(R, c0 + (int64_t)kTileTokens * lane, a.err);
+  // touch the first key of every step now: the address translations of all the
+  // segment's pages are then fetched together instead of one step at a time
+  int touch = 0;
+  if (mine.vlim > 0) touch = *(const int*)(a.k + mine.kidx0 * KOps<F>::kRowBytes);
+  QOps<F> qo;
+  qo.load(a.q, r, lane);
+  float wr[4][4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float4 wv = *(const float4*)(a.w + (int64_t)r * kHeads + 16 * h + 4 * g);
+    wr[h][0] = wv.x;
+    wr[h][1] = wv.y;
+    wr[h][2] = wv.z;
+    wr[h][3] = wv.w;
+  }
+  auto put = [&](int s, int32_t vlim, float v) { sb[s * kTileTokens + lane] = lane < vlim ? v : NEG_INF; };
+#if DSAIDX_SCAN_DEPTH == 3
+  // three register sets, A, B and C: the keys of steps s + 1 and s + 2 load while
+  // step s computes
+  KOps<F> ka[4], kb[4], kc[4];
+  float sa = 1.f, sbs = 1.f, sc = 1.f;
+  auto fetch = [&](KOps<F>(&ko)[4], float& scl, int s) -> int32_t {
+    int32_t v = 0;
+    if (s < nsteps) {
+      v = __builtin_amdgcn_readlane(mine.vlim, s);
+      if (v > 0) load_step<F>(ko, scl, a, readlane64(mine.kidx0, s), v, lane);
+    }
+    return v;
+  };
+  int32_t va = fetch(ka, sa, 0);
+  int32_t vb = fetch(kb, sbs, 1);
+  for (int s = 0; s < nsteps; s += 3) {
+    const int32_t vc = fetch(kc, sc, s + 2);
+    put(s, va, va > 0 ? score_step<F>(ka, sa, qo, wr) : NEG_INF);
+    if (s + 1 >= nsteps) break;
+    va = fetch(ka, sa, s + 3);
+    put(s + 1, vb, vb > 0 ? score_step<F>(kb, sbs, qo, wr) : NEG_INF);
+    if (s + 2 >= nsteps) break;
+    vb = fetch(kb, sbs, s + 4);
+    put(s + 2, vc, vc > 0 ? score_step<F>(kc, sc, qo, wr) : NEG_INF);
+  }
+#else
+  // two register sets, A and B: the keys of step s + 1 load while step s computes
+  KOps<F> ka[4], kb[4];
+  float sa = 1.f, sbs = 1.f;
+  int32_t va = __builtin_amdgcn_readlane(mine.vlim, 0);
+  if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, 0), va, lane);
+  for (int s = 0; s < nsteps; s += 2) {
+    int32_t vb = 0;
+    if (s + 1 < nsteps) {
+      vb = __builtin_amdgcn_readlane(mine.vlim, s + 1);
+      if (vb > 0) load_step<F>(kb, sbs, a, readlane64(mine.kidx0, s + 1), vb, lane);
+    }
+    put(s, va, va > 0 ? score_step<F>(ka, sa, qo, wr) : NEG_INF);
+    if (s + 1 >= nsteps) break;
+    va = 0;
+    if (s + 2 < nsteps) {
+      va = __builtin_amdgcn_readlane(mine.vlim, s + 2);
+      if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, s + 2), va, lane);
+    }
+    put(s + 1, vb, vb > 0 ? score_step<F>(kb, sbs, qo, wr) : NEG_INF);
+  }
+#endif
+  // LDS operations of one wave complete in order, so the lanes read what the wave
+  // wrote; the columns leave four scores per lane per instruction
+  __builtin_amdgcn_wave_barrier();
+  const int64_t cnt = c1 - c0;
+  float* o = out + c0;
+  const bool vec = ((uintptr_t)o & 15) == 0;
+  for (int64_t i = 4 * lane; i < cnt; i += 4 * kWave) {
+    const float4 v = *(const float4*)(sb + i);
+    if (vec && i + 4 <= cnt) {
+      *(float4*)(o + i) = v;
+    } else {
+      o[i] = v.x;
+      if (i + 1 < cnt) o[i + 1] = v.y;
+      if (i + 2 < cnt) o[i + 2] = v.z;
+      if (i + 3 < cnt) o[i + 3] = v.w;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // the next segment's scores wait for these reads
+  if (touch == 0x7F800001 && a.ld < 0) out[0] = 0.f;  // never true (ld > 0): keeps the touch load
+}
+
+// Scored steps of row r (steps of 64 columns up to the row's bound, clipped to ld).
+template <class Src>
+__device__ __forceinline__ int64_t row_steps(const ScanCommon& a, const Src& src, int r, bool report) {
+  const auto R = src.row(r, a.ld, a.err, report);
+  const int64_t n = min(src.bound(R), a.ld);
+  return n > 0 ? (n + kTileTokens - 1) / kTileTokens : 0;
+}
+
+// -inf into columns [from, ld) of row r within [f0, f1), four per lane per store.
+__device__ __forceinline__ void fill_neg_inf(float* out, int64_t f0, int64_t f1) {
+  const int lane = lane_id();
+  const float NEG_INF = -__builtin_inff();
+  if (f0 >= f1) return;
+  const int64_t head = min(f1, (f0 + 3) & ~(int64_t)3);  // to a 16-byte boundary (rows are 16-byte aligned)
+  if (lane < head - f0) out[f0 + lane] = NEG_INF;
+  const bool vec = ((uintptr_t)out & 15) == 0;
+  for (int64_t i = head + 4 * lane; i < f1; i += 4 * kWave) {
+    if (vec && i + 4 <= f1) {
+      *(float4*)(out + i) = make_float4(NEG_INF, NEG_INF, NEG_INF, NEG_INF);
+    } else {
+      for (int c = 0; c < 4 && i + c < f1; ++c) out[i + c] = NEG_INF;
+    }
+  }
+}
+
+// BALANCED: every wave sums the scored steps of all rows and takes an equal
+// contiguous share of them (crossing rows where needed), in segments of at most
+// kMaxSteps steps, so all waves finish together whatever the row lengths; then the
+// columns past each row's scored steps are filled with -inf in 4096-column pieces
+// (unless skip_tail). Otherwise items (row, chunk of chunk_tiles steps) are taken in a
+// grid-stride loop.
+template <int F, class Src, bool BALANCED>
+__global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
+  const int lane = lane_id();
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  const int64_t chunk = (int64_t)a.chunk_tiles * kTileTokens;
-  const float NEG_INF = -__builtin_inff();
-#if DSAIDX_SCAN_LDS_OUT
-  // the item's scores collect in this wave's LDS slice and leave in 1 KiB bursts
+  // the scores of a segment collect in this wave's LDS slice and leave in 1 KiB bursts
   __shared__ __align__(16) float sbuf[kBlock / kWave][kMaxSteps * kTileTokens];
   float* sb = sbuf[threadIdx.x / kWave];
-#endif
 
-  for (int64_t item = wave; item < a.n_items; item += nwaves) {
-    const int r = (int)(item % a.rows);
-    const int64_t c0 = (item / a.rows) * chunk;
-    if (c0 >= a.ld) continue;
-    const int64_t c1 = min(c0 + chunk, a.ld);
-    const int nsteps = (int)((c1 - c0 + kTileTokens - 1) / kTileTokens);
-    float* out = a.logits + (int64_t)r * a.ld;
-    const auto R = src.row(r, a.ld, a.err, c0 == 0);
-    if (c0 >= src.bound(R)) {
-      for (int64_t p = c0 + lane; p < c1; p += kWave) out[p] = NEG_INF;
-      continue;
+  if constexpr (BALANCED) {
+    // total scored steps; wave 0 reports bad row metadata
+    uint64_t total = 0;
+    for (int r0 = 0; r0 < a.rows; r0 += kWave) {
+      const int r = r0 + lane;
+      const uint32_t n = r < a.rows ? (uint32_t)row_steps(a, src, r, wave == 0) : 0u;
+      total += (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(n), kWave - 1);
     }
-    // lane s describes step s of this item
-    StepDesc mine{0, 0};
-    if (lane < nsteps) mine = src.step(R, c0 + (int64_t)kTileTokens * lane, a.err);
-    // touch the first key of every step now: the address translations of all the
-    // item's pages are then fetched together instead of one step at a time
-    int touch = 0;
-    if (mine.vlim > 0) touch = *(const int*)(a.k + mine.kidx0 * KOps<F>::kRowBytes);
-    QOps<F> qo;
-    qo.load(a.q, r, lane);
-    float wr[4][4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float4 wv = *(const float4*)(a.w + (int64_t)r * kHeads + 16 * h + 4 * g);
-      wr[h][0] = wv.x;
-      wr[h][1] = wv.y;
-      wr[h][2] = wv.z;
-      wr[h][3] = wv.w;
-    }
-#if DSAIDX_SCAN_LDS_OUT
-    auto put = [&](int s, int32_t vlim, float v) { sb[s * kTileTokens + lane] = lane < vlim ? v : NEG_INF; };
-#else
-    auto put = [&](int s, int32_t vlim, float v) {
-      const int64_t p = c0 + (int64_t)kTileTokens * s + lane;
-      if (p < c1) out[p] = lane < vlim ? v : NEG_INF;
-    };
-#endif
-    // two register sets, A and B: the keys of step s + 1 load while step s computes
-    KOps<F> ka[4], kb[4];
-    float sa = 1.f, sb_ = 1.f;
-    int32_t va = __builtin_amdgcn_readlane(mine.vlim, 0);
-    if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, 0), va, lane);
-    for (int s = 0; s < nsteps; s += 2) {
-      int32_t vb = 0;
-      if (s + 1 < nsteps) {
-        vb = __builtin_amdgcn_readlane(mine.vlim, s + 1);
-        if (vb > 0) load_step<F>(kb, sb_, a, readlane64(mine.kidx0, s + 1), vb, lane);
-      }
-      put(s, va, va > 0 ? score_step<F>(ka, sa, qo, wr) : NEG_INF);
-      if (s + 1 >= nsteps) break;
-      va = 0;
-      if (s + 2 < nsteps) {
-        va = __builtin_amdgcn_readlane(mine.vlim, s + 2);
-        if (va > 0) load_step<F>(ka, sa, a, readlane64(mine.kidx0, s + 2), va, lane);
-      }
-      put(s + 1, vb, vb > 0 ? score_step<F>(kb, sb_, qo, wr) : NEG_INF);
-    }
-#if DSAIDX_SCAN_LDS_OUT
-    // LDS operations of one wave complete in order, so the lanes read what the wave
-    // wrote; the row slice is written four scores per lane per instruction
-    __builtin_amdgcn_wave_barrier();
-    const int64_t cnt = c1 - c0;
-    float* o = out + c0;
-    const bool vec = ((uintptr_t)o & 15) == 0;
-    for (int64_t i = 4 * lane; i < cnt; i += 4 * kWave) {
-      const float4 v = *(const float4*)(sb + i);
-      if (vec && i + 4 <= cnt) {
-        *(float4*)(o + i) = v;
-      } else {
-        o[i] = v.x;
-        if (i + 1 < cnt) o[i + 1] = v.y;
-        if (i + 2 < cnt) o[i + 2] = v.z;
-        if (i + 3 < cnt) o[i + 3] = v.w;
+    const uint64_t beg = total * (uint64_t)wave / (uint64_t)nwaves;
+    const uint64_t end = total * (uint64_t)(wave + 1) / (uint64_t)nwaves;
+    uint64_t acc = 0;  // steps of the rows before the current one
+    for (int r0 = 0; r0 < a.rows && acc < end; r0 += kWave) {
+      const int r = r0 + lane;
+      const uint32_t n = r < a.rows ? (uint32_t)row_steps(a, src, r, false) : 0u;
+      const int m = min(kWave, a.rows - r0);
+      for (int j = 0; j < m && acc < end; ++j) {
+        const uint64_t nj = (uint32_t)__builtin_amdgcn_readlane((int)n, j);
+        const uint64_t lo = max(acc, beg), hi = min(acc + nj, end);
+        for (uint64_t s = lo; s < hi; s += kMaxSteps)
+          scan_segment<F>(a, src, r0 + j, (int64_t)(s - acc), (int)min((uint64_t)kMaxSteps, hi - s), sb);
+        acc += nj;
       }
     }
-    __builtin_amdgcn_wave_barrier();  // the next item's scores wait for these reads
-#endif
-    if (touch == 0x7F800001 && a.ld < 0) out[0] = 0.f;  // never true (ld > 0): keeps the touch load
-
+    if (!a.skip_tail) {
+      constexpr int64_t kFill = 4096;
+      const int64_t pieces = (a.ld + kFill - 1) / kFill;
+      for (int64_t it = wave; it < pieces * a.rows; it += nwaves) {
+        const int r = (int)(it % a.rows);
+        const int64_t f0 = (it / a.rows) * kFill;
+        const int64_t from = row_steps(a, src, r, false) * kTileTokens;
+        fill_neg_inf(a.logits + (int64_t)r * a.ld, max(f0, from), min(f0 + kFill, a.ld));
+      }
+    }
+  } else {
+    const int64_t chunk = (int64_t)a.chunk_tiles * kTileTokens;
+    for (int64_t item = wave; item < a.n_items; item += nwaves) {
+      const int r = (int)(item % a.rows);
+      const int64_t c0 = (item / a.rows) * chunk;
+      if (c0 >= a.ld) continue;
+      const int64_t c1 = min(c0 + chunk, a.ld);
+      const int64_t n = row_steps(a, src, r, c0 == 0);
+      const int64_t s0 = c0 / kTileTokens;
+      const int64_t s1 = min(s0 + a.chunk_tiles, n);
+      if (s1 > s0) scan_segment<F>(a, src, r, s0, (int)(s1 - s0), sb);
+      if (!a.skip_tail) fill_neg_inf(a.logits + (int64_t)r * a.ld, max(c0, s1 * kTileTokens), c1);
+    }
   }
 }
 
@@ -382,14 +476,14 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
 
 // Launch shape: the grid holds exactly the workgroups that are resident at once (from
 // the occupancy of each kernel instance), so no workgroup starts late and becomes a
-// tail; items are at most kMaxSteps 64-key steps (at most 64: one step per lane).
-template <int F, class Src>
+// tail.
+template <int F, class Src, bool BALANCED>
 static int resident_blocks_per_cu() {
   static std::once_flag once;
   static int n = 1;
   std::call_once(once, [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)scan_kernel<F, Src>, kBlock, 0) ==
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)scan_kernel<F, Src, BALANCED>, kBlock, 0) ==
             hipSuccess &&
         b > 0)
       n = b;
@@ -397,10 +491,10 @@ static int resident_blocks_per_cu() {
   return n;
 }
 
-template <int F, class Src>
-static hipError_t run(const ScoreCall& c, const Src& src, hipStream_t stream) {
+template <int F, class Src, bool BALANCED>
+static hipError_t run_sched(const ScoreCall& c, const Src& src, hipStream_t stream) {
   const int cus = device_cu_count();
-  const int64_t waves_total = (int64_t)cus * resident_blocks_per_cu<F, Src>() * (kBlock / kWave);
+  const int64_t waves_total = (int64_t)cus * resident_blocks_per_cu<F, Src, BALANCED>() * (kBlock / kWave);
   const int64_t tiles_per_row = (c.ld + kTileTokens - 1) / kTileTokens;
   const int64_t tiles = tiles_per_row * c.rows;
   int64_t ct = tiles / (2 * waves_total);
@@ -417,11 +511,20 @@ static hipError_t run(const ScoreCall& c, const Src& src, hipStream_t stream) {
   a.chunk_tiles = (int)ct;
   a.n_items = chunks * c.rows;
   a.err = c.err;
-  int64_t blocks = (a.n_items + (kBlock / kWave) - 1) / (kBlock / kWave);
-  const int64_t max_blocks = waves_total / (kBlock / kWave);
-  if (blocks > max_blocks) blocks = max_blocks;
-  hipLaunchKernelGGL((scan_kernel<F, Src>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a, src);
+  a.skip_tail = c.skip_tail;
+  int64_t blocks = waves_total / (kBlock / kWave);
+  if (!BALANCED) {
+    const int64_t need = (a.n_items + (kBlock / kWave) - 1) / (kBlock / kWave);
+    if (blocks > need) blocks = need;
+  }
+  hipLaunchKernelGGL((scan_kernel<F, Src, BALANCED>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a, src);
   return hipGetLastError();
+}
+
+template <int F, class Src>
+static hipError_t run(const ScoreCall& c, const Src& src, hipStream_t stream) {
+  if (c.rows <= kBalancedMaxRows) return run_sched<F, Src, true>(c, src, stream);
+  return run_sched<F, Src, false>(c, src, stream);
 }
 
 template <class Src>
