@@ -75,6 +75,61 @@ def stored_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 512 << 20
+SCAN_KERNEL = "scan_kernel<2, dsaidx::PagedSrc, true>"
+
+
+def summarize_counters(fetch_dir: str, write_dir: str) -> int:
+    """HBM bytes per scan launch from rocprofv3 counter runs. FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) of the scan are scaled by what the same counter reads for the
+    calibration copy, whose true traffic is COPY_BYTES read and COPY_BYTES written."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        # the scan run's files are named scan*, the copy run's copy*; only the copy
+        # run's device-to-device copies calibrate (the scan run's uploads read host memory)
+        vals = {"scan": {}, "copy": {}}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            run = os.path.basename(f).split("_")[0]
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                kind = None
+                if run == "scan" and SCAN_KERNEL in name:
+                    kind = "scan"
+                elif run == "copy" and "copy" in name.lower():
+                    kind = "copy"
+                if kind:
+                    key = (f, row["Dispatch_Id"])
+                    vals[kind][key] = vals[kind].get(key, 0.0) + float(row["Counter_Value"])
+        return {k: (sum(v.values()) / len(v) if v else None, len(v)) for k, v in vals.items()}
+
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    if None in (fetch["scan"][0], fetch["copy"][0], write["scan"][0], write["copy"][0]):
+        print(f"counter rows missing: fetch {fetch}, write {write}", file=sys.stderr)
+        return 1
+    f_scale = COPY_BYTES / fetch["copy"][0]   # bytes per counted KiB, reads
+    w_scale = COPY_BYTES / write["copy"][0]   # bytes per counted KiB, writes
+    rd, wr = fetch["scan"][0] * f_scale, write["scan"][0] * w_scale
+    out = {"kernel": SCAN_KERNEL, "workload": "paged_decode_128k",
+           "scan_source_sha": scan_source_hash(),
+           "fetch_kib_per_launch": fetch["scan"][0], "write_kib_per_launch": write["scan"][0],
+           "copy_fetch_kib": fetch["copy"][0], "copy_write_kib": write["copy"][0],
+           "copy_bytes_each_way": COPY_BYTES, "fetch_bytes_per_kib": f_scale, "write_bytes_per_kib": w_scale,
+           "dispatches": {"scan": [fetch["scan"][1], write["scan"][1]], "copy": [fetch["copy"][1], write["copy"][1]]},
+           "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+           "hbm_bytes_per_launch": rd + wr,
+           "commands": [f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv "
+                        f"-d <repo>/gpurun_out/pmc_{c} -o {run} -- python3 <repo>/bench.py --only {run} --steps 5 --warmup 2"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE") for run in ("scan", "copy")]
+                       + ["python3 bench.py --summarize-counters gpurun_out/pmc_FETCH_SIZE gpurun_out/pmc_WRITE_SIZE"]}
+    (PROFILES / "scan_paged_fp8_128k_counters.json").write_text(json.dumps(out, indent=1) + "\n")
+    print(json.dumps(out))
+    return 0
+
+
 def time_loop(fn, steps: int, warmup: int, stream):
     import torch
     for _ in range(warmup):
@@ -194,10 +249,16 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "scan", "select"], default="all",
-                    help="run one timed loop only (for profiler counter runs)")
+    ap.add_argument("--only", choices=["all", "scan", "select", "copy"], default="all",
+                    help="run one timed loop only (for profiler counter runs); copy: a plain "
+                         "512 MiB device-to-device copy, the counters' calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) over "
+                         "'--only scan' and '--only copy' into the scan's HBM traffic summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the indexer's rows shard "
               "across GPUs without any exchange, so per-GPU throughput is the figure.", file=sys.stderr)
@@ -211,6 +272,13 @@ def main() -> int:
 
     D.lib()
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        ms, _ = time_loop(lambda: dst.copy_(src), args.steps, args.warmup, torch.cuda.current_stream())
+        log(f"copy of {COPY_BYTES >> 20} MiB: {ms:.3f} ms ({2 * COPY_BYTES / (ms * 1e-3) / 1e9:.0f} GB/s read + write)")
+        return 0
     log("generating the 128K paged decode workload")
     case = synth.paged_decode(poison=False)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
