@@ -15,8 +15,8 @@
 //   * the 64 scores (-inf where the position is not scored) go to the wave's LDS
 //     slice; the item's scores leave in 1 KiB stores once it is done, so score
 //     stores do not interleave with the key stream.
-// The keys of step s + 1 load while step s computes (two register sets), and every
-// item first touches all of its pages so their address translations arrive together.
+// The keys of step s + 1 load while step s computes (two register sets); keys are
+// read once per call, so their loads are non-temporal.
 #include "device.h"
 #include "launch.h"
 
@@ -189,11 +189,11 @@ struct QOps<FMT_BF16> {
 
 template <>
 struct KOps<FMT_FP8> {
-  static constexpr int kRowBytes = kDim;
   v8i b;
   __device__ void load(const uint8_t* k, const void*, int64_t kidx, int g) {
     const uint8_t* row = k + kidx * kDim;
-    v4i lo = *(const v4i*)(row + 16 * g), hi = *(const v4i*)(row + 64 + 16 * g);
+    v4i lo = __builtin_nontemporal_load((const v4i*)(row + 16 * g));
+    v4i hi = __builtin_nontemporal_load((const v4i*)(row + 64 + 16 * g));
     b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ v4f mma(const QOps<FMT_FP8>& qo, int h) const {
@@ -203,11 +203,10 @@ struct KOps<FMT_FP8> {
 
 template <>
 struct KOps<FMT_MXFP4> {
-  static constexpr int kRowBytes = kDim / 2;
   v4i b;
   int sc;
   __device__ void load(const uint8_t* k, const void* scale, int64_t kidx, int g) {
-    b = *(const v4i*)(k + kidx * (kDim / 2) + 16 * g);
+    b = __builtin_nontemporal_load((const v4i*)(k + kidx * (kDim / 2) + 16 * g));
     sc = ((const uint8_t*)scale)[kidx * (kDim / 32) + g];
   }
   __device__ v4f mma(const QOps<FMT_MXFP4>& qo, int h) const {
@@ -218,12 +217,11 @@ struct KOps<FMT_MXFP4> {
 
 template <>
 struct KOps<FMT_BF16> {
-  static constexpr int kRowBytes = 2 * kDim;
   v8bf b[4];
   __device__ void load(const uint8_t* k, const void*, int64_t kidx, int g) {
     const v8bf* p = (const v8bf*)(k + (kidx * kDim + 8 * g) * 2);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = p[4 * s];
+    for (int s = 0; s < 4; ++s) b[s] = __builtin_nontemporal_load(p + 4 * s);
   }
   __device__ v4f mma(const QOps<FMT_BF16>& qo, int h) const {
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -273,7 +271,7 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
 }
 
 #ifndef DSAIDX_SCAN_MAX_STEPS
-#define DSAIDX_SCAN_MAX_STEPS 32
+#define DSAIDX_SCAN_MAX_STEPS 64
 #endif
 #ifndef DSAIDX_SCAN_DEPTH
 #define DSAIDX_SCAN_DEPTH 2
@@ -299,10 +297,6 @@ __device__ __forceinline__ void scan_segment(const ScanCommon& a, const Src& src
   // lane s describes step s of the segment
   StepDesc mine{0, 0};
   if (lane < nsteps) mine = src.step(R, c0 + (int64_t)kTileTokens * lane, a.err);
-  // touch the first key of every step now: the address translations of all the
-  // segment's pages are then fetched together instead of one step at a time
-  int touch = 0;
-  if (mine.vlim > 0) touch = *(const int*)(a.k + mine.kidx0 * KOps<F>::kRowBytes);
   QOps<F> qo;
   qo.load(a.q, r, lane);
   float wr[4][4];
@@ -380,7 +374,6 @@ __device__ __forceinline__ void scan_segment(const ScanCommon& a, const Src& src
     }
   }
   __builtin_amdgcn_wave_barrier();  // the next segment's scores wait for these reads
-  if (touch == 0x7F800001 && a.ld < 0) out[0] = 0.f;  // never true (ld > 0): keeps the touch load
 }
 
 // Scored steps of row r (steps of 64 columns up to the row's bound, clipped to ld).
