@@ -332,6 +332,12 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
   c.bt_rows = p->bt_rows;
   c.err = device_error_word();
   c.skip_tail = 1;  // the top-k below reads each row only up to its length
+  // the scan kernels clear the top-k's histogram and counters on their way
+  uint8_t* topk_ws = (uint8_t*)workspace + select_scores_bytes(p);
+  if (!prefill_applies(c)) {
+    c.zero = (uint32_t*)topk_ws;
+    c.zero_words = (int64_t)(topk_zeroed_bytes(p->rows, width) / 4);
+  }
   hipError_t e = launch_score(c, (hipStream_t)stream);
   if (e != hipSuccess) return launched(fn, e);
 
@@ -345,6 +351,7 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
   t.out_val = out_val;
   t.out_ld = out_ld;
   t.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
+  t.ws_zeroed = c.zero && c.zero_words > 0;
   if (p->mode == IDX_MODE_DENSE) {
     t.len_ks = p->row_ks;
     t.len_ke = p->row_ke;
@@ -356,7 +363,7 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
     t.cand_ld = p->cand_ld;
     t.block = p->block_size;
   }
-  return launched(fn, launch_topk(t, (uint8_t*)workspace + select_scores_bytes(p), (hipStream_t)stream));
+  return launched(fn, launch_topk(t, topk_ws, (hipStream_t)stream));
 }
 
 const char* idx_status_string(idx_status s) {

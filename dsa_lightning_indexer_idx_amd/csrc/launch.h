@@ -36,6 +36,8 @@ struct ScoreCall {
   unsigned* err;          // device error word (may be null)
   int skip_tail;          // 1: columns past a row's scored length stay unwritten (their
                           // reader knows the lengths); 0: they are set to -inf
+  uint32_t* zero;         // optional: words the kernel sets to 0 (a following top-k's
+  int64_t zero_words;     // histogram and counters)
 };
 
 // One top-k call.
@@ -55,6 +57,7 @@ struct TopkCall {
   const int32_t* cand;    // optional column -> token map
   int64_t cand_ld;
   int block;
+  int ws_zeroed;          // the workspace's zeroed prefix was cleared by the score kernel
 };
 
 hipError_t launch_score(const ScoreCall& c, hipStream_t stream);
@@ -65,6 +68,8 @@ constexpr int kPrefillMinRows = 256;
 bool prefill_applies(const ScoreCall& c);
 hipError_t launch_prefill(const ScoreCall& c, hipStream_t stream);
 size_t topk_workspace_bytes(int rows, int64_t n_cols);
+// Leading bytes of the top-k workspace that must be zero when the top-k starts.
+size_t topk_zeroed_bytes(int rows, int64_t n_cols);
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
 
 // Per-device error word (device address) and compute-unit count.

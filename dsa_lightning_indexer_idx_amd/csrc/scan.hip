@@ -36,6 +36,8 @@ struct ScanCommon {
   int64_t n_items;
   unsigned* err;
   int skip_tail;    // columns past a row's scored steps stay unwritten
+  uint32_t* zero;   // words to clear (every wave clears its share first)
+  int64_t zero_words;
 };
 
 // ------------------------------------------------------------------ key sources
@@ -415,6 +417,11 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
   // the scores of a segment collect in this wave's LDS slice and leave in 1 KiB bursts
   __shared__ __align__(16) float sbuf[kBlock / kWave][kMaxSteps * kTileTokens];
   float* sb = sbuf[threadIdx.x / kWave];
+  if (a.zero) {
+    const int64_t per = (a.zero_words + nwaves - 1) / nwaves;
+    const int64_t z1 = min(a.zero_words, (wave + 1) * per);
+    for (int64_t i = wave * per + lane; i < z1; i += kWave) a.zero[i] = 0u;
+  }
 
   if constexpr (BALANCED) {
     // total scored steps; wave 0 reports bad row metadata
@@ -505,6 +512,8 @@ static hipError_t run_sched(const ScoreCall& c, const Src& src, hipStream_t stre
   a.n_items = chunks * c.rows;
   a.err = c.err;
   a.skip_tail = c.skip_tail;
+  a.zero = c.zero;
+  a.zero_words = c.zero_words;
   int64_t blocks = waves_total / (kBlock / kWave);
   if (!BALANCED) {
     const int64_t need = (a.n_items + (kBlock / kWave) - 1) / (kBlock / kWave);

@@ -741,14 +741,16 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(TopkCall a, Long
 }
 
 // Candidates one filter workgroup stages in LDS; a segment with more forces its row
-// onto the full-row path (the candidate count is pushed past kCandCap).
+// onto the full-row path (the candidate count is pushed past kCandCap). The LDS lists
+// hold columns (4 bytes), so a workgroup needs 24 KiB and every segment of the
+// workloads' shapes is resident at once.
 constexpr int kSegCandCap = 4096;
 
 template <bool V4>
 __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, LongWs ws, int64_t seg, int segs) {
   __shared__ CutInfo ci;
-  __shared__ uint64_t lwin[kMaxK];
-  __shared__ uint64_t lcand[kSegCandCap];
+  __shared__ uint32_t lwin[kMaxK];
+  __shared__ uint32_t lcand[kSegCandCap];
   __shared__ uint32_t n_lwin, n_lcand, base_win, base_cand;
   const int r = (int)(blockIdx.x / (unsigned)segs);
   const int64_t n = row_len(a, r);
@@ -770,7 +772,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, Lo
 #pragma unroll
     for (int j = 0; j < kSegGroups; ++j) v[j] = load4<V4, true>(row, b + ((int64_t)j * kSegThreads + threadIdx.x) * 4, s1);
     bool tw[4 * kSegGroups], tc[4 * kSegGroups];
-    uint64_t key[4 * kSegGroups];
+    uint32_t col[4 * kSegGroups];
 #pragma unroll
     for (int j = 0; j < kSegGroups; ++j) {
       const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -781,11 +783,11 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, Lo
         const int bin = vk ? (int)(vk >> kBinShift) : -2;
         tw[4 * j + c] = bin > cut;
         tc[4 * j + c] = keep_cand && bin == cut;
-        key[4 * j + c] = sel_key(vk, i0 + c);
+        col[4 * j + c] = (uint32_t)(i0 + c);
       }
     }
-    wave_append<4 * kSegGroups>(tw, key, lwin, &n_lwin, (uint32_t)kMaxK);
-    wave_append<4 * kSegGroups>(tc, key, lcand, &n_lcand, (uint32_t)kSegCandCap);
+    wave_append<4 * kSegGroups>(tw, col, lwin, &n_lwin, (uint32_t)kMaxK);
+    wave_append<4 * kSegGroups>(tc, col, lcand, &n_lcand, (uint32_t)kSegCandCap);
   }
   __syncthreads();
   uint32_t* cnt = ws.counts + 2 * (int64_t)r;
@@ -801,11 +803,13 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, Lo
   __syncthreads();
   uint64_t* win = ws.win + (int64_t)r * kMaxK;
   uint64_t* cand = ws.cand + (int64_t)r * kCandCap;
+  // the selection keys, rebuilt from the (cached) row entries
+  auto key_of = [&](uint32_t c) { return sel_key(order_key(row[c]), c); };
   for (uint32_t i = threadIdx.x; i < nw; i += kSegThreads)
-    if (base_win + i < (uint32_t)kMaxK) win[base_win + i] = lwin[i];
+    if (base_win + i < (uint32_t)kMaxK) win[base_win + i] = key_of(lwin[i]);
   if (keep_cand && nc <= (uint32_t)kSegCandCap)
     for (uint32_t i = threadIdx.x; i < nc; i += kSegThreads)
-      if (base_cand + i < (uint32_t)kCandCap) cand[base_cand + i] = lcand[i];
+      if (base_cand + i < (uint32_t)kCandCap) cand[base_cand + i] = key_of(lcand[i]);
 }
 
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(TopkCall a, LongWs ws) {
@@ -872,6 +876,12 @@ size_t topk_workspace_bytes(int rows, int64_t n_cols) {
                   R * kCandCap * 8);
 }
 
+size_t topk_zeroed_bytes(int rows, int64_t n_cols) {
+  if (rows <= 0 || n_cols <= kShortRow) return 0;
+  const int64_t R = rows;
+  return (size_t)(round_up(R * kHistBins * 4, 256) + round_up(R * 2 * 4, 256));
+}
+
 template <bool V4>
 static hipError_t launch_short(const TopkCall& c, hipStream_t stream) {
   static std::once_flag once;
@@ -908,10 +918,12 @@ hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   ws.win = (uint64_t*)p;
   p += R * kMaxK * 8;
   ws.cand = (uint64_t*)p;
-  // histogram and counters start at zero (a fill kernel, not a memset node)
-  const int64_t nz = (int64_t)((uint8_t*)ws.win - (uint8_t*)workspace) / 4;
-  hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)std::min<int64_t>((nz + kSegThreads - 1) / kSegThreads, 1024)),
-                     dim3(kSegThreads), 0, stream, (uint32_t*)workspace, nz);
+  // histogram and counters start at zero (a fill kernel, not a memset node), unless the
+  // score kernel before this call cleared them
+  const int64_t nz = (int64_t)topk_zeroed_bytes(c.rows, c.n_cols) / 4;
+  if (!c.ws_zeroed)
+    hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)std::min<int64_t>((nz + kSegThreads - 1) / kSegThreads, 1024)),
+                       dim3(kSegThreads), 0, stream, (uint32_t*)workspace, nz);
   // about four segment workgroups per compute unit over all rows; segments are whole
   // passes of the segment loop
   const int cus = device_cu_count();
