@@ -19,9 +19,9 @@
 //     the previous ones, so the split is exact to 2^-20 of max |q'|), and the pieces of a
 //     wave's two queries fill rows 0..9 of one extra 16-row MFMA tile.
 //   * Per 16 keys and wave: 9 MFMAs (2 queries x 4 head tiles + the pieces; K = 128 in
-//     one instruction), 20 FMAs per query and lane, three lane swaps for the head sum,
-//     the key's fp8 scale and one 256-byte store per query (non-temporal: scores are
-//     not re-read here and must not push the keys out of L2).
+//     one instruction), 20 FMAs per query and lane; per tile three lane swaps for the
+//     head sum, the keys' fp8 scales and one 256-byte store per query, issued after the
+//     tile's stash (see there).
 #include "device.h"
 #include "launch.h"
 
@@ -288,15 +288,18 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
     epilogue(ra, p[0][2], p[1][2]);
     epilogue(rb, p[0][3], p[1][3]);
     const int64_t key = t0 + lane;
+    float vv[kQW];
 #pragma unroll
-    for (int u = 0; u < kQW; ++u) {
-      const float v = sum_lane_groups(p[u][0], p[u][1], p[u][2], p[u][3]) * sc;
-      if ((u == 0 ? act0 : act1) && key >= qs[u] && key < qe[u])
-        __builtin_nontemporal_store(v, &a.logits[(int64_t)(q0 + kQW * wave + u) * a.ld + (key - qs[u])]);
-    }
+    for (int u = 0; u < kQW; ++u) vv[u] = sum_lane_groups(p[u][0], p[u][1], p[u][2], p[u][3]) * sc;
     // slot (t + 2) % 3 last held tile t - 1, whose reads all finished in iteration t - 1
     if (t + 2 < ntiles) stash(t + 2, x0, x1, xs);
     __syncthreads();
+    // stores after the stash: the stash waits for the loads of tile t + 2, and memory
+    // operations count down in order, so stores issued before it would be waited for too
+#pragma unroll
+    for (int u = 0; u < kQW; ++u)
+      if ((u == 0 ? act0 : act1) && key >= qs[u] && key < qe[u])
+        a.logits[(int64_t)(q0 + kQW * wave + u) * a.ld + (key - qs[u])] = vv[u];
   }
 
   // columns past each query's length
