@@ -217,11 +217,11 @@ def other_workloads(D, np, torch, stream, args):
     out["batched_decode_tokens_per_s"] = c2.tokens / (ms * 1e-3)
     log(f"batched decode: select {ms*1e3:.1f} us ({c2.tokens/(ms*1e-3)/1e9:.2f} G keys/s)")
     del base, copies, probs, ws2, oi2
-    # two-level candidate blocks: 64 rows x 8192 candidate keys of 131072, MXFP4 (rotate 8
+    # two-level candidate blocks: 64 rows x 8192 candidate keys of 131072, MXFP4 (rotate 16
     # copies of the candidate data, as a graph)
     c5 = synth.sparse_blocks()
     base = [dev(a) for a in (c5.q, c5.w, c5.k, c5.k_scale, c5.row_ks, c5.row_ke, c5.cand, c5.n_cols)]
-    copies = [base] + [[t.clone() for t in base] for _ in range(7)]
+    copies = [base] + [[t.clone() for t in base] for _ in range(15)]
     probs = [D.sparse_problem(*cp, k_dtype="mxfp4", block_size=128) for cp in copies]
     ws5 = torch.empty(D.idx_select_workspace(probs[0], 2048), dtype=torch.uint8, device="cuda")
     oi5 = torch.empty((c5.rows, 2048), dtype=torch.int32, device="cuda")
@@ -241,6 +241,26 @@ def other_workloads(D, np, torch, stream, args):
     out["two_level_select_ms"] = ms
     out["two_level_tokens_per_s"] = c5.tokens / (ms * 1e-3)
     log(f"two-level: select {ms*1e3:.1f} us per call ({c5.tokens/(ms*1e-3)/1e9:.2f} G keys/s, graph of {len(probs)})")
+    del base, copies, probs, ws5, oi5, g
+    # the 128K paged decode workload with MXFP4 keys (64 B codes + 4 UE8M0 bytes per token)
+    c6 = synth.paged_decode_mxfp4()
+    q6, w6, kp6, sp6, bt6, sl6 = map(dev, (c6.q, c6.w, c6.k_pages, c6.k_scale_pages, c6.block_table, c6.seq_lens))
+    p6 = D.paged_problem(q6, w6, kp6, sp6, bt6, sl6, k_dtype="mxfp4")
+    ws6 = torch.empty(D.idx_select_workspace(p6, 2048), dtype=torch.uint8, device="cuda")
+    oi6 = torch.empty((c6.rows, 2048), dtype=torch.int32, device="cuda")
+    lg6 = torch.empty((c6.rows, c6.block_table.shape[1] * c6.page_size), dtype=torch.float32, device="cuda")
+    ms, _ = time_loop(lambda: D.idx_select(p6, 2048, values=False, out_idx=oi6, workspace=ws6), steps, 3, stream)
+    ms_scan, _ = time_loop(lambda: D.idx_logits_paged(q6, w6, kp6, sp6, bt6, sl6, k_dtype="mxfp4", out=lg6),
+                           steps, 3, stream)
+    L6 = c6.seq_lens.astype(np.int64)
+    b6 = int(L6.sum() * (64 + 4 + 4) + ((L6 + 63) // 64).sum() * 4 + c6.rows * (64 * 128 + 64 * 4)
+             + (lg6.shape[1] - L6).sum() * 4)
+    out["paged_mxfp4_select_ms"] = ms
+    out["paged_mxfp4_tokens_per_s"] = c6.tokens / (ms * 1e-3)
+    out["paged_mxfp4_scan_ms"] = ms_scan
+    out["paged_mxfp4_scan_hbm_frac"] = b6 / (ms_scan * 1e-3) / HBM_PEAK
+    log(f"128K paged, MXFP4 keys: select {ms*1e3:.1f} us ({c6.tokens/(ms*1e-3)/1e9:.2f} G keys/s), scan "
+        f"{ms_scan*1e3:.1f} us ({b6/(ms_scan*1e-3)/1e9:.0f} GB/s, {100*b6/(ms_scan*1e-3)/HBM_PEAK:.1f}% of 8 TB/s)")
     return out
 
 

@@ -272,20 +272,30 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
   return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-#ifndef DSAIDX_SCAN_MAX_STEPS
-#define DSAIDX_SCAN_MAX_STEPS 64
-#endif
+// Steps per segment: long segments start and drain the key pipeline rarely, but their
+// LDS score slices (256 B per step and wave) limit the resident workgroups. MXFP4 steps
+// move half the bytes of fp8 ones, so the MXFP4 kernels want more workgroups than the LDS
+// of 64-step slices allows. DSAIDX_SCAN_MAX_STEPS overrides both.
 #ifndef DSAIDX_SCAN_DEPTH
 #define DSAIDX_SCAN_DEPTH 2
 #endif
 static constexpr int kBlock = 256;
-static constexpr int kMaxSteps = DSAIDX_SCAN_MAX_STEPS;
-static_assert(kMaxSteps >= 1 && kMaxSteps <= kWave, "a segment describes one step per lane");
+template <int F>
+constexpr int max_steps() {
+#ifdef DSAIDX_SCAN_MAX_STEPS
+  return DSAIDX_SCAN_MAX_STEPS;
+#else
+  return F == FMT_MXFP4 ? 32 : 64;
+#endif
+}
+static_assert(max_steps<FMT_FP8>() >= 1 && max_steps<FMT_FP8>() <= kWave && max_steps<FMT_MXFP4>() >= 1 &&
+                  max_steps<FMT_MXFP4>() <= kWave,
+              "a segment describes one step per lane");
 // Row counts up to this take the balanced schedule (every wave reads all row lengths).
 static constexpr int kBalancedMaxRows = 512;
 
-// Scores steps [s0, s0 + nsteps) of row r (nsteps <= kMaxSteps) and writes their
-// columns, clipped to ld. sb: the wave's LDS slice of kMaxSteps * 64 floats.
+// Scores steps [s0, s0 + nsteps) of row r (nsteps <= max_steps<F>()) and writes their
+// columns, clipped to ld. sb: the wave's LDS slice of max_steps<F>() * 64 floats.
 template <int F, class Src>
 __device__ __forceinline__ void scan_segment(const ScanCommon& a, const Src& src, int r, int64_t s0, int nsteps,
                                              float* sb) {
@@ -405,7 +415,7 @@ __device__ __forceinline__ void fill_neg_inf(float* out, int64_t f0, int64_t f1)
 
 // BALANCED: every wave sums the scored steps of all rows and takes an equal
 // contiguous share of them (crossing rows where needed), in segments of at most
-// kMaxSteps steps, so all waves finish together whatever the row lengths; then the
+// max_steps<F>() steps, so all waves finish together whatever the row lengths; then the
 // columns past each row's scored steps are filled with -inf in 4096-column pieces
 // (unless skip_tail). Otherwise items (row, chunk of chunk_tiles steps) are taken in a
 // grid-stride loop.
@@ -415,6 +425,7 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
   // the scores of a segment collect in this wave's LDS slice and leave in 1 KiB bursts
+  constexpr int kMaxSteps = max_steps<F>();
   __shared__ __align__(16) float sbuf[kBlock / kWave][kMaxSteps * kTileTokens];
   float* sb = sbuf[threadIdx.x / kWave];
   if (a.zero) {
@@ -498,6 +509,7 @@ static hipError_t run_sched(const ScoreCall& c, const Src& src, hipStream_t stre
   const int64_t tiles_per_row = (c.ld + kTileTokens - 1) / kTileTokens;
   const int64_t tiles = tiles_per_row * c.rows;
   int64_t ct = tiles / (2 * waves_total);
+  constexpr int kMaxSteps = max_steps<F>();
   ct = ct < 1 ? 1 : (ct > kMaxSteps ? kMaxSteps : ct);
   const int64_t chunks = (tiles_per_row + ct - 1) / ct;
   ScanCommon a;

@@ -54,32 +54,30 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
-# e2m1 magnitudes in code order 0..7 (sign is bit 3), OCP MX v1.0 table for FP4 E2M1
-_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
-_E2M1_MID = (_E2M1_MAG[1:] + _E2M1_MAG[:-1]) / 2
-
-
 def to_mxfp4(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Encode float rows [..., D] (D % 32 == 0) as MXFP4 following OCP MX v1.0:
     per group of 32 the shared exponent is floor(log2(amax)) - 2 (2 = emax of e2m1),
     stored biased by 127 as UE8M0; each element v / 2^X is rounded to nearest-even on
     the e2m1 grid and saturated at +-6. Returns (codes [..., D/2] uint8 with element 2j
-    in the low nibble of byte j, scales [..., D/32] uint8)."""
-    x = np.asarray(x, dtype=np.float64)
+    in the low nibble of byte j, scales [..., D/32] uint8).
+
+    The e2m1 grid has step 0.5 below 2, step 1 in [2, 4) and step 2 in [4, 6], so the
+    rounding is rint (round half to even) of the magnitude in units of the local step;
+    a tie at a step boundary (1.75, 3.5) rounds to the even code either way."""
+    x = np.asarray(x, dtype=np.float32)
     *lead, d = x.shape
     assert d % 32 == 0
     g = x.reshape(*lead, d // 32, 32)
     amax = np.abs(g).max(axis=-1)
-    with np.errstate(divide="ignore"):
-        xexp = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
-    biased = np.clip(xexp + 127, 0, 254).astype(np.int64)
-    scaled = g / np.exp2(biased - 127)[..., None]
-    mag = np.minimum(np.abs(scaled), 6.0)
-    code = np.searchsorted(_E2M1_MID, mag, side="left")
-    tie = (code < 7) & (mag == _E2M1_MID[np.minimum(code, 6)])
-    code = code + (tie & (code % 2 == 1))
-    code = code | np.where(scaled < 0, 8, 0)
-    code = code.reshape(*lead, d).astype(np.uint8)
+    _, e = np.frexp(amax)  # amax = m 2^e with m in [0.5, 1): floor(log2(amax)) = e - 1
+    xexp = np.where(amax > 0, e.astype(np.int32) - 1 - 2, -127)
+    biased = np.clip(xexp + 127, 0, 254).astype(np.int32)
+    scaled = np.ldexp(g, (127 - biased)[..., None]).astype(np.float32)  # exact: a power of two
+    mag = np.minimum(np.abs(scaled), np.float32(6.0))
+    code = np.where(mag < 2, np.rint(mag * 2),
+                    np.where(mag < 4, np.rint(mag) + 2, np.rint(mag * 0.5) + 4)).astype(np.uint8)
+    code |= np.where(scaled < 0, 8, 0).astype(np.uint8)
+    code = code.reshape(*lead, d)
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
     return packed, biased.astype(np.uint8)
 
@@ -138,7 +136,7 @@ def _keys(rng, n: int, kdtype: str, scale_rng):
             g = np.random.Generator(np.random.PCG64(int(seeds[i])))
             codes[s:s + m], scales[s:s + m] = to_mxfp4(g.standard_normal((m, DIM), dtype=np.float32))
 
-        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
             list(ex.map(fill, range(len(starts))))
         return codes, scales
     raise ValueError(kdtype)
@@ -393,7 +391,13 @@ def sparse_blocks(seed: int = 5, rows: int = 64, ctx: int = 131072, n_blocks: in
                   block, topk, {"ctx": ctx, "n_blocks": n_blocks})
 
 
+def paged_decode_mxfp4(seed: int = 6):
+    """The long paged decode workload with MXFP4 keys (e2m1 codes + UE8M0 group scales)."""
+    return paged_decode(seed=seed, kdtype="mxfp4")
+
+
 def full_size(idx: int):
-    """The five workloads at their stated sizes, by number 1..5."""
+    """The five workloads at their stated sizes, by number 1..5, and 6: workload 3 with
+    MXFP4 keys."""
     return {1: tiny_dense, 2: batched_decode, 3: paged_decode, 4: prefill_chunk,
-            5: sparse_blocks}[idx]()
+            5: sparse_blocks, 6: paged_decode_mxfp4}[idx]()

@@ -1,5 +1,6 @@
-"""The five workloads at their stated sizes, generated once per test session and kept on the
-GPU (shared by the score, top-k and select tests)."""
+"""The five workloads at their stated sizes (and workload 3 with MXFP4 keys as number 6),
+generated once per test session and kept on the GPU (shared by the score, top-k and select
+tests)."""
 import synth
 from gpu_util import Uploaded, say
 

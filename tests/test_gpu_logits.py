@@ -121,10 +121,10 @@ def test_bad_device_metadata_is_clamped_and_reported():
     assert D.idx_device_errors() == 0
 
 
-FULL_SAMPLES = {2: [0, 17, 31], 3: [0, 40, 63], 4: [0, 1, 2047, 4095], 5: [0, 31, 63]}
+FULL_SAMPLES = {2: [0, 17, 31], 3: [0, 40, 63], 4: [0, 1, 2047, 4095], 5: [0, 31, 63], 6: [0, 22, 63]}
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_full_size_sampled_rows(cfg):
     """The workloads at their stated sizes, in the launch shape the benchmark uses; the oracle
     checks a sample of rows."""

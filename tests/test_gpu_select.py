@@ -107,10 +107,10 @@ def test_unsorted_select_same_set():
         assert sorted(a[r].tolist()) == sorted(b[r].tolist())
 
 
-FULL = {2: [0, 31], 3: [0, 63], 4: [0, 4095], 5: [0, 63]}
+FULL = {2: [0, 31], 3: [0, 63], 4: [0, 4095], 5: [0, 63], 6: [0, 63]}
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_full_size_select(cfg):
     """The workloads at full size through idx_select (the benchmark's call); the oracle
     checks sampled rows end to end, and every row is checked against idx_topk."""
