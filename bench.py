@@ -147,6 +147,21 @@ def time_loop(fn, steps: int, warmup: int, stream):
     return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
 
 
+def time_each(fn, n: int, warmup: int, stream):
+    """Per-launch times (ms) from a pair of HIP events around each of n launches."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def cpu_baseline(case, k: int, budget_s: float = 15.0):
     """The oracle (scores + top-k) on whole rows of the same workload. The oracle spreads
     rows over its OpenMP threads, so each batch holds one row per thread; batches run
@@ -338,6 +353,20 @@ def main() -> int:
         return 0
 
     extra = other_workloads(D, np, torch, stream, args)
+    # the select step timed launch by launch (median and spread)
+    per = time_each(select(2048), 50, 5, stream)
+    extra["select_us_median"], extra["select_us_p10"], extra["select_us_p90"] = (
+        float(np.percentile(per, 50)) * 1e3, float(np.percentile(per, 10)) * 1e3, float(np.percentile(per, 90)) * 1e3)
+    log(f"idx_select k=2048 per launch: median {extra['select_us_median']:.1f} us "
+        f"(p10 {extra['select_us_p10']:.1f}, p90 {extra['select_us_p90']:.1f})")
+    # what a plain streaming read achieves here (the scan's fraction is also given against it)
+    probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    probe_buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms_probe, _ = time_loop(lambda: D.idx_read_probe(probe_buf, sink), 10, 3, stream)
+    extra["read_probe_gbps"] = probe_buf.numel() / (ms_probe * 1e-3) / 1e9
+    del probe_buf
+    log(f"streaming-read probe: {extra['read_probe_gbps']:.0f} GB/s")
 
     ms = res["select"][0]
     sb = scan_bytes(case)
@@ -365,7 +394,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": stored_traffic(),
                      "kernel": "scan_kernel<fp8, paged>", "ms_per_launch": res["scan"],
-                     "bytes_per_launch": sb},
+                     "bytes_per_launch": sb,
+                     "frac_of_read_probe": achieved / 1e9 / extra["read_probe_gbps"]},
         "cpu_baseline": cpu,
         "extra": {**extra,
                   "ms_per_step_k1024": res["select_k1024"], "ms_per_step_k512": res["select_k512"],

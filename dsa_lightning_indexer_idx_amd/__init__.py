@@ -28,7 +28,7 @@ KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
 # Every symbol include/dsaidx.h declares.
 EXPORTS = ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
            "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
-           "idx_last_error", "idx_version", "idx_device_errors")
+           "idx_last_error", "idx_version", "idx_device_errors", "idx_read_probe")
 
 
 class IdxError(RuntimeError):
@@ -89,8 +89,9 @@ def lib() -> C.CDLL:
         L.idx_version.restype = I
         L.idx_device_errors.argtypes = [P]
         L.idx_device_errors.restype = I
+        L.idx_read_probe.argtypes = [P, SZ, P, P]
         for name in ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
-                     "idx_select"):
+                     "idx_select", "idx_read_probe"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -289,6 +290,12 @@ def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = 
 
 def idx_version() -> int:
     return int(lib().idx_version())
+
+
+def idx_read_probe(buf, sink, stream=None) -> None:
+    """Read the whole device tensor ``buf`` once and discard it (a bandwidth probe);
+    ``sink`` is a one-element int32 device tensor the probe may write."""
+    _check(lib().idx_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def idx_device_errors(stream=None) -> int:

@@ -381,6 +381,15 @@ const char* idx_last_error(void) { return g_last_error.c_str(); }
 
 int idx_version(void) { return 100; }
 
+idx_status idx_read_probe(const void* buf, size_t bytes, uint32_t* sink, idx_stream_t stream) {
+  const char* fn = "idx_read_probe";
+  REQUIRE(buf && sink, IDX_ERR_ARG, "%s: buf and sink must be non-null", fn);
+  REQUIRE(aligned(buf, 16) && bytes % 16 == 0, IDX_ERR_ARG, "%s: buf must be 16-byte aligned and bytes a multiple of 16",
+          fn);
+  REQUIRE(aligned(sink, 4), IDX_ERR_ARG, "%s: sink must be 4-byte aligned", fn);
+  return launched(fn, launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
+}
+
 int idx_device_errors(idx_stream_t stream) {
   unsigned* p = device_error_word();
   if (!p) {

@@ -72,6 +72,9 @@ size_t topk_workspace_bytes(int rows, int64_t n_cols);
 size_t topk_zeroed_bytes(int rows, int64_t n_cols);
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
 
+// Streaming-read probe (measurement aid).
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Per-device error word (device address) and compute-unit count.
 unsigned* device_error_word();
 int device_cu_count();

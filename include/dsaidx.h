@@ -245,6 +245,16 @@ int idx_version(void);
 #define IDX_DEVERR_BLOCK 4u  /* candidate block outside the row's key range */
 int idx_device_errors(idx_stream_t stream);
 
+/*
+ * Measurement aid, not part of the indexer path: reads ``bytes`` bytes of device
+ * memory at ``buf`` once (16-byte loads, non-temporal) and discards them, so the time
+ * of a call measures the read bandwidth this machine delivers, against which the
+ * scan's HBM fraction can be judged. buf 16-byte aligned, bytes a multiple of 16;
+ * ``sink`` is a device word the probe may write (to keep its loads). Asynchronous on
+ * ``stream``.
+ */
+idx_status idx_read_probe(const void* buf, size_t bytes, uint32_t* sink, idx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

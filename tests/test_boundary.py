@@ -216,3 +216,12 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(D, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         D.lib()
+
+
+def test_read_probe_rejects_bad_arguments(L):
+    """The bandwidth probe checks its arguments on the host before anything is enqueued."""
+    assert L.idx_read_probe(None, 1024, C.c_void_p(0x1000), None) == D.IDX_ERR_ARG
+    assert L.idx_read_probe(C.c_void_p(0x1000), 1024, None, None) == D.IDX_ERR_ARG
+    assert L.idx_read_probe(C.c_void_p(0x1008), 1024, C.c_void_p(0x2000), None) == D.IDX_ERR_ARG  # misaligned
+    assert L.idx_read_probe(C.c_void_p(0x1000), 1000, C.c_void_p(0x2000), None) == D.IDX_ERR_ARG  # not a multiple of 16
+    assert b"idx_read_probe" in L.idx_last_error()
