@@ -59,6 +59,12 @@ def _load(path) -> C.CDLL:
     L.ref_logits_sparse.argtypes = [P, I, P, P, P, I, P, P, P, I64, P, I, I, I, I, P, I64]
     L.ref_topk.restype = None
     L.ref_topk.argtypes = [P, I64, P, I64, I, I, P, P, I64]
+    L.ref_encode_fp8_e4m3fn.argtypes = [C.c_float]
+    L.ref_encode_fp8_e4m3fn.restype = C.c_uint8
+    L.ref_encode_e2m1.argtypes = [C.c_double]
+    L.ref_encode_e2m1.restype = C.c_uint8
+    L.ref_kcache_write.argtypes = [P, I64, P, I, P, P, I64]
+    L.ref_kcache_write.restype = I64
     return L
 
 
@@ -242,3 +248,30 @@ def subset_rows(case, rows):
         else:
             c.row_req = case.row_req[rows]
     return c
+
+
+def encode_fp8(y) -> np.ndarray:
+    """e4m3fn codes of float32 values (nearest code, ties to even, saturating)."""
+    y = np.asarray(y, np.float32)
+    f = lib().ref_encode_fp8_e4m3fn
+    return np.array([f(float(v)) for v in y.reshape(-1)], np.uint8).reshape(y.shape)
+
+
+def encode_e2m1(v) -> np.ndarray:
+    """e2m1 nibbles of values (nearest code, ties to even, saturating at 6)."""
+    v = np.asarray(v, np.float64)
+    f = lib().ref_encode_e2m1
+    return np.array([f(float(x)) for x in v.reshape(-1)], np.uint8).reshape(v.shape)
+
+
+def kcache_write(k_new_bf16, slot_mapping, k_dtype, cache, cache_scale):
+    """Quantise new keys (bf16 bits [n, 128]) into ``cache`` / ``cache_scale`` (numpy
+    arrays, updated in place) at their slots; returns the count of out-of-range slots.
+    fp8: cache uint8 [n_slots, 128], cache_scale float32 [n_slots]; MXFP4: cache uint8
+    [n_slots, 64], cache_scale uint8 [n_slots, 4]."""
+    kd = DTYPES[k_dtype]
+    k_new = _c(k_new_bf16, np.uint16)
+    slots = _c(slot_mapping, np.int64)
+    assert cache.flags.c_contiguous and cache_scale.flags.c_contiguous
+    return int(lib().ref_kcache_write(_p(k_new), k_new.shape[0], _p(slots), kd, _p(cache), _p(cache_scale),
+                                      cache.shape[0]))

@@ -295,6 +295,133 @@ void ref_topk(const float* logits, int64_t ld, const int32_t* lens, int64_t ncol
     }
 }
 
+/* ---------------------------------------------------------------- key-cache writer
+ *
+ * Each new key (128 bf16 values) is quantised into the cache format and stored at
+ * its slot. The vLLM sparse_indexer page names the formats (an fp8 key with a
+ * per-token fp32 scale, and MXFP4 with UE8M0 granularity-32 scales) but not the
+ * quantisation recipe, so the plainest readings are taken:
+ *  - fp8: scale = amax / 448 (amax the largest |value| of the token, 448 the largest
+ *    e4m3fn value), code = the e4m3fn value nearest to value * (448 / amax), ties to
+ *    the even code; both quotients and the product in float32; amax = 0 gives scale 0
+ *    and zero codes. A key decodes as code * scale, as the scan reads it.
+ *  - MXFP4 (OCP MX v1.0 conversion): per group of 32 the shared exponent X =
+ *    floor(log2(amax)) - 2 (2 = the largest e2m1 exponent), stored as UE8M0 X + 127
+ *    clamped to [0, 254]; each element value / 2^X goes to the nearest e2m1 value,
+ *    ties to the even code, magnitudes above 6 to 6.
+ * "Nearest" is found by trying every code of the format, so the encoders follow the
+ * definition of round-to-nearest-even directly. Signs carry over (-0 keeps its sign).
+ */
+
+/* e4m3fn code of a finite float (nearest of the 127 non-negative finite codes by
+ * magnitude, ties to the even code; magnitudes above 448 give 448). */
+uint8_t ref_encode_fp8_e4m3fn(float y)
+{
+    double a = fabs((double)y);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 127; c++) { /* 0x7F is NaN */
+        double d = fabs(ref_decode_fp8_e4m3fn((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* e2m1 nibble of a finite double (nearest of the 8 magnitudes, ties to the even
+ * code, saturating at 6). */
+uint8_t ref_encode_e2m1(double v)
+{
+    double a = fabs(v);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 8; c++) {
+        double d = fabs(ref_decode_e2m1((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 8 : 0));
+}
+
+/* One key row of 128 bf16 values into the cache format: fp8 -> 128 codes and one
+ * float scale; MXFP4 -> 64 bytes (element 2j in the low nibble of byte j) and 4
+ * UE8M0 bytes. */
+static void quantize_key(const uint16_t* x16, int k_dtype, uint8_t* codes, void* scale)
+{
+    float x[128];
+    for (int i = 0; i < 128; i++)
+        x[i] = (float)ref_decode_bf16(x16[i]);
+    if (k_dtype == REF_FP8_E4M3) {
+        float amax = 0.0f;
+        for (int i = 0; i < 128; i++)
+            if (fabsf(x[i]) > amax)
+                amax = fabsf(x[i]);
+        if (amax == 0.0f) {
+            for (int i = 0; i < 128; i++)
+                codes[i] = ref_encode_fp8_e4m3fn(x[i]); /* +-0 */
+            *(float*)scale = 0.0f;
+            return;
+        }
+        float inv = 448.0f / amax;
+        for (int i = 0; i < 128; i++)
+            codes[i] = ref_encode_fp8_e4m3fn(x[i] * inv);
+        *(float*)scale = amax / 448.0f;
+        return;
+    }
+    /* MXFP4 */
+    for (int g = 0; g < 4; g++) {
+        const float* xg = x + 32 * g;
+        float amax = 0.0f;
+        for (int i = 0; i < 32; i++)
+            if (fabsf(xg[i]) > amax)
+                amax = fabsf(xg[i]);
+        int X = -127;
+        if (amax > 0.0f) {
+            int e;
+            frexp((double)amax, &e); /* amax = m 2^e, m in [0.5, 1) */
+            X = (e - 1) - 2;
+        }
+        int biased = X + 127;
+        if (biased < 0)
+            biased = 0;
+        if (biased > 254)
+            biased = 254;
+        ((uint8_t*)scale)[g] = (uint8_t)biased;
+        for (int i = 0; i < 32; i += 2) {
+            uint8_t lo = ref_encode_e2m1(ldexp((double)xg[i], 127 - biased));
+            uint8_t hi = ref_encode_e2m1(ldexp((double)xg[i + 1], 127 - biased));
+            codes[16 * g + i / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+/* Writes n new keys (bf16 [n, 128]) into a cache of n_slots key rows: key i goes to
+ * slot slot_mapping[i]; a negative slot (a padding token) writes nothing. fp8: codes
+ * [n_slots, 128] + float scales [n_slots]; MXFP4: codes [n_slots, 64] + UE8M0
+ * [n_slots, 4]. Slots outside the cache are skipped and counted; returns that count. */
+int64_t ref_kcache_write(const uint16_t* k_new, int64_t n, const int64_t* slot_mapping, int k_dtype,
+                         uint8_t* cache, void* cache_scale, int64_t n_slots)
+{
+    const int kb = k_dtype == REF_FP8_E4M3 ? 128 : 64;
+    const int sb = k_dtype == REF_FP8_E4M3 ? 4 : 4;
+    int64_t bad = 0;
+    for (int64_t i = 0; i < n; i++) {
+        int64_t s = slot_mapping[i];
+        if (s < 0)
+            continue;
+        if (s >= n_slots) {
+            bad++;
+            continue;
+        }
+        quantize_key(k_new + i * 128, k_dtype, cache + s * kb, (uint8_t*)cache_scale + s * sb);
+    }
+    return bad;
+}
+
 int ref_version(void)
 {
     return 1;

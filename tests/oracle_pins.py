@@ -19,6 +19,7 @@ Sizes are tiny so that the whole list runs in seconds.
 """
 from __future__ import annotations
 
+import math
 from fractions import Fraction
 from pathlib import Path
 
@@ -474,6 +475,129 @@ def pin_sparse_columns():
                 assert lg[r, c] == dense[r, tok], f"row {r} col {c}"
             else:
                 assert lg[r, c] == -np.inf, f"row {r} col {c} should be masked"
+
+
+# ----------------------------------------------------------------------------- key-cache writer
+
+
+def pin_fp8_encode_roundtrip_and_saturation():
+    """Every finite e4m3fn value encodes to its own code; magnitudes just above 448 (as
+    value * (448 / amax) can give) stay at 448."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = torch_fp8(codes).astype(np.float32)
+    got = O.encode_fp8(vals)
+    assert np.array_equal(got, codes), "e4m3fn values do not encode to themselves"
+    assert O.encode_fp8(np.float32(448.0) * np.float32(1 + 2 ** -23)) == 0x7E
+    assert O.encode_fp8(-np.float32(460.0)) == 0xFE
+
+
+def pin_fp8_encode_vs_torch():
+    """Nearest-even e4m3fn encoding against torch's independent float8_e4m3fn cast, on
+    random values and on every midpoint between neighbouring codes (the ties)."""
+    rng = np.random.default_rng(81)
+    x = np.concatenate([rng.uniform(-448, 448, 3000), rng.standard_normal(1000) * 1e-2,
+                        rng.standard_normal(500) * 2.0 ** -9]).astype(np.float32)
+    pos = np.unique(np.abs(torch_fp8(np.arange(127, dtype=np.uint8))))
+    mid = (pos[1:] + pos[:-1]) / 2
+    mid = mid[mid.astype(np.float32).astype(np.float64) == mid].astype(np.float32)
+    x = np.concatenate([x, mid, -mid])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_fp8(x), want), "e4m3fn encoding differs from torch"
+
+
+def pin_e2m1_encode_ties():
+    """e2m1 encoding from the OCP table: grid values to their codes, each midpoint of two
+    neighbouring magnitudes to the neighbour with the even code, magnitudes above 6 to 6,
+    negative values to the same magnitude code with the sign bit."""
+    g = e2m1_golden()
+    mags = sorted((v, c) for c, v in g.items() if c < 8)
+    for v, c in mags:
+        assert O.encode_e2m1(v) == c and O.encode_e2m1(-v) == (c | 8), f"grid value {v}"
+    for (v0, c0), (v1, c1) in zip(mags, mags[1:]):
+        even = c0 if c0 % 2 == 0 else c1
+        assert O.encode_e2m1((v0 + v1) / 2) == even, f"tie between {v0} and {v1}"
+        assert O.encode_e2m1(v0 + (v1 - v0) * 0.49) == c0 and O.encode_e2m1(v0 + (v1 - v0) * 0.51) == c1
+    assert O.encode_e2m1(7.5) == 7 and O.encode_e2m1(-100.0) == 15
+
+
+def _bf16_keys(rng, n):
+    x = (rng.standard_normal((n, 128)) * rng.uniform(0.01, 10, (n, 1))).astype(np.float32)
+    x[0] = 0.0                       # all zero
+    x[1] = 0.0
+    x[1, 5] = -3.0e-3                # one non-zero entry
+    x[2, 17] = 3.0e4                 # one outlier
+    x[3, :64] = np.float32(2.0 ** -130)  # subnormal magnitudes next to normal ones
+    return synth.to_bf16_bits(x)
+
+
+def _writer_case(kd, seed):
+    rng = np.random.default_rng(seed)
+    n, n_slots = 40, 64
+    keys = _bf16_keys(rng, n)
+    slots = rng.permutation(n_slots)[:n].astype(np.int64)
+    slots[7] = -1                    # padding token: writes nothing
+    slots[9] = n_slots + 3           # outside the cache: skipped and counted
+    kb, sdt, sw = (128, np.float32, 1) if kd == "fp8" else (64, np.uint8, 4)
+    cache = np.full((n_slots, kb), 0x5A, np.uint8)
+    sc = np.full((n_slots, sw), 0x5A, np.uint8).view(sdt).reshape(n_slots, -1).copy() if kd != "fp8" \
+        else np.full(n_slots, 1234.5, np.float32)
+    bad = O.kcache_write(keys, slots, kd, cache, sc)
+    return keys, slots, cache, sc, bad
+
+
+def pin_kcache_fp8():
+    """fp8 writer: scale = amax / 448 in float32, codes = torch's e4m3fn cast of
+    value * (448 / amax), the largest element at +-448, padding and out-of-range slots
+    untouched."""
+    keys, slots, cache, sc, bad = _writer_case("fp8", 82)
+    assert bad == 1
+    x = torch_bf16(keys).astype(np.float32)
+    for i, s in enumerate(slots):
+        if s < 0 or s >= cache.shape[0]:
+            continue
+        amax = np.abs(x[i]).max()
+        if amax == 0:
+            assert sc[s] == 0 and np.all((cache[s] & 0x7F) == 0), f"zero key {i}"
+            continue
+        assert sc[s] == np.float32(amax) / np.float32(448.0), f"scale of key {i}"
+        y = x[i] * (np.float32(448.0) / np.float32(amax))
+        want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(cache[s], want), f"codes of key {i}"
+        assert (cache[s][np.argmax(np.abs(x[i]))] & 0x7F) == 0x7E
+    untouched = np.setdiff1d(np.arange(cache.shape[0]), slots[(slots >= 0) & (slots < cache.shape[0])])
+    assert np.all(cache[untouched] == 0x5A) and np.all(sc[untouched] == np.float32(1234.5))
+
+
+def pin_kcache_mxfp4():
+    """MXFP4 writer: per group of 32 the UE8M0 byte is floor(log2 amax) - 2 + 127 (closed
+    form from the exact value), every element decodes to within half a grid step of its
+    value (saturating at 6 * 2^X), and the codes equal the input generator's separate
+    OCP MX encoder."""
+    keys, slots, cache, sc, bad = _writer_case("mxfp4", 83)
+    assert bad == 1
+    x = torch_bf16(keys)
+    g = e2m1_golden()
+    for i, s in enumerate(slots):
+        if s < 0 or s >= cache.shape[0]:
+            continue
+        for grp in range(4):
+            xs = x[i, 32 * grp: 32 * grp + 32]
+            amax = float(np.abs(xs).max())
+            X = (math.frexp(amax)[1] - 1 - 2) if amax > 0 else -127
+            biased = min(max(X + 127, 0), 254)
+            assert sc[s, grp] == biased, f"key {i} group {grp} scale"
+            step = 2.0 ** (biased - 127)
+            for j in range(32):
+                b = cache[s, 16 * grp + j // 2]
+                nib = (b & 0xF) if j % 2 == 0 else (b >> 4)
+                v = g[int(nib)] * step
+                t = min(abs(xs[j]), 6.0 * step)
+                half = 0.25 * step if t < 2 * step else (0.5 * step if t < 4 * step else step)
+                assert abs(abs(v) - t) <= half * (1 + 1e-12), f"key {i} element {32 * grp + j}"
+        want_codes, want_sc = synth.to_mxfp4(torch_bf16(keys[i:i + 1]).astype(np.float32))
+        assert np.array_equal(cache[s], want_codes[0]) and np.array_equal(sc[s], want_sc[0]), f"key {i}"
+    untouched = np.setdiff1d(np.arange(cache.shape[0]), slots[(slots >= 0) & (slots < cache.shape[0])])
+    assert np.all(cache[untouched] == 0x5A) and np.all(sc[untouched] == 0x5A)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,16 @@ MUTANTS = {
                   "if (a->v < b->v)\n        return -1;\n    if (a->v > b->v)\n        return 1;"),
     "neg_inf_selected": ("if (isnan(v) || v == -INFINITY)", "if (isnan(v))"),
     "topk_len": ("int64_t n = lens ? lens[r] : ncols;", "int64_t n = ncols;"),
+    "fp8_enc_ties_odd": ("if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));",
+                         "if (d < best_d || (d == best_d && (c & 1) == 1 && (best & 1) == 0)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));"),
+    "fp8_enc_sign": ("return (uint8_t)(best | (signbit(y) ? 0x80 : 0));", "return (uint8_t)best;"),
+    "e2m1_enc_ties_odd": ("if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return (uint8_t)(best | (signbit(v) ? 8 : 0));",
+                          "if (d < best_d || (d == best_d && (c & 1) == 1 && (best & 1) == 0)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return (uint8_t)(best | (signbit(v) ? 8 : 0));"),
+    "writer_scale_inverted": ("*(float*)scale = amax / 448.0f;", "*(float*)scale = 448.0f / amax;"),
+    "writer_fp8_max": ("float inv = 448.0f / amax;", "float inv = 240.0f / amax;"),
+    "writer_mx_exponent": ("X = (e - 1) - 2;", "X = (e - 1) - 1;"),
+    "writer_mx_nibbles": ("codes[16 * g + i / 2] = (uint8_t)(lo | (hi << 4));", "codes[16 * g + i / 2] = (uint8_t)(hi | (lo << 4));"),
+    "writer_padding_slot": ("if (s < 0)\n            continue;", "if (s < 0)\n            s = 0;"),
 }
 
 
