@@ -276,6 +276,41 @@ def other_workloads(D, np, torch, stream, args):
     out["paged_mxfp4_scan_hbm_frac"] = b6 / (ms_scan * 1e-3) / HBM_PEAK
     log(f"128K paged, MXFP4 keys: select {ms*1e3:.1f} us ({c6.tokens/(ms*1e-3)/1e9:.2f} G keys/s), scan "
         f"{ms_scan*1e3:.1f} us ({b6/(ms_scan*1e-3)/1e9:.0f} GB/s, {100*b6/(ms_scan*1e-3)/HBM_PEAK:.1f}% of 8 TB/s)")
+    del q6, w6, kp6, sp6, bt6, sl6, p6, ws6, oi6, lg6
+    # key-cache writer: a whole 128K context of new bf16 keys into permuted page slots,
+    # and one decode step (64 new keys)
+    rng = np.random.default_rng(7)
+    n_new = 131072
+    keys = dev(synth.to_bf16_bits((rng.standard_normal((n_new, 128)) * 0.5).astype(np.float32)).view(np.int16))
+    keys = keys.view(torch.bfloat16)
+    slots = dev(rng.permutation(n_new + 4096)[:n_new].astype(np.int64))
+    for kd, row, srow in (("fp8", 128, 4), ("mxfp4", 64, 4)):
+        cache = torch.empty((n_new + 4096, row), dtype=torch.uint8, device="cuda")
+        sc = (torch.empty(n_new + 4096, dtype=torch.float32, device="cuda") if kd == "fp8"
+              else torch.empty((n_new + 4096, 4), dtype=torch.uint8, device="cuda"))
+        # as captured graphs of 16 launches: one call from Python costs about as much
+        # host time as the whole kernel
+        def graph_ms(n):
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            D.idx_kcache_write(keys[:n], slots[:n], cache, sc, kd)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(cap):
+                g.capture_begin()
+                for _ in range(16):
+                    D.idx_kcache_write(keys[:n], slots[:n], cache, sc, kd)
+                g.capture_end()
+            torch.cuda.synchronize()
+            t, _ = time_loop(g.replay, steps, 2, stream)
+            return t / 16
+        ms = graph_ms(n_new)
+        wb = n_new * (256 + 8 + row + srow)
+        ms64 = graph_ms(64)
+        out[f"kcache_write_{kd}_128k_ms"] = ms
+        out[f"kcache_write_{kd}_hbm_frac"] = wb / (ms * 1e-3) / HBM_PEAK
+        out[f"kcache_write_{kd}_64_keys_us"] = ms64 * 1e3
+        log(f"key-cache writer, {kd}: 131072 keys {ms*1e3:.1f} us ({wb/(ms*1e-3)/1e9:.0f} GB/s, "
+            f"{100*wb/(ms*1e-3)/HBM_PEAK:.1f}% of 8 TB/s); 64 keys {ms64*1e3:.1f} us")
     return out
 
 

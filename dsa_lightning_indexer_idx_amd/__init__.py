@@ -20,7 +20,7 @@ IDX_OK, IDX_ERR_ARG, IDX_ERR_UNSUPPORTED, IDX_ERR_WORKSPACE, IDX_ERR_HIP = 0, 1,
 IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
 IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS = 1, 2, 3
 IDX_TOPK_UNSORTED = 1
-IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK = 1, 2, 4
+IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK, IDX_DEVERR_SLOT = 1, 2, 4, 8
 IDX_HEADS, IDX_DIM, IDX_MAX_K = 64, 128, 2048
 
 KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
@@ -28,7 +28,7 @@ KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
 # Every symbol include/dsaidx.h declares.
 EXPORTS = ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
            "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
-           "idx_last_error", "idx_version", "idx_device_errors", "idx_read_probe")
+           "idx_last_error", "idx_version", "idx_device_errors", "idx_kcache_write", "idx_read_probe")
 
 
 class IdxError(RuntimeError):
@@ -90,8 +90,9 @@ def lib() -> C.CDLL:
         L.idx_device_errors.argtypes = [P]
         L.idx_device_errors.restype = I
         L.idx_read_probe.argtypes = [P, SZ, P, P]
+        L.idx_kcache_write.argtypes = [P, I, I64, P, P, P, I, I64, P]
         for name in ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
-                     "idx_select", "idx_read_probe"):
+                     "idx_select", "idx_read_probe", "idx_kcache_write"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -290,6 +291,20 @@ def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = 
 
 def idx_version() -> int:
     return int(lib().idx_version())
+
+
+def idx_kcache_write(k_new, slot_mapping, k_cache, k_scale, k_dtype="fp8", stream=None) -> None:
+    """Quantise new keys (bf16 [n, 128]) into the key cache at their slots (int64 [n];
+    negative = skip). fp8: k_cache uint8 with 128 bytes per slot (e.g. [pages, page, 128])
+    and k_scale float32 with one per slot; MXFP4: 64 bytes and 4 UE8M0 bytes per slot."""
+    import torch
+    assert k_new.dtype == torch.bfloat16 and k_new.shape[-1] == 128 and k_new.is_contiguous()
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+    kd = {"fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}[k_dtype]
+    row = 128 if kd == IDX_FP8_E4M3 else 64
+    n_slots = k_cache.numel() // row
+    _check(lib().idx_kcache_write(_ptr(k_new), IDX_BF16, k_new.numel() // 128, _ptr(slot_mapping), _ptr(k_cache),
+                                  _ptr(k_scale), kd, n_slots, _stream(stream)))
 
 
 def idx_read_probe(buf, sink, stream=None) -> None:

@@ -381,6 +381,33 @@ const char* idx_last_error(void) { return g_last_error.c_str(); }
 
 int idx_version(void) { return 100; }
 
+idx_status idx_kcache_write(const void* k_new, int new_dtype, int64_t n_new, const int64_t* slot_mapping,
+                            void* k_cache, void* k_scale, int k_dtype, int64_t n_slots, idx_stream_t stream) {
+  const char* fn = "idx_kcache_write";
+  REQUIRE(n_new >= 0 && n_slots >= 0, IDX_ERR_ARG, "%s: n_new = %lld and n_slots = %lld must be >= 0", fn,
+          (long long)n_new, (long long)n_slots);
+  REQUIRE(new_dtype == IDX_BF16, IDX_ERR_UNSUPPORTED, "%s: new keys must be IDX_BF16 (got %d)", fn, new_dtype);
+  REQUIRE(k_dtype == IDX_FP8_E4M3 || k_dtype == IDX_MXFP4, IDX_ERR_UNSUPPORTED,
+          "%s: the cache must be IDX_FP8_E4M3 or IDX_MXFP4 (got %d)", fn, k_dtype);
+  if (n_new == 0) return ok();
+  REQUIRE(k_new && slot_mapping && k_cache && k_scale, IDX_ERR_ARG,
+          "%s: k_new, slot_mapping, k_cache and k_scale must be non-null", fn);
+  REQUIRE(aligned(k_new, 16) && aligned(slot_mapping, 8), IDX_ERR_ARG,
+          "%s: k_new must be 16-byte and slot_mapping 8-byte aligned", fn);
+  REQUIRE(aligned(k_cache, 16) && aligned(k_scale, 4), IDX_ERR_ARG,
+          "%s: k_cache must be 16-byte and k_scale 4-byte aligned", fn);
+  KcacheCall c{};
+  c.k_new = k_new;
+  c.slots = slot_mapping;
+  c.n_new = n_new;
+  c.fmt = k_dtype == IDX_FP8_E4M3 ? FMT_FP8 : FMT_MXFP4;
+  c.cache = (uint8_t*)k_cache;
+  c.scale = k_scale;
+  c.n_slots = n_slots;
+  c.err = device_error_word();
+  return launched(fn, launch_kcache_write(c, (hipStream_t)stream));
+}
+
 idx_status idx_read_probe(const void* buf, size_t bytes, uint32_t* sink, idx_stream_t stream) {
   const char* fn = "idx_read_probe";
   REQUIRE(buf && sink, IDX_ERR_ARG, "%s: buf and sink must be non-null", fn);

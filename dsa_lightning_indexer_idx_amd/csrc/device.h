@@ -22,6 +22,7 @@ constexpr int kTileTokens = 64;  // tokens one wave scores per step: four 16-tok
 constexpr unsigned kErrRange = 1u;
 constexpr unsigned kErrPage = 2u;
 constexpr unsigned kErrBlock = 4u;
+constexpr unsigned kErrSlot = 8u;
 
 __device__ __forceinline__ void flag_error(unsigned* err, unsigned bits) {
   if (err) atomicOr(err, bits);

@@ -72,6 +72,19 @@ size_t topk_workspace_bytes(int rows, int64_t n_cols);
 size_t topk_zeroed_bytes(int rows, int64_t n_cols);
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
 
+// One key-cache write (new bf16 keys quantised into the cache at their slots).
+struct KcacheCall {
+  const void* k_new;      // bf16 [n_new, 128]
+  const int64_t* slots;   // [n_new]; < 0: skip
+  int64_t n_new;
+  int fmt;                // FMT_FP8 or FMT_MXFP4
+  uint8_t* cache;         // fp8 [n_slots, 128] / MXFP4 [n_slots, 64]
+  void* scale;            // fp8 float [n_slots] / MXFP4 UE8M0 [n_slots, 4]
+  int64_t n_slots;
+  unsigned* err;
+};
+hipError_t launch_kcache_write(const KcacheCall& c, hipStream_t stream);
+
 // Streaming-read probe (measurement aid).
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

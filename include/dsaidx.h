@@ -243,7 +243,34 @@ int idx_version(void);
 #define IDX_DEVERR_RANGE 1u  /* row_ks/row_ke/seq_lens/n_cols outside the buffers */
 #define IDX_DEVERR_PAGE 2u   /* block-table entry outside [0, n_pages) */
 #define IDX_DEVERR_BLOCK 4u  /* candidate block outside the row's key range */
+#define IDX_DEVERR_SLOT 8u   /* key-cache slot at or past n_slots (idx_kcache_write) */
 int idx_device_errors(idx_stream_t stream);
+
+/* ------------------------------------------------------------------ key-cache writer */
+
+/*
+ * Quantises new indexer keys into the key cache at their slots: the step that fills
+ * the cache the scan reads (one extra 128-element key per token and layer, DeepSeek-
+ * V3.2 architecture section; fp8 and MXFP4 cache formats of the vLLM sparse_indexer
+ * page). The pages give no quantisation recipe; the readings:
+ *   IDX_FP8_E4M3: scale = amax / 448 (amax = largest |value| of the key), code =
+ *     e4m3fn nearest-even of value * (448 / amax), in float32; amax = 0 gives scale 0
+ *     and zero codes. A key then decodes as code * scale, as idx_logits* read it.
+ *   IDX_MXFP4: OCP MX v1.0 per group of 32: UE8M0 byte = floor(log2 amax) - 2 + 127,
+ *     clamped to [0, 254]; elements value / 2^(byte - 127) to the nearest e2m1 value,
+ *     ties to even, magnitudes above 6 to 6; element 2j in the low nibble of byte j.
+ *
+ * k_new       bf16 [n_new, 128] (new_dtype must be IDX_BF16), 16-byte aligned.
+ * slot_mapping int64 [n_new]: key i goes to cache row slot_mapping[i]; a negative slot
+ *             (a padding token) writes nothing; a slot >= n_slots writes nothing and
+ *             sets IDX_DEVERR_SLOT. For pages of page_size keys, slot = page *
+ *             page_size + offset, the layout idx_logits_paged reads.
+ * k_cache     fp8: uint8 [n_slots, 128]; MXFP4: uint8 [n_slots, 64]; 16-byte aligned.
+ * k_scale     fp8: float [n_slots]; MXFP4: uint8 [n_slots, 4]; 4-byte aligned.
+ * Two entries naming the same slot race (either key may win). Asynchronous on stream.
+ */
+idx_status idx_kcache_write(const void* k_new, int new_dtype, int64_t n_new, const int64_t* slot_mapping,
+                            void* k_cache, void* k_scale, int k_dtype, int64_t n_slots, idx_stream_t stream);
 
 /*
  * Measurement aid, not part of the indexer path: reads ``bytes`` bytes of device

@@ -225,3 +225,23 @@ def test_read_probe_rejects_bad_arguments(L):
     assert L.idx_read_probe(C.c_void_p(0x1008), 1024, C.c_void_p(0x2000), None) == D.IDX_ERR_ARG  # misaligned
     assert L.idx_read_probe(C.c_void_p(0x1000), 1000, C.c_void_p(0x2000), None) == D.IDX_ERR_ARG  # not a multiple of 16
     assert b"idx_read_probe" in L.idx_last_error()
+
+
+def test_kcache_write_rejects_bad_arguments(L):
+    """The key-cache writer checks its arguments on the host before anything is enqueued."""
+    ok = dict(k=C.c_void_p(0x1000), nd=D.IDX_BF16, n=4, s=C.c_void_p(0x2000), c=C.c_void_p(0x3000),
+              sc=C.c_void_p(0x4000), kd=D.IDX_FP8_E4M3, ns=64)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.idx_kcache_write(a["k"], a["nd"], a["n"], a["s"], a["c"], a["sc"], a["kd"], a["ns"], None)
+
+    assert call(nd=D.IDX_FP8_E4M3) == D.IDX_ERR_UNSUPPORTED     # new keys must be bf16
+    assert call(kd=D.IDX_BF16) == D.IDX_ERR_UNSUPPORTED         # cache must be fp8 or MXFP4
+    assert call(n=-1) == D.IDX_ERR_ARG
+    assert call(ns=-5) == D.IDX_ERR_ARG
+    assert call(s=None) == D.IDX_ERR_ARG
+    assert call(c=C.c_void_p(0x3004)) == D.IDX_ERR_ARG        # cache not 16-byte aligned
+    assert call(k=C.c_void_p(0x1008)) == D.IDX_ERR_ARG        # keys not 16-byte aligned
+    assert call(n=0, s=None, c=None) == D.IDX_OK              # nothing to write
+    assert b"idx_kcache_write" in L.idx_last_error() or L.idx_last_error() == b""
