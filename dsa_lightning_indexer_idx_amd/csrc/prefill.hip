@@ -2,8 +2,11 @@
 // query rows that share one key array (a prefill chunk against its context, causal
 // mask carried by row_ke).
 //
-//   * A workgroup owns kQB consecutive queries (two per wave) and walks the union of
-//     their key ranges in 64-key tiles; query blocks run longest range first.
+//   * A workgroup owns kQB consecutive queries (two per wave) and walks one of kSplit
+//     pieces of the union of their key ranges in 64-key tiles; query blocks run longest
+//     range first. Two pieces per block let short causal blocks' workgroups backfill
+//     behind long ones (every workgroup of the chunk is resident at once otherwise, so
+//     the longest block alone would set the time).
 //   * Tiles are staged in LDS, three slots deep: all 256 threads load tile t + 2 (one
 //     16-byte chunk each per load) while tile t computes, and store it chunk-major
 //     (chunk c of key k at c * 1 KiB + k * 16) so the stores and the MFMA-layout reads
@@ -32,12 +35,16 @@ namespace dsaidx {
 #ifndef DSAIDX_PREFILL_QW
 #define DSAIDX_PREFILL_QW 2
 #endif
+#ifndef DSAIDX_PREFILL_SPLIT
+#define DSAIDX_PREFILL_SPLIT 2
+#endif
 #ifndef DSAIDX_PREFILL_WAVES_PER_SIMD
 #define DSAIDX_PREFILL_WAVES_PER_SIMD 2
 #endif
 constexpr int kQW = DSAIDX_PREFILL_QW;  // queries per wave
 constexpr int kPThreads = 256;          // 4 waves
 constexpr int kQB = 4 * kQW;            // queries per workgroup
+constexpr int kSplit = DSAIDX_PREFILL_SPLIT;  // workgroups per query block (key-range pieces)
 constexpr int kSlots = 3;        // LDS tile slots
 constexpr int kTileBytes = kTileTokens * kDim;
 struct PrefillArgs {
@@ -79,7 +86,8 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
   const int wave = tid / kWave;
   const int g = lane >> 4, c16 = lane & 15;
   const int nblocks = (a.rows + kQB - 1) / kQB;
-  const int qb = nblocks - 1 - (int)blockIdx.x;  // longest ranges first (causal chunks)
+  const int qb = nblocks - 1 - (int)blockIdx.x / kSplit;  // longest ranges first (causal chunks)
+  const int piece = (int)blockIdx.x % kSplit;
   const int q0 = qb * kQB;
 
   // key range of each of this wave's two queries, and of the whole block
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
       s = min(max(s0, (int64_t)0), a.n_keys);
       e = min(max(e0, s), a.n_keys);
       e = min(e, s + a.ld);
-      if (lane == 0 && (s != s0 || e != e0)) flag_error(a.err, kErrRange);
+      if (lane == 0 && piece == 0 && (s != s0 || e != e0)) flag_error(a.err, kErrRange);
     }
     qs[u] = s;
     qe[u] = e;
@@ -161,7 +169,10 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
   }
   __syncthreads();
   const int64_t lo = s_lo, hi = s_hi;
-  const int ntiles = hi > lo ? (int)((hi - lo + kTileTokens - 1) / kTileTokens) : 0;
+  const int ntiles_all = hi > lo ? (int)((hi - lo + kTileTokens - 1) / kTileTokens) : 0;
+  // this workgroup's piece of the block's tiles: [t_begin, ntiles)
+  const int t_begin = (int)((int64_t)ntiles_all * piece / kSplit);
+  const int ntiles = (int)((int64_t)ntiles_all * (piece + 1) / kSplit);
 
   // A operand of the pieces tile: row rho = l % 16 < 10 holds piece rho % 5 of query
   // rho / 5 (dims 32g .. 32g+31, the same K order as the keys); coefficient of the
@@ -226,13 +237,13 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
 
   v4i x0, x1;
   float xs = 0.f;
-  if (ntiles > 0) {
-    fetch(0, x0, x1, xs);
-    stash(0, x0, x1, xs);
+  if (t_begin < ntiles) {
+    fetch(t_begin, x0, x1, xs);
+    stash(t_begin, x0, x1, xs);
   }
-  if (ntiles > 1) {
-    fetch(1, x0, x1, xs);
-    stash(1, x0, x1, xs);
+  if (t_begin + 1 < ntiles) {
+    fetch(t_begin + 1, x0, x1, xs);
+    stash(t_begin + 1, x0, x1, xs);
   }
   __syncthreads();
   // Per tile, the four 16-key groups are software-pipelined in source order: the 9
@@ -262,8 +273,8 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
 #pragma unroll
       for (int i = 0; i < 4; ++i) p1 = fmaf(wr[kQW - 1][h][i], fabsf(r[5 + h][i]), p1);
   };
-  v8i kb_next = read_b(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
+  v8i kb_next = read_b(t_begin, 0);
+  for (int t = t_begin; t < ntiles; ++t) {
     if (t + 2 < ntiles) fetch(t + 2, x0, x1, xs);
     const int64_t t0 = lo + (int64_t)t * kTileTokens;
     const bool act0 = qv[0] && t0 < qe[0] && t0 + kTileTokens > qs[0];
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
   // columns past each query's length
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (!qv[u] || a.skip_tail) continue;
+    if (!qv[u] || a.skip_tail || piece != 0) continue;
     float* out = a.logits + (int64_t)(q0 + kQW * wave + u) * a.ld;
     for (int64_t c = (qe[u] - qs[u]) + lane; c < a.ld; c += kWave) __builtin_nontemporal_store(-__builtin_inff(), &out[c]);
   }
@@ -330,7 +341,7 @@ hipError_t launch_prefill(const ScoreCall& c, hipStream_t stream) {
   a.err = c.err;
   a.skip_tail = c.skip_tail;
   const int nblocks = (c.rows + kQB - 1) / kQB;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)nblocks), dim3(kPThreads), 0, stream, a);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)(nblocks * kSplit)), dim3(kPThreads), 0, stream, a);
   return hipGetLastError();
 }
 
