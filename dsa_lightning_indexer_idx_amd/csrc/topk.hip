@@ -93,6 +93,32 @@ __device__ __forceinline__ void wave_append(const bool (&take)[U], const T (&ite
   }
 }
 
+// Appends item[j] for every take[j] (U per lane) to an LDS list: each lane counts its
+// own entries, one wave prefix sum and one LDS atomic per wave place them, and each lane
+// writes its entries in order. Cheaper than wave_append when a lane holds many entries
+// and few are taken. Every lane of the wave must call it.
+template <int U, class T>
+__device__ __forceinline__ void lane_append(const bool (&take)[U], const T (&item)[U], T* list, uint32_t* count,
+                                            uint32_t cap) {
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < U; ++j) mine += take[j] ? 1u : 0u;
+  const uint32_t incl = wave_inclusive_sum(mine);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+  if (tot == 0) return;
+  uint32_t base = 0;
+  if (lane_id() == 0) base = atomicAdd(count, tot);
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+  uint32_t slot = base + incl - mine;
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    if (take[j]) {
+      if (slot < cap) list[slot] = item[j];
+      ++slot;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ radix select
 
 struct RadixShared {
@@ -204,10 +230,15 @@ __device__ void find_cut(const uint32_t* h, int k, CutInfo& ci) {
   constexpr int waves = NT / kWave;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
-  // thread t owns bins kHistBins-1-per*t down to kHistBins-per*(t+1), highest first
+  // thread t owns bins kHistBins-1-per*t down to kHistBins-per*(t+1), highest first;
+  // they stay in registers for the search below (one round of loads, not one per step)
+  uint32_t hb[per];
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < per; ++j) c += h[kHistBins - 1 - per * tid - j];
+  for (int j = 0; j < per; ++j) {
+    hb[j] = h[kHistBins - 1 - per * tid - j];
+    c += hb[j];
+  }
   uint32_t incl = wave_inclusive_sum(c);
   if (lane_id() == kWave - 1) ci.sums[wave] = incl;
   __syncthreads();
@@ -230,16 +261,16 @@ __device__ void find_cut(const uint32_t* h, int k, CutInfo& ci) {
   }
   if (total > (uint32_t)k && excl < (uint32_t)k && (uint32_t)k <= incl) {
     uint32_t cum = excl;
+    bool found = false;
+#pragma unroll
     for (int j = 0; j < per; ++j) {
-      const int b = kHistBins - 1 - per * tid - j;
-      const uint32_t hb = h[b];
-      if (cum + hb >= (uint32_t)k) {
-        ci.bin = b;
+      if (!found && cum + hb[j] >= (uint32_t)k) {
+        ci.bin = kHistBins - 1 - per * tid - j;
         ci.above = cum;
-        ci.count = hb;
-        break;
+        ci.count = hb[j];
+        found = true;
       }
-      cum += hb;
+      cum += hb[j];
     }
   }
   __syncthreads();
@@ -648,8 +679,8 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkCall a) {
       tc[j] = compact && bin == cut;
       col[j] = (uint16_t)i;
     }
-    wave_append<U2>(tw, col, sel, &n_sel, (uint32_t)kMaxK);
-    wave_append<U2>(tc, col, u.cand, &n_cand, (uint32_t)kShortCandCap);
+    lane_append<U2>(tw, col, sel, &n_sel, (uint32_t)kMaxK);
+    lane_append<U2>(tc, col, u.cand, &n_cand, (uint32_t)kShortCandCap);
   }
   __syncthreads();
 
@@ -770,7 +801,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, Lo
   for (int64_t b = s0; b < s1; b += kSegStep) {
     float4 v[kSegGroups];
 #pragma unroll
-    for (int j = 0; j < kSegGroups; ++j) v[j] = load4<V4, true>(row, b + ((int64_t)j * kSegThreads + threadIdx.x) * 4, s1);
+    for (int j = 0; j < kSegGroups; ++j) v[j] = load4<V4, false>(row, b + ((int64_t)j * kSegThreads + threadIdx.x) * 4, s1);
     bool tw[4 * kSegGroups], tc[4 * kSegGroups];
     uint32_t col[4 * kSegGroups];
 #pragma unroll
@@ -786,8 +817,8 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, Lo
         col[4 * j + c] = (uint32_t)(i0 + c);
       }
     }
-    wave_append<4 * kSegGroups>(tw, col, lwin, &n_lwin, (uint32_t)kMaxK);
-    wave_append<4 * kSegGroups>(tc, col, lcand, &n_lcand, (uint32_t)kSegCandCap);
+    lane_append<4 * kSegGroups>(tw, col, lwin, &n_lwin, (uint32_t)kMaxK);
+    lane_append<4 * kSegGroups>(tc, col, lcand, &n_lcand, (uint32_t)kSegCandCap);
   }
   __syncthreads();
   uint32_t* cnt = ws.counts + 2 * (int64_t)r;
