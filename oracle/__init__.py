@@ -65,6 +65,8 @@ def _load(path) -> C.CDLL:
     L.ref_encode_e2m1.restype = C.c_uint8
     L.ref_kcache_write.argtypes = [P, I64, P, I, P, P, I64]
     L.ref_kcache_write.restype = I64
+    L.ref_candidate_blocks.argtypes = [P, I64, P, I64, I, I, I, P, I64, P]
+    L.ref_candidate_blocks.restype = None
     return L
 
 
@@ -190,6 +192,21 @@ def topk(logits, k, lens=None):
     val = np.empty((rows, k), np.float32)
     lib().ref_topk(_p(lg), ncols, _p(ln), ncols, rows, k, _p(idx), _p(val), k)
     return idx, val
+
+
+def candidate_blocks(logits, block, n_top, lens=None):
+    """Candidate-source step of the two-level indexer: (cand int32 [rows, n_top], n_cand
+    int32 [rows]). A block's score is the largest score of its tokens; the n_top best
+    blocks (higher score first, equal scores by lower id) in ascending id, -1 padded.
+    Row r covers its first lens[r] tokens (all columns when lens is None)."""
+    lg = _c(logits, np.float32)
+    rows, ncols = lg.shape
+    ln = None if lens is None else _c(lens, np.int32)
+    cand = np.empty((rows, n_top), np.int32)
+    n_cand = np.empty(rows, np.int32)
+    lib().ref_candidate_blocks(_p(lg), ncols, _p(ln), ncols, rows, block, n_top,
+                               _p(cand), n_top, _p(n_cand))
+    return cand, n_cand
 
 
 def columns_to_tokens(col_idx, cand, block):

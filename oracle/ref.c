@@ -295,6 +295,67 @@ void ref_topk(const float* logits, int64_t ld, const int32_t* lens, int64_t ncol
     }
 }
 
+/* ---------------------------------------------------------------- candidate blocks
+ *
+ * The two-level indexer (vLLM sparse_indexer page: a candidate-source layer publishes
+ * candidate_topk_blocks blocks of candidate_block_size tokens that the consuming
+ * layers score; DeepGEMM release note: consumers score only the blocks handed to
+ * them). The pages do not say how the source layer ranks blocks; the reading taken
+ * here: a block's score is the largest score of its tokens (-inf and NaN entries do
+ * not count, and a block with no other entry has no score and is never published);
+ * the n_top blocks first in the selection order above (higher score first, equal
+ * scores by lower block id) are published, in ascending block id as the consumers
+ * require, then -1 up to n_top. Returns nothing; n_cand[r] gets the published count.
+ * Row r covers tokens 0 .. lens[r]-1 (lens clamped to [0, ncols]); block b covers
+ * tokens b*block .. b*block+block-1 of those. */
+void ref_candidate_blocks(const float* logits, int64_t ld, const int32_t* lens, int64_t ncols, int rows,
+                          int block, int n_top, int32_t* cand, int64_t cand_ld, int32_t* n_cand)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < rows; r++) {
+        int64_t n = lens ? lens[r] : ncols;
+        if (n < 0)
+            n = 0;
+        if (n > ncols)
+            n = ncols;
+        const int64_t nblk = (n + block - 1) / block;
+        scored* buf = malloc(sizeof(scored) * (size_t)(nblk > 0 ? nblk : 1));
+        int64_t m = 0;
+        for (int64_t b = 0; b < nblk; b++) {
+            int have = 0;
+            float best = 0.0f;
+            for (int64_t c = b * block; c < n && c < (b + 1) * block; c++) {
+                float v = logits[r * ld + c];
+                if (!(v > -INFINITY)) /* -inf or NaN */
+                    continue;
+                if (!have || v > best)
+                    best = v;
+                have = 1;
+            }
+            if (have) {
+                buf[m].v = best;
+                buf[m].idx = (int32_t)b;
+                m++;
+            }
+        }
+        qsort(buf, (size_t)m, sizeof(scored), by_score);
+        const int64_t take = m < n_top ? m : n_top;
+        /* publish in ascending block id: mark the chosen blocks, then walk the ids */
+        unsigned char* chosen = calloc((size_t)(nblk > 0 ? nblk : 1), 1);
+        for (int64_t i = 0; i < take; i++)
+            chosen[buf[i].idx] = 1;
+        int64_t o = 0;
+        for (int64_t b = 0; b < nblk; b++)
+            if (chosen[b])
+                cand[r * cand_ld + o++] = (int32_t)b;
+        for (; o < n_top; o++)
+            cand[r * cand_ld + o] = -1;
+        n_cand[r] = (int32_t)take;
+        free(chosen);
+        free(buf);
+    }
+}
+
 /* ---------------------------------------------------------------- key-cache writer
  *
  * Each new key (128 bf16 values) is quantised into the cache format and stored at

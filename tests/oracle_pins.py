@@ -401,6 +401,69 @@ def pin_topk_pads_short_rows():
     assert val[0, :3].tolist() == [5.0, 2.0, 1.0] and np.all(val[0, 3:] == -np.inf)
 
 
+# ----------------------------------------------------------------------------- candidate blocks
+
+
+def pin_candidate_blocks_by_hand():
+    """Blocks of 4: scores [.1 .5 -1 2 | 3 0 0 0 | 1 1 1 1 | -inf x4 | 3 -inf nan 2].
+    Block maxima 2, 3, 1, (none), 3: the best two are blocks 1 and 4 (equal 3, lower id
+    first), published ascending; with n_top = 4 block 0 joins, block 3 never does."""
+    lg = np.array([[0.1, 0.5, -1, 2, 3, 0, 0, 0, 1, 1, 1, 1, -np.inf, -np.inf, -np.inf, -np.inf,
+                    3, -np.inf, np.nan, 2]], np.float32)
+    cand, n = O.candidate_blocks(lg, 4, 2)
+    assert cand.tolist() == [[1, 4]] and n.tolist() == [2]
+    cand, n = O.candidate_blocks(lg, 4, 3)
+    assert cand.tolist() == [[0, 1, 4]] and n.tolist() == [3]
+    cand, n = O.candidate_blocks(lg, 4, 6)
+    assert cand.tolist() == [[0, 1, 2, 4, -1, -1]] and n.tolist() == [4]
+    # the last block may be partial: lens 17 keeps token 16 (score 3) of block 4
+    cand, n = O.candidate_blocks(lg, 4, 1, lens=np.array([17], np.int32))
+    assert cand.tolist() == [[1]] and n.tolist() == [1]
+    cand, n = O.candidate_blocks(lg, 4, 2, lens=np.array([16], np.int32))
+    assert cand.tolist() == [[0, 1]] and n.tolist() == [2]
+
+
+def pin_candidate_blocks_vs_token_ranking():
+    """The n_top best blocks by maximum are the first n_top distinct blocks met walking
+    the row's tokens in the exact top-k order (value desc, index asc): a block's rank is
+    that of its best token, and equal maxima order by the lower token, hence the lower
+    block. Checked by that walk over rows with ties, signed zeros, absent entries and
+    ragged lengths."""
+    rng = np.random.default_rng(53)
+    rows, n = 7, 900
+    lg = rng.integers(-12, 12, size=(rows, n)).astype(np.float32) / 4
+    lg[rng.random((rows, n)) < 0.05] = -0.0
+    lg[rng.random((rows, n)) < 0.2] = -np.inf
+    lg[rng.random((rows, n)) < 0.02] = np.nan
+    lg[4, 128:512] = -np.inf
+    lg[5] = 1.5
+    lens = np.array([n, n - 5, 640, 129, n, 300, 0], np.int32)
+    for block, n_top in ((64, 5), (128, 3), (128, 8), (256, 2)):
+        cand, n_cand = O.candidate_blocks(lg, block, n_top, lens)
+        for r in range(rows):
+            cols = np.arange(lens[r])
+            v = lg[r, :lens[r]].astype(np.float64)
+            ok = ~np.isnan(v) & (v != -np.inf)
+            cols, v = cols[ok], np.where(v[ok] == 0, 0.0, v[ok])
+            seen = []
+            for c in cols[np.lexsort((cols, -v))]:
+                if int(c) // block not in seen:
+                    seen.append(int(c) // block)
+                if len(seen) == n_top:
+                    break
+            want = sorted(seen) + [-1] * (n_top - len(seen))
+            assert cand[r].tolist() == want, f"row {r} block {block}: {cand[r]} != {want}"
+            assert n_cand[r] == len(seen)
+
+
+def pin_candidate_blocks_all_equal():
+    lg = np.full((2, 1000), -2.25, np.float32)
+    cand, n = O.candidate_blocks(lg, 128, 3)
+    assert cand.tolist() == [[0, 1, 2]] * 2 and n.tolist() == [3, 3]
+    cand, n = O.candidate_blocks(lg, 128, 10)
+    assert cand.tolist() == [list(range(8)) + [-1, -1]] * 2 and n.tolist() == [8, 8]
+
+
 # ----------------------------------------------------------------------------- key sources
 
 

@@ -51,6 +51,13 @@ MUTANTS = {
     "writer_fp8_max": ("float inv = 448.0f / amax;", "float inv = 240.0f / amax;"),
     "writer_mx_exponent": ("X = (e - 1) - 2;", "X = (e - 1) - 1;"),
     "writer_mx_nibbles": ("codes[16 * g + i / 2] = (uint8_t)(lo | (hi << 4));", "codes[16 * g + i / 2] = (uint8_t)(hi | (lo << 4));"),
+    "cand_first_not_max": ("if (!have || v > best)", "if (!have)"),
+    "cand_min_not_max": ("if (!have || v > best)", "if (!have || v < best)"),
+    "cand_partial_block_dropped": ("const int64_t nblk = (n + block - 1) / block;", "const int64_t nblk = n / block;"),
+    "cand_selection_order": ("if (chosen[b])\n                cand[r * cand_ld + o++] = (int32_t)b;",
+                             "if (b < take)\n                cand[r * cand_ld + o++] = buf[b].idx;"),
+    "cand_absent_counted": ("if (!(v > -INFINITY)) /* -inf or NaN */", "if (isnan(v))"),
+    "cand_lens_ignored": ("int64_t n = lens ? lens[r] : ncols;\n        if (n < 0)", "int64_t n = ncols;\n        if (n < 0)"),
     "writer_padding_slot": ("if (s < 0)\n            continue;", "if (s < 0)\n            s = 0;"),
 }
 
