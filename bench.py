@@ -277,6 +277,34 @@ def other_workloads(D, np, torch, stream, args):
     log(f"128K paged, MXFP4 keys: select {ms*1e3:.1f} us ({c6.tokens/(ms*1e-3)/1e9:.2f} G keys/s), scan "
         f"{ms_scan*1e3:.1f} us ({b6/(ms_scan*1e-3)/1e9:.0f} GB/s, {100*b6/(ms_scan*1e-3)/HBM_PEAK:.1f}% of 8 TB/s)")
     del q6, w6, kp6, sp6, bt6, sl6, p6, ws6, oi6, lg6
+    # candidate-source step: publish 64 blocks of 128 per row from the scores of a 128K
+    # source layer (64 rows x 131072 columns, 32 MiB: 8 copies rotated in one graph)
+    cs = synth.candidate_scores()
+    lgs = [dev(cs.logits)]
+    lgs += [lgs[0].clone() for _ in range(7)]
+    lns = dev(cs.lens)
+    cnd = torch.empty((cs.rows, cs.n_top), dtype=torch.int32, device="cuda")
+    ncd = torch.empty(cs.rows, dtype=torch.int32, device="cuda")
+    wsc = torch.empty(D.idx_candidate_blocks_workspace(cs.rows, cs.logits.shape[1]), dtype=torch.uint8, device="cuda")
+    for t in lgs:
+        D.idx_candidate_blocks(t, cs.block, cs.n_top, lens=lns, cand=cnd, n_cand=ncd, workspace=wsc)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        g.capture_begin()
+        for t in lgs:
+            D.idx_candidate_blocks(t, cs.block, cs.n_top, lens=lns, cand=cnd, n_cand=ncd, workspace=wsc)
+        g.capture_end()
+    torch.cuda.synchronize()
+    ms, _ = time_loop(g.replay, steps, 2, stream)
+    ms /= len(lgs)
+    cb = int(cs.lens.astype(np.int64).sum()) * 4 + cs.rows * (cs.n_top + 2) * 4
+    out["candidate_blocks_ms"] = ms
+    out["candidate_blocks_hbm_frac"] = cb / (ms * 1e-3) / HBM_PEAK
+    log(f"candidate blocks (64 rows x 128K scores, 64 of 128): {ms*1e3:.1f} us per call "
+        f"({cb/(ms*1e-3)/1e9:.0f} GB/s, {100*cb/(ms*1e-3)/HBM_PEAK:.1f}% of 8 TB/s, graph of {len(lgs)})")
+    del lgs, lns, cnd, ncd, wsc, g
     # key-cache writer: a whole 128K context of new bf16 keys into permuted page slots,
     # and one decode step (64 new keys)
     rng = np.random.default_rng(7)

@@ -28,7 +28,8 @@ KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
 # Every symbol include/dsaidx.h declares.
 EXPORTS = ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
            "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
-           "idx_last_error", "idx_version", "idx_device_errors", "idx_kcache_write", "idx_read_probe")
+           "idx_last_error", "idx_version", "idx_device_errors", "idx_kcache_write", "idx_read_probe",
+           "idx_candidate_blocks", "idx_candidate_blocks_workspace")
 
 
 class IdxError(RuntimeError):
@@ -91,8 +92,11 @@ def lib() -> C.CDLL:
         L.idx_device_errors.restype = I
         L.idx_read_probe.argtypes = [P, SZ, P, P]
         L.idx_kcache_write.argtypes = [P, I, I64, P, P, P, I, I64, P]
+        L.idx_candidate_blocks.argtypes = [P, I64, P, I64, I, I, I, P, I64, P, P, SZ, P]
+        L.idx_candidate_blocks_workspace.argtypes = [I, I64]
+        L.idx_candidate_blocks_workspace.restype = SZ
         for name in ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
-                     "idx_select", "idx_read_probe", "idx_kcache_write"):
+                     "idx_select", "idx_read_probe", "idx_kcache_write", "idx_candidate_blocks"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -216,6 +220,36 @@ def idx_topk(logits, k: int, *, lens=None, n_cols: int | None = None, sorted: bo
                           _ptr(out_val), out_idx.shape[1], 0 if sorted else IDX_TOPK_UNSORTED,
                           _ptr(workspace), wsb, _stream(stream)))
     return out_idx, out_val
+
+
+def idx_candidate_blocks_workspace(rows: int, n_cols: int) -> int:
+    return int(lib().idx_candidate_blocks_workspace(rows, n_cols))
+
+
+def idx_candidate_blocks(logits, block_size: int, n_top: int, *, lens=None, n_cols: int | None = None,
+                         cand=None, n_cand=None, workspace=None, stream=None):
+    """Candidate blocks of each row (C: idx_candidate_blocks). Returns (cand int32
+    [rows, n_top] ascending block ids, -1 padded; n_cand int32 [rows]). ``logits`` may be
+    a view of whole rows of a wider matrix (unit column stride; ld = its row stride)."""
+    import torch
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit column stride")
+    _need(lens, "lens")
+    rows = logits.shape[0]
+    ld = max(logits.stride(0), logits.shape[1], 1)
+    n_cols = logits.shape[1] if n_cols is None else n_cols
+    if cand is None:
+        cand = torch.empty((rows, n_top), dtype=torch.int32, device=logits.device)
+    if n_cand is None:
+        n_cand = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    need = idx_candidate_blocks_workspace(rows, n_cols)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().idx_candidate_blocks(_ptr(logits), ld, _ptr(lens), n_cols, rows, block_size, n_top,
+                                      _ptr(cand), cand.shape[1], _ptr(n_cand), _ptr(workspace), wsb,
+                                      _stream(stream)))
+    return cand, n_cand
 
 
 class Problem:

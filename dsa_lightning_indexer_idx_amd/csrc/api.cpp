@@ -34,6 +34,7 @@ idx_status ok() {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int64_t kMaxCols = 0x7FFFFFFF;
+constexpr int kMaxCandBlockSize = 4096;
 
 #define REQUIRE(cond, status, ...) \
   do {                             \
@@ -380,6 +381,46 @@ const char* idx_status_string(idx_status s) {
 const char* idx_last_error(void) { return g_last_error.c_str(); }
 
 int idx_version(void) { return 100; }
+
+size_t idx_candidate_blocks_workspace(int rows, int64_t n_cols) { return cand_workspace_bytes(rows, n_cols); }
+
+idx_status idx_candidate_blocks(const float* logits, int64_t ld, const int32_t* lens, int64_t n_cols, int rows,
+                                int block_size, int n_top, int32_t* cand_blocks, int64_t cand_ld, int32_t* n_cand,
+                                void* workspace, size_t workspace_bytes, idx_stream_t stream) {
+  const char* fn = "idx_candidate_blocks";
+  REQUIRE(rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, rows);
+  REQUIRE(block_size >= 64 && block_size % 64 == 0 && block_size <= kMaxCandBlockSize, IDX_ERR_UNSUPPORTED,
+          "%s: block_size = %d must be a multiple of 64 in [64, %d]", fn, block_size, kMaxCandBlockSize);
+  REQUIRE(n_top >= 1, IDX_ERR_ARG, "%s: n_top = %d must be >= 1", fn, n_top);
+  if (rows == 0) return ok();
+  REQUIRE(logits && cand_blocks && n_cand, IDX_ERR_ARG, "%s: logits, cand_blocks and n_cand must be non-null", fn);
+  REQUIRE(n_cols >= 0 && n_cols <= kMaxCols, IDX_ERR_ARG, "%s: n_cols = %lld out of range", fn, (long long)n_cols);
+  REQUIRE(ld >= n_cols && ld >= 1, IDX_ERR_ARG, "%s: ld = %lld < n_cols = %lld", fn, (long long)ld,
+          (long long)n_cols);
+  REQUIRE(cand_ld >= n_top, IDX_ERR_ARG, "%s: cand_ld = %lld < n_top = %d", fn, (long long)cand_ld, n_top);
+  REQUIRE((n_cols + block_size - 1) / block_size <= kCandMaxBlocks, IDX_ERR_UNSUPPORTED,
+          "%s: %lld columns make more than %d blocks of %d", fn, (long long)n_cols, kCandMaxBlocks, block_size);
+  REQUIRE(aligned(logits, 4) && aligned(cand_blocks, 4) && aligned(n_cand, 4), IDX_ERR_ARG,
+          "%s: arrays must be 4-byte aligned", fn);
+  idx_status s = check_ints(fn, {lens});
+  if (s != IDX_OK) return s;
+  const size_t need = cand_workspace_bytes(rows, n_cols);
+  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), IDX_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(need == 0 || aligned(workspace, 256), IDX_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
+  CandCall c{};
+  c.logits = logits;
+  c.ld = ld;
+  c.lens = lens;
+  c.n_cols = n_cols;
+  c.rows = rows;
+  c.block = block_size;
+  c.n_top = n_top;
+  c.cand = cand_blocks;
+  c.cand_ld = cand_ld;
+  c.n_cand = n_cand;
+  return launched(fn, launch_candidate_blocks(c, workspace, (hipStream_t)stream));
+}
 
 idx_status idx_kcache_write(const void* k_new, int new_dtype, int64_t n_new, const int64_t* slot_mapping,
                             void* k_cache, void* k_scale, int k_dtype, int64_t n_slots, idx_stream_t stream) {

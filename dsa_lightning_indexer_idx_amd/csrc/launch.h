@@ -85,6 +85,24 @@ struct KcacheCall {
 };
 hipError_t launch_kcache_write(const KcacheCall& c, hipStream_t stream);
 
+// One candidate-block publication (the candidate-source step of the two-level indexer).
+struct CandCall {
+  const float* logits;    // [rows, ld]
+  int64_t ld;
+  const int32_t* lens;    // optional: row length, clamped to [0, n_cols]
+  int64_t n_cols;
+  int rows;
+  int block;              // tokens per block, a multiple of 64
+  int n_top;
+  int32_t* cand;          // [rows, cand_ld]
+  int64_t cand_ld;
+  int32_t* n_cand;        // [rows]
+};
+// Most blocks one row may have (LDS of the selection workgroup).
+constexpr int kCandMaxBlocks = 16384;
+size_t cand_workspace_bytes(int rows, int64_t n_cols);
+hipError_t launch_candidate_blocks(const CandCall& c, void* workspace, hipStream_t stream);
+
 // Streaming-read probe (measurement aid).
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

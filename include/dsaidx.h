@@ -171,6 +171,39 @@ idx_status idx_topk(const float* logits, int64_t ld, const int32_t* lens, int64_
 
 size_t idx_topk_workspace(int rows, int64_t n_cols, int k);
 
+/* ------------------------------------------------------------------ candidate blocks */
+
+/*
+ * idx_candidate_blocks: the candidate-source step of the two-level indexer. A layer
+ * that scored its whole context publishes, per row, the candidate blocks the
+ * consuming layers then score with idx_logits_sparse_blocks (vLLM sparse_indexer
+ * page: candidate_topk_blocks blocks of candidate_block_size tokens published by the
+ * candidate-source layer; DeepGEMM sparse MQA-logits release note).
+ *
+ * Row r considers logits[r * ld + c] for c < n, n = lens ? lens[r] : n_cols (clamped
+ * to [0, n_cols]); block b holds columns b * block_size .. b * block_size +
+ * block_size - 1 of those (the last block may be partial). The pages give no
+ * ranking rule; the reading taken: a block's score is the largest score of its
+ * columns (-inf and NaN entries do not count; a block with none has no score and is
+ * never published). The n_top blocks first in the order "higher score first, equal
+ * scores (-0.0 == +0.0) by lower block id" are written in ASCENDING block id to
+ * cand_blocks[r * cand_ld + i], i < n_cand[r] = min(n_top, blocks with a score), and
+ * -1 to positions n_cand[r] .. n_top-1 (positions from n_top on are not written).
+ * Equivalently: the first n_top distinct blocks met walking the row in idx_topk's
+ * order. cand_blocks and n_cand (times block_size, as the valid column count) are the
+ * cand_blocks and n_cols arguments of idx_logits_sparse_blocks.
+ *
+ * block_size: a multiple of 64 in [64, 4096] (IDX_ERR_UNSUPPORTED otherwise), and
+ * ceil(n_cols / block_size) <= 16384. 1 <= n_top <= cand_ld; n_cols <= ld.
+ * workspace: idx_candidate_blocks_workspace(rows, n_cols) bytes, 256-byte aligned
+ * (may be NULL when that is 0). Asynchronous on stream.
+ */
+idx_status idx_candidate_blocks(const float* logits, int64_t ld, const int32_t* lens, int64_t n_cols, int rows,
+                                int block_size, int n_top, int32_t* cand_blocks, int64_t cand_ld,
+                                int32_t* n_cand, void* workspace, size_t workspace_bytes, idx_stream_t stream);
+
+size_t idx_candidate_blocks_workspace(int rows, int64_t n_cols);
+
 /* ------------------------------------------------------------------ fused select */
 
 typedef enum idx_mode {

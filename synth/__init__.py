@@ -391,6 +391,64 @@ def sparse_blocks(seed: int = 5, rows: int = 64, ctx: int = 131072, n_blocks: in
                   block, topk, {"ctx": ctx, "n_blocks": n_blocks})
 
 
+@dataclass
+class Scores:
+    """A candidate-source layer's score matrix (fp32 [rows, ld]) with row lengths."""
+    name: str
+    logits: np.ndarray
+    lens: np.ndarray
+    block: int
+    n_top: int
+    info: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return self.logits.shape[0]
+
+
+POISON_SCORE = np.float32(1e30)  # past a row's length: would win every block if read
+
+
+def candidate_scores(seed: int = 7, rows: int = 64, min_len: int = 65536, max_len: int = 131072,
+                     ld: int | None = None, block: int = 128, n_top: int = 64,
+                     adversarial: bool = False) -> Scores:
+    """Scores of a layer that scored its whole context, the input of the candidate-block
+    step: len_r ~ U{min_len..max_len} (the long paged decode recipe), scores N(0, 1) in
+    fp32, columns at or past len_r set to a huge poison score. ``adversarial`` gives row r
+    the pattern r % 8 instead: Gaussian; multiples of 1/4 in [-3, 3) (many equal block
+    maxima); one constant; signed zeros; Gaussian with -inf stretches (masked keys) and
+    NaN holes; a row of fewer than n_top blocks; an empty row; huge magnitudes."""
+    r = _rngs(seed)
+    ld = max_len if ld is None else ld
+    lens = r["lens"].integers(min_len, max_len + 1, size=rows).astype(np.int32)
+    g = r["extra"]
+    lg = g.standard_normal((rows, ld), dtype=np.float32)
+    if adversarial:
+        for i in range(rows):
+            kind = i % 8
+            if kind == 1:
+                lg[i] = g.integers(-12, 12, ld) / 4
+            elif kind == 2:
+                lg[i] = 0.75
+            elif kind == 3:
+                lg[i] = np.where(g.random(ld) < 0.5, 0.0, -0.0)
+            elif kind == 4:
+                starts = g.integers(0, ld, 6)
+                for s0 in starts:
+                    lg[i, s0:s0 + int(g.integers(1, 4 * block))] = -np.inf
+                lg[i, g.random(ld) < 0.01] = np.nan
+            elif kind == 5:
+                lens[i] = min(lens[i], max(1, (n_top // 2) * block - int(g.integers(0, block))))
+            elif kind == 6:
+                lens[i] = 0
+            elif kind == 7:
+                lg[i] = np.where(g.random(ld) < 0.5, 3.0e38, -3.0e38)
+    for i in range(rows):
+        lg[i, lens[i]:] = POISON_SCORE
+    return Scores("candidate_scores", lg, lens, block, n_top,
+                  {"min_len": min_len, "max_len": max_len, "adversarial": adversarial})
+
+
 def paged_decode_mxfp4(seed: int = 6):
     """The long paged decode workload with MXFP4 keys (e2m1 codes + UE8M0 group scales)."""
     return paged_decode(seed=seed, kdtype="mxfp4")

@@ -245,3 +245,34 @@ def test_kcache_write_rejects_bad_arguments(L):
     assert call(k=C.c_void_p(0x1008)) == D.IDX_ERR_ARG        # keys not 16-byte aligned
     assert call(n=0, s=None, c=None) == D.IDX_OK              # nothing to write
     assert b"idx_kcache_write" in L.idx_last_error() or L.idx_last_error() == b""
+
+
+def test_candidate_blocks_rejects_bad_arguments(L):
+    """The candidate-block publisher checks its arguments on the host before anything is
+    enqueued."""
+    ok = dict(lg=C.c_void_p(0x1000), ld=4096, lens=None, n=4096, rows=8, bs=128, top=16, c=C.c_void_p(0x2000),
+              cld=16, nc=C.c_void_p(0x3000), ws=C.c_void_p(0x10000), wsb=1 << 20)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.idx_candidate_blocks(a["lg"], a["ld"], a["lens"], a["n"], a["rows"], a["bs"], a["top"], a["c"],
+                                      a["cld"], a["nc"], a["ws"], a["wsb"], None)
+
+    assert L.idx_candidate_blocks_workspace(8, 4096) == 8 * 64 * 4
+    assert L.idx_candidate_blocks_workspace(3, 65) == 256  # 2 pieces per row, rounded to 4
+    assert L.idx_candidate_blocks_workspace(8, 0) == 0
+    assert call(bs=100) == D.IDX_ERR_UNSUPPORTED           # not a multiple of 64
+    assert call(bs=8192) == D.IDX_ERR_UNSUPPORTED          # above 4096
+    assert call(n=64 * 16385, ld=64 * 16385, bs=64) == D.IDX_ERR_UNSUPPORTED  # more than 16384 blocks
+    assert call(top=0) == D.IDX_ERR_ARG
+    assert call(top=17) == D.IDX_ERR_ARG                    # cand_ld < n_top
+    assert call(ld=4095) == D.IDX_ERR_ARG                   # ld < n_cols
+    assert call(rows=-1) == D.IDX_ERR_ARG
+    assert call(lg=None) == D.IDX_ERR_ARG
+    assert call(nc=None) == D.IDX_ERR_ARG
+    assert call(c=C.c_void_p(0x2002)) == D.IDX_ERR_ARG       # misaligned
+    assert call(ws=None) == D.IDX_ERR_WORKSPACE
+    assert call(wsb=100) == D.IDX_ERR_WORKSPACE
+    assert call(ws=C.c_void_p(0x10010)) == D.IDX_ERR_ARG     # workspace not 256-byte aligned
+    assert call(rows=0, lg=None, c=None, nc=None) == D.IDX_OK
+    assert b"idx_candidate_blocks" in L.idx_last_error() or L.idx_last_error() == b""
