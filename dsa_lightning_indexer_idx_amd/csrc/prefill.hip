@@ -7,8 +7,9 @@
 //     range first. Two pieces per block let short causal blocks' workgroups backfill
 //     behind long ones (every workgroup of the chunk is resident at once otherwise, so
 //     the longest block alone would set the time).
-//   * Tiles are staged in LDS, three slots deep: all 256 threads load tile t + 2 (one
-//     16-byte chunk each per load) while tile t computes, and store it chunk-major
+//   * Tiles are staged in LDS, three slots deep: as tile t finishes, all 256 threads
+//     issue the loads of tile t + 3 (two 16-byte chunks each), which land in registers
+//     while tile t + 1 computes and are stashed after it, chunk-major
 //     (chunk c of key k at c * 1 KiB + k * 16) so the stores and the MFMA-layout reads
 //     (16 keys of one chunk per 16 lanes) touch contiguous LDS. One barrier per tile.
 //   * Because tile t + 1 is already visible while tile t computes, a wave reads the B
@@ -63,6 +64,7 @@ struct PrefillArgs {
 };
 
 constexpr int kPieces = 5;  // fp8 pieces of q' per query
+
 
 // fp8 e4m3fn byte of x (RNE; |x| <= 448) and its value.
 __device__ __forceinline__ uint32_t to_fp8(float x) {
@@ -274,8 +276,8 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
       for (int i = 0; i < 4; ++i) p1 = fmaf(wr[kQW - 1][h][i], fabsf(r[5 + h][i]), p1);
   };
   v8i kb_next = read_b(t_begin, 0);
+  if (t_begin + 2 < ntiles) fetch(t_begin + 2, x0, x1, xs);
   for (int t = t_begin; t < ntiles; ++t) {
-    if (t + 2 < ntiles) fetch(t + 2, x0, x1, xs);
     const int64_t t0 = lo + (int64_t)t * kTileTokens;
     const bool act0 = qv[0] && t0 < qe[0] && t0 + kTileTokens > qs[0];
     const bool act1 = qv[1] && t0 < qe[1] && t0 + kTileTokens > qs[1];
@@ -305,12 +307,16 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
     // slot (t + 2) % 3 last held tile t - 1, whose reads all finished in iteration t - 1
     if (t + 2 < ntiles) stash(t + 2, x0, x1, xs);
     __syncthreads();
-    // stores after the stash: the stash waits for the loads of tile t + 2, and memory
-    // operations count down in order, so stores issued before it would be waited for too
+    // Memory operations count down in order, so a wait for loads also waits for every
+    // store issued before them. The loads of tile t + 3 therefore go out here, ahead of
+    // this tile's stores, and the stash that waits for them (next iteration) lets those
+    // stores stay in flight. The scores are written once and not read again by this
+    // kernel: non-temporal stores keep them from displacing the key tiles in the cache.
+    if (t + 3 < ntiles) fetch(t + 3, x0, x1, xs);
 #pragma unroll
     for (int u = 0; u < kQW; ++u)
       if ((u == 0 ? act0 : act1) && key >= qs[u] && key < qe[u])
-        a.logits[(int64_t)(q0 + kQW * wave + u) * a.ld + (key - qs[u])] = vv[u];
+        __builtin_nontemporal_store(vv[u], &a.logits[(int64_t)(q0 + kQW * wave + u) * a.ld + (key - qs[u])]);
   }
 
   // columns past each query's length
