@@ -127,3 +127,26 @@ def test_full_size_select(cfg):
         inter, total = assert_selection_matches(s_idx[rows], r_idx, _ref_scores_fn(sub, r_lg), kth,
                                                 f"workload {cfg} k={k}")
         say(f"[select] full workload {cfg} k={k}: sampled overlap {inter}/{total}")
+
+
+def test_long_rows_adversarial():
+    """Rows of up to 131072 columns (the long-row top-k path) with adversarial content:
+    equal scores everywhere (w = 0: the cut bin holds the whole row, more than the
+    candidate lists keep, so the row is finished from itself), a short row among long
+    ones, a row of tiny scores; each k equals idx_topk over the same scores bit for bit,
+    and the oracle confirms the equal-score and short rows."""
+    require_gpu()
+    case = synth.paged_decode(seed=140, rows=8, min_len=40000, max_len=131072)
+    case.w[1] = 0.0
+    case.w[2] *= np.float32(1e-20)
+    case.seq_lens[3] = 5000
+    up = Uploaded(case)
+    for k in (2048, 512, 64):
+        say(f"[select] long adversarial rows k={k}")
+        s_idx, _ = _self_consistent(up, k)
+        rows = [1, 3]
+        sub = O.subset_rows(case, rows)
+        r_idx, r_val, r_lg = O.select_case(sub, k=k, with_logits=True)
+        kth = np.array([r_val[i][max(0, int((r_idx[i] >= 0).sum()) - 1)] for i in range(len(rows))])
+        assert_selection_matches(s_idx[rows], r_idx, _ref_scores_fn(sub, r_lg), kth, f"long rows k={k}")
+        assert np.array_equal(s_idx[1], np.arange(k, dtype=np.int32)), "equal scores: the first k"
