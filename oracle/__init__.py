@@ -292,3 +292,54 @@ def kcache_write(k_new_bf16, slot_mapping, k_dtype, cache, cache_scale):
     assert cache.flags.c_contiguous and cache_scale.flags.c_contiguous
     return int(lib().ref_kcache_write(_p(k_new), k_new.shape[0], _p(slots), kd, _p(cache), _p(cache_scale),
                                       cache.shape[0]))
+
+
+# ------------------------------------------------------------------ sparse attention
+
+_BF16_TABLE = None
+
+
+def _bf16_table() -> np.ndarray:
+    """float64 value of every bf16 bit pattern, from the decoder above."""
+    global _BF16_TABLE
+    if _BF16_TABLE is None:
+        _BF16_TABLE = decode_bf16(np.arange(65536, dtype=np.uint32)).astype(np.float64)
+    return _BF16_TABLE
+
+
+def sparse_attn_paged(q_bits, kv_bits, block_table, seq_lens, indices, scale, row_req=None, page_size=64):
+    """The attention of Eq. (2) over the selected entries (DeepSeek-V3.2 architecture
+    section: the output attends only the key-value entries whose index scores are in the
+    row's top-k), in MLA's single-shared-entry form: every token keeps one 576-element
+    entry c_s, shared by all heads; head h scores it as scale * (q_h . c_s) and reads its
+    first 512 elements as the value (the 512- and 576-element vectors of the llama.cpp
+    thread). Plain numpy in float64.
+
+    q_bits [rows, H, 576] and kv_bits [n_pages, page_size, 576] are bf16 bit patterns
+    (uint16); row r's logical position s lives in page block_table[req(r)][s // page_size],
+    slot s % page_size. indices [rows, k]: logical positions, -1 (or any position outside
+    [0, seq_lens[r])) is skipped. Returns (out float32 [rows, H, 512], lse float32
+    [rows, H]): out = sum_i p_i c_{s_i}[:512] with p the softmax of the scores over the
+    valid selected entries; lse = log sum_i exp(score_i); a row with no valid entry gets
+    out = 0 and lse = -inf."""
+    tab = _bf16_table()
+    q = tab[np.asarray(q_bits, np.uint16)]
+    kv = np.asarray(kv_bits, np.uint16)
+    bt = np.asarray(block_table)
+    idx = np.asarray(indices)
+    rows, H, D = q.shape
+    out = np.zeros((rows, H, 512), np.float64)
+    lse = np.full((rows, H), -np.inf, np.float64)
+    for r in range(rows):
+        req = r if row_req is None else int(row_req[r])
+        pos = [int(s) for s in idx[r] if 0 <= s < seq_lens[r]]
+        if not pos:
+            continue
+        c = np.stack([tab[kv[bt[req][s // page_size], s % page_size]] for s in pos])
+        z = scale * (q[r] @ c.T)                   # [H, n]
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        den = e.sum(axis=1, keepdims=True)
+        out[r] = (e / den) @ c[:, :512]
+        lse[r] = (m + np.log(den))[:, 0]
+    return out.astype(np.float32), lse.astype(np.float32)

@@ -663,4 +663,99 @@ def pin_kcache_mxfp4():
     assert np.all(cache[untouched] == 0x5A) and np.all(sc[untouched] == 0x5A)
 
 
+
+
+# ----------------------------------------------------------------------------- sparse attention
+
+
+def _bf16_bits(x) -> np.ndarray:
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _attn_case(seed, rows=3, H=16, n=150, pages=None):
+    rng = np.random.default_rng(seed)
+    q = _bf16_bits(rng.standard_normal((rows, H, 576)) * 0.08)
+    P = pages if pages is not None else (n + 63) // 64
+    kv = _bf16_bits(rng.standard_normal((rows * P, 64, 576)))
+    bt = np.arange(rows * P, dtype=np.int32).reshape(rows, P)
+    return q, kv, bt, np.full(rows, n, np.int32)
+
+
+def pin_attn_single_entry():
+    """One selected entry: softmax weight 1, the output is that entry's first 512 values."""
+    q, kv, bt, sl = _attn_case(60)
+    idx = np.array([[17, -1], [-1, 130], [5, 5000]], np.int32)
+    out, lse = O.sparse_attn_paged(q, kv, bt, sl, idx, 0.1)
+    vals = torch_bf16(kv).reshape(-1, 576)
+    for r, s in enumerate([17, 130, 5]):
+        assert np.array_equal(out[r], np.broadcast_to(vals[bt[r][s // 64] * 64 + s % 64][:512], (16, 512)).astype(np.float32))
+    assert np.all(np.isfinite(lse))
+
+
+def pin_attn_uniform_weights():
+    """q = 0: every score is 0, the output is the mean of the selected values, lse = log n."""
+    q, kv, bt, sl = _attn_case(61)
+    q[:] = 0
+    idx = np.array([[1, 2, 3, 64], [0, 149, -1, -1], [7, 8, 9, 10]], np.int32)
+    out, lse = O.sparse_attn_paged(q, kv, bt, sl, idx, 0.3)
+    vals = torch_bf16(kv).reshape(-1, 576).astype(np.float64)
+    for r in range(3):
+        sel = [s for s in idx[r] if s >= 0]
+        mean = np.mean([vals[bt[r][s // 64] * 64 + s % 64][:512] for s in sel], axis=0)
+        assert np.allclose(out[r], mean[None, :], rtol=1e-6, atol=1e-7)
+        assert np.allclose(lse[r], np.log(len(sel)), rtol=1e-6)
+
+
+def pin_attn_vs_sdpa():
+    """Against torch's scaled-dot-product attention in float64 (an independent
+    implementation): all positions selected, and a random subset through a boolean mask
+    (so the result must use the selected positions, not the first k)."""
+    q, kv, bt, sl = _attn_case(62, rows=2, H=16, n=128)
+    scale = 0.06
+    rng = np.random.default_rng(63)
+    sub = np.sort(rng.choice(128, size=40, replace=False)).astype(np.int32)
+    for r, sel in ((0, np.arange(128, dtype=np.int32)), (1, sub)):
+        idx = np.full((2, 128), -1, np.int32)
+        idx[r, :len(sel)] = rng.permutation(sel)
+        out, lse = O.sparse_attn_paged(q, kv, bt, sl, idx, scale)
+        vals = torch.from_numpy(torch_bf16(kv)[bt[r]].reshape(-1, 576).astype(np.float64))  # the row's 128 tokens
+        qq = torch.from_numpy(torch_bf16(q[r]).astype(np.float64))[:, None, :]               # [H, 1, 576]
+        mask = torch.zeros(128, dtype=torch.bool)
+        mask[torch.from_numpy(sel.astype(np.int64))] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, vals[None].expand(16, -1, -1), vals[None, :, :512].expand(16, -1, -1),
+            attn_mask=mask[None, None, :].expand(16, 1, -1), scale=scale)[:, 0, :].numpy()
+        assert np.allclose(out[r], ref, rtol=1e-5, atol=1e-6), f"row {r} differs from SDPA"
+        z = (qq[:, 0, :] @ vals.T).numpy() * scale
+        ref_lse = np.log(np.exp(z[:, sel]).sum(axis=1))
+        assert np.allclose(lse[r], ref_lse, rtol=1e-6)
+
+
+def pin_attn_index_order_and_padding():
+    """The selection is a set: permuting it, or adding -1 / out-of-range entries, changes
+    nothing."""
+    q, kv, bt, sl = _attn_case(64)
+    rng = np.random.default_rng(65)
+    base = np.stack([np.sort(rng.choice(150, 30, replace=False)) for _ in range(3)]).astype(np.int32)
+    a, la = O.sparse_attn_paged(q, kv, bt, sl, base, 0.09)
+    shuf = np.stack([rng.permutation(b) for b in base])
+    padded = np.concatenate([shuf, np.full((3, 5), -1, np.int32), np.full((3, 2), 150, np.int32)], axis=1)
+    b, lb = O.sparse_attn_paged(q, kv, bt, sl, padded, 0.09)
+    assert np.allclose(a, b, rtol=1e-6, atol=1e-7) and np.allclose(la, lb, rtol=1e-6)
+
+
+def pin_attn_paged_equals_contiguous():
+    """A permuted page table over permuted pages gives the contiguous result."""
+    q, kv, bt, sl = _attn_case(66)
+    rng = np.random.default_rng(67)
+    idx = np.stack([rng.choice(150, 40, replace=False) for _ in range(3)]).astype(np.int32)
+    a, la = O.sparse_attn_paged(q, kv, bt, sl, idx, 0.05)
+    perm = rng.permutation(kv.shape[0])
+    kv2 = np.empty_like(kv)
+    kv2[perm] = kv
+    bt2 = perm[bt].astype(np.int32)
+    b, lb = O.sparse_attn_paged(q, kv2, bt2, sl, idx, 0.05)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

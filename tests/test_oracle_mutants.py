@@ -86,3 +86,37 @@ def test_planted_mistake_is_caught(name, mutant_dir, oracle_lib):
                 failed.append(pin.__name__)
                 break
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+# The sparse-attention oracle is numpy code: its mutants are copies of the function with
+# one planted mistake each, swapped in for the pins.
+ATTN_MUTANTS = {
+    "attn_scale_dropped": ("z = scale * (q[r] @ c.T)", "z = (q[r] @ c.T)"),
+    "attn_value_slice": ("out[r] = (e / den) @ c[:, :512]", "out[r] = (e / den) @ c[:, 64:]"),
+    "attn_first_k": ("pos = [int(s) for s in idx[r] if 0 <= s < seq_lens[r]]",
+                     "pos = list(range(sum(1 for s in idx[r] if 0 <= s < seq_lens[r])))"),
+    "attn_padding_kept": ("pos = [int(s) for s in idx[r] if 0 <= s < seq_lens[r]]",
+                          "pos = [int(s) for s in idx[r] if s < seq_lens[r]]"),
+    "attn_page_slot": ("bt[req][s // page_size], s % page_size]", "bt[req][s // page_size], (s + 1) % page_size]"),
+    "attn_not_normalised": ("out[r] = (e / den) @ c[:, :512]", "out[r] = e @ c[:, :512]"),
+    "attn_lse_without_max": ("lse[r] = (m + np.log(den))[:, 0]", "lse[r] = np.log(den)[:, 0]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_planted_attention_mistake_is_caught(name, monkeypatch, oracle_lib):
+    import inspect
+    import textwrap
+    old, new = ATTN_MUTANTS[name]
+    src = textwrap.dedent(inspect.getsource(oracle.sparse_attn_paged))
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new, 1), f"<{name}>", "exec"), ns)
+    monkeypatch.setattr(oracle, "sparse_attn_paged", ns["sparse_attn_paged"])
+    failed = []
+    for pin in [p for p in pins.ALL_PINS if p.__name__.startswith("pin_attn")]:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches {name}"
