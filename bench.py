@@ -26,6 +26,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "indexer tokens scored/s + top-k rows/s at 128K ctx; % of HBM roofline"
+BF16_PEAK = 2.5e15  # MI355X dense bf16 MFMA, FLOP/s
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 PROFILES = ROOT / "profiles"
 SCAN_SOURCES = [ROOT / "dsa_lightning_indexer_idx_amd" / "csrc" / f for f in
@@ -323,6 +324,45 @@ def other_workloads(D, np, torch, stream, args):
     log(f"candidate blocks (64 rows x 128K scores, 64 of 128): {ms*1e3:.1f} us per call "
         f"({cb/(ms*1e-3)/1e9:.0f} GB/s, {100*cb/(ms*1e-3)/HBM_PEAK:.1f}% of 8 TB/s, graph of {len(lgs)})")
     del lgs, lns, cnd, ncd, wsc, g
+    # sparse attention over the selection (the step the indexer feeds): the long paged
+    # decode's 64 rows and table, 128 heads, a 576-element bf16 cache on the same pages
+    # (~7.3 GB, made on the GPU), 2048 positions per row drawn at random; then the whole
+    # per-layer decode step: idx_select on the 128K workload and attention on its output
+    c3 = synth.paged_decode(poison=False)
+    P3 = c3.k_pages.shape[0]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    kv3 = torch.randn((P3, 64, 576), generator=gen, device="cuda", dtype=torch.bfloat16)
+    qa3 = (torch.randn((c3.rows, 128, 576), generator=gen, device="cuda", dtype=torch.float32) / 16).to(torch.bfloat16)
+    rng3 = np.random.default_rng(12)
+    ix3 = dev(np.stack([rng3.choice(int(n), size=2048, replace=False) for n in c3.seq_lens]).astype(np.int32))
+    bt3, sl3 = dev(c3.block_table), dev(c3.seq_lens)
+    ao3 = torch.empty((c3.rows, 128, 512), dtype=torch.float32, device="cuda")
+    al3 = torch.empty((c3.rows, 128), dtype=torch.float32, device="cuda")
+    aw3 = torch.empty(max(1, D.idx_sparse_attn_workspace(c3.rows, 128, 2048)), dtype=torch.uint8, device="cuda")
+    attn = lambda ix: D.idx_sparse_attn_paged(qa3, kv3, bt3, sl3, ix, 1 / np.sqrt(192), out=ao3, lse=al3,
+                                              workspace=aw3)
+    ms, _ = time_loop(lambda: attn(ix3), steps, 3, stream, warm_s=0.2)
+    ab = c3.rows * (2048 * 1152 + 128 * 576 * 2 + 128 * 512 * 4 + 128 * 4 + 2048 * 4)
+    af = 2.0 * c3.rows * 128 * 2048 * (576 + 512)
+    out["sparse_attn_ms"] = ms
+    out["sparse_attn_hbm_frac"] = ab / (ms * 1e-3) / HBM_PEAK
+    out["sparse_attn_bf16_frac"] = af / (ms * 1e-3) / BF16_PEAK
+    log(f"sparse attention (64 rows x 128 heads x 2048 selected, 576-element bf16 entries): {ms*1e3:.1f} us "
+        f"({ab/(ms*1e-3)/1e9:.0f} GB/s, {100*ab/(ms*1e-3)/HBM_PEAK:.1f}% of 8 TB/s; "
+        f"{af/(ms*1e-3)/1e12:.0f} TFLOP/s, {100*af/(ms*1e-3)/BF16_PEAK:.1f}% of bf16 peak)")
+    q3, w3, kp3, sp3 = dev(c3.q), dev(c3.w), dev(c3.k_pages), dev(c3.k_scale_pages)
+    p3 = D.paged_problem(q3, w3, kp3, sp3, bt3, sl3, k_dtype="fp8")
+    ws3 = torch.empty(D.idx_select_workspace(p3, 2048), dtype=torch.uint8, device="cuda")
+    oi3 = torch.empty((c3.rows, 2048), dtype=torch.int32, device="cuda")
+
+    def layer_step():
+        D.idx_select(p3, 2048, values=False, out_idx=oi3, workspace=ws3)
+        attn(oi3)
+    ms2, _ = time_loop(layer_step, steps, 3, stream, warm_s=0.2)
+    out["decode_layer_step_ms"] = ms2
+    log(f"decode layer step (idx_select 128K + sparse attention on its selection): {ms2*1e3:.1f} us")
+    del kv3, qa3, ix3, bt3, sl3, ao3, al3, aw3, q3, w3, kp3, sp3, p3, ws3, oi3
     # key-cache writer: a whole 128K context of new bf16 keys into permuted page slots,
     # and one decode step (64 new keys)
     rng = np.random.default_rng(7)

@@ -29,7 +29,8 @@ KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
 EXPORTS = ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
            "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
            "idx_last_error", "idx_version", "idx_device_errors", "idx_kcache_write", "idx_read_probe",
-           "idx_candidate_blocks", "idx_candidate_blocks_workspace")
+           "idx_candidate_blocks", "idx_candidate_blocks_workspace", "idx_sparse_attn_paged",
+           "idx_sparse_attn_workspace")
 
 
 class IdxError(RuntimeError):
@@ -95,8 +96,13 @@ def lib() -> C.CDLL:
         L.idx_candidate_blocks.argtypes = [P, I64, P, I64, I, I, I, P, I64, P, P, SZ, P]
         L.idx_candidate_blocks_workspace.argtypes = [I, I64]
         L.idx_candidate_blocks_workspace.restype = SZ
+        L.idx_sparse_attn_paged.argtypes = [P, I, P, I64, I, P, I64, I64, P, P, P, I64, I, I, C.c_float, P, P,
+                                            P, SZ, P]
+        L.idx_sparse_attn_workspace.argtypes = [I, I, I]
+        L.idx_sparse_attn_workspace.restype = SZ
         for name in ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
-                     "idx_select", "idx_read_probe", "idx_kcache_write", "idx_candidate_blocks"):
+                     "idx_select", "idx_read_probe", "idx_kcache_write", "idx_candidate_blocks",
+                     "idx_sparse_attn_paged"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -250,6 +256,37 @@ def idx_candidate_blocks(logits, block_size: int, n_top: int, *, lens=None, n_co
                                       _ptr(cand), cand.shape[1], _ptr(n_cand), _ptr(workspace), wsb,
                                       _stream(stream)))
     return cand, n_cand
+
+
+def idx_sparse_attn_workspace(rows: int, heads: int, k: int) -> int:
+    return int(lib().idx_sparse_attn_workspace(rows, heads, k))
+
+
+def idx_sparse_attn_paged(q, kv_pages, block_table, seq_lens, indices, scale: float, *, k: int | None = None,
+                          row_req=None, out=None, lse=None, with_lse: bool = True, workspace=None, stream=None):
+    """Attention over each row's selected entries (C: idx_sparse_attn_paged). q bf16
+    [rows, heads, 576]; kv_pages bf16 [n_pages, 64, 576]; indices int32 [rows, >= k].
+    Returns (out fp32 [rows, heads, 512], lse fp32 [rows, heads] or None)."""
+    import torch
+    for t, name in ((q, "q"), (kv_pages, "kv_pages"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+                    (indices, "indices"), (row_req, "row_req")):
+        _need(t, name)
+    rows, heads, _ = q.shape
+    k = indices.shape[1] if k is None else k
+    if out is None:
+        out = torch.empty((rows, heads, 512), dtype=torch.float32, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((rows, heads), dtype=torch.float32, device=q.device)
+    need = idx_sparse_attn_workspace(rows, heads, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().idx_sparse_attn_paged(_ptr(q), heads, _ptr(kv_pages), kv_pages.shape[0], kv_pages.shape[1],
+                                       _ptr(block_table), block_table.shape[0], block_table.shape[1],
+                                       _ptr(seq_lens), _ptr(row_req), _ptr(indices), indices.shape[1], k, rows,
+                                       float(scale), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
+                                       _stream(stream)))
+    return out, lse
 
 
 class Problem:

@@ -4,6 +4,8 @@
 #include "dsaidx.h"
 #include "launch.h"
 
+#include <cmath>
+
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -420,6 +422,61 @@ idx_status idx_candidate_blocks(const float* logits, int64_t ld, const int32_t* 
   c.cand_ld = cand_ld;
   c.n_cand = n_cand;
   return launched(fn, launch_candidate_blocks(c, workspace, (hipStream_t)stream));
+}
+
+size_t idx_sparse_attn_workspace(int rows, int heads, int k) {
+  if (rows <= 0 || k <= 0 || heads <= 0) return 0;
+  return attn_workspace_bytes(rows, heads, k);
+}
+
+idx_status idx_sparse_attn_paged(const void* q, int heads, const void* kv_pages, int64_t n_pages, int page_size,
+                                 const int32_t* block_table, int64_t bt_rows, int64_t bt_ld,
+                                 const int32_t* seq_lens, const int32_t* row_req, const int32_t* indices,
+                                 int64_t idx_ld, int k, int rows, float scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, idx_stream_t stream) {
+  const char* fn = "idx_sparse_attn_paged";
+  REQUIRE(rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, rows);
+  REQUIRE(heads == 16 || heads == 32 || heads == 64 || heads == 128, IDX_ERR_UNSUPPORTED,
+          "%s: heads = %d must be 16, 32, 64 or 128", fn, heads);
+  REQUIRE(page_size == 64, IDX_ERR_UNSUPPORTED, "%s: page_size = %d must be 64", fn, page_size);
+  REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
+  if (rows == 0) return ok();
+  REQUIRE(q && kv_pages && block_table && seq_lens && indices && out, IDX_ERR_ARG,
+          "%s: q, kv_pages, block_table, seq_lens, indices and out must be non-null", fn);
+  REQUIRE(n_pages >= 1 && bt_rows >= 1 && bt_ld >= 1 && idx_ld >= k, IDX_ERR_ARG,
+          "%s: n_pages, bt_rows, bt_ld must be >= 1 and idx_ld >= k", fn);
+  REQUIRE(row_req || bt_rows >= rows, IDX_ERR_ARG, "%s: bt_rows = %lld < rows without row_req", fn,
+          (long long)bt_rows);
+  REQUIRE(std::isfinite(scale), IDX_ERR_ARG, "%s: scale must be finite", fn);
+  REQUIRE(aligned(q, 16) && aligned(kv_pages, 16), IDX_ERR_ARG, "%s: q and kv_pages must be 16-byte aligned", fn);
+  REQUIRE(aligned(out, 16) && (!lse || aligned(lse, 4)), IDX_ERR_ARG,
+          "%s: out must be 16-byte and lse 4-byte aligned", fn);
+  idx_status s = check_ints(fn, {block_table, seq_lens, row_req, indices});
+  if (s != IDX_OK) return s;
+  const size_t need = idx_sparse_attn_workspace(rows, heads, k);
+  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), IDX_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(need == 0 || aligned(workspace, 256), IDX_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
+  AttnCall c{};
+  c.q = q;
+  c.kv = kv_pages;
+  c.n_pages = n_pages;
+  c.page_size = page_size;
+  c.block_table = block_table;
+  c.bt_rows = bt_rows;
+  c.bt_ld = bt_ld;
+  c.seq_lens = seq_lens;
+  c.row_req = row_req;
+  c.indices = indices;
+  c.idx_ld = idx_ld;
+  c.k = k;
+  c.rows = rows;
+  c.heads = heads;
+  c.scale = scale;
+  c.out = out;
+  c.lse = lse;
+  c.err = device_error_word();
+  return launched(fn, launch_sparse_attn(c, workspace, (hipStream_t)stream));
 }
 
 idx_status idx_kcache_write(const void* k_new, int new_dtype, int64_t n_new, const int64_t* slot_mapping,

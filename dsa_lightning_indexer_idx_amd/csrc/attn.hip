@@ -1,0 +1,367 @@
+// Sparse attention over the selected entries, the step the indexer feeds (Eq. (2) of the
+// DeepSeek-V3.2 architecture section: the output attends only the key-value entries
+// whose index scores are in the row's top-k). MLA keeps one 576-element entry per token,
+// shared by every head (the 512- and 576-element vectors of the llama.cpp thread); head
+// h scores entry c as scale * (q_h . c) and reads its first 512 elements as the value.
+//
+// attn_partial_kernel: one workgroup per (row, split of the row's selected positions),
+// one wave per 16 heads. Per 32-position tile:
+//   * gather: the 32 entries (paged, through the block table) land in LDS twice, token-
+//     major for the scores (B operand: 8 consecutive dims of one token) and dim-major
+//     for the value product (B operand: 8 consecutive tokens of one dim). The loads of
+//     tile t + 1 are issued into registers before tile t computes; the split's entry
+//     addresses are resolved once, up front.
+//   * scores S[16 heads x 32 tokens] = Q K^T: v_mfma_f32_16x16x32_bf16 over the 576 dims
+//     (18 K-steps, two 16-token columns), Q held in registers as A operands.
+//   * online softmax in the base-2 domain (scale folded with log2 e): per head the tile
+//     maximum and sum across the 16 lanes of a row by DPP, rescaling of the running sum
+//     and of the output.
+//   * O[16 heads x 512] += P V: P (bf16) goes through a small per-wave LDS buffer into
+//     the A-operand layout; 32 MFMAs, one per 16 value dims.
+// The split's (O, m, l) go to the workspace; attn_combine_kernel merges the splits into
+// the output and the log-sum-exp. With one split the partial kernel writes both itself.
+#include "device.h"
+#include "launch.h"
+
+#include <algorithm>
+#include <mutex>
+
+namespace dsaidx {
+
+constexpr int kAttnD = 576;          // entry / query length
+constexpr int kAttnDV = 512;         // value length (the entry's first 512 elements)
+constexpr int kAttnT = 32;           // positions per tile
+constexpr int kKPitch = kAttnD + 8;  // token-major tile row (bf16): 1168 B, conflict-free reads
+constexpr int kVPitch = kAttnT + 8;  // dim-major tile row (bf16): 80 B
+constexpr int kPPitch = kAttnT + 8;  // per-wave P rows (bf16)
+constexpr int kChunks = kAttnT * kAttnD / 8;  // 16-byte pieces of a tile (2304)
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint16_t* q;       // [rows, heads, 576] bf16
+  const uint16_t* kv;      // [n_pages, page_size, 576] bf16
+  int64_t n_pages;
+  int page_size;
+  const int32_t* bt;
+  int64_t bt_rows;
+  int64_t bt_ld;
+  const int32_t* seq_lens;
+  const int32_t* row_req;
+  const int32_t* idx;      // [rows, idx_ld]
+  int64_t idx_ld;
+  int k;
+  int rows;
+  int heads;
+  float scale2;            // scale * log2(e)
+  int nsplit;
+  int split_len;           // selected positions per split (a multiple of kAttnT)
+  float* out;              // [rows, heads, 512]
+  float* lse;              // [rows, heads] or null
+  float* part_o;           // [rows, nsplit, heads, 512]
+  float* part_ml;          // [rows, nsplit, heads, 2]
+  unsigned* err;
+};
+
+__device__ __forceinline__ float dpp_row_max(float v) {
+  // butterfly over the 16 lanes of a row: quad xor 1, xor 2, half-row mirror, row mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
+  return v;
+}
+
+__device__ __forceinline__ float dpp_row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  // round to nearest even (scores and weights are finite here)
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a) {
+  constexpr int NT = NW * kWave;
+  constexpr int kPer = (kChunks + NT - 1) / NT;  // 16-byte pieces each thread gathers per tile
+  __shared__ __align__(16) uint16_t kt[kAttnT * kKPitch];
+  __shared__ __align__(16) uint16_t vt[kAttnDV * kVPitch];
+  __shared__ __align__(16) uint16_t pb[NW][16 * kPPitch];
+  extern __shared__ int64_t ent[];  // the split's entry rows (-1: not a valid entry)
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int r = blockIdx.x / a.nsplit;
+  const int split = blockIdx.x % a.nsplit;
+  const int i0 = split * a.split_len;
+  const int i1 = min(a.k, i0 + a.split_len);
+  const int ntok = max(i1 - i0, 0);
+  const int ntiles = (ntok + kAttnT - 1) / kAttnT;
+
+  // entry rows of the split's positions
+  {
+    const int64_t req = a.row_req ? (int64_t)a.row_req[r] : (int64_t)r;
+    const bool req_ok = req >= 0 && req < a.bt_rows;
+    const int64_t len = a.seq_lens[r];
+    for (int i = tid; i < ntiles * kAttnT; i += NT) {
+      int64_t e = -1;
+      if (i < ntok && req_ok) {
+        const int64_t pos = a.idx[(int64_t)r * a.idx_ld + i0 + i];
+        if (pos >= 0 && pos < len && pos / a.page_size < a.bt_ld) {
+          const int64_t page = a.bt[req * a.bt_ld + pos / a.page_size];
+          if (page >= 0 && page < a.n_pages)
+            e = page * a.page_size + pos % a.page_size;
+          else
+            flag_error(a.err, kErrPage);
+        }
+      }
+      ent[i] = e;
+    }
+    if (tid == 0 && !req_ok && ntok > 0) flag_error(a.err, kErrRange);
+  }
+  __syncthreads();
+
+  // the wave's 16 heads: A operands of the 18 K-steps (row c16 = head, dims 32s + 8g ..)
+  const int head0 = 16 * wave;
+  const uint16_t* qrow = a.q + ((int64_t)r * a.heads + head0 + c16) * kAttnD + 8 * g;
+  v8bf qa[kAttnD / 32];
+#pragma unroll
+  for (int s = 0; s < kAttnD / 32; ++s) qa[s] = *(const v8bf*)(qrow + 32 * s);
+
+  // gather: piece c of the tile is token c % 32, 16-byte chunk c / 32 of its entry
+  v4i pre[kPer];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = tid + u * NT;
+      if (c < kChunks) {
+        const int64_t e = ent[t * kAttnT + (c % kAttnT)];
+        const int64_t row = e >= 0 ? e : 0;
+        pre[u] = *(const v4i*)(a.kv + row * kAttnD + 8 * (c / kAttnT));
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = tid + u * NT;
+      if (c < kChunks) {
+        const int tok = c % kAttnT, ch = c / kAttnT;
+        *(v4i*)(&kt[tok * kKPitch + 8 * ch]) = pre[u];
+        if (ch < kAttnDV / 8) {
+          const uint32_t w4[4] = {(uint32_t)pre[u][0], (uint32_t)pre[u][1], (uint32_t)pre[u][2], (uint32_t)pre[u][3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vt[(8 * ch + e) * kVPitch + tok] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  };
+
+  float m[4], l[4];
+  v4f o[kAttnDV / 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -__builtin_inff();
+    l[i] = 0.f;
+  }
+#pragma unroll
+  for (int n = 0; n < kAttnDV / 16; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) fetch(0);
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();  // every wave is done with tile t - 1
+    stash();
+    __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
+
+    // scores of the tile's two 16-token columns
+    v4f sc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < kAttnD / 32; ++s) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v8bf kb = *(const v8bf*)(&kt[(16 * j + c16) * kKPitch + 32 * s + 8 * g]);
+        sc[j] = mfma_bf16(qa[s], kb, sc[j]);
+      }
+    }
+    // lane (g, c16): heads 4g + i, tokens c16 and 16 + c16 of the tile
+    const bool v0 = ent[t * kAttnT + c16] >= 0, v1 = ent[t * kAttnT + 16 + c16] >= 0;
+    float p[2][4], alpha[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s0 = v0 ? sc[0][i] * a.scale2 : -__builtin_inff();
+      const float s1 = v1 ? sc[1][i] * a.scale2 : -__builtin_inff();
+      const float mt = dpp_row_max(fmaxf(s0, s1));
+      const float mn = fmaxf(m[i], mt);
+      // all -inf so far: keep weights 0 (exp2(-inf) = 0, and no -inf - -inf)
+      const float base = mn == -__builtin_inff() ? 0.f : mn;
+      alpha[i] = exp2f(m[i] - base);
+      p[0][i] = exp2f(s0 - base);
+      p[1][i] = exp2f(s1 - base);
+      l[i] = l[i] * alpha[i] + dpp_row_sum(p[0][i] + p[1][i]);
+      m[i] = mn;
+    }
+#pragma unroll
+    for (int n = 0; n < kAttnDV / 16; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[n][i] *= alpha[i];
+    // P into the A-operand layout: row = head, 8 consecutive tokens per lane group
+    uint16_t* pw = pb[wave];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[(4 * g + i) * kPPitch + 16 * j + c16] = f32_to_bf16(p[j][i]);
+    __builtin_amdgcn_wave_barrier();  // one wave's LDS operations complete in order
+    const v8bf pa = *(const v8bf*)(&pw[c16 * kPPitch + 8 * g]);
+#pragma unroll
+    for (int n = 0; n < kAttnDV / 16; ++n) {
+      const v8bf vb = *(const v8bf*)(&vt[(16 * n + c16) * kVPitch + 8 * g]);
+      o[n] = mfma_bf16(pa, vb, o[n]);
+    }
+    __builtin_amdgcn_wave_barrier();  // the P reads finish before the next tile's writes
+  }
+
+  // lane (g, c16) holds O[head 4g + i][dim 16n + c16]
+  if (a.nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = head0 + 4 * g + i;
+      const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
+      float* orow = a.out + ((int64_t)r * a.heads + h) * kAttnDV;
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 16; ++n) orow[16 * n + c16] = o[n][i] * inv;
+      if (a.lse && c16 == 0)
+        a.lse[(int64_t)r * a.heads + h] = l[i] > 0.f ? (m[i] + log2f(l[i])) * 0.69314718055994531f : -__builtin_inff();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = head0 + 4 * g + i;
+      const int64_t slot = ((int64_t)r * a.nsplit + split) * a.heads + h;
+      float* orow = a.part_o + slot * kAttnDV;
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 16; ++n) orow[16 * n + c16] = o[n][i];
+      if (c16 == 0) {
+        a.part_ml[2 * slot] = m[i];
+        a.part_ml[2 * slot + 1] = l[i];
+      }
+    }
+  }
+}
+
+// One wave per (row, head): merges the splits' (O, m, l).
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int64_t wv = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kWave;
+  if (wv >= (int64_t)a.rows * a.heads) return;
+  const int lane = lane_id();
+  const int64_t r = wv / a.heads, h = wv % a.heads;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, a.part_ml[2 * ((r * a.nsplit + s) * a.heads + h)]);
+  const float base = mx == -__builtin_inff() ? 0.f : mx;
+  float L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.nsplit; ++s) {
+    const int64_t slot = (r * a.nsplit + s) * a.heads + h;
+    const float w = exp2f(a.part_ml[2 * slot] - base);
+    L += w * a.part_ml[2 * slot + 1];
+    const float4* src = (const float4*)(a.part_o + slot * kAttnDV) + 2 * lane;
+    const float4 x0 = src[0], x1 = src[1];
+    acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
+    acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float4* dst = (float4*)(a.out + (r * a.heads + h) * kAttnDV) + 2 * lane;
+  dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if (a.lse && lane == 0) a.lse[r * a.heads + h] = L > 0.f ? (mx + log2f(L)) * 0.69314718055994531f : -__builtin_inff();
+}
+
+int attn_splits(int rows, int heads, int k) {
+  // about one workgroup per compute unit of the MI355X (256); each split at least four
+  // tiles (a fixed count keeps the workspace size independent of the device)
+  (void)heads;
+  constexpr int kTargetGroups = 256;
+  const int want = (kTargetGroups + rows - 1) / rows;
+  const int most = std::max(1, (k + 4 * kAttnT - 1) / (4 * kAttnT));
+  return std::max(1, std::min(want, most));
+}
+
+static int split_len(int k, int nsplit) {
+  const int per = (k + nsplit - 1) / nsplit;
+  return (per + kAttnT - 1) / kAttnT * kAttnT;
+}
+
+size_t attn_workspace_bytes(int rows, int heads, int k) {
+  const int ns = attn_splits(rows, heads, k);
+  if (ns <= 1 || rows <= 0) return 0;
+  const size_t o = (size_t)rows * ns * heads * kAttnDV * sizeof(float);
+  const size_t ml = (size_t)rows * ns * heads * 2 * sizeof(float);
+  return (o + 255) / 256 * 256 + (ml + 255) / 256 * 256;
+}
+
+// The entry list is dynamic LDS (up to IDX_MAX_K rows) next to ~88 KB of static LDS.
+template <int NW>
+static hipError_t launch_partial(dim3 grid, size_t ent_bytes, hipStream_t stream, const AttnArgs& a) {
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute((const void*)attn_partial_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               2048 * (int)sizeof(int64_t));
+  });
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(attn_partial_kernel<NW>, grid, dim3(NW * kWave), ent_bytes, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const AttnCall& c, void* workspace, hipStream_t stream) {
+  if (c.rows <= 0) return hipSuccess;
+  AttnArgs a{};
+  a.q = (const uint16_t*)c.q;
+  a.kv = (const uint16_t*)c.kv;
+  a.n_pages = c.n_pages;
+  a.page_size = c.page_size;
+  a.bt = c.block_table;
+  a.bt_rows = c.bt_rows;
+  a.bt_ld = c.bt_ld;
+  a.seq_lens = c.seq_lens;
+  a.row_req = c.row_req;
+  a.idx = c.indices;
+  a.idx_ld = c.idx_ld;
+  a.k = c.k;
+  a.rows = c.rows;
+  a.heads = c.heads;
+  a.scale2 = c.scale * kLog2e;
+  a.nsplit = attn_splits(c.rows, c.heads, c.k);
+  a.split_len = split_len(c.k, a.nsplit);
+  a.out = c.out;
+  a.lse = c.lse;
+  a.err = c.err;
+  if (a.nsplit > 1) {
+    const size_t o = (size_t)c.rows * a.nsplit * c.heads * kAttnDV * sizeof(float);
+    a.part_o = (float*)workspace;
+    a.part_ml = (float*)((uint8_t*)workspace + (o + 255) / 256 * 256);
+  }
+  const dim3 grid((unsigned)(c.rows * a.nsplit));
+  const size_t ent_bytes = (size_t)a.split_len * sizeof(int64_t);
+  hipError_t e = hipSuccess;
+  switch (c.heads) {
+    case 16: e = launch_partial<1>(grid, ent_bytes, stream, a); break;
+    case 32: e = launch_partial<2>(grid, ent_bytes, stream, a); break;
+    case 64: e = launch_partial<4>(grid, ent_bytes, stream, a); break;
+    default: e = launch_partial<8>(grid, ent_bytes, stream, a); break;
+  }
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const int64_t waves = (int64_t)c.rows * c.heads;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsaidx

@@ -103,6 +103,31 @@ constexpr int kCandMaxBlocks = 16384;
 size_t cand_workspace_bytes(int rows, int64_t n_cols);
 hipError_t launch_candidate_blocks(const CandCall& c, void* workspace, hipStream_t stream);
 
+// One sparse-attention call (attention over each row's selected entries).
+struct AttnCall {
+  const void* q;          // bf16 [rows, heads, 576]
+  const void* kv;         // bf16 [n_pages, page_size, 576]
+  int64_t n_pages;
+  int page_size;
+  const int32_t* block_table;
+  int64_t bt_rows;
+  int64_t bt_ld;
+  const int32_t* seq_lens;
+  const int32_t* row_req;
+  const int32_t* indices; // [rows, idx_ld] logical positions, -1 skipped
+  int64_t idx_ld;
+  int k;
+  int rows;
+  int heads;              // 16, 32, 64 or 128
+  float scale;
+  float* out;             // [rows, heads, 512]
+  float* lse;             // [rows, heads] or null
+  unsigned* err;
+};
+int attn_splits(int rows, int heads, int k);
+size_t attn_workspace_bytes(int rows, int heads, int k);
+hipError_t launch_sparse_attn(const AttnCall& c, void* workspace, hipStream_t stream);
+
 // Streaming-read probe (measurement aid).
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

@@ -204,6 +204,40 @@ idx_status idx_candidate_blocks(const float* logits, int64_t ld, const int32_t* 
 
 size_t idx_candidate_blocks_workspace(int rows, int64_t n_cols);
 
+/* ------------------------------------------------------------------ sparse attention */
+
+/*
+ * idx_sparse_attn_paged: the attention the indexer's selection feeds (DeepSeek-V3.2
+ * architecture section, Eq. (2): the output of a query attends only the key-value
+ * entries whose index scores are in its top-k). MLA keeps one 576-element entry per
+ * token, shared by all heads (the 512- and 576-element vectors of the llama.cpp thread).
+ * The pages do not spell the attention out; the reading taken (MLA in its single-shared-
+ * entry form): head h of row r scores entry c_s as z = scale * (q[r][h] . c_s) over the
+ * row's selected positions, and
+ *     out[r][h] = sum_i softmax(z)_i * c_{s_i}[0:512],   lse[r][h] = log sum_i exp(z_i).
+ *
+ * q        bf16 [rows, heads, 576], 16-byte aligned; heads 16, 32, 64 or 128.
+ * kv_pages bf16 [n_pages, page_size, 576] (page_size 64), 16-byte aligned; the logical
+ *          position s of row r is in page block_table[req(r) * bt_ld + s / 64], slot
+ *          s % 64 (req(r) = row_req ? row_req[r] : r), the indexer cache's addressing.
+ * indices  int32 [rows, idx_ld], the first k used: logical positions (idx_select's
+ *          paged output). Entries < 0 or >= seq_lens[r] are skipped; a page id outside
+ *          [0, n_pages) skips the entry and sets IDX_DEVERR_PAGE.
+ * out      fp32 [rows, heads, 512] (16-byte aligned); lse fp32 [rows, heads] or NULL.
+ *          A row with no valid entry gets out = 0 and lse = -inf.
+ * Scores and the softmax run in fp32 (bf16 products are exact in fp32); the weights
+ * are rounded to bf16 for the value product, so |out - exact| <= about 2^-8 * max|value|.
+ * workspace: idx_sparse_attn_workspace(rows, heads, k) bytes, 256-byte aligned (may be
+ * NULL when that is 0). 1 <= k <= IDX_MAX_K. Asynchronous on stream.
+ */
+idx_status idx_sparse_attn_paged(const void* q, int heads, const void* kv_pages, int64_t n_pages, int page_size,
+                                 const int32_t* block_table, int64_t bt_rows, int64_t bt_ld,
+                                 const int32_t* seq_lens, const int32_t* row_req, const int32_t* indices,
+                                 int64_t idx_ld, int k, int rows, float scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, idx_stream_t stream);
+
+size_t idx_sparse_attn_workspace(int rows, int heads, int k);
+
 /* ------------------------------------------------------------------ fused select */
 
 typedef enum idx_mode {
