@@ -4,11 +4,17 @@
 // shared by every head (the 512- and 576-element vectors of the llama.cpp thread); head
 // h scores entry c as scale * (q_h . c) and reads its first 512 elements as the value.
 //
-// attn_partial_kernel: one workgroup per (row, split of the row's selected positions),
-// one wave per 16 heads. Per 32-position tile:
-//   * gather: the 32 entries (paged, through the block table) land in LDS twice, token-
-//     major for the scores (B operand: 8 consecutive dims of one token) and dim-major
-//     for the value product (B operand: 8 consecutive tokens of one dim). The loads of
+// attn_partial_kernel: one workgroup per (row, group of up to 64 heads, split of the
+// row's selected positions), one wave per 16 heads, one wave per SIMD: the wave holds Q
+// (72 VGPRs), O (128), the next tile's gather and a batch of operand reads, more than
+// two waves per SIMD could (which would serialise every MFMA on its LDS read). The
+// head groups of one (row, split) go to the same XCD (workgroup ids 8 apart), so the
+// second gather of a tile mostly hits that XCD's L2. Per 32-position tile:
+//   * gather: the 32 entries (paged, through the block table) land in LDS token-major.
+//     The scores read B operands (8 consecutive dims of one token) with 16-byte loads;
+//     the value product needs 8 consecutive tokens of one dim, which gfx950's
+//     transposing LDS read delivers from the same layout (in each 16-lane group, lane j
+//     reads 4 dims of token j / 4 and lane i receives 4 tokens of dim i). The loads of
 //     tile t + 1 are issued into registers before tile t computes; the split's entry
 //     addresses are resolved once, up front.
 //   * scores S[16 heads x 32 tokens] = Q K^T: v_mfma_f32_16x16x32_bf16 over the 576 dims
@@ -31,8 +37,7 @@ namespace dsaidx {
 constexpr int kAttnD = 576;          // entry / query length
 constexpr int kAttnDV = 512;         // value length (the entry's first 512 elements)
 constexpr int kAttnT = 32;           // positions per tile
-constexpr int kKPitch = kAttnD + 8;  // token-major tile row (bf16): 1168 B, conflict-free reads
-constexpr int kVPitch = kAttnT + 8;  // dim-major tile row (bf16): 80 B
+constexpr int kKPitch = kAttnD + 8;  // token-major tile row (bf16): 1168 B, conflict-free score reads
 constexpr int kPPitch = kAttnT + 8;  // per-wave P rows (bf16)
 constexpr int kChunks = kAttnT * kAttnD / 8;  // 16-byte pieces of a tile (2304)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -55,6 +60,7 @@ struct AttnArgs {
   float scale2;            // scale * log2(e)
   int nsplit;
   int split_len;           // selected positions per split (a multiple of kAttnT)
+  int hgroups;             // head groups (workgroups) per (row, split)
   float* out;              // [rows, heads, 512]
   float* lse;              // [rows, heads] or null
   float* part_o;           // [rows, nsplit, heads, 512]
@@ -90,7 +96,6 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
   constexpr int NT = NW * kWave;
   constexpr int kPer = (kChunks + NT - 1) / NT;  // 16-byte pieces each thread gathers per tile
   __shared__ __align__(16) uint16_t kt[kAttnT * kKPitch];
-  __shared__ __align__(16) uint16_t vt[kAttnDV * kVPitch];
   __shared__ __align__(16) uint16_t pb[NW][16 * kPPitch];
   extern __shared__ int64_t ent[];  // the split's entry rows (-1: not a valid entry)
 
@@ -98,8 +103,13 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int g = lane >> 4, c16 = lane & 15;
-  const int r = blockIdx.x / a.nsplit;
-  const int split = blockIdx.x % a.nsplit;
+  // (row, split) unit p and head group hg: ids 8 apart share an XCD
+  const int b = blockIdx.x;
+  const int p = (b / (8 * a.hgroups)) * 8 + (b % 8);
+  const int hg = (b / 8) % a.hgroups;
+  if (p >= a.rows * a.nsplit) return;
+  const int r = p / a.nsplit;
+  const int split = p % a.nsplit;
   const int i0 = split * a.split_len;
   const int i1 = min(a.k, i0 + a.split_len);
   const int ntok = max(i1 - i0, 0);
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
   __syncthreads();
 
   // the wave's 16 heads: A operands of the 18 K-steps (row c16 = head, dims 32s + 8g ..)
-  const int head0 = 16 * wave;
+  const int head0 = hg * 16 * NW + 16 * wave;
   const uint16_t* qrow = a.q + ((int64_t)r * a.heads + head0 + c16) * kAttnD + 8 * g;
   v8bf qa[kAttnD / 32];
 #pragma unroll
@@ -152,17 +162,18 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = tid + u * NT;
-      if (c < kChunks) {
-        const int tok = c % kAttnT, ch = c / kAttnT;
-        *(v4i*)(&kt[tok * kKPitch + 8 * ch]) = pre[u];
-        if (ch < kAttnDV / 8) {
-          const uint32_t w4[4] = {(uint32_t)pre[u][0], (uint32_t)pre[u][1], (uint32_t)pre[u][2], (uint32_t)pre[u][3]};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            vt[(8 * ch + e) * kVPitch + tok] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-        }
-      }
+      if (c < kChunks) *(v4i*)(&kt[(c % kAttnT) * kKPitch + 8 * (c / kAttnT)]) = pre[u];
     }
+  };
+  // value operand of dims 16n .. 16n + 15: lane (g, c16) gets tokens 8g .. 8g + 7 of dim
+  // 16n + c16, from two transposing reads (tokens 8g + c16 / 4 and 8g + 4 + c16 / 4, dims
+  // 16n + 4 (c16 % 4) .. + 3)
+  typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+  const int tr_off = (8 * g + (c16 >> 2)) * kKPitch + 4 * (c16 & 3);
+  auto read_v = [&](int n) -> v8bf {
+    const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(&kt[tr_off + 16 * n]));
+    const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(&kt[tr_off + 4 * kKPitch + 16 * n]));
+    return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
   float m[4], l[4];
@@ -182,16 +193,18 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
     __syncthreads();
     if (t + 1 < ntiles) fetch(t + 1);
 
-    // scores of the tile's two 16-token columns
+    // scores of the tile's two 16-token columns: all 36 operand reads are issued before
+    // the MFMAs, which then wait for them in order instead of one LDS round trip each
     v4f sc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    v8bf kb[2][kAttnD / 32];
 #pragma unroll
-    for (int s = 0; s < kAttnD / 32; ++s) {
+    for (int s = 0; s < kAttnD / 32; ++s)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const v8bf kb = *(const v8bf*)(&kt[(16 * j + c16) * kKPitch + 32 * s + 8 * g]);
-        sc[j] = mfma_bf16(qa[s], kb, sc[j]);
-      }
-    }
+      for (int j = 0; j < 2; ++j) kb[j][s] = *(const v8bf*)(&kt[(16 * j + c16) * kKPitch + 32 * s + 8 * g]);
+#pragma unroll
+    for (int s = 0; s < kAttnD / 32; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sc[j] = mfma_bf16(qa[s], kb[j][s], sc[j]);
     // lane (g, c16): heads 4g + i, tokens c16 and 16 + c16 of the tile
     const bool v0 = ent[t * kAttnT + c16] >= 0, v1 = ent[t * kAttnT + 16 + c16] >= 0;
     float p[2][4], alpha[4];
@@ -221,10 +234,14 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
       for (int i = 0; i < 4; ++i) pw[(4 * g + i) * kPPitch + 16 * j + c16] = f32_to_bf16(p[j][i]);
     __builtin_amdgcn_wave_barrier();  // one wave's LDS operations complete in order
     const v8bf pa = *(const v8bf*)(&pw[c16 * kPPitch + 8 * g]);
+    // value operands in two batches of 16 reads, each ahead of its MFMAs
 #pragma unroll
-    for (int n = 0; n < kAttnDV / 16; ++n) {
-      const v8bf vb = *(const v8bf*)(&vt[(16 * n + c16) * kVPitch + 8 * g]);
-      o[n] = mfma_bf16(pa, vb, o[n]);
+    for (int h = 0; h < 2; ++h) {
+      v8bf vb[kAttnDV / 32];
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 32; ++n) vb[n] = read_v(16 * h + n);
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 32; ++n) o[16 * h + n] = mfma_bf16(pa, vb[n], o[16 * h + n]);
     }
     __builtin_amdgcn_wave_barrier();  // the P reads finish before the next tile's writes
   }
@@ -284,12 +301,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (a.lse && lane == 0) a.lse[r * a.heads + h] = L > 0.f ? (mx + log2f(L)) * 0.69314718055994531f : -__builtin_inff();
 }
 
+static int head_waves(int heads) { return std::min(heads, 64) / 16; }
+
 int attn_splits(int rows, int heads, int k) {
   // about one workgroup per compute unit of the MI355X (256); each split at least four
   // tiles (a fixed count keeps the workspace size independent of the device)
-  (void)heads;
   constexpr int kTargetGroups = 256;
-  const int want = (kTargetGroups + rows - 1) / rows;
+  const int hgroups = heads / (16 * head_waves(heads));
+  const int want = (kTargetGroups + rows * hgroups - 1) / (rows * hgroups);
   const int most = std::max(1, (k + 4 * kAttnT - 1) / (4 * kAttnT));
   return std::max(1, std::min(want, most));
 }
@@ -341,6 +360,8 @@ hipError_t launch_sparse_attn(const AttnCall& c, void* workspace, hipStream_t st
   a.scale2 = c.scale * kLog2e;
   a.nsplit = attn_splits(c.rows, c.heads, c.k);
   a.split_len = split_len(c.k, a.nsplit);
+  const int nw = head_waves(c.heads);
+  a.hgroups = c.heads / (16 * nw);
   a.out = c.out;
   a.lse = c.lse;
   a.err = c.err;
@@ -349,14 +370,14 @@ hipError_t launch_sparse_attn(const AttnCall& c, void* workspace, hipStream_t st
     a.part_o = (float*)workspace;
     a.part_ml = (float*)((uint8_t*)workspace + (o + 255) / 256 * 256);
   }
-  const dim3 grid((unsigned)(c.rows * a.nsplit));
+  const int64_t units = (int64_t)c.rows * a.nsplit;
+  const dim3 grid((unsigned)((units + 7) / 8 * 8 * a.hgroups));
   const size_t ent_bytes = (size_t)a.split_len * sizeof(int64_t);
   hipError_t e = hipSuccess;
-  switch (c.heads) {
-    case 16: e = launch_partial<1>(grid, ent_bytes, stream, a); break;
-    case 32: e = launch_partial<2>(grid, ent_bytes, stream, a); break;
-    case 64: e = launch_partial<4>(grid, ent_bytes, stream, a); break;
-    default: e = launch_partial<8>(grid, ent_bytes, stream, a); break;
+  switch (nw) {
+    case 1: e = launch_partial<1>(grid, ent_bytes, stream, a); break;
+    case 2: e = launch_partial<2>(grid, ent_bytes, stream, a); break;
+    default: e = launch_partial<4>(grid, ent_bytes, stream, a); break;
   }
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t waves = (int64_t)c.rows * c.heads;
