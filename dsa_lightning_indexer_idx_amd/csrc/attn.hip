@@ -145,16 +145,17 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
 #pragma unroll
   for (int s = 0; s < kAttnD / 32; ++s) qa[s] = *(const v8bf*)(qrow + 32 * s);
 
-  // gather: piece c of the tile is token c % 32, 16-byte chunk c / 32 of its entry
+  // gather: piece c of the tile is 16-byte chunk c % 72 of token c / 72, so a wave's
+  // load reads 1 KiB of one entry (8 cache lines) rather than 16 bytes of 32 entries
   v4i pre[kPer];
   auto fetch = [&](int t) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = tid + u * NT;
       if (c < kChunks) {
-        const int64_t e = ent[t * kAttnT + (c % kAttnT)];
+        const int64_t e = ent[t * kAttnT + c / (kAttnD / 8)];
         const int64_t row = e >= 0 ? e : 0;
-        pre[u] = *(const v4i*)(a.kv + row * kAttnD + 8 * (c / kAttnT));
+        pre[u] = *(const v4i*)(a.kv + row * kAttnD + 8 * (c % (kAttnD / 8)));
       }
     }
   };
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = tid + u * NT;
-      if (c < kChunks) *(v4i*)(&kt[(c % kAttnT) * kKPitch + 8 * (c / kAttnT)]) = pre[u];
+      if (c < kChunks) *(v4i*)(&kt[(c / (kAttnD / 8)) * kKPitch + 8 * (c % (kAttnD / 8))]) = pre[u];
     }
   };
   // value operand of dims 16n .. 16n + 15: lane (g, c16) gets tokens 8g .. 8g + 7 of dim
