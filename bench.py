@@ -207,6 +207,29 @@ def cpu_baseline(case, k: int, budget_s: float = 15.0):
 FP8_PEAK = 5.0e15  # MI355X dense fp8 MFMA, FLOP/s
 
 
+def attn_workload(D, np, torch, synth):
+    """The sparse-attention workload: the long paged decode's 64 rows and block table,
+    128 heads, a 576-element bf16 MLA cache on the same pages (~7.3 GB, made on the GPU
+    by torch's seeded generator), 2048 positions per row drawn at random. Returns the
+    case, the tensors and attn(indices) -> one idx_sparse_attn_paged call."""
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    c3 = synth.paged_decode(poison=False)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    kv3 = torch.randn((c3.k_pages.shape[0], 64, 576), generator=gen, device="cuda", dtype=torch.bfloat16)
+    qa3 = (torch.randn((c3.rows, 128, 576), generator=gen, device="cuda", dtype=torch.float32) / 16).to(torch.bfloat16)
+    rng3 = np.random.default_rng(12)
+    ix3 = dev(np.stack([rng3.choice(int(n), size=2048, replace=False) for n in c3.seq_lens]).astype(np.int32))
+    bt3, sl3 = dev(c3.block_table), dev(c3.seq_lens)
+    ao3 = torch.empty((c3.rows, 128, 512), dtype=torch.float32, device="cuda")
+    al3 = torch.empty((c3.rows, 128), dtype=torch.float32, device="cuda")
+    aw3 = torch.empty(max(1, D.idx_sparse_attn_workspace(c3.rows, 128, 2048)), dtype=torch.uint8, device="cuda")
+
+    def attn(ix):
+        D.idx_sparse_attn_paged(qa3, kv3, bt3, sl3, ix, 1 / np.sqrt(192), out=ao3, lse=al3, workspace=aw3)
+    return c3, kv3, qa3, ix3, bt3, sl3, attn
+
+
 def other_workloads(D, np, torch, stream, args):
     """Rates of the other workloads (reported next to the headline): the prefill chunk's
     score kernel against the fp8 MFMA peak, and idx_select on batched decode and on the
@@ -328,20 +351,7 @@ def other_workloads(D, np, torch, stream, args):
     # decode's 64 rows and table, 128 heads, a 576-element bf16 cache on the same pages
     # (~7.3 GB, made on the GPU), 2048 positions per row drawn at random; then the whole
     # per-layer decode step: idx_select on the 128K workload and attention on its output
-    c3 = synth.paged_decode(poison=False)
-    P3 = c3.k_pages.shape[0]
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(11)
-    kv3 = torch.randn((P3, 64, 576), generator=gen, device="cuda", dtype=torch.bfloat16)
-    qa3 = (torch.randn((c3.rows, 128, 576), generator=gen, device="cuda", dtype=torch.float32) / 16).to(torch.bfloat16)
-    rng3 = np.random.default_rng(12)
-    ix3 = dev(np.stack([rng3.choice(int(n), size=2048, replace=False) for n in c3.seq_lens]).astype(np.int32))
-    bt3, sl3 = dev(c3.block_table), dev(c3.seq_lens)
-    ao3 = torch.empty((c3.rows, 128, 512), dtype=torch.float32, device="cuda")
-    al3 = torch.empty((c3.rows, 128), dtype=torch.float32, device="cuda")
-    aw3 = torch.empty(max(1, D.idx_sparse_attn_workspace(c3.rows, 128, 2048)), dtype=torch.uint8, device="cuda")
-    attn = lambda ix: D.idx_sparse_attn_paged(qa3, kv3, bt3, sl3, ix, 1 / np.sqrt(192), out=ao3, lse=al3,
-                                              workspace=aw3)
+    c3, kv3, qa3, ix3, bt3, sl3, attn = attn_workload(D, np, torch, synth)
     ms, _ = time_loop(lambda: attn(ix3), steps, 3, stream, warm_s=0.2)
     ab = c3.rows * (2048 * 1152 + 128 * 576 * 2 + 128 * 512 * 4 + 128 * 4 + 2048 * 4)
     af = 2.0 * c3.rows * 128 * 2048 * (576 + 512)
@@ -362,7 +372,7 @@ def other_workloads(D, np, torch, stream, args):
     ms2, _ = time_loop(layer_step, steps, 3, stream, warm_s=0.2)
     out["decode_layer_step_ms"] = ms2
     log(f"decode layer step (idx_select 128K + sparse attention on its selection): {ms2*1e3:.1f} us")
-    del kv3, qa3, ix3, bt3, sl3, ao3, al3, aw3, q3, w3, kp3, sp3, p3, ws3, oi3
+    del kv3, qa3, ix3, bt3, sl3, attn, q3, w3, kp3, sp3, p3, ws3, oi3
     # key-cache writer: a whole 128K context of new bf16 keys into permuted page slots,
     # and one decode step (64 new keys)
     rng = np.random.default_rng(7)
@@ -405,9 +415,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "scan", "select", "copy"], default="all",
-                    help="run one timed loop only (for profiler counter runs); copy: a plain "
-                         "512 MiB device-to-device copy, the counters' calibration")
+    ap.add_argument("--only", choices=["all", "scan", "select", "copy", "attn"], default="all",
+                    help="run one timed loop only (for profiler runs); copy: a plain 512 MiB "
+                         "device-to-device copy, the counters' calibration; attn: the sparse "
+                         "attention workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) over "
@@ -450,6 +461,12 @@ def main() -> int:
         src.fill_(1)
         ms, _ = time_loop(lambda: dst.copy_(src), args.steps, args.warmup, torch.cuda.current_stream())
         log(f"copy of {COPY_BYTES >> 20} MiB: {ms:.3f} ms ({2 * COPY_BYTES / (ms * 1e-3) / 1e9:.0f} GB/s read + write)")
+        return 0
+    if args.only == "attn":
+        _, _, _, ix, _, _, attn = attn_workload(D, np, torch, synth)
+        # the kernel repeated for 0.5 s first: its clock settles only under its own load
+        ms, _ = time_loop(lambda: attn(ix), args.steps, args.warmup, torch.cuda.current_stream(), warm_s=0.5)
+        log(f"sparse attention: {ms * 1e3:.1f} us per call")
         return 0
     log("generating the 128K paged decode workload")
     case = synth.paged_decode(poison=False)
