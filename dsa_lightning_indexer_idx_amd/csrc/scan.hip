@@ -189,16 +189,42 @@ struct QOps<FMT_BF16> {
   }
 };
 
+// fp8 keys are read in whole 1 KiB blocks (8 key rows; lane l takes 16 bytes: row
+// l / 8, chunk l % 8), which the memory system serves faster than the operand order
+// (every 16-lane quarter of a load instruction then reads two whole cache lines instead
+// of pieces of 16 rows); the operand is then assembled across lanes. Tile j is blocks
+// 2j (rows 0..7 of the tile) and 2j + 1 (rows 8..15); lane (g, c) of the operand needs
+// chunks g and g + 4 of row c, which sit in lanes 8(c % 8) + g and + 4 of block
+// 2j + c / 8. One row_shr:4 / row_shl:4 merge of the two blocks puts, in each 8-lane
+// group, the low chunks of both blocks in one register and the high chunks in another,
+// so that one backward permute per register fetches both halves of the operand.
 template <>
 struct KOps<FMT_FP8> {
-  v8i b;
-  __device__ void load(const uint8_t* k, const void*, int64_t kidx, int g) {
-    const uint8_t* row = k + kidx * kDim;
-    v4i lo = __builtin_nontemporal_load((const v4i*)(row + 16 * g));
-    v4i hi = __builtin_nontemporal_load((const v4i*)(row + 64 + 16 * g));
-    b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  v4i raw[2];
+  __device__ void load_rows(const uint8_t* k, int64_t kidx0, int j, int last, int lane) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = min(16 * j + 8 * h + (lane >> 3), last);
+      raw[h] = __builtin_nontemporal_load((const v4i*)(k + (kidx0 + t) * kDim + 16 * (lane & 7)));
+    }
   }
-  __device__ v4f mma(const QOps<FMT_FP8>& qo, int h) const {
+  __device__ v8i operand(int lane) const {
+    const int c = lane & 15, g = lane >> 4;
+    const int src = 4 * (8 * (c & 7) + g + 4 * (c >> 3));
+    v8i b;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // the merges write only the lanes of chunks 4..7 (DPP banks 1 and 3: lanes 4..7 and
+      // 12..15 of each row), resp. of chunks 0..3 (banks 0 and 2); the other lanes keep
+      // the first operand, so no lane-dependent branch is needed around the shifts
+      const int s1 = __builtin_amdgcn_update_dpp(raw[0][d], raw[1][d], 0x114, 0xF, 0xA, false);  // row_shr:4
+      const int s2 = __builtin_amdgcn_update_dpp(raw[1][d], raw[0][d], 0x104, 0xF, 0x5, false);  // row_shl:4
+      b[d] = __builtin_amdgcn_ds_bpermute(src, s1);
+      b[4 + d] = __builtin_amdgcn_ds_bpermute(src, s2);
+    }
+    return b;
+  }
+  static __device__ v4f mma(const QOps<FMT_FP8>& qo, int h, const v8i& b) {
     return mfma_fp8_fp8(qo.a[h], b, v4f{0.f, 0.f, 0.f, 0.f});
   }
 };
@@ -211,9 +237,10 @@ struct KOps<FMT_MXFP4> {
     b = __builtin_nontemporal_load((const v4i*)(k + kidx * (kDim / 2) + 16 * g));
     sc = ((const uint8_t*)scale)[kidx * (kDim / 32) + g];
   }
-  __device__ v4f mma(const QOps<FMT_MXFP4>& qo, int h) const {
-    v8i bb = v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-    return mfma_fp8_fp4(qo.a[h], bb, sc, v4f{0.f, 0.f, 0.f, 0.f});
+  __device__ const KOps& operand(int) const { return *this; }
+  static __device__ v4f mma(const QOps<FMT_MXFP4>& qo, int h, const KOps& ko) {
+    v8i bb = v8i{ko.b[0], ko.b[1], ko.b[2], ko.b[3], 0, 0, 0, 0};
+    return mfma_fp8_fp4(qo.a[h], bb, ko.sc, v4f{0.f, 0.f, 0.f, 0.f});
   }
 };
 
@@ -225,10 +252,11 @@ struct KOps<FMT_BF16> {
 #pragma unroll
     for (int s = 0; s < 4; ++s) b[s] = __builtin_nontemporal_load(p + 4 * s);
   }
-  __device__ v4f mma(const QOps<FMT_BF16>& qo, int h) const {
+  __device__ const KOps& operand(int) const { return *this; }
+  static __device__ v4f mma(const QOps<FMT_BF16>& qo, int h, const KOps& ko) {
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_bf16(qo.a[h][s], b[s], acc);
+    for (int s = 0; s < 4; ++s) acc = mfma_bf16(qo.a[h][s], ko.b[s], acc);
     return acc;
   }
 };
@@ -242,21 +270,28 @@ __device__ __forceinline__ void load_step(KOps<F> (&ko)[4], float& sc, const Sca
                                           int32_t vlim, int lane) {
   const int g = lane >> 4, c16 = lane & 15;
   const int last = vlim - 1;
+  if constexpr (F == FMT_FP8) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ko[j].load(a.k, a.k_scale, kidx0 + min(16 * j + c16, last), g);
-  if constexpr (F == FMT_FP8) sc = ((const float*)a.k_scale)[kidx0 + min(lane, last)];
+    for (int j = 0; j < 4; ++j) ko[j].load_rows(a.k, kidx0, j, last, lane);
+    sc = ((const float*)a.k_scale)[kidx0 + min(lane, last)];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ko[j].load(a.k, a.k_scale, kidx0 + min(16 * j + c16, last), g);
+  }
 }
 
 template <int F>
 __device__ __forceinline__ float score_step(const KOps<F> (&ko)[4], float sc, const QOps<F>& qo,
                                            const float (&wr)[4][4]) {
+  const int lane = lane_id();
   float p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     p[j] = 0.f;
+    const auto b = ko[j].operand(lane);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const v4f s = ko[j].mma(qo, h);
+      const v4f s = KOps<F>::mma(qo, h, b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[j] = fmaf(wr[h][i], relu(s[i]), p[j]);
     }

@@ -737,8 +737,16 @@ __global__ __launch_bounds__(kSegThreads) void topk_zero_kernel(uint32_t* p, int
 
 // Four-entry groups per thread per pass of the segment loops: independent loads issued
 // together so the loop is not bound by one memory latency per load.
-constexpr int kSegGroups = 4;
+constexpr int kSegGroups = 4;  // 16 entries per thread: one 16-bit mask per list in the filter
+static_assert(kSegGroups * 4 <= 16, "the filter packs per-lane counts into 16-bit halves");
 constexpr int kSegStep = kSegThreads * 4 * kSegGroups;
+
+// Histogram bin of a present score (not -inf or NaN): order_key's bin with
+// branch-free arithmetic (-0 is folded onto +0 by adding +0).
+__device__ __forceinline__ uint32_t hist_bin(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) >> kBinShift;
+}
 
 template <bool V4>
 __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(TopkCall a, LongWs ws, int64_t seg, int segs) {
@@ -759,10 +767,8 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(TopkCall a, Long
     for (int j = 0; j < kSegGroups; ++j) {
       const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t key = order_key(e[c]);
-        if (key) atomicAdd(&hist[key >> kBinShift], 1u);
-      }
+      for (int c = 0; c < 4; ++c)
+        if (e[c] > -__builtin_inff()) atomicAdd(&hist[hist_bin(e[c])], 1u);
     }
   }
   __syncthreads();
@@ -777,53 +783,88 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(TopkCall a, Long
 // workloads' shapes is resident at once.
 constexpr int kSegCandCap = 4096;
 
+// Appends the columns of the set bits of bits (bit j = entry j of the lane's group
+// pattern, col(j)) to an LDS list at slot, one lane-serial store per set bit.
+template <class Col>
+__device__ __forceinline__ void append_bits(uint32_t bits, uint32_t slot, uint32_t* list, uint32_t cap, const Col& col) {
+  for (; bits != 0u; bits &= bits - 1u, ++slot)
+    if (slot < cap) list[slot] = col(__builtin_ctz(bits));
+}
+
 template <bool V4>
 __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(TopkCall a, LongWs ws, int64_t seg, int segs) {
   __shared__ CutInfo ci;
   __shared__ uint32_t lwin[kMaxK];
   __shared__ uint32_t lcand[kSegCandCap];
-  __shared__ uint32_t n_lwin, n_lcand, base_win, base_cand;
+  __shared__ unsigned long long n_list;  // winners << 32 | candidates
+  __shared__ uint32_t base_win, base_cand;
   const int r = (int)(blockIdx.x / (unsigned)segs);
   const int64_t n = row_len(a, r);
   const int64_t s0 = (int64_t)(blockIdx.x % (unsigned)segs) * seg;
   const int64_t s1 = min(s0 + seg, n);
   if (s0 >= s1) return;
-  if (threadIdx.x == 0) {
-    n_lwin = 0;
-    n_lcand = 0;
-  }
+  if (threadIdx.x == 0) n_list = 0;
   find_cut<kSegThreads>(ws.hist + (int64_t)r * kHistBins, a.k, ci);
   const int cut = ci.bin;
   // a cut bin too large for the workspace is resolved from the row itself
   const bool keep_cand = ci.count <= (uint32_t)kCandCap;
+  // The cut bin as value bounds, so that classifying an entry takes two compares: it
+  // is a winner when its bin is above the cut, x >= t_hi (the smallest value of bin
+  // cut + 1), and a candidate when it is in the cut bin, x >= t_lo and not a winner.
+  // -inf and NaN compare false and -0 == +0, as in order_key. Bins below 8 hold only
+  // the keys of NaN and -inf, which are never counted, so a cut bin's bounds are real
+  // values; past +inf's bin nothing is a winner (a NaN bound compares false).
+  const float no_bound = __builtin_nanf("");
+  float t_hi, t_lo;
+  if (cut < 0) {  // at most k present entries: all are winners
+    t_hi = -__FLT_MAX__;
+    t_lo = no_bound;
+  } else {
+    const uint64_t hk = (uint64_t)(cut + 1) << kBinShift;
+    t_hi = hk > 0xFF800000ull ? no_bound : key_value((uint32_t)hk);
+    t_lo = keep_cand ? key_value((uint32_t)cut << kBinShift) : no_bound;
+  }
   const float* row = a.logits + (int64_t)r * a.ld;
   // every thread runs the same number of iterations so whole waves vote together
   for (int64_t b = s0; b < s1; b += kSegStep) {
     float4 v[kSegGroups];
 #pragma unroll
     for (int j = 0; j < kSegGroups; ++j) v[j] = load4<V4, false>(row, b + ((int64_t)j * kSegThreads + threadIdx.x) * 4, s1);
-    bool tw[4 * kSegGroups], tc[4 * kSegGroups];
-    uint32_t col[4 * kSegGroups];
+    // bit 4j + c of a lane's masks: entry c of its group j
+    uint32_t wbits = 0u, cbits = 0u;
 #pragma unroll
     for (int j = 0; j < kSegGroups; ++j) {
       const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-      const int64_t i0 = b + ((int64_t)j * kSegThreads + threadIdx.x) * 4;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t vk = order_key(e[c]);
-        const int bin = vk ? (int)(vk >> kBinShift) : -2;
-        tw[4 * j + c] = bin > cut;
-        tc[4 * j + c] = keep_cand && bin == cut;
-        col[4 * j + c] = (uint32_t)(i0 + c);
+        const bool w = e[c] >= t_hi;
+        wbits |= w ? 1u << (4 * j + c) : 0u;
+        cbits |= (!w && e[c] >= t_lo) ? 1u << (4 * j + c) : 0u;
       }
     }
-    lane_append<4 * kSegGroups>(tw, col, lwin, &n_lwin, (uint32_t)kMaxK);
-    lane_append<4 * kSegGroups>(tc, col, lcand, &n_lcand, (uint32_t)kSegCandCap);
+    // one wave prefix sum and one LDS atomic place both lists' entries (a lane holds
+    // at most 16 of each, so the packed halves winners << 16 | candidates never carry)
+    const uint32_t mine = ((uint32_t)__popc(wbits) << 16) | (uint32_t)__popc(cbits);
+    const uint32_t incl = wave_inclusive_sum(mine);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    if (tot != 0u) {
+      unsigned long long base = 0;
+      if (lane_id() == 0) base = atomicAdd(&n_list, ((unsigned long long)(tot >> 16) << 32) | (tot & 0xFFFFu));
+      const uint32_t bw = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+      const uint32_t bc = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+      const uint32_t excl = incl - mine;
+      auto col = [&](int bit) {
+        return (uint32_t)(b + ((int64_t)(bit >> 2) * kSegThreads + threadIdx.x) * 4 + (bit & 3));
+      };
+      append_bits(wbits, bw + (excl >> 16), lwin, (uint32_t)kMaxK, col);
+      append_bits(cbits, bc + (excl & 0xFFFFu), lcand, (uint32_t)kSegCandCap, col);
+    }
   }
   __syncthreads();
   uint32_t* cnt = ws.counts + 2 * (int64_t)r;
-  const uint32_t nw = min(n_lwin, (uint32_t)kMaxK);
-  const uint32_t nc = n_lcand;
+  const unsigned long long nl = n_list;
+  const uint32_t nw = min((uint32_t)(nl >> 32), (uint32_t)kMaxK);
+  const uint32_t nc = (uint32_t)nl;
   if (threadIdx.x == 0) {
     base_win = nw ? atomicAdd(&cnt[0], nw) : 0u;
     // an overflowing segment, or a cut bin too large to keep, pushes the row's count
