@@ -1,6 +1,8 @@
-// Streaming-read probe: reads a device buffer once with wide non-temporal loads and
+// Streaming-read probe: reads a device buffer once with non-temporal 16-byte loads and
 // discards the data. It is the measuring stick for the scan's HBM fraction (what this
-// machine actually delivers to a plain read), not part of the indexer path.
+// machine actually delivers to a plain read), not part of the indexer path. Each wave
+// reads whole 8 KiB blocks (eight 1 KiB load instructions per block, two blocks in
+// flight), the access shape the memory system serves best here.
 #include "device.h"
 #include "launch.h"
 
@@ -9,20 +11,30 @@
 namespace dsaidx {
 
 constexpr int kProbeThreads = 256;
-constexpr int kProbeUnroll = 8;
+constexpr int kProbeBlockVecs = 512;  // 16-byte vectors per 8 KiB block
+constexpr int kProbeDepth = 2;        // blocks in flight per wave
 
 __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const v4i* __restrict__ p, int64_t n, uint32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * kProbeThreads + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kProbeThreads / kWave);
+  const int64_t nblk = n / kProbeBlockVecs;
   v4i acc = {0, 0, 0, 0};
-  for (; i + (kProbeUnroll - 1) * stride < n; i += kProbeUnroll * stride) {
-    v4i v[kProbeUnroll];
+  for (int64_t b = wave * kProbeDepth; b < nblk; b += nwaves * kProbeDepth) {
+    v4i v[kProbeDepth][8];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+    for (int d = 0; d < kProbeDepth; ++d) {
+      const int64_t bb = min(b + d, nblk - 1);
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u];
+      for (int u = 0; u < 8; ++u) v[d][u] = __builtin_nontemporal_load(p + bb * kProbeBlockVecs + u * kWave + lane);
+    }
+#pragma unroll
+    for (int d = 0; d < kProbeDepth; ++d)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[d][u];
   }
-  for (; i < n; i += stride) acc ^= p[i];
+  // the tail past the last whole block
+  for (int64_t i = nblk * kProbeBlockVecs + wave * kWave + lane; i < n; i += nwaves * kWave) acc += p[i];
   // never true for the probe's buffers in practice; keeps the loads
   if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x7A5A5A5A) sink[0] = 1u;
 }
@@ -30,7 +42,8 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const v4i* __
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
   const int64_t n = (int64_t)(bytes / 16);
   if (n == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>(32 * (int64_t)device_cu_count(), (n + kProbeThreads - 1) / kProbeThreads);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(2 * (int64_t)device_cu_count(),
+                                                               (n / kProbeBlockVecs + 7) / 8));
   hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream, (const v4i*)buf, n,
                      sink);
   return hipGetLastError();

@@ -3,10 +3,10 @@
 //
 // Work split: an item is (row, chunk of positions); waves take items in a
 // grid-stride loop. A wave scores 64 positions per step:
-//   * each lane loads 32 K-elements of block (lane / 16) for the token at column
-//     lane % 16 of each of the four 16-token tiles (16-byte loads; the four lane
-//     groups together read each key row once, each load instruction whole 64-byte
-//     halves of 16 rows),
+//   * the step's 64 key rows are loaded with 16-byte loads: fp8 rows in whole 1 KiB
+//     blocks of 8 rows, then moved across lanes into the MFMA operand order (lane
+//     l % 16 = token column of a 16-token tile, l / 16 = K block); MXFP4 and bf16 rows
+//     directly in operand order (each load instruction reads 1 KiB of 16 rows),
 //   * 16 MFMAs (4 head tiles x 4 token tiles) give S[head, token] = q_head . k,
 //   * each lane applies ReLU and its 16 head weights in registers, three lane
 //     swaps finish the 64-head sum, and lane l holds the score of position l,
