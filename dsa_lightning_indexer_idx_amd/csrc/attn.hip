@@ -37,7 +37,7 @@ namespace dsaidx {
 constexpr int kAttnD = 576;          // entry / query length
 constexpr int kAttnDV = 512;         // value length (the entry's first 512 elements)
 constexpr int kAttnT = 32;           // positions per tile
-constexpr int kKPitch = kAttnD + 8;  // token-major tile row (bf16): 1168 B, conflict-free score reads
+constexpr int kKPitch = kAttnD + 48;  // token-major tile row (bf16): 1248 B (fewest bank conflicts of the pads tried)
 constexpr int kPPitch = kAttnT + 8;  // per-wave P rows (bf16)
 constexpr int kChunks = kAttnT * kAttnD / 8;  // 16-byte pieces of a tile (2304)
 constexpr float kLog2e = 1.4426950408889634f;

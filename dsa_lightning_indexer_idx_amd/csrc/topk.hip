@@ -514,11 +514,9 @@ __device__ void bucket_sort_write(const TopkCall& a, int r, const Key& key, int 
       }
     }
     __syncthreads();
-    if (ss.big) {
-      sort_and_write<NT>(a, r, key, cnt, tmp);
-      return;
-    }
-    // exclusive scan of the bucket counts, in place
+    // exclusive scan of the bucket counts, in place (a row with a full bucket leaves
+    // after the scan's first barrier: the scan only touches counts, which the bitonic
+    // path does not read)
     static_assert(per % 4 == 0, "bucket counts are read four at a time");
     uint32_t c[per], sum = 0;
 #pragma unroll
@@ -534,6 +532,10 @@ __device__ void bucket_sort_write(const TopkCall& a, int r, const Key& key, int 
     uint32_t incl = wave_inclusive_sum(sum);
     if (lane_id() == kWave - 1) ss.sums[tid / kWave] = incl;
     __syncthreads();
+    if (ss.big) {
+      sort_and_write<NT>(a, r, key, cnt, tmp);
+      return;
+    }
     uint32_t off = incl - sum;
 #pragma unroll
     for (int w = 0; w < waves; ++w) off += w < tid / kWave ? ss.sums[w] : 0u;
@@ -573,14 +575,22 @@ __device__ void bucket_sort_write(const TopkCall& a, int r, const Key& key, int 
 #pragma unroll
         for (int q = 0; q < 4; ++q) pos[e] += (j + q < len[e]) & (v[e][q] > x[e]);
     }
-    // the keys in order into LDS (over the counts, read above), then a coalesced row
-    uint64_t* sorted = (uint64_t*)counts;
-    __syncthreads();
+    // each key straight to its position of the row (the row's 8 KiB are written whole
+    // by the block, so the scattered 4-byte stores combine in the cache), and the
+    // padding past cnt
+    int32_t* oi = a.out_idx + (int64_t)r * a.out_ld;
+    float* ov = a.out_val ? a.out_val + (int64_t)r * a.out_ld : nullptr;
+    const int32_t* cand_row = a.cand ? a.cand + (int64_t)r * a.cand_ld : nullptr;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (ib[e] >= 0) sorted[pos[e]] = x[e];
-    __syncthreads();
-    write_list<NT>(a, r, [&](int i) { return sorted[i]; }, cnt);
+      if (ib[e] >= 0 && pos[e] < (uint32_t)a.k) {
+        oi[pos[e]] = out_index(a, cand_row, key_col(x[e]));
+        if (ov) ov[pos[e]] = key_value((uint32_t)(x[e] >> 32));
+      }
+    for (int i = cnt + tid; i < a.k; i += NT) {
+      oi[i] = -1;
+      if (ov) ov[i] = -__builtin_inff();
+    }
     return;
   }
   write_list<NT>(a, r, [&](int i) { return 0ull; }, 0);
