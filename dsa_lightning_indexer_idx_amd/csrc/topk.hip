@@ -41,7 +41,7 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kBinShift = 32 - kHistBits;  // bin of a 32-bit value key
 constexpr int kKeyBinShift = 64 - kHistBits;  // bin of a 64-bit selection key
 constexpr int kCandCap = 8192;         // long rows: candidates kept per row in the workspace
-constexpr int kShortCandCap = 2 * kHistBins;  // short rows: candidate columns (u16) over the histogram
+constexpr int kShortCandCap = 2 * kHistBins - 512;  // short rows: candidate columns (u16) over the histogram
 constexpr int kSegThreads = 256;
 constexpr int kFinishThreads = 1024;
 constexpr int kShortThreads = 512;
@@ -122,7 +122,6 @@ __device__ __forceinline__ void lane_append(const bool (&take)[U], const T (&ite
 // ------------------------------------------------------------------ radix select
 
 struct RadixShared {
-  uint32_t hist[256];
   uint64_t prefix;
   uint32_t krem, stop, total;
 };
@@ -132,7 +131,8 @@ struct RadixShared {
 // >= T. Keys are unique; needs 1 <= want <= the number of such keys. Every thread of
 // the block must call it.
 template <int NT, class Get>
-__device__ uint64_t radix_threshold(const Get& get, int64_t n, uint32_t want, RadixShared& sh, uint64_t prefix = 0,
+__device__ uint64_t radix_threshold(const Get& get, int64_t n, uint32_t want, RadixShared& sh, uint32_t* rh,
+                                    uint64_t prefix = 0,
                                     int top = 64) {
   const int tid = threadIdx.x;
   uint64_t mask = top >= 64 ? 0ull : ~0ull << top;
@@ -140,19 +140,19 @@ __device__ uint64_t radix_threshold(const Get& get, int64_t n, uint32_t want, Ra
   uint32_t krem = want;
   while (top > 0) {
     const int shift = top > 8 ? top - 8 : 0;  // the last digit may overlap fixed bits
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
+    for (int i = tid; i < 256; i += NT) rh[i] = 0;
     if (tid == 0) sh.stop = 0;
     __syncthreads();
     for (int64_t i = tid; i < n; i += NT) {
       const uint64_t key = get(i);
-      if (key != 0 && (key & mask) == prefix) atomicAdd(&sh.hist[(uint32_t)(key >> shift) & 255u], 1u);
+      if (key != 0 && (key & mask) == prefix) atomicAdd(&rh[(uint32_t)(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < kWave) {
       uint32_t c[4], tot = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = sh.hist[255 - 4 * tid - j];
+        c[j] = rh[255 - 4 * tid - j];
         tot += c[j];
       }
       const uint32_t incl = wave_inclusive_sum(tot);
@@ -624,15 +624,21 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkCall a) {
   extern __shared__ uint4 dyn[];                 // the row's value keys (n_cols rounded up to 4, at
                                                  // least kMaxK keys' worth), then the sorted keys
   uint32_t* vkeys = (uint32_t*)dyn;
+  // value histogram, then the cut bin's columns and the radix select's digit counts,
+  // then the bucket counts (LDS small enough for three workgroups per CU at 8192 columns)
   __shared__ __align__(16) union {
-    uint32_t hist[kHistBins];                    // value histogram, then
-    uint16_t cand[kShortCandCap];                // the cut bin's columns, then the bucket counts
+    uint32_t hist[kHistBins];
+    struct {
+      uint16_t cand[kShortCandCap];
+      uint32_t rh[256];
+    } c;
   } u;
   __shared__ uint16_t sel[kMaxK];                // selected columns
   __shared__ RadixShared sh;
   __shared__ CutInfo ci;
   __shared__ SortShared ss;
   __shared__ uint32_t n_sel, n_cand;
+  __shared__ unsigned long long n_list;  // the filter's winners << 32 | candidates
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
   const int64_t n = row_len(a, r);
@@ -640,6 +646,7 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkCall a) {
   if (tid == 0) {
     n_sel = 0;
     n_cand = 0;
+    n_list = 0;
   }
   __syncthreads();
 
@@ -676,21 +683,41 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkCall a) {
   const uint32_t keff = min((uint32_t)a.k, ci.total);
 
   // 3. winners above the cut, candidates in it
+  // each lane marks its winners and candidates in two bit masks (bit j: entry
+  // b + j NT + tid); one wave prefix sum of the packed counts (winners << 16 |
+  // candidates, at most 8 each per lane) and one LDS atomic place both lists
   constexpr int U2 = 8;
   for (int64_t b = 0; b < n; b += (int64_t)NT * U2) {
-    bool tw[U2], tc[U2];
-    uint16_t col[U2];
+    uint32_t wbits = 0u, cbits = 0u;
 #pragma unroll
     for (int j = 0; j < U2; ++j) {
       const int64_t i = b + (int64_t)j * NT + tid;
       const uint32_t v = i < n ? vkeys[i] : 0u;
       const int bin = v ? (int)(v >> kBinShift) : -2;
-      tw[j] = bin > cut;
-      tc[j] = compact && bin == cut;
-      col[j] = (uint16_t)i;
+      wbits |= bin > cut ? 1u << j : 0u;
+      cbits |= compact && bin == cut ? 1u << j : 0u;
     }
-    lane_append<U2>(tw, col, sel, &n_sel, (uint32_t)kMaxK);
-    lane_append<U2>(tc, col, u.cand, &n_cand, (uint32_t)kShortCandCap);
+    const uint32_t mine = ((uint32_t)__popc(wbits) << 16) | (uint32_t)__popc(cbits);
+    const uint32_t incl = wave_inclusive_sum(mine);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    if (tot != 0u) {
+      unsigned long long base = 0;
+      if (lane_id() == 0) base = atomicAdd(&n_list, ((unsigned long long)(tot >> 16) << 32) | (tot & 0xFFFFu));
+      const uint32_t bw = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+      const uint32_t bc = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+      const uint32_t excl = incl - mine;
+      auto col = [&](int bit) { return (uint32_t)(b + (int64_t)bit * NT + tid); };
+      uint32_t ws = bw + (excl >> 16), cs = bc + (excl & 0xFFFFu);
+      for (; wbits != 0u; wbits &= wbits - 1u, ++ws)
+        if (ws < (uint32_t)kMaxK) sel[ws] = (uint16_t)col(__builtin_ctz(wbits));
+      for (; cbits != 0u; cbits &= cbits - 1u, ++cs)
+        if (cs < (uint32_t)kShortCandCap) u.c.cand[cs] = (uint16_t)col(__builtin_ctz(cbits));
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    n_sel = (uint32_t)(n_list >> 32);
+    n_cand = (uint32_t)n_list;
   }
   __syncthreads();
 
@@ -702,18 +729,18 @@ __global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkCall a) {
     if (compact) {
       const uint32_t nc = n_cand;
       auto get = [&](int64_t i) -> uint64_t {
-        const uint32_t c = u.cand[i];
+        const uint32_t c = u.c.cand[i];
         return sel_key(vkeys[c], c);
       };
-      const uint64_t thr = need == nc ? 1ull : radix_threshold<NT>(get, nc, need, sh, pre, kKeyBinShift);
-      gather_at_least<NT, uint16_t>(get, [&](int64_t i) { return u.cand[i]; }, nc, thr, sel, &n_sel,
+      const uint64_t thr = need == nc ? 1ull : radix_threshold<NT>(get, nc, need, sh, u.c.rh, pre, kKeyBinShift);
+      gather_at_least<NT, uint16_t>(get, [&](int64_t i) { return u.c.cand[i]; }, nc, thr, sel, &n_sel,
                                     (uint32_t)kMaxK);
     } else {
       auto get = [&](int64_t i) -> uint64_t {
         const uint32_t v = vkeys[i];
         return (int)(v >> kBinShift) == cut ? sel_key(v, i) : 0ull;
       };
-      const uint64_t thr = radix_threshold<NT>(get, n, need, sh, pre, kKeyBinShift);
+      const uint64_t thr = radix_threshold<NT>(get, n, need, sh, u.c.rh, pre, kKeyBinShift);
       gather_at_least<NT, uint16_t>(get, [&](int64_t i) { return (uint16_t)i; }, n, thr, sel, &n_sel,
                                     (uint32_t)kMaxK);
     }
@@ -899,6 +926,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(TopkCall a,
   __shared__ uint64_t sel[kMaxK];
   __shared__ __align__(16) uint64_t cand[kCandCap];  // then the sort's bucket counts and keys
   __shared__ RadixShared sh;
+  __shared__ uint32_t rh[256];  // the radix select's digit counts
   __shared__ SortShared ss;
   __shared__ uint32_t count;
   const int r = blockIdx.x;
@@ -920,7 +948,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(TopkCall a,
     auto get = [&](int64_t i) -> uint64_t { return cand[i]; };
     if (need > 0) {
       const uint64_t pre = cand[0];
-      const uint64_t thr = need == n_cand ? 1ull : radix_threshold<NT>(get, n_cand, need, sh, pre, kKeyBinShift);
+      const uint64_t thr = need == n_cand ? 1ull : radix_threshold<NT>(get, n_cand, need, sh, rh, pre, kKeyBinShift);
       gather_at_least<NT, uint64_t>(get, get, n_cand, thr, sel, &count, (uint32_t)kMaxK);
     }
     cnt = (int)(n_win + need);
@@ -933,7 +961,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(TopkCall a,
     };
     const uint32_t total = count_present<NT>(get, n, sh);
     const uint32_t keff = min((uint32_t)a.k, total);
-    const uint64_t thr = keff == 0 ? ~0ull : (keff == total ? 1ull : radix_threshold<NT>(get, n, keff, sh));
+    const uint64_t thr = keff == 0 ? ~0ull : (keff == total ? 1ull : radix_threshold<NT>(get, n, keff, sh, rh));
     if (threadIdx.x == 0) count = 0;
     __syncthreads();
     gather_at_least<NT, uint64_t>(get, get, n, thr, sel, &count, (uint32_t)kMaxK);
