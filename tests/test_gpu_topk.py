@@ -83,7 +83,9 @@ def test_unsorted_flag_gives_the_same_set():
 
 
 @pytest.mark.parametrize("shape", [(64, 131072, 2048), (64, 131072, 512), (32, 32768, 2048),
-                                   (4096, 8192, 2048), (64, 8192, 2048)])
+                                   (4096, 8192, 2048), (64, 8192, 2048),
+                                   # one or few very long rows: the most segments per row
+                                   (1, 1 << 22, 2048), (3, 1 << 20, 1024)])
 def test_full_size_shapes(shape):
     """Rows of the workloads' sizes (synthetic scores with heavy ties), every row checked."""
     require_gpu()
