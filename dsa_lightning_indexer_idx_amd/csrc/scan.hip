@@ -155,9 +155,9 @@ struct KOps;
 // fp8 q, head tile h, lane l: row 16h + l%16, dims 16g .. 16g+15 and 64+16g ..
 // 64+16g+15 (g = l / 16), which is the 8-bit operand's own K order (measured on gfx950
 // with one-hot inputs). Against fp8 keys any K order shared by both operands would
-// do; this one lets each key load instruction read whole 64-byte halves of the key
-// rows. Against MXFP4 keys it is required: the fp4 operand of lane group g holds
-// dims 32g .. 32g+31 (one UE8M0 group) in hardware order.
+// do (the key operand is assembled in this order from whole-row loads). Against MXFP4
+// keys it is required: the fp4 operand of lane group g holds dims 32g .. 32g+31 (one
+// UE8M0 group) in hardware order.
 template <int F>
 struct QOps {
   static_assert(F == FMT_FP8 || F == FMT_MXFP4, "8-bit q operand");
