@@ -36,6 +36,8 @@ namespace dsaidx {
 
 constexpr int kMaxK = 2048;
 constexpr int kShortRow = 16384;       // rows up to this width take the one-kernel path
+constexpr int kWideRow = 32768;        // and up to this width too when there are at most as
+                                       // many rows as compute units (1024 threads per row)
 constexpr int kHistBits = 12;          // bins of the value histogram
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kBinShift = 32 - kHistBits;  // bin of a 32-bit value key
@@ -45,6 +47,7 @@ constexpr int kShortCandCap = 2 * kHistBins - 512;  // short rows: candidate col
 constexpr int kSegThreads = 256;
 constexpr int kFinishThreads = 1024;
 constexpr int kShortThreads = 512;
+constexpr int kWideThreads = 1024;
 
 __device__ __forceinline__ uint64_t sel_key(uint32_t vkey, int64_t col) {
   return ((uint64_t)vkey << 32) | (uint32_t)(~(uint32_t)col);
@@ -618,9 +621,8 @@ __device__ __forceinline__ float4 load4(const float* row, int64_t i, int64_t n) 
 
 // ------------------------------------------------------------------ short rows
 
-template <bool V4>
-__global__ __launch_bounds__(kShortThreads) void topk_short_kernel(TopkCall a) {
-  constexpr int NT = kShortThreads;
+template <bool V4, int NT>
+__global__ __launch_bounds__(NT) void topk_short_kernel(TopkCall a) {
   extern __shared__ uint4 dyn[];                 // the row's value keys (n_cols rounded up to 4, at
                                                  // least kMaxK keys' worth), then the sorted keys
   uint32_t* vkeys = (uint32_t*)dyn;
@@ -992,17 +994,20 @@ size_t topk_zeroed_bytes(int rows, int64_t n_cols) {
   return (size_t)(round_up(R * kHistBins * 4, 256) + round_up(R * 2 * 4, 256));
 }
 
-template <bool V4>
+// NT = kShortThreads for rows up to kShortRow, kWideThreads up to kWideRow (the row's
+// value keys in LDS: up to 128 KiB, one workgroup per CU).
+template <bool V4, int NT>
 static hipError_t launch_short(const TopkCall& c, hipStream_t stream) {
+  constexpr int kMaxRow = NT == kWideThreads ? kWideRow : kShortRow;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute((const void*)topk_short_kernel<V4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               kShortRow * (int)sizeof(uint32_t));
+    attr = hipFuncSetAttribute((const void*)topk_short_kernel<V4, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kMaxRow * (int)sizeof(uint32_t));
   });
   if (attr != hipSuccess) return attr;
   const size_t lds = (size_t)std::max<int64_t>(round_up(c.n_cols, 4) * 4, kMaxK * 8);
-  hipLaunchKernelGGL(topk_short_kernel<V4>, dim3((unsigned)c.rows), dim3(kShortThreads), lds, stream, c);
+  hipLaunchKernelGGL((topk_short_kernel<V4, NT>), dim3((unsigned)c.rows), dim3(NT), lds, stream, c);
   return hipGetLastError();
 }
 
@@ -1017,7 +1022,12 @@ hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   if (c.rows <= 0) return hipSuccess;
   // rows start on 16-byte boundaries: whole groups of four are read with one load
   const bool v4 = ((uintptr_t)c.logits % 16 == 0) && (c.ld % 4 == 0);
-  if (c.n_cols <= kShortRow) return v4 ? launch_short<true>(c, stream) : launch_short<false>(c, stream);
+  if (c.n_cols <= kShortRow)
+    return v4 ? launch_short<true, kShortThreads>(c, stream) : launch_short<false, kShortThreads>(c, stream);
+  // a few rows of up to kWideRow: one pass over each row, all rows at once, beats the
+  // long-row path's four kernels (its workspace, sized for the long path, goes unused)
+  if (c.n_cols <= kWideRow && c.rows <= device_cu_count())
+    return v4 ? launch_short<true, kWideThreads>(c, stream) : launch_short<false, kWideThreads>(c, stream);
   const int64_t R = c.rows;
   uint8_t* p = (uint8_t*)workspace;
   LongWs ws;
