@@ -295,8 +295,11 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
     mfmas(ra, kb);
     epilogue(rb, p[0][1], p[1][1]);
     kb = kb_next;
-    // the first 16 keys of tile t + 1 (already visible)
-    if (t + 1 < ntiles) kb_next = read_b(t + 1, 0);
+    // the first 16 keys of tile t + 1 (already visible). Read unconditionally: after the
+    // last tile the slot holds stale keys that are never used, and a conditional read
+    // would make the compiler copy the previous operand into its registers, which
+    // waits for that operand's LDS read at once.
+    kb_next = read_b(t + 1, 0);
     mfmas(rb, kb);
     epilogue(ra, p[0][2], p[1][2]);
     epilogue(rb, p[0][3], p[1][3]);
