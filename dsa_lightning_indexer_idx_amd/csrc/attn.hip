@@ -217,9 +217,11 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
       const float mn = fmaxf(m[i], mt);
       // all -inf so far: keep weights 0 (exp2(-inf) = 0, and no -inf - -inf)
       const float base = mn == -__builtin_inff() ? 0.f : mn;
-      alpha[i] = exp2f(m[i] - base);
-      p[0][i] = exp2f(s0 - base);
-      p[1][i] = exp2f(s1 - base);
+      // v_exp_f32 directly (exp2f adds a denormal-range fix): arguments are <= 0 or
+      // -inf, and a weight below 2^-126 of the row maximum may flush to 0
+      alpha[i] = __builtin_amdgcn_exp2f(m[i] - base);
+      p[0][i] = __builtin_amdgcn_exp2f(s0 - base);
+      p[1][i] = __builtin_amdgcn_exp2f(s1 - base);
       l[i] = l[i] * alpha[i] + dpp_row_sum(p[0][i] + p[1][i]);
       m[i] = mn;
     }
