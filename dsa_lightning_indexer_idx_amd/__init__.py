@@ -117,12 +117,69 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
-def _need(t, name):
+# Shape checks of the binding: the kernels take plain pointers and trust the sizes they
+# are given, so a tensor that is on the host, strided or smaller than its role needs is
+# rejected here rather than read or written out of bounds on the device.
+_HEADS, _DIM = 64, 128
+_KEY_BYTES = {"fp8": 128, "bf16": 256, "mxfp4": 64}  # one key row
+_SCALE_BYTES = {"fp8": 4, "mxfp4": 4}                 # one key's scale(s)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(t, name, dtype=None, numel=None, min_numel=None, nbytes=None):
+    """``t`` (or None) as a contiguous device tensor of the given dtype and size."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {min_numel}")
+    if nbytes is not None and _nbytes(t) != nbytes:
+        raise ValueError(f"{name} has {_nbytes(t)} bytes, expected {nbytes}")
     return t
+
+
+def _rows_out(t, name, rows, dtype, min_cols):
+    """A [rows, >= min_cols] output matrix; returns its column count."""
+    _need(t, name, dtype)
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] < min_cols:
+        raise ValueError(f"{name} must be [{rows}, >= {min_cols}], got {list(t.shape)}")
+    return t.shape[1]
+
+
+def _check_score_inputs(q, w, k, k_scale, k_dtype, n_tokens):
+    """q [rows, 64, 128] (fp8 bytes or bf16), w fp32 [rows, 64], key rows and scales of
+    n_tokens tokens in the layout of k_dtype; returns rows."""
+    import torch
+    if k_dtype not in _KEY_BYTES:
+        raise ValueError(f"k_dtype must be one of {sorted(_KEY_BYTES)}, got {k_dtype!r}")
+    rows = q.shape[0]
+    _need(q, "q", nbytes=rows * _HEADS * _DIM * (2 if k_dtype == "bf16" else 1))
+    _need(w, "w", torch.float32, numel=rows * _HEADS)
+    _need(k, "k", nbytes=n_tokens * _KEY_BYTES[k_dtype])
+    if k_dtype == "bf16":
+        _need(k_scale, "k_scale")
+    else:
+        if k_scale is None:
+            raise ValueError(f"k_scale is required for {k_dtype} keys")
+        _need(k_scale, "k_scale", nbytes=n_tokens * _SCALE_BYTES[k_dtype])
+    return rows
+
+
+def _workspace_bytes(workspace) -> int:
+    if workspace is None:
+        return 0
+    _need(workspace, "workspace")
+    return _nbytes(workspace)
 
 
 def _stream(stream):
@@ -142,40 +199,65 @@ def idx_logits(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, ld: int | None
                out=None, stream=None):
     """Scores of rows over contiguous key ranges (C: idx_logits). Returns fp32 [rows, ld]."""
     import torch
-    for t, n in ((q, "q"), (w, "w"), (k, "k"), (k_scale, "k_scale"), (row_ks, "row_ks"),
-                 (row_ke, "row_ke")):
-        _need(t, n)
-    rows = q.shape[0]
+    rows = _check_score_inputs(q, w, k, k_scale, k_dtype, k.shape[0])
+    _need(row_ks, "row_ks", torch.int32, numel=rows)
+    _need(row_ke, "row_ke", torch.int32, numel=rows)
     if out is None:
         if ld is None:
             raise ValueError("give ld or out")
         out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
-    ld = out.shape[1] if out.dim() == 2 else ld
+    ld = _rows_out(out, "out", rows, torch.float32, 1)
     _check(lib().idx_logits(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k), _ptr(k_scale),
                             KDTYPES[k_dtype], k.shape[0], _ptr(row_ks), _ptr(row_ke), rows,
-                            _ptr(_need(out, "out")), ld, _stream(stream)))
+                            _ptr(out), ld, _stream(stream)))
     return out
+
+
+def _check_paged_inputs(q, w, k_pages, k_scale_pages, block_table, seq_lens, row_req, k_dtype):
+    """Paged score inputs: k_pages [n_pages, page_size, key bytes]; returns (rows,
+    page_size, bt_rows, bt_ld)."""
+    import torch
+    if k_pages.dim() < 2:
+        raise ValueError("k_pages must be [n_pages, page_size, ...]")
+    page = k_pages.shape[1]
+    rows = _check_score_inputs(q, w, k_pages, k_scale_pages, k_dtype, k_pages.shape[0] * page)
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [bt_rows, bt_ld]")
+    _need(seq_lens, "seq_lens", torch.int32, min_numel=rows)
+    _need(row_req, "row_req", torch.int32, numel=rows)
+    return rows, page, block_table.shape[0], block_table.shape[1]
 
 
 def idx_logits_paged(q, w, k_pages, k_scale_pages, block_table, seq_lens, *, k_dtype: str,
                      row_req=None, ld: int | None = None, out=None, stream=None):
     """Scores of rows over a paged key cache (C: idx_logits_paged)."""
     import torch
-    for t, n in ((q, "q"), (w, "w"), (k_pages, "k_pages"), (k_scale_pages, "k_scale_pages"),
-                 (block_table, "block_table"), (seq_lens, "seq_lens"), (row_req, "row_req")):
-        _need(t, n)
-    rows = q.shape[0]
-    page = k_pages.shape[1]
-    bt_rows, bt_ld = block_table.shape
+    rows, page, bt_rows, bt_ld = _check_paged_inputs(q, w, k_pages, k_scale_pages, block_table, seq_lens,
+                                                     row_req, k_dtype)
     if out is None:
         ld = bt_ld * page if ld is None else ld
         out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
+    _rows_out(out, "out", rows, torch.float32, 1)
     _check(lib().idx_logits_paged(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k_pages),
                                   _ptr(k_scale_pages), KDTYPES[k_dtype], k_pages.shape[0], page,
                                   _ptr(block_table), bt_rows, bt_ld, _ptr(seq_lens),
-                                  _ptr(row_req), rows, _ptr(_need(out, "out")), out.shape[1],
+                                  _ptr(row_req), rows, _ptr(out), out.shape[1],
                                   _stream(stream)))
     return out
+
+
+def _check_sparse_inputs(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, k_dtype):
+    """Candidate-block score inputs; returns (rows, cand_ld)."""
+    import torch
+    rows = _check_score_inputs(q, w, k, k_scale, k_dtype, k.shape[0])
+    _need(row_ks, "row_ks", torch.int32, numel=rows)
+    _need(row_ke, "row_ke", torch.int32, numel=rows)
+    _need(cand_blocks, "cand_blocks", torch.int32)
+    if cand_blocks.dim() != 2 or cand_blocks.shape[0] != rows:
+        raise ValueError(f"cand_blocks must be [{rows}, cand_ld]")
+    _need(n_cols, "n_cols", torch.int32, numel=rows)
+    return rows, cand_blocks.shape[1]
 
 
 def idx_logits_sparse_blocks(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, *,
@@ -183,18 +265,15 @@ def idx_logits_sparse_blocks(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_co
                              out=None, stream=None):
     """Scores of two-level rows over their candidate blocks (C: idx_logits_sparse_blocks)."""
     import torch
-    for t, n in ((q, "q"), (w, "w"), (k, "k"), (k_scale, "k_scale"), (row_ks, "row_ks"),
-                 (row_ke, "row_ke"), (cand_blocks, "cand_blocks"), (n_cols, "n_cols")):
-        _need(t, n)
-    rows = q.shape[0]
-    cand_ld = cand_blocks.shape[1]
+    rows, cand_ld = _check_sparse_inputs(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, k_dtype)
     if out is None:
         ld = cand_ld * block_size if ld is None else ld
         out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
+    _rows_out(out, "out", rows, torch.float32, 1)
     _check(lib().idx_logits_sparse_blocks(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k),
                                           _ptr(k_scale), KDTYPES[k_dtype], k.shape[0],
                                           _ptr(row_ks), _ptr(row_ke), _ptr(cand_blocks), cand_ld,
-                                          _ptr(n_cols), block_size, rows, _ptr(_need(out, "out")),
+                                          _ptr(n_cols), block_size, rows, _ptr(out),
                                           out.shape[1], _stream(stream)))
     return out
 
@@ -210,18 +289,23 @@ def idx_topk(logits, k: int, *, lens=None, n_cols: int | None = None, sorted: bo
              values: bool = True, out_idx=None, out_val=None, workspace=None, stream=None):
     """Exact top-k per row (C: idx_topk). Returns (idx int32 [rows, k], val fp32 or None)."""
     import torch
-    _need(logits, "logits")
-    _need(lens, "lens")
+    _need(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, ld]")
     rows, ld = logits.shape
+    _need(lens, "lens", torch.int32, min_numel=rows)
     n_cols = ld if n_cols is None else n_cols
     if out_idx is None:
         out_idx = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
     if values and out_val is None:
         out_val = torch.empty((rows, k), dtype=torch.float32, device=logits.device)
+    _rows_out(out_idx, "out_idx", rows, torch.int32, k)
+    if out_val is not None and (_rows_out(out_val, "out_val", rows, torch.float32, k) != out_idx.shape[1]):
+        raise ValueError("out_val must have the shape of out_idx")
     need = idx_topk_workspace(rows, n_cols, k)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wsb = _workspace_bytes(workspace)
     _check(lib().idx_topk(_ptr(logits), ld, _ptr(lens), n_cols, rows, k, _ptr(out_idx),
                           _ptr(out_val), out_idx.shape[1], 0 if sorted else IDX_TOPK_UNSORTED,
                           _ptr(workspace), wsb, _stream(stream)))
@@ -240,18 +324,24 @@ def idx_candidate_blocks(logits, block_size: int, n_top: int, *, lens=None, n_co
     import torch
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be 2-D with unit column stride")
-    _need(lens, "lens")
+    if not logits.is_cuda or logits.dtype != torch.float32:
+        raise ValueError("logits must be a float32 device tensor")
     rows = logits.shape[0]
+    _need(lens, "lens", torch.int32, min_numel=rows)
     ld = max(logits.stride(0), logits.shape[1], 1)
     n_cols = logits.shape[1] if n_cols is None else n_cols
+    if n_cols > logits.shape[1]:
+        raise ValueError(f"n_cols = {n_cols} exceeds the {logits.shape[1]} columns of logits")
     if cand is None:
         cand = torch.empty((rows, n_top), dtype=torch.int32, device=logits.device)
     if n_cand is None:
         n_cand = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _rows_out(cand, "cand", rows, torch.int32, n_top)
+    _need(n_cand, "n_cand", torch.int32, min_numel=rows)
     need = idx_candidate_blocks_workspace(rows, n_cols)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wsb = _workspace_bytes(workspace)
     _check(lib().idx_candidate_blocks(_ptr(logits), ld, _ptr(lens), n_cols, rows, block_size, n_top,
                                       _ptr(cand), cand.shape[1], _ptr(n_cand), _ptr(workspace), wsb,
                                       _stream(stream)))
@@ -268,19 +358,29 @@ def idx_sparse_attn_paged(q, kv_pages, block_table, seq_lens, indices, scale: fl
     [rows, heads, 576]; kv_pages bf16 [n_pages, 64, 576]; indices int32 [rows, >= k].
     Returns (out fp32 [rows, heads, 512], lse fp32 [rows, heads] or None)."""
     import torch
-    for t, name in ((q, "q"), (kv_pages, "kv_pages"), (block_table, "block_table"), (seq_lens, "seq_lens"),
-                    (indices, "indices"), (row_req, "row_req")):
-        _need(t, name)
+    if q.dim() != 3 or kv_pages.dim() < 2 or block_table.dim() != 2 or indices.dim() != 2:
+        raise ValueError("q must be [rows, heads, 576], kv_pages [n_pages, 64, 576], block_table and "
+                         "indices 2-D")
     rows, heads, _ = q.shape
+    _need(q, "q", nbytes=rows * heads * 576 * 2)
+    _need(kv_pages, "kv_pages", nbytes=kv_pages.shape[0] * kv_pages.shape[1] * 576 * 2)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32, min_numel=rows)
+    _need(indices, "indices", torch.int32)
+    if indices.shape[0] != rows:
+        raise ValueError(f"indices must have {rows} rows")
+    _need(row_req, "row_req", torch.int32, numel=rows)
     k = indices.shape[1] if k is None else k
     if out is None:
         out = torch.empty((rows, heads, 512), dtype=torch.float32, device=q.device)
     if with_lse and lse is None:
         lse = torch.empty((rows, heads), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, numel=rows * heads * 512)
+    _need(lse, "lse", torch.float32, numel=rows * heads)
     need = idx_sparse_attn_workspace(rows, heads, k)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wsb = _workspace_bytes(workspace)
     _check(lib().idx_sparse_attn_paged(_ptr(q), heads, _ptr(kv_pages), kv_pages.shape[0], kv_pages.shape[1],
                                        _ptr(block_table), block_table.shape[0], block_table.shape[1],
                                        _ptr(seq_lens), _ptr(row_req), _ptr(indices), indices.shape[1], k, rows,
@@ -302,6 +402,10 @@ class Problem:
 
 
 def dense_problem(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, max_cols: int) -> Problem:
+    import torch
+    rows = _check_score_inputs(q, w, k, k_scale, k_dtype, k.shape[0])
+    _need(row_ks, "row_ks", torch.int32, numel=rows)
+    _need(row_ke, "row_ke", torch.int32, numel=rows)
     st = idx_problem(mode=IDX_MODE_DENSE, rows=q.shape[0], q=q.data_ptr(),
                      q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
                      k=k.data_ptr(), k_scale=None if k_scale is None else k_scale.data_ptr(),
@@ -312,6 +416,7 @@ def dense_problem(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, max_cols: i
 
 def paged_problem(q, w, k_pages, k_scale_pages, block_table, seq_lens, *, k_dtype: str,
                   row_req=None) -> Problem:
+    _check_paged_inputs(q, w, k_pages, k_scale_pages, block_table, seq_lens, row_req, k_dtype)
     st = idx_problem(mode=IDX_MODE_PAGED, rows=q.shape[0], q=q.data_ptr(),
                      q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
                      k=k_pages.data_ptr(), k_scale=k_scale_pages.data_ptr(),
@@ -324,6 +429,7 @@ def paged_problem(q, w, k_pages, k_scale_pages, block_table, seq_lens, *, k_dtyp
 
 def sparse_problem(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, *, k_dtype: str,
                    block_size: int = 128) -> Problem:
+    _check_sparse_inputs(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, k_dtype)
     st = idx_problem(mode=IDX_MODE_SPARSE_BLOCKS, rows=q.shape[0], q=q.data_ptr(),
                      q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
                      k=k.data_ptr(), k_scale=k_scale.data_ptr(), n_keys=k.shape[0],
@@ -347,10 +453,13 @@ def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = 
         out_idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
     if values and out_val is None:
         out_val = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    _rows_out(out_idx, "out_idx", rows, torch.int32, k)
+    if out_val is not None and (_rows_out(out_val, "out_val", rows, torch.float32, k) != out_idx.shape[1]):
+        raise ValueError("out_val must have the shape of out_idx")
     if workspace is None:
         workspace = torch.empty(max(idx_select_workspace(problem, k), 1), dtype=torch.uint8,
                                 device=dev)
-    wsb = workspace.numel() * workspace.element_size()
+    wsb = _workspace_bytes(workspace)
     _check(lib().idx_select(C.byref(problem.st), k, _ptr(out_idx), _ptr(out_val),
                             out_idx.shape[1], 0 if sorted else IDX_TOPK_UNSORTED,
                             _ptr(workspace), wsb, _stream(stream)))
@@ -369,18 +478,30 @@ def idx_kcache_write(k_new, slot_mapping, k_cache, k_scale, k_dtype="fp8", strea
     negative = skip). fp8: k_cache uint8 with 128 bytes per slot (e.g. [pages, page, 128])
     and k_scale float32 with one per slot; MXFP4: 64 bytes and 4 UE8M0 bytes per slot."""
     import torch
-    assert k_new.dtype == torch.bfloat16 and k_new.shape[-1] == 128 and k_new.is_contiguous()
-    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+    if k_dtype not in ("fp8", "mxfp4"):
+        raise ValueError(f"k_dtype must be 'fp8' or 'mxfp4', got {k_dtype!r}")
+    _need(k_new, "k_new", torch.bfloat16)
+    if k_new.shape[-1] != 128:
+        raise ValueError("k_new must be [n, 128]")
+    n_new = k_new.numel() // 128
+    _need(slot_mapping, "slot_mapping", torch.int64, numel=n_new)
     kd = {"fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}[k_dtype]
     row = 128 if kd == IDX_FP8_E4M3 else 64
-    n_slots = k_cache.numel() // row
-    _check(lib().idx_kcache_write(_ptr(k_new), IDX_BF16, k_new.numel() // 128, _ptr(slot_mapping), _ptr(k_cache),
+    _need(k_cache, "k_cache")
+    n_slots = _nbytes(k_cache) // row
+    _need(k_scale, "k_scale", min_numel=0)
+    if _nbytes(k_scale) < n_slots * 4:
+        raise ValueError(f"k_scale holds {_nbytes(k_scale)} bytes, {n_slots * 4} needed for {n_slots} slots")
+    _check(lib().idx_kcache_write(_ptr(k_new), IDX_BF16, n_new, _ptr(slot_mapping), _ptr(k_cache),
                                   _ptr(k_scale), kd, n_slots, _stream(stream)))
 
 
 def idx_read_probe(buf, sink, stream=None) -> None:
     """Read the whole device tensor ``buf`` once and discard it (a bandwidth probe);
     ``sink`` is a one-element int32 device tensor the probe may write."""
+    import torch
+    _need(buf, "buf")
+    _need(sink, "sink", torch.int32, min_numel=1)
     _check(lib().idx_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 

@@ -115,7 +115,7 @@ idx_status check_problem(const char* fn, const idx_problem* p, ScoreCall* c, con
     if (p->rows == 0) return IDX_OK;
     REQUIRE(p->n_keys >= 1, IDX_ERR_ARG, "%s: n_pages must be >= 1", fn);
     REQUIRE(p->block_table && p->seq_lens, IDX_ERR_ARG, "%s: block_table and seq_lens must be non-null", fn);
-    REQUIRE(p->bt_ld >= 1 && p->bt_ld * p->page_size <= kMaxCols, IDX_ERR_ARG,
+    REQUIRE(p->bt_ld >= 1 && p->bt_ld <= kMaxCols / p->page_size, IDX_ERR_ARG,
             "%s: bt_ld = %lld out of range", fn, (long long)p->bt_ld);
     c->page_size = p->page_size;
     c->block_table = p->block_table;
@@ -133,7 +133,7 @@ idx_status check_problem(const char* fn, const idx_problem* p, ScoreCall* c, con
     REQUIRE(p->n_keys >= 0, IDX_ERR_ARG, "%s: n_keys is negative", fn);
     REQUIRE(p->row_ks && p->row_ke && p->cand_blocks && p->n_cols, IDX_ERR_ARG,
             "%s: row_ks, row_ke, cand_blocks and n_cols must be non-null", fn);
-    REQUIRE(p->cand_ld >= 1 && p->cand_ld * p->block_size <= kMaxCols, IDX_ERR_ARG,
+    REQUIRE(p->cand_ld >= 1 && p->cand_ld <= kMaxCols / p->block_size, IDX_ERR_ARG,
             "%s: cand_ld = %lld out of range", fn, (long long)p->cand_ld);
     c->row_ks = p->row_ks;
     c->row_ke = p->row_ke;

@@ -127,6 +127,8 @@ CASES = [
     ("paged null table", _paged, dict(bt=None), ARG),
     ("paged null lens", _paged, dict(sl=None), ARG),
     ("paged bt_ld zero", _paged, dict(bt_ld=0), ARG),
+    ("paged bt_ld too large", _paged, dict(bt_ld=1 << 25), ARG),
+    ("paged bt_ld wrapping", _paged, dict(bt_ld=1 << 58), ARG),
     ("paged too few table rows", _paged, dict(bt_rows=3), ARG),
     ("paged misaligned row_req", _paged, dict(rr=SL + 2), ARG),
     ("sparse block 100", _sparse, dict(block=100), UNS),
@@ -135,6 +137,7 @@ CASES = [
     ("sparse null cand", _sparse, dict(cand=None), ARG),
     ("sparse null n_cols", _sparse, dict(nc=None), ARG),
     ("sparse cand_ld zero", _sparse, dict(cand_ld=0), ARG),
+    ("sparse cand_ld wrapping", _sparse, dict(cand_ld=1 << 57, ld=1 << 40), ARG),
     ("topk k zero", _topk, dict(k=0), UNS),
     ("topk k too large", _topk, dict(k=2049, old=4096), UNS),
     ("topk out_ld < k", _topk, dict(old=255), ARG),
@@ -276,3 +279,24 @@ def test_candidate_blocks_rejects_bad_arguments(L):
     assert call(ws=C.c_void_p(0x10010)) == D.IDX_ERR_ARG     # workspace not 256-byte aligned
     assert call(rows=0, lg=None, c=None, nc=None) == D.IDX_OK
     assert b"idx_candidate_blocks" in L.idx_last_error() or L.idx_last_error() == b""
+
+
+def test_python_binding_rejects_host_tensors():
+    """The kernels take device pointers: host tensors are refused before any call."""
+    import torch
+    q = torch.zeros((2, 64, 128), dtype=torch.uint8)
+    w = torch.zeros((2, 64), dtype=torch.float32)
+    k = torch.zeros((256, 128), dtype=torch.uint8)
+    sc = torch.ones(256, dtype=torch.float32)
+    ks = torch.zeros(2, dtype=torch.int32)
+    ke = torch.full((2,), 256, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        D.idx_logits(q, w, k, sc, ks, ke, k_dtype="fp8", ld=256)
+    with pytest.raises(ValueError, match="device tensor"):
+        D.dense_problem(q, w, k, sc, ks, ke, k_dtype="fp8", max_cols=256)
+    with pytest.raises(ValueError, match="device tensor"):
+        D.idx_topk(torch.zeros((2, 256), dtype=torch.float32), 8)
+    with pytest.raises(ValueError, match="device tensor"):
+        D.idx_read_probe(torch.zeros(16, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="k_dtype"):
+        D.idx_logits(q, w, k, sc, ks, ke, k_dtype="fp16", ld=256)

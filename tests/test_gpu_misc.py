@@ -1,4 +1,5 @@
-"""GPU checks of the measurement aid (the streaming-read probe)."""
+"""GPU checks of the measurement aid (the streaming-read probe) and of the binding's
+argument checks on device tensors."""
 import pytest
 import torch
 
@@ -17,3 +18,44 @@ def test_read_probe_runs_and_leaves_the_buffer_alone():
     D.idx_read_probe(buf[:4], sink)  # one 16-byte vector
     torch.cuda.synchronize()
     assert torch.equal(buf, before)
+
+
+def test_binding_rejects_wrong_sizes_before_any_launch():
+    """Sizes, dtypes and output shapes are checked in the binding: a tensor smaller than
+    its role would otherwise be read or written out of bounds by the kernels."""
+    require_gpu()
+    dev = dict(device="cuda")
+    q = torch.zeros((2, 64, 128), dtype=torch.uint8, **dev)
+    w = torch.zeros((2, 64), dtype=torch.float32, **dev)
+    k = torch.zeros((256, 128), dtype=torch.uint8, **dev)
+    sc = torch.ones(256, dtype=torch.float32, **dev)
+    ks = torch.zeros(2, dtype=torch.int32, **dev)
+    ke = torch.full((2,), 256, dtype=torch.int32, **dev)
+    with pytest.raises(ValueError, match="q has"):
+        D.idx_logits(torch.zeros((2, 32, 128), dtype=torch.uint8, **dev), w, k, sc, ks, ke, k_dtype="fp8", ld=256)
+    with pytest.raises(ValueError, match="contiguous"):
+        D.idx_logits(q[:, :, ::2], w, k, sc, ks, ke, k_dtype="fp8", ld=256)
+    with pytest.raises(ValueError, match="k_scale has"):
+        D.idx_logits(q, w, k, sc[:128], ks, ke, k_dtype="fp8", ld=256)
+    with pytest.raises(TypeError, match="row_ks"):
+        D.idx_logits(q, w, k, sc, ks.long(), ke, k_dtype="fp8", ld=256)
+    with pytest.raises(ValueError, match="out must be"):
+        D.idx_logits(q, w, k, sc, ks, ke, k_dtype="fp8", out=torch.empty((1, 256), dtype=torch.float32, **dev))
+    lg = torch.zeros((2, 256), dtype=torch.float32, **dev)
+    with pytest.raises(ValueError, match="out_idx must be"):
+        D.idx_topk(lg, 8, out_idx=torch.empty((2, 4), dtype=torch.int32, **dev))
+    with pytest.raises(ValueError, match="lens has"):
+        D.idx_topk(lg, 8, lens=torch.zeros(1, dtype=torch.int32, **dev))
+    p = D.dense_problem(q, w, k, sc, ks, ke, k_dtype="fp8", max_cols=256)
+    with pytest.raises(ValueError, match="out_idx must be"):
+        D.idx_select(p, 8, out_idx=torch.empty((3, 8), dtype=torch.int32, **dev))
+    qa = torch.zeros((2, 64, 576), dtype=torch.bfloat16, **dev)
+    kv = torch.zeros((4, 64, 576), dtype=torch.bfloat16, **dev)
+    bt = torch.zeros((2, 4), dtype=torch.int32, **dev)
+    sl = torch.full((2,), 10, dtype=torch.int32, **dev)
+    ix = torch.zeros((2, 16), dtype=torch.int32, **dev)
+    with pytest.raises(ValueError, match="out has"):
+        D.idx_sparse_attn_paged(qa, kv, bt, sl, ix, 0.1, out=torch.empty((2, 64, 256), dtype=torch.float32, **dev))
+    with pytest.raises(ValueError, match="indices must have"):
+        D.idx_sparse_attn_paged(qa, kv, bt, sl, ix[:1], 0.1)
+    torch.cuda.synchronize()
