@@ -307,10 +307,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 static int head_waves(int heads) { return std::min(heads, 64) / 16; }
 
 int attn_splits(int rows, int heads, int k) {
-  // about one workgroup per compute unit of the MI355X (256); each split at least four
-  // tiles (a fixed count keeps the workspace size independent of the device)
-  constexpr int kTargetGroups = 256;
-  const int hgroups = heads / (16 * head_waves(heads));
+  // enough workgroups to fill the MI355X's 256 compute units once: one 4-wave group per
+  // CU (registers), two 2-wave groups, three 1-wave groups (LDS); each split at least
+  // four tiles (a fixed count keeps the workspace size independent of the device)
+  const int nw = head_waves(heads);
+  const int kTargetGroups = nw == 1 ? 768 : nw == 2 ? 512 : 256;
+  const int hgroups = heads / (16 * nw);
   const int want = (kTargetGroups + rows * hgroups - 1) / (rows * hgroups);
   const int most = std::max(1, (k + 4 * kAttnT - 1) / (4 * kAttnT));
   return std::max(1, std::min(want, most));
