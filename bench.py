@@ -428,10 +428,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "scan", "select", "copy", "attn"], default="all",
+    ap.add_argument("--only", choices=["all", "scan", "select", "copy", "attn", "prefill"], default="all",
                     help="run one timed loop only (for profiler runs); copy: a plain 512 MiB "
                          "device-to-device copy, the counters' calibration; attn: the sparse "
-                         "attention workload")
+                         "attention workload; prefill: the prefill chunk's score kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) over "
@@ -480,6 +480,16 @@ def main() -> int:
         # the kernel repeated for 0.5 s first: its clock settles only under its own load
         ms, _ = time_loop(lambda: attn(ix), args.steps, args.warmup, torch.cuda.current_stream(), warm_s=0.5)
         log(f"sparse attention: {ms * 1e3:.1f} us per call")
+        return 0
+    if args.only == "prefill":
+        c4 = synth.prefill_chunk()
+        dev4 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        q4, w4, k4, sc4, ks4, ke4 = map(dev4, (c4.q, c4.w, c4.k, c4.k_scale, c4.row_ks, c4.row_ke))
+        lg4 = torch.empty((c4.rows, c4.max_cols), dtype=torch.float32, device="cuda")
+        ms, _ = time_loop(lambda: D.idx_logits(q4, w4, k4, sc4, ks4, ke4, k_dtype="fp8", out=lg4), args.steps,
+                          args.warmup, torch.cuda.current_stream(), warm_s=0.5)
+        flop = float((c4.row_ke.astype(np.int64) - c4.row_ks).sum()) * 64 * 128 * 2
+        log(f"prefill scores: {ms * 1e3:.1f} us per call ({100 * flop / (ms * 1e-3) / FP8_PEAK:.1f}% fp8 MFMA)")
         return 0
     log("generating the 128K paged decode workload")
     case = synth.paged_decode(poison=False)
