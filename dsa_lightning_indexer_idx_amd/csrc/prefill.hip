@@ -7,11 +7,12 @@
 //     range first. Two pieces per block let short causal blocks' workgroups backfill
 //     behind long ones (every workgroup of the chunk is resident at once otherwise, so
 //     the longest block alone would set the time).
-//   * Tiles are staged in LDS, three slots deep: as tile t finishes, all 256 threads
-//     issue the loads of tile t + 3 (two 16-byte chunks each), which land in registers
-//     while tile t + 1 computes and are stashed after it, chunk-major
-//     (chunk c of key k at c * 1 KiB + k * 16) so the stores and the MFMA-layout reads
-//     (16 keys of one chunk per 16 lanes) touch contiguous LDS. One barrier per tile.
+//   * Tiles are staged in LDS, three slots deep, chunk-major (chunk c of key k at
+//     c * 1 KiB + k * 16, so one 64-lane load of 16 bytes per lane fills a chunk of the
+//     tile and the MFMA-layout reads, 16 keys of one chunk per 16 lanes, are contiguous).
+//     As tile t finishes, the waves load tile t + 3 straight from memory into tile t's
+//     slot (two loads per wave, no registers); it lands while tile t + 1 computes and is
+//     waited for at the end of it. One barrier per tile.
 //   * Because tile t + 1 is already visible while tile t computes, a wave reads the B
 //     operands of the next 16 keys (crossing into tile t + 1) while the current 16
 //     compute, and no LDS read waits on a barrier.
@@ -24,8 +25,8 @@
 //     wave's two queries fill rows 0..9 of one extra 16-row MFMA tile.
 //   * Per 16 keys and wave: 9 MFMAs (2 queries x 4 head tiles + the pieces; K = 128 in
 //     one instruction), 20 FMAs per query and lane; per tile three lane swaps for the
-//     head sum, the keys' fp8 scales and one 256-byte store per query, issued after the
-//     tile's stash (see there).
+//     head sum, the keys' fp8 scales and one 256-byte store per query, issued ahead of
+//     the next tile's loads (see there).
 #include "device.h"
 #include "launch.h"
 
@@ -74,6 +75,21 @@ __device__ __forceinline__ float from_fp8(uint32_t b) { return __builtin_amdgcn_
 
 // LDS byte offset of 16-byte chunk c (0..7) of key k (0..63) in a tile slot.
 __device__ __forceinline__ int tile_off(int k, int c) { return c * (kTileTokens * 16) + (k << 4); }
+
+// Loads from global memory straight into LDS: lane l's 16 (4) bytes land at m0 + 16 l
+// (4 l). Inline assembly, so the compiler adds no wait for them before LDS reads; the
+// kernel waits for them itself (vmcnt) and orders the waves with barriers. The no-op
+// covers the one wait state the load needs after m0 is written.
+__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_load4(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
+}
 
 __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kSlots][kTileBytes];
@@ -212,22 +228,19 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
     }
   }
 
-  // cooperative tile load: thread t moves chunks t / 64 and t / 64 + 4 of key t % 64
+  // tile loads: wave w moves chunks w and w + 4 of the tile's 64 keys (lane l: key l,
+  // the chunk-major slot layout is exactly a load's lane order) and wave 0 the scales;
+  // keys past the last one repeat it (their scores are never stored)
   const int64_t last_key = a.n_keys - 1;
-  const int lkey = tid & (kTileTokens - 1), lchunk = tid >> 6;
-  auto fetch = [&](int t, v4i& x0, v4i& x1, float& sc) {
-    const int64_t base = lo + (int64_t)t * kTileTokens;
-    const uint8_t* src = a.k + min(base + lkey, last_key) * kDim + (lchunk << 4);
-    x0 = *(const v4i*)src;
-    x1 = *(const v4i*)(src + 64);
-    sc = tid < kTileTokens ? a.k_scale[min(base + tid, last_key)] : 0.f;
-  };
-  auto stash = [&](int t, const v4i& x0, const v4i& x1, float sc) {
+  auto load_tile = [&](int t) {
     const int slot = t % kSlots;
-    *(v4i*)(&tile[slot][tile_off(lkey, lchunk)]) = x0;
-    *(v4i*)(&tile[slot][tile_off(lkey, lchunk + 4)]) = x1;
-    if (tid < kTileTokens) tscale[slot][tid] = sc;
+    const int64_t key = min(lo + (int64_t)t * kTileTokens + lane, last_key);
+    const uint8_t* src = a.k + key * kDim + (wave << 4);
+    lds_load16(src, lds_addr(&tile[slot][tile_off(0, wave)]));
+    lds_load16(src + 64, lds_addr(&tile[slot][tile_off(0, wave + 4)]));
+    if (wave == 0) lds_load4(a.k_scale + key, lds_addr(&tscale[slot][0]));
   };
+  auto wait_tiles = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
   // B operand of 16-key group j of tile t: key 16j + c16, chunks 2g and 2g + 1
   auto read_b = [&](int t, int j) -> v8i {
     const int slot = t % kSlots;
@@ -237,16 +250,9 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
     return v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
   };
 
-  v4i x0, x1;
-  float xs = 0.f;
-  if (t_begin < ntiles) {
-    fetch(t_begin, x0, x1, xs);
-    stash(t_begin, x0, x1, xs);
-  }
-  if (t_begin + 1 < ntiles) {
-    fetch(t_begin + 1, x0, x1, xs);
-    stash(t_begin + 1, x0, x1, xs);
-  }
+  if (t_begin < ntiles) load_tile(t_begin);
+  if (t_begin + 1 < ntiles) load_tile(t_begin + 1);
+  wait_tiles();
   __syncthreads();
   // Per tile, the four 16-key groups are software-pipelined in source order: the 9
   // MFMAs of group j are written before the FMAs of group j - 1, so the FMAs can
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
       for (int i = 0; i < 4; ++i) p1 = fmaf(wr[kQW - 1][h][i], fabsf(r[5 + h][i]), p1);
   };
   v8i kb_next = read_b(t_begin, 0);
-  if (t_begin + 2 < ntiles) fetch(t_begin + 2, x0, x1, xs);
+  if (t_begin + 2 < ntiles) load_tile(t_begin + 2);  // its slot is still unused
   for (int t = t_begin; t < ntiles; ++t) {
     const int64_t t0 = lo + (int64_t)t * kTileTokens;
     const bool act0 = qv[0] && t0 < qe[0] && t0 + kTileTokens > qs[0];
@@ -307,19 +313,19 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
     float vv[kQW];
 #pragma unroll
     for (int u = 0; u < kQW; ++u) vv[u] = sum_lane_groups(p[u][0], p[u][1], p[u][2], p[u][3]) * sc;
-    // slot (t + 2) % 3 last held tile t - 1, whose reads all finished in iteration t - 1
-    if (t + 2 < ntiles) stash(t + 2, x0, x1, xs);
+    // Tile t + 2 (loaded since the end of iteration t - 1) is complete and visible after
+    // this wait and barrier, and every wave is done with tile t. The stores go out before
+    // the next tile's loads: the wait at the end of the next iteration then covers both
+    // without counting the (conditional) stores. The scores are written once and not read
+    // again by this kernel: non-temporal stores keep them from displacing the key tiles in
+    // the cache.
+    wait_tiles();
     __syncthreads();
-    // Memory operations count down in order, so a wait for loads also waits for every
-    // store issued before them. The loads of tile t + 3 therefore go out here, ahead of
-    // this tile's stores, and the stash that waits for them (next iteration) lets those
-    // stores stay in flight. The scores are written once and not read again by this
-    // kernel: non-temporal stores keep them from displacing the key tiles in the cache.
-    if (t + 3 < ntiles) fetch(t + 3, x0, x1, xs);
 #pragma unroll
     for (int u = 0; u < kQW; ++u)
       if ((u == 0 ? act0 : act1) && key >= qs[u] && key < qe[u])
         __builtin_nontemporal_store(vv[u], &a.logits[(int64_t)(q0 + kQW * wave + u) * a.ld + (key - qs[u])]);
+    if (t + 3 < ntiles) load_tile(t + 3);  // into tile t's slot
   }
 
   // columns past each query's length
