@@ -39,6 +39,7 @@ constexpr int kAttnDV = 512;         // value length (the entry's first 512 elem
 constexpr int kAttnT = 32;           // positions per tile
 constexpr int kKPitch = kAttnD + 48;  // token-major tile row (bf16): 1248 B (fewest bank conflicts of the pads tried)
 constexpr int kPPitch = kAttnT + 8;  // per-wave P rows (bf16)
+constexpr int kTail = kAttnD - kAttnDV;  // dims 512..575 of a token: 128 B, 8 chunks of 16 B
 constexpr int kChunks = kAttnT * kAttnD / 8;  // 16-byte pieces of a tile (2304)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -277,6 +278,234 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
   }
 }
 
+// ---- 16 heads: one wave per (row, split), gathering with direct-to-LDS loads
+//
+// A single wave staging a whole tile in registers would need 144 of them; instead the
+// entries go from memory straight into LDS (no registers), dims 0..511 token-major as
+// above and dims 512..575 in a side array.
+
+// 16 bytes per lane from global memory into LDS at m0 + 16 lane (lanes in order). Issued
+// as inline assembly so the compiler adds no wait for it before later LDS reads: the
+// kernel waits for these loads itself (vmcnt) and orders waves with barriers. The no-op
+// covers the one wait state the load needs after m0 is written.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// s_waitcnt operand: vmcnt(n) (6 bits, split over [3:0] and [15:14]), expcnt and
+// lgkmcnt at their maxima (no wait)
+constexpr int vmcnt_enc(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+__global__ __launch_bounds__(kWave, 1) void attn_partial_1w_kernel(AttnArgs a) {
+  constexpr int NW = 1, NT = kWave;
+  __shared__ __align__(16) uint16_t kt[1][kAttnT * kKPitch];  // dims 0..511, token-major
+  __shared__ __align__(16) uint16_t kl[1][kAttnT * kTail];     // dims 512..575, swizzled
+  __shared__ __align__(16) uint16_t pb[NW][16 * kPPitch];
+  extern __shared__ int64_t ent[];  // the split's entry rows (-1: not a valid entry)
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane >> 4, c16 = lane & 15;
+  // (row, split) unit p and head group hg: ids 8 apart share an XCD
+  const int b = blockIdx.x;
+  const int p = (b / (8 * a.hgroups)) * 8 + (b % 8);
+  const int hg = (b / 8) % a.hgroups;
+  if (p >= a.rows * a.nsplit) return;
+  const int r = p / a.nsplit;
+  const int split = p % a.nsplit;
+  const int i0 = split * a.split_len;
+  const int i1 = min(a.k, i0 + a.split_len);
+  const int ntok = max(i1 - i0, 0);
+  const int ntiles = (ntok + kAttnT - 1) / kAttnT;
+
+  // entry rows of the split's positions
+  {
+    const int64_t req = a.row_req ? (int64_t)a.row_req[r] : (int64_t)r;
+    const bool req_ok = req >= 0 && req < a.bt_rows;
+    const int64_t len = a.seq_lens[r];
+    for (int i = tid; i < ntiles * kAttnT; i += NT) {
+      int64_t e = -1;
+      if (i < ntok && req_ok) {
+        const int64_t pos = a.idx[(int64_t)r * a.idx_ld + i0 + i];
+        if (pos >= 0 && pos < len && pos / a.page_size < a.bt_ld) {
+          const int64_t page = a.bt[req * a.bt_ld + pos / a.page_size];
+          if (page >= 0 && page < a.n_pages)
+            e = page * a.page_size + pos % a.page_size;
+          else
+            flag_error(a.err, kErrPage);
+        }
+      }
+      ent[i] = e;
+    }
+    if (tid == 0 && !req_ok && ntok > 0) flag_error(a.err, kErrRange);
+  }
+  __syncthreads();
+
+  // the wave's 16 heads: A operands of the 18 K-steps (row c16 = head, dims 32s + 8g ..)
+  const int head0 = hg * 16 * NW + 16 * wave;
+  const uint16_t* qrow = a.q + ((int64_t)r * a.heads + head0 + c16) * kAttnD + 8 * g;
+  v8bf qa[kAttnD / 32];
+#pragma unroll
+  for (int s = 0; s < kAttnD / 32; ++s) qa[s] = *(const v8bf*)(qrow + 32 * s);
+
+  // gather: tile t's entries go from memory straight into tile buffer bs (16-byte loads
+  // that write LDS at the wave-uniform base + 16 l for lane l). Wave w moves dims 0..511
+  // of tokens w, w + NW, ... (one 1 KiB load each) and dims 512..575 of 8 tokens per load
+  // (lane l: token 8q + l / 8, chunk (l % 8) ^ (token % 8), so the 16 rows a score read
+  // touches spread over the banks). Positions without a valid entry read entry 0, which
+  // always exists: their weights are exactly 0, and its values are finite.
+  // (the entry rows are read ahead of the loads, up to 8 tokens at a time: the loads
+  // are ordered with LDS accesses, so a read between two of them costs a round trip)
+  auto dma = [&](int t, int bs) {
+    constexpr int kMain = kAttnT / NW, kChunk = kMain < 8 ? kMain : 8;
+    const uint32_t mbase = lds_addr(kt[bs]), tbase = lds_addr(kl[bs]);
+    int64_t tv[4 / NW];
+#pragma unroll
+    for (int v = 0; v < 4 / NW; ++v) tv[v] = ent[t * kAttnT + 8 * (wave + v * NW) + (lane >> 3)];
+#pragma unroll
+    for (int c = 0; c < kMain; c += kChunk) {
+      int64_t ev[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) ev[u] = ent[t * kAttnT + wave + (c + u) * NW];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int j = wave + (c + u) * NW;
+        dma16(a.kv + (ev[u] >= 0 ? ev[u] : 0) * kAttnD + 8 * lane, mbase + 2 * j * kKPitch);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4 / NW; ++v) {
+      const int q = wave + v * NW;
+      const int j = 8 * q + (lane >> 3);
+      dma16(a.kv + (tv[v] >= 0 ? tv[v] : 0) * kAttnD + kAttnDV + 8 * ((lane & 7) ^ (j & 7)), tbase + 1024 * q);
+    }
+  };
+  // one wave's gather loads per tile
+  constexpr int kLoads = kAttnT / NW + 4 / NW;
+  // value operand of dims 16n .. 16n + 15: lane (g, c16) gets tokens 8g .. 8g + 7 of dim
+  // 16n + c16, from two transposing reads (tokens 8g + c16 / 4 and 8g + 4 + c16 / 4, dims
+  // 16n + 4 (c16 % 4) .. + 3)
+  typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+  const int tr_off = (8 * g + (c16 >> 2)) * kKPitch + 4 * (c16 & 3);
+  auto read_v = [&](const uint16_t* kt, int n) -> v8bf {
+    const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(&kt[tr_off + 16 * n]));
+    const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(&kt[tr_off + 4 * kKPitch + 16 * n]));
+    return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+
+  float m[4], l[4];
+  v4f o[kAttnDV / 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -__builtin_inff();
+    l[i] = 0.f;
+  }
+#pragma unroll
+  for (int n = 0; n < kAttnDV / 16; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto tile = [&](const uint16_t* km, const uint16_t* kd, bool v0, bool v1) {
+
+    // scores of the tile's two 16-token columns: all 36 operand reads are issued before
+    // the MFMAs, which then wait for them in order instead of one LDS round trip each
+    v4f sc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    v8bf kb[2][kAttnD / 32];
+#pragma unroll
+    for (int s = 0; s < kAttnD / 32; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int tok = 16 * j + c16;
+        kb[j][s] = s < kAttnDV / 32 ? *(const v8bf*)(&km[tok * kKPitch + 32 * s + 8 * g])
+                                    : *(const v8bf*)(&kd[tok * kTail + 8 * ((4 * (s - kAttnDV / 32) + g) ^ (c16 & 7))]);
+      }
+#pragma unroll
+    for (int s = 0; s < kAttnD / 32; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sc[j] = mfma_bf16(qa[s], kb[j][s], sc[j]);
+    // lane (g, c16): heads 4g + i, tokens c16 and 16 + c16 of the tile
+    float p[2][4], alpha[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s0 = v0 ? sc[0][i] * a.scale2 : -__builtin_inff();
+      const float s1 = v1 ? sc[1][i] * a.scale2 : -__builtin_inff();
+      const float mt = dpp_row_max(fmaxf(s0, s1));
+      const float mn = fmaxf(m[i], mt);
+      // all -inf so far: keep weights 0 (exp2(-inf) = 0, and no -inf - -inf)
+      const float base = mn == -__builtin_inff() ? 0.f : mn;
+      alpha[i] = __builtin_amdgcn_exp2f(m[i] - base);
+      p[0][i] = __builtin_amdgcn_exp2f(s0 - base);
+      p[1][i] = __builtin_amdgcn_exp2f(s1 - base);
+      l[i] = l[i] * alpha[i] + dpp_row_sum(p[0][i] + p[1][i]);
+      m[i] = mn;
+    }
+#pragma unroll
+    for (int n = 0; n < kAttnDV / 16; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[n][i] *= alpha[i];
+    // P into the A-operand layout: row = head, 8 consecutive tokens per lane group
+    uint16_t* pw = pb[wave];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[(4 * g + i) * kPPitch + 16 * j + c16] = f32_to_bf16(p[j][i]);
+    __builtin_amdgcn_wave_barrier();  // one wave's LDS operations complete in order
+    const v8bf pa = *(const v8bf*)(&pw[c16 * kPPitch + 8 * g]);
+    // value operands in two batches of 16 reads, each ahead of its MFMAs
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8bf vb[kAttnDV / 32];
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 32; ++n) vb[n] = read_v(km, 16 * h + n);
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 32; ++n) o[16 * h + n] = mfma_bf16(pa, vb[n], o[16 * h + n]);
+    }
+    __builtin_amdgcn_wave_barrier();  // the P reads finish before the next tile's writes
+  };
+  // One tile buffer (three workgroups share a compute unit, so their loads and math
+  // overlap one another's). The fence before each load completes this wave's LDS reads
+  // of the previous tile; the one after the wait orders the tile's reads behind it.
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    dma(t, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    __syncthreads();
+    const bool v0 = ent[t * kAttnT + c16] >= 0;
+    const bool v1 = ent[t * kAttnT + 16 + c16] >= 0;
+    tile(kt[0], kl[0], v0, v1);
+  }
+
+  // lane (g, c16) holds O[head 4g + i][dim 16n + c16]
+  if (a.nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = head0 + 4 * g + i;
+      const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
+      float* orow = a.out + ((int64_t)r * a.heads + h) * kAttnDV;
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 16; ++n) orow[16 * n + c16] = o[n][i] * inv;
+      if (a.lse && c16 == 0)
+        a.lse[(int64_t)r * a.heads + h] = l[i] > 0.f ? (m[i] + log2f(l[i])) * 0.69314718055994531f : -__builtin_inff();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = head0 + 4 * g + i;
+      const int64_t slot = ((int64_t)r * a.nsplit + split) * a.heads + h;
+      float* orow = a.part_o + slot * kAttnDV;
+#pragma unroll
+      for (int n = 0; n < kAttnDV / 16; ++n) orow[16 * n + c16] = o[n][i];
+      if (c16 == 0) {
+        a.part_ml[2 * slot] = m[i];
+        a.part_ml[2 * slot + 1] = l[i];
+      }
+    }
+  }
+}
+
 // One wave per (row, head): merges the splits' (O, m, l).
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t wv = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kWave;
@@ -332,6 +561,11 @@ size_t attn_workspace_bytes(int rows, int heads, int k) {
 }
 
 // The entry list is dynamic LDS (up to IDX_MAX_K rows) next to ~88 KB of static LDS.
+static hipError_t launch_partial_1w(dim3 grid, size_t ent_bytes, hipStream_t stream, const AttnArgs& a) {
+  hipLaunchKernelGGL(attn_partial_1w_kernel, grid, dim3(kWave), ent_bytes, stream, a);
+  return hipGetLastError();
+}
+
 template <int NW>
 static hipError_t launch_partial(dim3 grid, size_t ent_bytes, hipStream_t stream, const AttnArgs& a) {
   static std::once_flag once;
@@ -380,7 +614,7 @@ hipError_t launch_sparse_attn(const AttnCall& c, void* workspace, hipStream_t st
   const size_t ent_bytes = (size_t)a.split_len * sizeof(int64_t);
   hipError_t e = hipSuccess;
   switch (nw) {
-    case 1: e = launch_partial<1>(grid, ent_bytes, stream, a); break;
+    case 1: e = launch_partial_1w(grid, ent_bytes, stream, a); break;
     case 2: e = launch_partial<2>(grid, ent_bytes, stream, a); break;
     default: e = launch_partial<4>(grid, ent_bytes, stream, a); break;
   }
