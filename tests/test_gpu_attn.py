@@ -102,14 +102,15 @@ def test_tables_and_empty_rows():
     check(c, 0.01, "identity table, flat scores")
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("heads", [128, 16])
+def test_graph_replay_matches_eager(heads):
     require_gpu()
-    c = make_case(94, 8, 128, [6000] * 8, 1024, q_std=1.5, pad=0.05)
+    c = make_case(94, 8, heads, [6000] * 8, 1024, q_std=1.5, pad=0.05)
     q, kv, bt, sl, idx = dev(c["q"]), dev(c["kv"]), dev(c["bt"]), dev(c["sl"]), dev(c["idx"])
-    out = torch.empty((8, 128, 512), dtype=torch.float32, device="cuda")
-    lse = torch.empty((8, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, D.idx_sparse_attn_workspace(8, 128, 1024)), dtype=torch.uint8, device="cuda")
-    say("sparse attn: eager")
+    out = torch.empty((8, heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((8, heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, D.idx_sparse_attn_workspace(8, heads, 1024)), dtype=torch.uint8, device="cuda")
+    say(f"sparse attn: eager, {heads} heads")
     D.idx_sparse_attn_paged(q, kv, bt, sl, idx, 0.07, out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     want_o, want_l = host(out).copy(), host(lse).copy()
@@ -134,9 +135,11 @@ def test_graph_replay_matches_eager():
 
 def test_full_size_long_decode():
     """The long paged decode's shape: 64 rows of U{65536..131072} positions in 64-token
-    pages (the indexer workload's table), 128 heads, 2048 selected positions per row drawn
-    at random; a 576-element bf16 cache of ~98K pages made on the GPU by torch's seeded
-    generator. Rows 0 and 63 are checked against the oracle (their pages copied back)."""
+    pages (the indexer workload's table), 2048 selected positions per row drawn at random;
+    a 576-element bf16 cache of ~98K pages made on the GPU by torch's seeded generator.
+    128 heads, then the first 16 of them (one GPU's share of 128 heads split 8 ways, its
+    own single-wave kernel), each in the launch shape the bench times. Rows 0 and 63 are
+    checked against the oracle (their pages copied back)."""
     import synth
     require_gpu()
     c = synth.paged_decode(poison=False)
@@ -144,22 +147,27 @@ def test_full_size_long_decode():
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
     kv = torch.randn((P, 64, 576), generator=gen, device="cuda", dtype=torch.bfloat16)
-    q = (torch.randn((64, 128, 576), generator=gen, device="cuda", dtype=torch.float32) / 16).to(torch.bfloat16)
+    q128 = (torch.randn((64, 128, 576), generator=gen, device="cuda", dtype=torch.float32) / 16).to(torch.bfloat16)
     rng = np.random.default_rng(12)
     idx = np.stack([rng.choice(int(n), size=2048, replace=False) for n in c.seq_lens]).astype(np.int32)
-    say("sparse attn: full size")
-    out, lse = D.idx_sparse_attn_paged(q.contiguous(), kv, dev(c.block_table), dev(c.seq_lens), dev(idx),
-                                       1 / np.sqrt(192))
-    torch.cuda.synchronize()
-    out, lse = host(out), host(lse)
-    qb = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    kvr = {}
     for r in (0, 63):
         npg = int((c.seq_lens[r] + 63) // 64)
         pages = torch.from_numpy(c.block_table[r, :npg].astype(np.int64)).cuda()
-        kvr = kv.index_select(0, pages).view(torch.int16).cpu().numpy().view(np.uint16)
-        bt = np.arange(npg, dtype=np.int32)[None]
-        r_out, r_lse = O.sparse_attn_paged(qb[r:r + 1], kvr, bt, c.seq_lens[r:r + 1], idx[r:r + 1], 1 / np.sqrt(192))
-        vmax = np.abs(O._bf16_table()[kvr[..., :512]]).max()
-        err = np.abs(out[r] - r_out[0]).max()
-        assert err <= 2.0 ** -8 * vmax + 1e-5, f"full size row {r}: max error {err:.3g}"
-        assert np.allclose(lse[r], r_lse[0], rtol=0, atol=1e-4)
+        kvr[r] = kv.index_select(0, pages).view(torch.int16).cpu().numpy().view(np.uint16)
+    for heads in (128, 16):
+        q = q128[:, :heads].contiguous()
+        say(f"sparse attn: full size, {heads} heads")
+        out, lse = D.idx_sparse_attn_paged(q, kv, dev(c.block_table), dev(c.seq_lens), dev(idx), 1 / np.sqrt(192))
+        torch.cuda.synchronize()
+        out, lse = host(out), host(lse)
+        qb = q.view(torch.int16).cpu().numpy().view(np.uint16)
+        for r in (0, 63):
+            npg = kvr[r].shape[0]
+            bt = np.arange(npg, dtype=np.int32)[None]
+            r_out, r_lse = O.sparse_attn_paged(qb[r:r + 1], kvr[r], bt, c.seq_lens[r:r + 1], idx[r:r + 1],
+                                               1 / np.sqrt(192))
+            vmax = np.abs(O._bf16_table()[kvr[r][..., :512]]).max()
+            err = np.abs(out[r] - r_out[0]).max()
+            assert err <= 2.0 ** -8 * vmax + 1e-5, f"full size, {heads} heads, row {r}: max error {err:.3g}"
+            assert np.allclose(lse[r], r_lse[0], rtol=0, atol=1e-4), f"full size, {heads} heads, row {r}: lse"
