@@ -284,22 +284,6 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
 // entries go from memory straight into LDS (no registers), dims 0..511 token-major as
 // above and dims 512..575 in a side array.
 
-// 16 bytes per lane from global memory into LDS at m0 + 16 lane (lanes in order). Issued
-// as inline assembly so the compiler adds no wait for it before later LDS reads: the
-// kernel waits for these loads itself (vmcnt) and orders waves with barriers. The no-op
-// covers the one wait state the load needs after m0 is written.
-__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
-}
-
-// s_waitcnt operand: vmcnt(n) (6 bits, split over [3:0] and [15:14]), expcnt and
-// lgkmcnt at their maxima (no wait)
-constexpr int vmcnt_enc(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 __global__ __launch_bounds__(kWave, 1) void attn_partial_1w_kernel(AttnArgs a) {
   constexpr int NW = 1, NT = kWave;
   __shared__ __align__(16) uint16_t kt[1][kAttnT * kKPitch];  // dims 0..511, token-major
@@ -375,14 +359,14 @@ __global__ __launch_bounds__(kWave, 1) void attn_partial_1w_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const int j = wave + (c + u) * NW;
-        dma16(a.kv + (ev[u] >= 0 ? ev[u] : 0) * kAttnD + 8 * lane, mbase + 2 * j * kKPitch);
+        lds_load16(a.kv + (ev[u] >= 0 ? ev[u] : 0) * kAttnD + 8 * lane, mbase + 2 * j * kKPitch);
       }
     }
 #pragma unroll
     for (int v = 0; v < 4 / NW; ++v) {
       const int q = wave + v * NW;
       const int j = 8 * q + (lane >> 3);
-      dma16(a.kv + (tv[v] >= 0 ? tv[v] : 0) * kAttnD + kAttnDV + 8 * ((lane & 7) ^ (j & 7)), tbase + 1024 * q);
+      lds_load16(a.kv + (tv[v] >= 0 ? tv[v] : 0) * kAttnD + kAttnDV + 8 * ((lane & 7) ^ (j & 7)), tbase + 1024 * q);
     }
   };
   // one wave's gather loads per tile

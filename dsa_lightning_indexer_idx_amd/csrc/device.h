@@ -29,6 +29,29 @@ __device__ __forceinline__ void flag_error(unsigned* err, unsigned bits) {
   if (err) atomicOr(err, bits);
 }
 
+// ---------------------------------------------------------------- global -> LDS loads
+//
+// One 64-lane load from global memory straight into LDS: lane l's 16 (4) bytes land at
+// m0 + 16 l (4 l), in lane order. Issued as inline assembly so the compiler adds no wait
+// for them before later LDS reads (without alias information it would make every LDS
+// read wait for all such loads in flight): the caller waits for them itself (vmcnt) and
+// orders the waves with barriers, whose fence also completes earlier LDS reads of the
+// target. The no-op covers the one wait state the load needs after m0 is written.
+__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_load4(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+// LDS byte address of a pointer into a __shared__ array
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
+}
+// s_waitcnt operand: vmcnt(n) (6 bits, split over [3:0] and [15:14]), expcnt and lgkmcnt
+// at their maxima (no wait)
+constexpr int vmcnt_enc(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 // ---------------------------------------------------------------- MFMA wrappers
 //
 // v_mfma_scale_f32_16x16x128_f8f6f4: D[16 x 16] += A[16 x 128] * B[128 x 16].

@@ -76,21 +76,6 @@ __device__ __forceinline__ float from_fp8(uint32_t b) { return __builtin_amdgcn_
 // LDS byte offset of 16-byte chunk c (0..7) of key k (0..63) in a tile slot.
 __device__ __forceinline__ int tile_off(int k, int c) { return c * (kTileTokens * 16) + (k << 4); }
 
-// Loads from global memory straight into LDS: lane l's 16 (4) bytes land at m0 + 16 l
-// (4 l). Inline assembly, so the compiler adds no wait for them before LDS reads; the
-// kernel waits for them itself (vmcnt) and orders the waves with barriers. The no-op
-// covers the one wait state the load needs after m0 is written.
-__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void lds_load4(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
-}
-template <class T>
-__device__ __forceinline__ uint32_t lds_addr(const T* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
-}
-
 __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kSlots][kTileBytes];
   __shared__ float tscale[kSlots][kTileTokens];
@@ -240,7 +225,7 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
     lds_load16(src + 64, lds_addr(&tile[slot][tile_off(0, wave + 4)]));
     if (wave == 0) lds_load4(a.k_scale + key, lds_addr(&tscale[slot][0]));
   };
-  auto wait_tiles = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  auto wait_tiles = [] { __builtin_amdgcn_s_waitcnt(vmcnt_enc(0)); };
   // B operand of 16-key group j of tile t: key 16j + c16, chunks 2g and 2g + 1
   auto read_b = [&](int t, int j) -> v8i {
     const int slot = t % kSlots;
