@@ -46,6 +46,9 @@ SMALL = {
     "dense_many_rows_disjoint": lambda: synth.batched_decode(seed=116, rows=300, n=700, ragged=True,
                                                              gap=9),
     "prefill_q1030_prior64": lambda: synth.prefill_chunk(seed=117, q_tokens=1030, prior=64),
+    # no prior context: the first query blocks see fewer keys than one 64-key tile, and the
+    # 260-key array ends in a 4-key tile (tile loads clamped to the last key)
+    "prefill_q260_prior0": lambda: synth.prefill_chunk(seed=118, q_tokens=260, prior=0),
 }
 
 
