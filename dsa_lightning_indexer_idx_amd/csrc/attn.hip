@@ -369,8 +369,6 @@ __global__ __launch_bounds__(kWave, 1) void attn_partial_1w_kernel(AttnArgs a) {
       lds_load16(a.kv + (tv[v] >= 0 ? tv[v] : 0) * kAttnD + kAttnDV + 8 * ((lane & 7) ^ (j & 7)), tbase + 1024 * q);
     }
   };
-  // one wave's gather loads per tile
-  constexpr int kLoads = kAttnT / NW + 4 / NW;
   // value operand of dims 16n .. 16n + 15: lane (g, c16) gets tokens 8g .. 8g + 7 of dim
   // 16n + c16, from two transposing reads (tokens 8g + c16 / 4 and 8g + 4 + c16 / 4, dims
   // 16n + 4 (c16 % 4) .. + 3)
