@@ -55,6 +55,23 @@ def test_select_long_rows_under_capture():
     _replays_match(g, (oi, ov), want, lambda rep: ws.copy_(noise.fill_(rep * 37 % 256)))
 
 
+def test_prefill_select_under_capture():
+    """A prefill chunk of 300 queries (the tiled prefill kernel, whose key tiles go from
+    memory straight into LDS, then the short-row top-k) replayed from a graph."""
+    require_gpu()
+    case = synth.prefill_chunk(seed=153, q_tokens=300, prior=900, topk=512)
+    up = Uploaded(case)
+    p = up.problem()
+    ws = torch.empty(D.idx_select_workspace(p, 512), dtype=torch.uint8, device="cuda")
+    oi = torch.empty((case.rows, 512), dtype=torch.int32, device="cuda")
+    ov = torch.empty((case.rows, 512), dtype=torch.float32, device="cuda")
+    D.idx_select(p, 512, out_idx=oi, out_val=ov, workspace=ws)
+    torch.cuda.synchronize()
+    want = (oi.clone(), ov.clone())
+    g = _capture(lambda: D.idx_select(p, 512, out_idx=oi, out_val=ov, workspace=ws))
+    _replays_match(g, (oi, ov), want, lambda rep: ws.fill_(rep * 53 % 256))
+
+
 def test_topk_and_short_rows_under_capture():
     require_gpu()
     rng = np.random.default_rng(152)
