@@ -428,10 +428,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "scan", "select", "copy", "attn", "prefill"], default="all",
+    ap.add_argument("--only", choices=["all", "scan", "select", "copy", "attn", "attn16", "prefill"], default="all",
                     help="run one timed loop only (for profiler runs); copy: a plain 512 MiB "
                          "device-to-device copy, the counters' calibration; attn: the sparse "
-                         "attention workload; prefill: the prefill chunk's score kernel")
+                         "attention workload (attn16: with 16 of its heads); prefill: the prefill "
+                         "chunk's score kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) over "
@@ -474,6 +475,17 @@ def main() -> int:
         src.fill_(1)
         ms, _ = time_loop(lambda: dst.copy_(src), args.steps, args.warmup, torch.cuda.current_stream())
         log(f"copy of {COPY_BYTES >> 20} MiB: {ms:.3f} ms ({2 * COPY_BYTES / (ms * 1e-3) / 1e9:.0f} GB/s read + write)")
+        return 0
+    if args.only == "attn16":
+        c3, kv3, qa3, ix, bt3, sl3, _ = attn_workload(D, np, torch, synth)
+        q16 = qa3[:, :16].contiguous()
+        o16 = torch.empty((c3.rows, 16, 512), dtype=torch.float32, device="cuda")
+        l16 = torch.empty((c3.rows, 16), dtype=torch.float32, device="cuda")
+        w16 = torch.empty(max(1, D.idx_sparse_attn_workspace(c3.rows, 16, 2048)), dtype=torch.uint8, device="cuda")
+        ms, _ = time_loop(lambda: D.idx_sparse_attn_paged(q16, kv3, bt3, sl3, ix, 1 / np.sqrt(192), out=o16, lse=l16,
+                                                          workspace=w16),
+                          args.steps, args.warmup, torch.cuda.current_stream(), warm_s=0.5)
+        log(f"sparse attention, 16 heads: {ms * 1e3:.1f} us per call")
         return 0
     if args.only == "attn":
         _, _, _, ix, _, _, attn = attn_workload(D, np, torch, synth)

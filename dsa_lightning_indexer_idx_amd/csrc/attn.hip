@@ -489,24 +489,56 @@ __global__ __launch_bounds__(kWave, 1) void attn_partial_1w_kernel(AttnArgs a) {
 }
 
 // One wave per (row, head): merges the splits' (O, m, l).
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Lane s reads split s's (m, l) (at most 64 splits; the split count never exceeds 16),
+// then the splits' output rows are read up to four at a time, all their loads issued
+// before any is used.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t wv = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kWave;
   if (wv >= (int64_t)a.rows * a.heads) return;
   const int lane = lane_id();
   const int64_t r = wv / a.heads, h = wv % a.heads;
-  float mx = -__builtin_inff();
-  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, a.part_ml[2 * ((r * a.nsplit + s) * a.heads + h)]);
+  const int ns = a.nsplit;
+  float ms = -__builtin_inff(), ls = 0.f;
+  if (lane < ns) {
+    const int64_t slot = (r * ns + lane) * a.heads + h;
+    ms = a.part_ml[2 * slot];
+    ls = a.part_ml[2 * slot + 1];
+  }
+  const float mx = wave_max_f(ms);
   const float base = mx == -__builtin_inff() ? 0.f : mx;
-  float L = 0.f;
+  const float ws = lane < ns ? exp2f(ms - base) : 0.f;  // 0 for a split without entries
+  const float L = wave_sum_f(ws * ls);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t slot = (r * a.nsplit + s) * a.heads + h;
-    const float w = exp2f(a.part_ml[2 * slot] - base);
-    L += w * a.part_ml[2 * slot + 1];
-    const float4* src = (const float4*)(a.part_o + slot * kAttnDV) + 2 * lane;
-    const float4 x0 = src[0], x1 = src[1];
-    acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
-    acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+  for (int s0 = 0; s0 < ns; s0 += 4) {
+    float4 x[4][2];
+    float w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // past the last split: nothing read, weight 0 (the condition is wave-uniform)
+      w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), s0 + q));
+      x[q][0] = x[q][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s0 + q < ns) {
+        const float4* src = (const float4*)(a.part_o + ((r * ns + s0 + q) * a.heads + h) * kAttnDV) + 2 * lane;
+        x[q][0] = src[0];
+        x[q][1] = src[1];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[0] += w[q] * x[q][0].x; acc[1] += w[q] * x[q][0].y; acc[2] += w[q] * x[q][0].z; acc[3] += w[q] * x[q][0].w;
+      acc[4] += w[q] * x[q][1].x; acc[5] += w[q] * x[q][1].y; acc[6] += w[q] * x[q][1].z; acc[7] += w[q] * x[q][1].w;
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float4* dst = (float4*)(a.out + (r * a.heads + h) * kAttnDV) + 2 * lane;
@@ -581,6 +613,7 @@ hipError_t launch_sparse_attn(const AttnCall& c, void* workspace, hipStream_t st
   a.scale2 = c.scale * kLog2e;
   a.nsplit = attn_splits(c.rows, c.heads, c.k);
   a.split_len = split_len(c.k, a.nsplit);
+  if (a.nsplit > kWave) return hipErrorInvalidValue;  // the combine gives each split a lane
   const int nw = head_waves(c.heads);
   a.hgroups = c.heads / (16 * nw);
   a.out = c.out;
