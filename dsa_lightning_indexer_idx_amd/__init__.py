@@ -20,6 +20,7 @@ IDX_OK, IDX_ERR_ARG, IDX_ERR_UNSUPPORTED, IDX_ERR_WORKSPACE, IDX_ERR_HIP = 0, 1,
 IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
 IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS = 1, 2, 3
 IDX_TOPK_UNSORTED = 1
+IDX_SELECT_NO_CUTOFF = 2
 IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK, IDX_DEVERR_SLOT = 1, 2, 4, 8
 IDX_HEADS, IDX_DIM, IDX_MAX_K = 64, 128, 2048
 
@@ -444,8 +445,9 @@ def idx_select_workspace(problem: Problem, k: int) -> int:
 
 
 def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = True,
-               out_idx=None, out_val=None, workspace=None, stream=None):
-    """Scores + exact top-k in one call (C: idx_select). Returns (idx, val or None)."""
+               out_idx=None, out_val=None, workspace=None, cutoff: bool = True, stream=None):
+    """Scores + exact top-k in one call (C: idx_select). Returns (idx, val or None).
+    cutoff=False sets IDX_SELECT_NO_CUTOFF (every scored entry goes to the exact finish)."""
     import torch
     dev = problem._keep[0].device
     rows = problem.rows
@@ -461,7 +463,8 @@ def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = 
                                 device=dev)
     wsb = _workspace_bytes(workspace)
     _check(lib().idx_select(C.byref(problem.st), k, _ptr(out_idx), _ptr(out_val),
-                            out_idx.shape[1], 0 if sorted else IDX_TOPK_UNSORTED,
+                            out_idx.shape[1],
+                            (0 if sorted else IDX_TOPK_UNSORTED) | (0 if cutoff else IDX_SELECT_NO_CUTOFF),
                             _ptr(workspace), wsb, _stream(stream)))
     return out_idx, out_val
 

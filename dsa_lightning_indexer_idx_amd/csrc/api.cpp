@@ -8,8 +8,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <set>
 #include <string>
 
 using namespace dsaidx;
@@ -31,6 +36,28 @@ idx_status fail(idx_status s, const char* fmt, ...) {
 idx_status ok() {
   g_last_error.clear();
   return IDX_OK;
+}
+
+// IDX_LOG=1 in the environment: one stderr line per distinct dispatch decision.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("IDX_LOG");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void log_once(const char* fmt, ...) {
+  if (!log_enabled()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  static std::mutex mu;
+  static std::set<std::string> seen;
+  std::lock_guard<std::mutex> lock(mu);
+  if (seen.insert(buf).second) fprintf(stderr, "[dsaidx] %s\n", buf);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -157,6 +184,69 @@ int64_t select_width(const idx_problem* p) {
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// idx_select workspace. Two layouts, the larger one sized:
+//  - one-pass selection (rows that read their own keys, kSelMinRows..kBalancedMaxRows rows):
+//    the histogram slots, arrival counters, row step offsets, per-segment counts and
+//    survivor regions of SelectState, then the spill score rows [rows, ldw];
+//  - scores then top-k (prefill chunks, more rows): the score matrix [rows, ldw], the
+//    rows' scored lengths, then the top-k workspace.
+// Every region starts on a 256-byte boundary; ldw = width rounded up to 64 columns.
+struct SelectLayout {
+  size_t slots, arrive, acc, seg_info, surv, spill, total;
+};
+
+SelectLayout select_layout(const idx_problem* p) {
+  const int64_t R = p->rows, ldw = round_up(select_width(p), 64), steps = R * (ldw / 64);
+  SelectLayout L{};
+  size_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t at = o;
+    o += (size_t)round_up(bytes, 256);
+    return at;
+  };
+  L.slots = take((int64_t)kSelMaxBlocks * 2 * kSelSlotWords * 4);
+  L.arrive = take(R * 8);
+  L.acc = take((R + 1) * 8);
+  L.seg_info = take(steps * 4);
+  L.surv = take(steps * 64 * 8);
+  L.spill = take(R * ldw * 4);
+  L.total = o;
+  return L;
+}
+
+size_t select_scores_bytes(const idx_problem* p) {
+  return (size_t)round_up((int64_t)p->rows * round_up(select_width(p), 64) * (int64_t)sizeof(float), 256);
+}
+
+size_t select_lens_bytes(const idx_problem* p) { return (size_t)round_up((int64_t)p->rows * 4, 256); }
+
+// Whether the problem can take the one-pass selection (the balanced scan of rows that read
+// their own keys); the launch must also fit the finish's segment table (checked per call).
+// Fewer rows than this take scores then top-k: each row would span more than
+// kSelMaxSpan of the CUs' workgroups, too many to exchange histograms between.
+constexpr int kSelMinRows = 8;
+
+bool select_one_pass_shape(const idx_problem* p) {
+  if (p->rows < kSelMinRows || p->rows > kBalancedMaxRows) return false;
+  if (p->mode == IDX_MODE_DENSE && p->q_dtype == IDX_FP8_E4M3 && p->k_dtype == IDX_FP8_E4M3 &&
+      p->rows >= kPrefillMinRows)
+    return false;  // a prefill chunk: the tiled prefill kernel, then the top-k
+  return true;
+}
+
+// Group size of the one-pass cutoff: 16 columns, halved while a row of the call's width
+// would have fewer than 4k groups (the cutoff is the k-th largest group maximum).
+int select_group_shift(int64_t width, int k) {
+  int gs = 4;
+  while (gs > 0 && (width >> gs) < 4 * (int64_t)k) --gs;
+  return gs;
+}
+
+// Limit of a row wait (the device's 100 MHz real-time clock): far beyond the few
+// microseconds the waves of a row finish apart.
+constexpr int64_t kSelectWaitTicks = 200000;
+
 
 }  // namespace
 
@@ -286,18 +376,14 @@ idx_status idx_topk(const float* logits, int64_t ld, const int32_t* lens, int64_
   return launched(fn, launch_topk(c, workspace, (hipStream_t)stream));
 }
 
-// idx_select workspace: the score matrix [rows, round_up(width, 64)] fp32, then the
-// top-k workspace at the next 256-byte boundary.
-size_t select_scores_bytes(const idx_problem* p) {
-  return (size_t)round_up((int64_t)p->rows * round_up(select_width(p), 64) * (int64_t)sizeof(float), 256);
-}
-
 size_t idx_select_workspace(const idx_problem* p, int k) {
   (void)k;
   if (!p || p->rows <= 0) return 0;
   int64_t width = select_width(p);
   if (width <= 0) return 0;
-  return select_scores_bytes(p) + topk_workspace_bytes(p->rows, width);
+  const size_t two_pass = select_scores_bytes(p) + select_lens_bytes(p) + topk_workspace_bytes(p->rows, width);
+  if (!select_one_pass_shape(p)) return two_pass;
+  return std::max(two_pass, select_layout(p).total);
 }
 
 idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_val, int64_t out_ld,
@@ -305,7 +391,8 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
   const char* fn = "idx_select";
   REQUIRE(p, IDX_ERR_ARG, "%s: problem is null", fn);
   REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
-  REQUIRE((flags & ~IDX_TOPK_UNSORTED) == 0, IDX_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
+  REQUIRE((flags & ~(IDX_TOPK_UNSORTED | IDX_SELECT_NO_CUTOFF)) == 0, IDX_ERR_ARG, "%s: unknown flags 0x%x", fn,
+          flags);
   REQUIRE(p->rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, p->rows);
   const int64_t width = select_width(p);
   ScoreCall c;
@@ -329,23 +416,13 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
   REQUIRE(aligned(workspace, 256), IDX_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
 
   const int64_t ldw = round_up(width, 64);
-  float* scores = (float*)workspace;
-  c.logits = scores;
+  uint8_t* ws = (uint8_t*)workspace;
   c.ld = ldw;
   c.bt_rows = p->bt_rows;
   c.err = device_error_word();
-  c.skip_tail = 1;  // the top-k below reads each row only up to its length
-  // the scan kernels clear the top-k's histogram and counters on their way
-  uint8_t* topk_ws = (uint8_t*)workspace + select_scores_bytes(p);
-  if (!prefill_applies(c)) {
-    c.zero = (uint32_t*)topk_ws;
-    c.zero_words = (int64_t)(topk_zeroed_bytes(p->rows, width) / 4);
-  }
-  hipError_t e = launch_score(c, (hipStream_t)stream);
-  if (e != hipSuccess) return launched(fn, e);
+  c.skip_tail = 1;  // the top-k below reads each row only up to its scored length
 
   TopkCall t{};
-  t.logits = scores;
   t.ld = ldw;
   t.n_cols = width;
   t.rows = p->rows;
@@ -354,18 +431,53 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
   t.out_val = out_val;
   t.out_ld = out_ld;
   t.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
-  t.ws_zeroed = c.zero && c.zero_words > 0;
-  if (p->mode == IDX_MODE_DENSE) {
-    t.len_ks = p->row_ks;
-    t.len_ke = p->row_ke;
-  } else if (p->mode == IDX_MODE_PAGED) {
-    t.lens = p->seq_lens;
-  } else {
-    t.lens = p->n_cols;
+  if (p->mode == IDX_MODE_SPARSE_BLOCKS) {
     t.cand = p->cand_blocks;
     t.cand_ld = p->cand_ld;
     t.block = p->block_size;
   }
+
+  const int64_t blocks = select_one_pass_shape(p) ? select_scan_blocks(c) : 0;
+  if (blocks >= 1 && blocks <= kSelMaxBlocks) {
+    const SelectLayout L = select_layout(p);
+    SelectState st{};
+    st.slots = (uint32_t*)(ws + L.slots);
+    st.arrive = (unsigned long long*)(ws + L.arrive);
+    st.acc = (int64_t*)(ws + L.acc);
+    st.seg_info = (uint32_t*)(ws + L.seg_info);
+    st.surv = (uint64_t*)(ws + L.surv);
+    st.spill = (float*)(ws + L.spill);
+    st.k = k;
+    st.gshift = select_group_shift(ldw, k);
+    st.wait_ticks = (flags & IDX_SELECT_NO_CUTOFF) ? 0 : kSelectWaitTicks;
+    c.logits = st.spill;
+    c.sel = &st;
+    log_once("idx_select: one pass (rows %d, width %lld, k %d, groups of %d, %lld scan workgroups)", p->rows,
+             (long long)width, k, 1 << st.gshift, (long long)blocks);
+    hipError_t e = launch_score(c, (hipStream_t)stream);
+    if (e != hipSuccess) return launched(fn, e);
+    return launched(fn, launch_select_finish(t, st, blocks, (hipStream_t)stream));
+  }
+
+  // scores to the workspace, then the top-k over each row's scored length
+  float* scores = (float*)ws;
+  int32_t* lens = (int32_t*)(ws + select_scores_bytes(p));
+  uint8_t* topk_ws = ws + select_scores_bytes(p) + select_lens_bytes(p);
+  c.logits = scores;
+  c.lens_out = lens;
+  // the scan kernels clear the top-k's histogram and counters on their way
+  const bool prefill = prefill_applies(c);
+  if (!prefill) {
+    c.zero = (uint32_t*)topk_ws;
+    c.zero_words = (int64_t)(topk_zeroed_bytes(p->rows, width) / 4);
+  }
+  log_once("idx_select: %s then top-k (rows %d, width %lld, k %d)", prefill ? "prefill tiles" : "scan", p->rows,
+           (long long)width, k);
+  hipError_t e = launch_score(c, (hipStream_t)stream);
+  if (e != hipSuccess) return launched(fn, e);
+  t.logits = scores;
+  t.lens = lens;
+  t.ws_zeroed = c.zero && c.zero_words > 0;
   return launched(fn, launch_topk(t, topk_ws, (hipStream_t)stream));
 }
 

@@ -119,6 +119,19 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Workgroup barrier that orders LDS accesses only: global stores issued before it need not
+// have completed (__syncthreads also waits for those).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Set bits of a 64-lane mask below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Wave-wide inclusive prefix sum (lane order): a scan inside each 16-lane row with
 // DPP row shifts (lanes without a source add 0), then the row totals, read from lanes
 // 15, 31 and 47, added to the rows above them.

@@ -7,7 +7,39 @@
 namespace dsaidx {
 
 enum SourceKind { SRC_DENSE = 1, SRC_PAGED = 2, SRC_SPARSE = 3 };
+
+// Per-device state (error word, CU count, occupancy, kernel attributes) is kept for
+// device ids below this.
+constexpr int kMaxDevices = 64;
 enum KeyFmt { FMT_BF16 = 1, FMT_FP8 = 2, FMT_MXFP4 = 3 };
+
+// idx_select's one-pass selection for rows that read their own keys (the balanced scan).
+// A scan workgroup keeps the scores of its step range in LDS and builds, per row it
+// meets, a histogram of the largest order key of each group of 2^gshift columns. The
+// k-th largest group maximum of a row is a value that at least k entries reach, so the
+// entries at or above it (the survivors) hold the row's top k. A row inside one workgroup
+// is cut at once; the two rows a workgroup may share with its neighbours (its first and
+// last) are cut once every workgroup of the row has published its histogram. Each
+// workgroup writes its survivors to its own region; a finish kernel selects exactly
+// among them.
+constexpr int kSelFineBins = 4096;    // histogram of the top 12 bits of the order key
+constexpr int kSelCoarseBins = 256;   // and of its top 8 bits (16 fine bins each)
+constexpr int kSelSlotWords = kSelFineBins / 2 + kSelCoarseBins;  // 16-bit fine counts in pairs, coarse
+constexpr int kSelMaxBlocks = 1024;   // workgroups of a one-pass scan launch
+constexpr int kSelMaxSpan = 32;       // workgroups a row may span and still be cut
+struct SelectState {
+  uint32_t* slots;               // [kSelMaxBlocks, 2, kSelSlotWords]: histogram of a workgroup's
+                                 // first (0) and last (1) row when shared with other workgroups
+  unsigned long long* arrive;    // [rows] workgroups done with the row (counts up, never cleared)
+  int64_t* acc;                  // [rows + 1] first step of each row in the call's step order
+  uint32_t* seg_info;            // [steps] at a segment's first step: survivors | (1 << 31) when
+                                 // the segment kept every entry (no cutoff)
+  uint64_t* surv;                // [steps, 64] survivor keys from the segment's first step on
+  float* spill;                  // [rows, ld] scores of ranges that do not fit in LDS
+  int k;
+  int gshift;                    // group size 2^gshift columns, 0..4
+  int64_t wait_ticks;            // limit of a row wait (100 MHz clock); 0: no cutoff
+};
 
 // One scoring call, validated by the C-ABI layer.
 struct ScoreCall {
@@ -38,6 +70,8 @@ struct ScoreCall {
                           // reader knows the lengths); 0: they are set to -inf
   uint32_t* zero;         // optional: words the kernel sets to 0 (a following top-k's
   int64_t zero_words;     // histogram and counters)
+  const SelectState* sel; // optional: the one-pass selection (balanced scan only)
+  int32_t* lens_out;      // optional: each row's scored length (columns a top-k may read)
 };
 
 // One top-k call.
@@ -61,6 +95,15 @@ struct TopkCall {
 };
 
 hipError_t launch_score(const ScoreCall& c, hipStream_t stream);
+
+// Rows up to this count take the balanced scan (and can take the one-pass selection).
+constexpr int kBalancedMaxRows = 512;
+// Workgroups of the balanced scan launch for this call (the one-pass selection's part
+// boundaries depend on it); 0 if the call does not take the balanced scan.
+int64_t select_scan_blocks(const ScoreCall& c);
+// The finish of the one-pass selection: one workgroup per row selects among the row's
+// survivors and writes the row.
+hipError_t launch_select_finish(const TopkCall& t, const SelectState& s, int64_t blocks, hipStream_t stream);
 
 // Dense fp8 calls with at least this many rows are taken as prefill chunks (rows that
 // share their keys) and run the tiled prefill kernel; fewer rows run the decode scan.

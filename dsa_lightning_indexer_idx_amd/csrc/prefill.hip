@@ -62,6 +62,7 @@ struct PrefillArgs {
   int64_t ld;
   unsigned* err;
   int skip_tail;  // 1: columns past a query's length stay unwritten
+  int32_t* lens_out;  // optional: each query's scored length
 };
 
 constexpr int kPieces = 5;  // fp8 pieces of q' per query
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
       e = min(max(e0, s), a.n_keys);
       e = min(e, s + a.ld);
       if (lane == 0 && piece == 0 && (s != s0 || e != e0)) flag_error(a.err, kErrRange);
+      if (lane == 0 && piece == 0 && a.lens_out) a.lens_out[r] = (int32_t)(e - s);
     }
     qs[u] = s;
     qe[u] = e;
@@ -340,6 +342,7 @@ hipError_t launch_prefill(const ScoreCall& c, hipStream_t stream) {
   a.ld = c.ld;
   a.err = c.err;
   a.skip_tail = c.skip_tail;
+  a.lens_out = c.lens_out;
   const int nblocks = (c.rows + kQB - 1) / kQB;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)(nblocks * kSplit)), dim3(kPThreads), 0, stream, a);
   return hipGetLastError();

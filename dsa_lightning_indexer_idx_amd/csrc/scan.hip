@@ -38,6 +38,7 @@ struct ScanCommon {
   int skip_tail;    // columns past a row's scored steps stay unwritten
   uint32_t* zero;   // words to clear (every wave clears its share first)
   int64_t zero_words;
+  int32_t* lens_out;  // optional: each row's scored length (clipped to ld)
 };
 
 // ------------------------------------------------------------------ key sources
@@ -45,7 +46,10 @@ struct ScanCommon {
 // Pages and candidate blocks hold a multiple of 64 keys and steps start at multiples
 // of 64 positions, so the 64 positions of a step name 64 consecutive key rows. A
 // source describes step s of a row by its first key row and by how many leading
-// positions of the step are scored (its valid prefix, <= 0 when none is).
+// positions of the step are scored (its valid prefix, <= 0 when none is). The lookup
+// has two halves so a caller can issue the table load early and use it later:
+// step_raw loads the table entry the step needs (page or candidate block id), step_desc
+// turns it into the description; step is both at once.
 
 struct StepDesc {
   int64_t kidx0;
@@ -69,8 +73,12 @@ struct DenseSrc {
     return {s2, len};
   }
   __device__ int64_t bound(const Row& R) const { return R.len; }
-  __device__ StepDesc step(const Row& R, int64_t pos0, unsigned*) const {
+  __device__ int64_t step_raw(const Row&, int64_t) const { return 0; }
+  __device__ StepDesc step_desc(const Row& R, int64_t pos0, int64_t, unsigned*) const {
     return {R.base + pos0, (int32_t)min(R.len - pos0, (int64_t)kTileTokens)};
+  }
+  __device__ StepDesc step(const Row& R, int64_t pos0, unsigned* err) const {
+    return step_desc(R, pos0, 0, err);
   }
 };
 
@@ -95,9 +103,14 @@ struct PagedSrc {
     return {bt + req2 * bt_ld, L2};
   }
   __device__ int64_t bound(const Row& R) const { return R.len; }
+  __device__ int64_t step_raw(const Row& R, int64_t pos0) const {
+    return pos0 < R.len ? (int64_t)R.bt_row[pos0 / page] : 0;
+  }
   __device__ StepDesc step(const Row& R, int64_t pos0, unsigned* err) const {
+    return step_desc(R, pos0, step_raw(R, pos0), err);
+  }
+  __device__ StepDesc step_desc(const Row& R, int64_t pos0, int64_t pg, unsigned* err) const {
     if (pos0 >= R.len) return {0, 0};
-    int64_t pg = R.bt_row[pos0 / page];
     if (pg < 0 || pg >= n_pages) {
       flag_error(err, kErrPage);
       pg = min(max(pg, (int64_t)0), n_pages - 1);
@@ -132,9 +145,14 @@ struct SparseSrc {
     return {s2, e2 - s2, cand + (int64_t)r * cand_ld, nc2};
   }
   __device__ int64_t bound(const Row& R) const { return R.ncols; }
+  __device__ int64_t step_raw(const Row& R, int64_t pos0) const {
+    return pos0 < R.ncols ? (int64_t)R.cand_row[pos0 / block] : 0;
+  }
   __device__ StepDesc step(const Row& R, int64_t pos0, unsigned* err) const {
+    return step_desc(R, pos0, step_raw(R, pos0), err);
+  }
+  __device__ StepDesc step_desc(const Row& R, int64_t pos0, int64_t cb, unsigned* err) const {
     if (pos0 >= R.ncols) return {0, 0};
-    const int64_t cb = R.cand_row[pos0 / block];
     if (cb < 0) {
       flag_error(err, kErrBlock);
       return {0, 0};
@@ -326,12 +344,10 @@ constexpr int max_steps() {
 static_assert(max_steps<FMT_FP8>() >= 1 && max_steps<FMT_FP8>() <= kWave && max_steps<FMT_MXFP4>() >= 1 &&
                   max_steps<FMT_MXFP4>() <= kWave,
               "a segment describes one step per lane");
-// Row counts up to this take the balanced schedule (every wave reads all row lengths).
-static constexpr int kBalancedMaxRows = 512;
 
-// Scores steps [s0, s0 + nsteps) of row r (nsteps <= max_steps<F>()) and writes their
-// columns, clipped to ld. sb: the wave's LDS slice of max_steps<F>() * 64 floats.
-template <int F, class Src>
+// Scores steps [s0, s0 + nsteps) of row r (nsteps <= max_steps<F>()) into sb[0, 64 nsteps)
+// (LDS) and, if STORE, writes them to their columns of the score row, clipped to ld.
+template <int F, class Src, bool STORE = true>
 __device__ __forceinline__ void scan_segment(const ScanCommon& a, const Src& src, int r, int64_t s0, int nsteps,
                                              float* sb) {
   const int lane = lane_id();
@@ -406,6 +422,7 @@ __device__ __forceinline__ void scan_segment(const ScanCommon& a, const Src& src
   // LDS operations of one wave complete in order, so the lanes read what the wave
   // wrote; the columns leave four scores per lane per instruction
   __builtin_amdgcn_wave_barrier();
+  if constexpr (!STORE) return;
   const int64_t cnt = c1 - c0;
   float* o = out + c0;
   const bool vec = ((uintptr_t)o & 15) == 0;
@@ -421,6 +438,13 @@ __device__ __forceinline__ void scan_segment(const ScanCommon& a, const Src& src
     }
   }
   __builtin_amdgcn_wave_barrier();  // the next segment's scores wait for these reads
+}
+
+// Scored columns of row r: its bound (length or valid sparse columns) clipped to ld.
+template <class Src>
+__device__ __forceinline__ int64_t row_cols(const ScanCommon& a, const Src& src, int r) {
+  const auto R = src.row(r, a.ld, a.err, false);
+  return max(min(src.bound(R), a.ld), (int64_t)0);
 }
 
 // Scored steps of row r (steps of 64 columns up to the row's bound, clipped to ld).
@@ -448,18 +472,13 @@ __device__ __forceinline__ void fill_neg_inf(float* out, int64_t f0, int64_t f1)
   }
 }
 
-// BALANCED: every wave sums the scored steps of all rows and takes an equal
-// contiguous share of them (crossing rows where needed), in segments of at most
-// max_steps<F>() steps, so all waves finish together whatever the row lengths; then the
-// columns past each row's scored steps are filled with -inf in 4096-column pieces
-// (unless skip_tail). Otherwise items (row, chunk of chunk_tiles steps) are taken in a
-// grid-stride loop.
-template <int F, class Src, bool BALANCED>
-__global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
+// Rows beyond kBalancedMaxRows: items (row, chunk of chunk_tiles steps) taken by the waves
+// in a grid-stride loop, each scored through the wave's LDS slice and stored.
+template <int F, class Src>
+__global__ __launch_bounds__(kBlock) void scan_items_kernel(ScanCommon a, Src src) {
   const int lane = lane_id();
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  // the scores of a segment collect in this wave's LDS slice and leave in 1 KiB bursts
   constexpr int kMaxSteps = max_steps<F>();
   __shared__ __align__(16) float sbuf[kBlock / kWave][kMaxSteps * kTileTokens];
   float* sb = sbuf[threadIdx.x / kWave];
@@ -468,52 +487,619 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
     const int64_t z1 = min(a.zero_words, (wave + 1) * per);
     for (int64_t i = wave * per + lane; i < z1; i += kWave) a.zero[i] = 0u;
   }
+  const int64_t chunk = (int64_t)a.chunk_tiles * kTileTokens;
+  for (int64_t item = wave; item < a.n_items; item += nwaves) {
+    const int r = (int)(item % a.rows);
+    const int64_t c0 = (item / a.rows) * chunk;
+    if (c0 >= a.ld) continue;
+    const int64_t c1 = min(c0 + chunk, a.ld);
+    const int64_t n = row_steps(a, src, r, c0 == 0);
+    if (c0 == 0 && a.lens_out && lane == 0) a.lens_out[r] = (int32_t)row_cols(a, src, r);
+    const int64_t s0 = c0 / kTileTokens;
+    const int64_t s1 = min(s0 + a.chunk_tiles, n);
+    if (s1 > s0) scan_segment<F>(a, src, r, s0, (int)(s1 - s0), sb);
+    if (!a.skip_tail) fill_neg_inf(a.logits + (int64_t)r * a.ld, max(c0, s1 * kTileTokens), c1);
+  }
+}
 
-  if constexpr (BALANCED) {
-    // total scored steps; wave 0 reports bad row metadata
-    uint64_t total = 0;
-    for (int r0 = 0; r0 < a.rows; r0 += kWave) {
-      const int r = r0 + lane;
-      const uint32_t n = r < a.rows ? (uint32_t)row_steps(a, src, r, wave == 0) : 0u;
-      total += (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(n), kWave - 1);
+// ------------------------------------------------------------------ balanced scan
+//
+// Up to kBalancedMaxRows rows. The scored steps of all rows, in row order, are split into
+// equal contiguous ranges, one per workgroup (one 8-wave workgroup per compute unit, so
+// the ranges start and end together whatever the length mix). Inside a workgroup the
+// waves do not take fixed shares: on each SIMD the older of its two waves issues first
+// whenever both are ready and would finish its share well before the younger one. The
+// range is cut instead into units of kUnit steps (never crossing a row) that the waves
+// take from an LDS counter as they go; a wave issues the loads of its next step across
+// unit boundaries, and looks up the table entries of its next unit one unit ahead.
+// When the range fits the workgroup's LDS buffer (kBlockSteps steps) its scores stay
+// there and leave in one burst at the end (or, for idx_select, never leave: see the
+// one-pass selection below); a longer range is split evenly between the waves, each
+// scoring its part in LDS-slice segments that are stored as they complete.
+
+constexpr int kBalThreads = 512;
+constexpr int kBalWaves = kBalThreads / kWave;
+constexpr int kUnit = 2;
+constexpr int kBlockSteps = kBalWaves * kWave;   // 512 steps, 128 KiB of scores
+constexpr int kMaxParts = kBalancedMaxRows;      // rows one range can meet
+
+// The rows meeting a workgroup's range, in order (built by wave 0).
+struct BlockParts {
+  int n, nunits;
+  int r[kMaxParts];
+  int rs0[kMaxParts];   // first step of the part within its row
+  int rlen[kMaxParts];  // steps of the whole row
+  int off[kMaxParts];   // first step of the part within the range
+  int len[kMaxParts];   // steps of the part
+  int ub[kMaxParts + 1];  // first unit of the part
+};
+
+// Step descriptors of a workgroup's LDS-resident range, step i of the range in slot i.
+struct StepTab {
+  int64_t kidx0[kBlockSteps];
+  int32_t vlim[kBlockSteps];
+  int32_t row[kBlockSteps];
+};
+
+// Block-wide: the descriptors of the range's n steps (one thread per step).
+template <class Src>
+__device__ __forceinline__ void build_steps(const ScanCommon& a, const Src& src, const BlockParts& P, int n,
+                                            StepTab& T) {
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    int lo = 0, hi = P.n;  // the part holding step t: P.off[lo] <= t < P.off[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.off[mid] <= t) lo = mid;
+      else hi = mid;
     }
-    const uint64_t beg = total * (uint64_t)wave / (uint64_t)nwaves;
-    const uint64_t end = total * (uint64_t)(wave + 1) / (uint64_t)nwaves;
-    uint64_t acc = 0;  // steps of the rows before the current one
+    const int r = P.r[lo];
+    const auto R = src.row(r, a.ld, a.err, false);
+    const StepDesc d = src.step(R, ((int64_t)P.rs0[lo] + (t - P.off[lo])) * kTileTokens, a.err);
+    T.kidx0[t] = d.kidx0;
+    T.vlim[t] = d.vlim;
+    T.row[t] = r;
+  }
+}
+
+// Scores the n steps of the range into buf (LDS, step i's 64 scores at buf + 64 i), taking
+// units of kUnit consecutive steps from *ctr until none is left. A wave keeps the next unit
+// taken one unit ahead and issues the loads of its next step across unit boundaries.
+template <int F>
+__device__ __forceinline__ void bal_stream(const ScanCommon& a, const StepTab& T, int n, uint32_t* ctr, float* buf) {
+  const int lane = lane_id();
+  const float NEG_INF = -__builtin_inff();
+  const int nunits = (n + kUnit - 1) / kUnit;
+  auto grab = [&]() __attribute__((always_inline)) -> int {
+    int id = 0;
+    if (lane == 0) id = (int)atomicAdd(ctr, 1u);
+    return __builtin_amdgcn_readfirstlane(id);
+  };
+  int ucur = grab();
+  if (ucur >= nunits) return;
+  int unxt = grab();
+  int sc = ucur * kUnit;  // the step being computed
+  int qrow = T.row[sc];
+  QOps<F> qo;
+  float wr[4][4];
+  auto load_qw = [&](int r) __attribute__((always_inline)) {
+    qo.load(a.q, r, lane);
+    const int g = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float4 wv = *(const float4*)(a.w + (int64_t)r * kHeads + 16 * h + 4 * g);
+      wr[h][0] = wv.x;
+      wr[h][1] = wv.y;
+      wr[h][2] = wv.z;
+      wr[h][3] = wv.w;
+    }
+  };
+  load_qw(qrow);
+  KOps<F> ka[4], kb[4];
+  float sca = 1.f, scb = 1.f;
+  int32_t va = T.vlim[sc], vb = 0;
+  if (va > 0) load_step<F>(ka, sca, a, T.kidx0[sc], va, lane);
+  // computes step sc (keys in kc) after issuing the loads of the step after it into kn;
+  // false when there is none
+  auto phase = [&](KOps<F>(&kc)[4], float scc, int32_t vc, KOps<F>(&kn)[4], float& scn,
+                   int32_t& vn) __attribute__((always_inline)) -> bool {
+    int sn = sc + 1;
+    if (sn >= n || sn % kUnit == 0) {  // the next unit's first step
+      sn = unxt < nunits ? unxt * kUnit : -1;
+      if (sn >= 0) unxt = grab();
+    }
+    vn = sn >= 0 ? T.vlim[sn] : 0;
+    if (vn > 0) load_step<F>(kn, scn, a, T.kidx0[sn], vn, lane);
+    const float v = vc > 0 ? score_step<F>(kc, scc, qo, wr) : NEG_INF;
+    buf[sc * kTileTokens + lane] = lane < vc ? v : NEG_INF;
+    if (sn < 0) return false;
+    sc = sn;
+    const int rn = T.row[sn];
+    if (rn != qrow) {
+      qrow = rn;
+      load_qw(qrow);
+    }
+    return true;
+  };
+  for (;;) {
+    if (!phase(ka, sca, va, kb, scb, vb)) break;
+    if (!phase(kb, scb, vb, ka, sca, va)) break;
+  }
+}
+
+// ------------------------------------------------------------------ one-pass selection
+//
+// idx_select on the balanced scan. After scoring its range (kept in LDS), a workgroup
+// takes each row part in turn:
+//   * the histogram of the part's group maxima (the largest order key of each group of
+//     2^gshift columns) is built in LDS: 4096 fine bins of 16-bit counts in pairs (the
+//     step table's space, free once the range is scored) and 256 coarse bins;
+//   * a row inside the workgroup's range is cut at once from that histogram;
+//   * a row shared with other workgroups (only the range's first and last can be) is
+//     cut once each of the row's workgroups has published its histogram to its slot and
+//     counted itself in the row's arrival counter: the histograms of the row's slots are
+//     added up, coarse bins first;
+//   * the cut is the lower edge of the fine bin holding the k-th largest group maximum,
+//     so at least k groups, hence k entries, reach it; the part's entries at or above it
+//     go, as selection keys, to the workgroup's region at the part's first step * 64,
+//     their count to seg_info at the part's first step.
+// Slots and counters are shared by all XCDs, so they are written and read with device-
+// scope atomic operations only. A wait that runs past wait_ticks, or a row spanning more
+// than kSelMaxSpan workgroups, keeps every entry of the part: correct in every case, only
+// slower to finish. The arrival counters are never cleared: a workgroup waits for its
+// row's counter to pass the value it read before scoring by the number of workgroups of
+// the row (nothing of the row can have arrived then: arrivals follow a scored range).
+
+__device__ __forceinline__ uint32_t atomic_ld(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_st(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The workgroup of the balanced split that holds step s (steps [total b / B,
+// total (b + 1) / B) belong to workgroup b).
+__device__ __forceinline__ int64_t sel_block_of(uint64_t s, uint64_t total, int64_t B) {
+  return (int64_t)(((s + 1) * (uint64_t)B - 1) / total);
+}
+
+// Block-wide: histogram (LDS: hf fine pairs, hc coarse) of the group maxima of the
+// n_ent scores at sc (LDS or global; group i = entries i 2^gs .. (i + 1) 2^gs - 1).
+__device__ __forceinline__ void sel_hist(const float* sc, int64_t n_ent, int gs, uint32_t* hf, uint32_t* hc) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kSelFineBins / 2; i += blockDim.x) hf[i] = 0u;
+  lds_barrier();
+  const int64_t ng = n_ent >> gs;
+  for (int64_t i = tid; i < ng; i += blockDim.x) {
+    // the group's largest score (fmaxf passes over NaN), then its order key
+    const float* g = sc + (i << gs);
+    float m = -__builtin_inff();
+    if (gs >= 2) {
+      for (int e = 0; e < (1 << gs); e += 4) {
+        const float4 v = *(const float4*)(g + e);
+        m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+      }
+    } else {
+      for (int e = 0; e < (1 << gs); ++e) m = fmaxf(m, g[e]);
+    }
+    const uint32_t mk = order_key(m);
+    if (mk) {
+      const uint32_t fb = mk >> 20;
+      atomicAdd(&hf[fb >> 1], 1u << (16 * (fb & 1)));
+    }
+  }
+  lds_barrier();
+  for (int c = tid; c < kSelCoarseBins; c += blockDim.x) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = hf[c * 8 + j];
+      t += (w & 0xFFFFu) + (w >> 16);
+    }
+    hc[c] = t;
+  }
+  lds_barrier();
+}
+
+// Wave-wide, the coarse half of a cut: coarse4(c) gives lane l the coarse bins 255 - 4l ..
+// 252 - 4l (highest first). Returns false when fewer than k groups are counted (the cut is
+// then 1, every present entry); else the coarse bin holding the k-th largest group maximum
+// and the count of the bins above it.
+template <class Coarse4>
+__device__ __forceinline__ bool sel_cut_coarse(uint32_t k, const Coarse4& coarse4, int& cbin, uint32_t& above) {
+  const int lane = lane_id();
+  uint32_t c[4];
+  coarse4(c);
+  const uint32_t t = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_inclusive_sum(t);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+  if (tot < k) return false;
+  const uint32_t excl = incl - t;
+  const uint64_t hit = __ballot(excl < k && k <= incl);
+  const int hl = __builtin_ctzll(hit);
+  int cb = 0;
+  uint32_t ab = 0;
+  if (lane == hl) {
+    uint32_t cum = excl;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && cum + c[j] >= k) {
+        cb = kSelCoarseBins - 1 - 4 * lane - j;
+        ab = cum;
+        found = true;
+      }
+      cum += c[j];
+    }
+  }
+  cbin = __builtin_amdgcn_readlane(cb, hl);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)ab, hl);
+  return true;
+}
+
+// Wave-wide, the fine half: fine16(j) is the count of fine bin cbin * 16 + j. The cut is the
+// lower edge of the fine bin holding the k-th largest group maximum.
+template <class Fine16>
+__device__ __forceinline__ uint32_t sel_cut_fine(uint32_t k, int cbin, uint32_t above, const Fine16& fine16) {
+  const int lane = lane_id();
+  const uint32_t f = lane < 16 ? fine16(15 - lane) : 0u;  // highest first
+  const uint32_t fi = wave_inclusive_sum(f);
+  const uint64_t fh = __ballot(lane < 16 && above + fi - f < k && k <= above + fi);
+  if (!fh) return max((uint32_t)cbin << 24, 1u);  // counts out of step: the coarse edge is still a bound
+  return max((uint32_t)(cbin * 16 + 15 - __builtin_ctzll(fh)) << 20, 1u);
+}
+
+// One lane: waits (bounded) until row r's arrival counter has moved `parts` past `base`.
+__device__ __forceinline__ bool sel_wait(const SelectState& st, int r, unsigned long long base, int64_t parts) {
+  const unsigned long long* p = st.arrive + r;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    const unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v - base >= (unsigned long long)parts) return true;
+    if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > st.wait_ticks) return false;
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// Block-wide: the n_ent scores at sc (columns col0 ..) at or above the cut T, as
+// selection keys to out (each wave's in one contiguous run); returns their count. An
+// entry's order key is at least T exactly when its score is at least T's value (the order
+// key is monotone; NaN compares false, -0 == +0); T = 1 keeps every present entry (-inf
+// and NaN excluded).
+__device__ __forceinline__ uint32_t sel_filter(const float* sc, int64_t n_ent, int64_t col0, uint32_t T,
+                                               uint64_t* out, uint32_t* wsum) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  const int nw = blockDim.x / kWave;
+  const int64_t step = 4 * (int64_t)blockDim.x;
+  const float t = T <= 1u ? -__FLT_MAX__ : key_value(T);
+  auto vals = [&](int64_t i) __attribute__((always_inline)) -> float4 {
+    float4 v = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
+    if (i < n_ent) v = *(const float4*)(sc + i);
+    return v;
+  };
+  uint32_t mine = 0;
+  for (int64_t i = 4 * tid; i < n_ent; i += step) {
+    const float4 v = vals(i);
+    mine += (v.x >= t ? 1u : 0u) + (v.y >= t ? 1u : 0u) + (v.z >= t ? 1u : 0u) + (v.w >= t ? 1u : 0u);
+  }
+  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(mine), kWave - 1);
+  lds_barrier();  // wsum may still be read by the previous call
+  if (lane == 0) wsum[wv] = wtot;
+  lds_barrier();
+  uint32_t base = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t v = wsum[w];
+    base += w < wv ? v : 0u;
+    tot += v;
+  }
+  // the wave's survivors in order of (pass, entry of the lane's four, lane)
+  if (wtot) {
+    for (int64_t i0 = 4 * (int64_t)wv * kWave; i0 < n_ent; i0 += step) {
+      const int64_t i = i0 + 4 * lane;
+      const float4 v = vals(i);
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool take = e[j] >= t;
+        const uint64_t m = __ballot(take);
+        if (take) out[base + lanes_below(m)] = ((uint64_t)order_key(e[j]) << 32) | (uint32_t)(~(uint32_t)(col0 + i + j));
+        base += (uint32_t)__popcll(m);
+      }
+    }
+  }
+  return tot;
+}
+
+// ------------------------------------------------------------------ balanced kernel
+
+template <int F, class Src, bool SELECT>
+__global__ __launch_bounds__(kBalThreads) void scan_bal_kernel(ScanCommon a, Src src, SelectState st) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wib = tid / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * kBalWaves;
+  const int64_t wave = (int64_t)blockIdx.x * kBalWaves + wib;
+  const int64_t B = gridDim.x, b = blockIdx.x;
+  __shared__ __align__(16) float buf[kBlockSteps * kTileTokens];
+  __shared__ BlockParts P;
+  __shared__ StepTab T;
+  __shared__ uint32_t ctr;
+  __shared__ unsigned long long sbase[2];
+  __shared__ uint32_t hc[SELECT ? kSelCoarseBins : 1];
+  __shared__ uint32_t wsum[kBalWaves];
+  __shared__ uint32_t s_T, s_ok, s_above, s_f16[16];
+  __shared__ int s_cbin;
+  if (!SELECT && a.zero) {
+    const int64_t per = (a.zero_words + nwaves - 1) / nwaves;
+    const int64_t z1 = min(a.zero_words, (wave + 1) * per);
+    for (int64_t i = wave * per + lane; i < z1; i += kWave) a.zero[i] = 0u;
+  }
+
+  // total scored steps; wave 0 of workgroup 0 reports bad row metadata, the rows' scored
+  // lengths and (idx_select) each row's first step
+  const bool first = b == 0 && wib == 0;
+  uint64_t total = 0;
+  for (int r0 = 0; r0 < a.rows; r0 += kWave) {
+    const int r = r0 + lane;
+    const uint32_t n = r < a.rows ? (uint32_t)row_steps(a, src, r, first) : 0u;
+    const uint32_t incl = wave_inclusive_sum(n);
+    if (first && r < a.rows) {
+      if (a.lens_out) a.lens_out[r] = (int32_t)row_cols(a, src, r);
+      if (SELECT) st.acc[r] = (int64_t)(total + incl - n);
+    }
+    total += (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+  }
+  if (SELECT && first && lane == 0) st.acc[a.rows] = (int64_t)total;
+  const uint64_t beg = total * (uint64_t)b / (uint64_t)B;
+  const uint64_t end = total * (uint64_t)(b + 1) / (uint64_t)B;
+  const bool resident = end - beg <= (uint64_t)kBlockSteps;
+
+  // the rows meeting [beg, end); units of kUnit steps over them
+  if (wib == 0) {
+    uint64_t acc = 0;
+    int np = 0;
     for (int r0 = 0; r0 < a.rows && acc < end; r0 += kWave) {
       const int r = r0 + lane;
       const uint32_t n = r < a.rows ? (uint32_t)row_steps(a, src, r, false) : 0u;
-      const int m = min(kWave, a.rows - r0);
-      for (int j = 0; j < m && acc < end; ++j) {
-        const uint64_t nj = (uint32_t)__builtin_amdgcn_readlane((int)n, j);
-        const uint64_t lo = max(acc, beg), hi = min(acc + nj, end);
-        for (uint64_t s = lo; s < hi; s += kMaxSteps)
-          scan_segment<F>(a, src, r0 + j, (int64_t)(s - acc), (int)min((uint64_t)kMaxSteps, hi - s), sb);
-        acc += nj;
+      const uint32_t incl = wave_inclusive_sum(n);
+      const uint64_t s = acc + incl - n, e = acc + incl;
+      const uint64_t lo = max(s, beg), hi = min(e, end);
+      const bool meet = r < a.rows && lo < hi;
+      const uint64_t m = __ballot(meet);
+      if (meet) {
+        const int p = np + (int)lanes_below(m);
+        P.r[p] = r;
+        P.rs0[p] = (int)(lo - s);
+        P.rlen[p] = (int)n;
+        P.off[p] = (int)(lo - beg);
+        P.len[p] = (int)(hi - lo);
       }
+      np += (int)__popcll(m);
+      acc += (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
     }
-    if (!a.skip_tail) {
-      constexpr int64_t kFill = 4096;
-      const int64_t pieces = (a.ld + kFill - 1) / kFill;
-      for (int64_t it = wave; it < pieces * a.rows; it += nwaves) {
-        const int r = (int)(it % a.rows);
-        const int64_t f0 = (it / a.rows) * kFill;
-        const int64_t from = row_steps(a, src, r, false) * kTileTokens;
-        fill_neg_inf(a.logits + (int64_t)r * a.ld, max(f0, from), min(f0 + kFill, a.ld));
+    int ub = 0;
+    for (int p0 = 0; p0 < np; p0 += kWave) {
+      const int p = p0 + lane;
+      const uint32_t u = p < np ? (uint32_t)((P.len[p] + kUnit - 1) / kUnit) : 0u;
+      const uint32_t incl = wave_inclusive_sum(u);
+      if (p < np) P.ub[p] = ub + (int)(incl - u);
+      ub += (int)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    }
+    if (lane == 0) {
+      P.n = np;
+      P.nunits = ub;
+      P.ub[np] = ub;
+      ctr = 0;
+    }
+  }
+  __syncthreads();
+  const int np = P.n;
+
+  // idx_select: the arrival counters of the first and last rows, when shared with other
+  // workgroups, read before scoring
+  if constexpr (SELECT) {
+    if (tid < 2 && np > 0) {
+      const int p = tid == 0 ? 0 : np - 1;
+      sbase[tid] = __hip_atomic_load(st.arrive + P.r[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // score the range
+  if (resident) {
+    build_steps(a, src, P, (int)(end - beg), T);
+    __syncthreads();
+    bal_stream<F>(a, T, (int)(end - beg), &ctr, buf);
+    __syncthreads();
+    if constexpr (!SELECT) {
+      // the range's scores to their rows, four per thread per store
+      for (int p = 0; p < np; ++p) {
+        const int64_t c0 = (int64_t)P.rs0[p] * kTileTokens;
+        const int64_t cnt = min((int64_t)P.len[p] * kTileTokens, a.ld - c0);
+        float* o = a.logits + (int64_t)P.r[p] * a.ld + c0;
+        const float* sp = buf + P.off[p] * kTileTokens;
+        const bool vec = ((uintptr_t)o & 15) == 0;
+        for (int64_t i = 4 * tid; i < cnt; i += 4 * kBalThreads) {
+          const float4 v = *(const float4*)(sp + i);
+          if (vec && i + 4 <= cnt) {
+            *(float4*)(o + i) = v;
+          } else {
+            o[i] = v.x;
+            if (i + 1 < cnt) o[i + 1] = v.y;
+            if (i + 2 < cnt) o[i + 2] = v.z;
+            if (i + 3 < cnt) o[i + 3] = v.w;
+          }
+        }
       }
     }
   } else {
-    const int64_t chunk = (int64_t)a.chunk_tiles * kTileTokens;
-    for (int64_t item = wave; item < a.n_items; item += nwaves) {
-      const int r = (int)(item % a.rows);
-      const int64_t c0 = (item / a.rows) * chunk;
-      if (c0 >= a.ld) continue;
-      const int64_t c1 = min(c0 + chunk, a.ld);
-      const int64_t n = row_steps(a, src, r, c0 == 0);
-      const int64_t s0 = c0 / kTileTokens;
-      const int64_t s1 = min(s0 + a.chunk_tiles, n);
-      if (s1 > s0) scan_segment<F>(a, src, r, s0, (int)(s1 - s0), sb);
-      if (!a.skip_tail) fill_neg_inf(a.logits + (int64_t)r * a.ld, max(c0, s1 * kTileTokens), c1);
+    // too long for LDS: each wave an equal part of the range, in stored slice segments
+    const uint64_t wbeg = beg + (end - beg) * wib / kBalWaves, wend = beg + (end - beg) * (wib + 1) / kBalWaves;
+    float* sl = buf + wib * kWave * kTileTokens;
+    for (int p = 0; p < np; ++p) {
+      const uint64_t ps = beg + P.off[p], pe = ps + P.len[p];
+      const uint64_t lo = max(ps, wbeg), hi = min(pe, wend);
+      for (uint64_t s0 = lo; s0 < hi; s0 += kWave) {
+        const int n = (int)min((uint64_t)kWave, hi - s0);
+        scan_segment<F>(a, src, P.r[p], (int64_t)(s0 - ps) + P.rs0[p], n, sl);
+      }
+    }
+  }
+
+  if constexpr (SELECT) {
+    static_assert(sizeof(StepTab) >= kSelFineBins * 2, "the fine histogram reuses the step table");
+    uint32_t* hf = (uint32_t*)&T;
+    __syncthreads();
+    // f(scores of part p): in LDS, or in the spill rows. Two calls, so that each inlined
+    // copy reads through a pointer of known memory (a pointer that may be either takes
+    // generic loads, which wait like global ones)
+    auto with_scores = [&](int p, auto&& f) __attribute__((always_inline)) {
+      if (resident) f(buf + P.off[p] * kTileTokens);
+      else f(st.spill + (int64_t)P.r[p] * a.ld + (int64_t)P.rs0[p] * kTileTokens);
+    };
+    auto row_first = [&](int p) -> uint64_t { return beg + P.off[p] - P.rs0[p]; };
+    // the row of part p spans workgroups b_lo..b_hi; returns how many of them hold steps
+    // (with fewer steps than workgroups some hold none, and every other one holds one step)
+    auto span = [&](int p, int64_t& b_lo, int64_t& b_hi) -> int64_t {
+      const uint64_t acc_r = row_first(p);
+      b_lo = sel_block_of(acc_r, total, B);
+      b_hi = sel_block_of(acc_r + P.rlen[p] - 1, total, B);
+      return total >= (uint64_t)B ? b_hi - b_lo + 1 : (int64_t)P.rlen[p];
+    };
+    // publish the histograms of the shared first and last rows, then count this workgroup
+    for (int which = 0; which < 2; ++which) {
+      const int p = which == 0 ? 0 : np - 1;
+      if (np == 0 || (which == 1 && np == 1)) break;
+      int64_t b_lo, b_hi;
+      const int64_t nb = span(p, b_lo, b_hi);
+      if (nb <= 1 || nb > kSelMaxSpan) continue;
+      with_scores(p, [&](const float* sc) { sel_hist(sc, (int64_t)P.len[p] * kTileTokens, st.gshift, hf, hc); });
+      uint32_t* slot = st.slots + (b * 2 + which) * (int64_t)kSelSlotWords;
+      for (int i = tid; i < kSelFineBins / 2; i += kBalThreads) atomic_st(slot + i, hf[i]);
+      for (int i = tid; i < kSelCoarseBins; i += kBalThreads) atomic_st(slot + kSelFineBins / 2 + i, hc[i]);
+      __builtin_amdgcn_s_waitcnt(0);  // the slot is written before the workgroup counts itself
+      __syncthreads();
+      if (tid == 0)
+        (void)__hip_atomic_fetch_add(st.arrive + P.r[p], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int p = 0; p < np; ++p) {
+      const int r = P.r[p];
+      int64_t b_lo, b_hi;
+      const int64_t nb = span(p, b_lo, b_hi);
+      const int64_t n_ent = (int64_t)P.len[p] * kTileTokens;
+      if (nb == 1) {
+        // the whole row is here
+        with_scores(p, [&](const float* sc) { sel_hist(sc, n_ent, st.gshift, hf, hc); });
+        if (wib == 0) {
+          int cbin;
+          uint32_t above, T2 = 1u;
+          if (sel_cut_coarse(
+                  (uint32_t)st.k,
+                  [&](uint32_t (&c)[4]) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) c[j] = hc[kSelCoarseBins - 1 - 4 * lane - j];
+                  },
+                  cbin, above))
+            T2 = sel_cut_fine((uint32_t)st.k, cbin, above, [&](int j) {
+              const int f = cbin * 16 + j;
+              return (hf[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
+            });
+          if (lane == 0) {
+            s_T = T2;
+            s_ok = 1;
+          }
+        }
+      } else if (nb <= kSelMaxSpan && (p == 0 || p == np - 1)) {
+        if (tid == 0) s_ok = st.wait_ticks > 0 && sel_wait(st, r, sbase[p == 0 ? 0 : 1], nb);
+        // the row's slots: slot 1 of a workgroup where the row starts inside the range (it is
+        // that range's last row), slot 0 where it covers the range's start
+        const uint64_t acc_r = row_first(p);
+        auto bbeg = [&](int64_t bb) -> uint64_t { return total * (uint64_t)bb / (uint64_t)B; };
+        auto slot_of = [&](int64_t bb) -> const uint32_t* {
+          return st.slots + (bb * 2 + (acc_r > bbeg(bb) ? 1 : 0)) * (int64_t)kSelSlotWords;
+        };
+        const int nbb = (int)(b_hi - b_lo + 1);  // the workgroups b_lo..b_hi, some maybe without steps
+        for (int i = tid; i < kSelCoarseBins; i += kBalThreads) hc[i] = 0u;
+        if (tid < 16) s_f16[tid] = 0u;
+        __syncthreads();
+        if (s_ok) {
+          // coarse bins summed over the slots, all loads of a thread issued together
+          constexpr int kU = 8;
+          for (int base = 0; base < nbb * kSelCoarseBins; base += kU * kBalThreads) {
+            uint32_t v[kU];
+            int bin[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+              const int i = base + u * kBalThreads + tid;
+              v[u] = 0u;
+              bin[u] = i % kSelCoarseBins;
+              const int64_t bb = b_lo + i / kSelCoarseBins;
+              if (i < nbb * kSelCoarseBins && bbeg(bb + 1) > bbeg(bb))
+                v[u] = atomic_ld(slot_of(bb) + kSelFineBins / 2 + bin[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+              if (v[u]) atomicAdd(&hc[bin[u]], v[u]);
+          }
+        }
+        lds_barrier();
+        if (wib == 0) {
+          int cbin = -1;
+          uint32_t above = 0;
+          const bool cut = s_ok && sel_cut_coarse(
+                                       (uint32_t)st.k,
+                                       [&](uint32_t (&c)[4]) {
+#pragma unroll
+                                         for (int j = 0; j < 4; ++j) c[j] = hc[kSelCoarseBins - 1 - 4 * lane - j];
+                                       },
+                                       cbin, above);
+          if (lane == 0) {
+            s_cbin = cut ? cbin : -1;
+            s_above = above;
+          }
+        }
+        lds_barrier();
+        const int cbin = s_cbin;
+        if (cbin >= 0) {
+          // the 16 fine bins of the coarse bin, summed over the slots: one load per thread
+          for (int i = tid; i < 16 * nbb; i += kBalThreads) {
+            const int64_t bb = b_lo + i / 16;
+            const int f = cbin * 16 + i % 16;
+            if (bbeg(bb + 1) > bbeg(bb)) {
+              const uint32_t w = atomic_ld(slot_of(bb) + (f >> 1));
+              const uint32_t v = (w >> (16 * (f & 1))) & 0xFFFFu;
+              if (v) atomicAdd(&s_f16[i % 16], v);
+            }
+          }
+        }
+        lds_barrier();
+        if (tid < kWave) {
+          const uint32_t T2 = cbin >= 0 ? sel_cut_fine((uint32_t)st.k, cbin, s_above, [&](int j) { return s_f16[j]; })
+                                        : 1u;
+          if (lane == 0) s_T = T2;
+        }
+      } else {
+        if (tid == 0) {
+          s_T = 1u;  // spans too many workgroups: every entry survives
+          s_ok = 0;
+        }
+      }
+      lds_barrier();
+      uint32_t cnt = 0;
+      with_scores(p, [&](const float* sc) {
+        cnt = sel_filter(sc, n_ent, (int64_t)P.rs0[p] * kTileTokens, s_T,
+                         st.surv + (int64_t)(beg + P.off[p]) * kTileTokens, wsum);
+      });
+      if (tid == 0) st.seg_info[beg + P.off[p]] = cnt | (s_ok ? 0u : 0x80000000u);
+      lds_barrier();
+    }
+  } else if (!a.skip_tail) {
+    // -inf past each row's scored steps, in 4096-column pieces spread over all waves
+    constexpr int64_t kFill = 4096;
+    const int64_t pieces = (a.ld + kFill - 1) / kFill;
+    for (int64_t it = wave; it < pieces * a.rows; it += nwaves) {
+      const int r = (int)(it % a.rows);
+      const int64_t f0 = (it / a.rows) * kFill;
+      const int64_t from = row_steps(a, src, r, false) * kTileTokens;
+      fill_neg_inf(a.logits + (int64_t)r * a.ld, max(f0, from), min(f0 + kFill, a.ld));
     }
   }
 }
@@ -521,26 +1107,48 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(ScanCommon a, Src src) {
 // ------------------------------------------------------------------ launcher
 
 // Launch shape: the grid holds exactly the workgroups that are resident at once (from
-// the occupancy of each kernel instance), so no workgroup starts late and becomes a
-// tail.
-template <int F, class Src, bool BALANCED>
-static int resident_blocks_per_cu() {
-  static std::once_flag once;
-  static int n = 1;
-  std::call_once(once, [] {
-    int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)scan_kernel<F, Src, BALANCED>, kBlock, 0) ==
-            hipSuccess &&
-        b > 0)
-      n = b;
-  });
-  return n;
+// the occupancy of each kernel instance on the current device), so no workgroup starts
+// late and becomes a tail.
+enum SchedKind { SCHED_ITEMS = 0, SCHED_BALANCED = 1, SCHED_SELECT = 2 };
+
+template <int F, class Src, int KIND>
+static const void* scan_fn() {
+  if constexpr (KIND == SCHED_ITEMS) return (const void*)scan_items_kernel<F, Src>;
+  else return (const void*)scan_bal_kernel<F, Src, KIND == SCHED_SELECT>;
 }
 
-template <int F, class Src, bool BALANCED>
+template <int KIND>
+constexpr int sched_threads() {
+  return KIND == SCHED_ITEMS ? kBlock : kBalThreads;
+}
+
+template <int F, class Src, int KIND>
+static int resident_blocks_per_cu() {
+  static std::mutex mu;
+  static int cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, scan_fn<F, Src, KIND>(), sched_threads<KIND>(), 0) !=
+            hipSuccess ||
+        b <= 0)
+      b = 1;
+    cache[dev] = b;
+  }
+  return cache[dev];
+}
+
+template <int F, class Src, int KIND>
+static int64_t sched_blocks() {
+  return (int64_t)device_cu_count() * resident_blocks_per_cu<F, Src, KIND>();
+}
+
+template <int F, class Src, int KIND>
 static hipError_t run_sched(const ScoreCall& c, const Src& src, hipStream_t stream) {
-  const int cus = device_cu_count();
-  const int64_t waves_total = (int64_t)cus * resident_blocks_per_cu<F, Src, BALANCED>() * (kBlock / kWave);
+  int64_t blocks = sched_blocks<F, Src, KIND>();
+  const int64_t waves_total = blocks * (sched_threads<KIND>() / kWave);
   const int64_t tiles_per_row = (c.ld + kTileTokens - 1) / kTileTokens;
   const int64_t tiles = tiles_per_row * c.rows;
   int64_t ct = tiles / (2 * waves_total);
@@ -561,19 +1169,29 @@ static hipError_t run_sched(const ScoreCall& c, const Src& src, hipStream_t stre
   a.skip_tail = c.skip_tail;
   a.zero = c.zero;
   a.zero_words = c.zero_words;
-  int64_t blocks = waves_total / (kBlock / kWave);
-  if (!BALANCED) {
+  a.lens_out = c.lens_out;
+  if constexpr (KIND == SCHED_ITEMS) {
     const int64_t need = (a.n_items + (kBlock / kWave) - 1) / (kBlock / kWave);
     if (blocks > need) blocks = need;
+    hipLaunchKernelGGL((scan_items_kernel<F, Src>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a, src);
+  } else if constexpr (KIND == SCHED_SELECT) {
+    a.logits = c.sel->spill;
+    hipLaunchKernelGGL((scan_bal_kernel<F, Src, true>), dim3((unsigned)blocks), dim3(kBalThreads), 0, stream, a, src,
+                       *c.sel);
+  } else {
+    hipLaunchKernelGGL((scan_bal_kernel<F, Src, false>), dim3((unsigned)blocks), dim3(kBalThreads), 0, stream, a,
+                       src, SelectState{});
   }
-  hipLaunchKernelGGL((scan_kernel<F, Src, BALANCED>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a, src);
   return hipGetLastError();
 }
 
 template <int F, class Src>
 static hipError_t run(const ScoreCall& c, const Src& src, hipStream_t stream) {
-  if (c.rows <= kBalancedMaxRows) return run_sched<F, Src, true>(c, src, stream);
-  return run_sched<F, Src, false>(c, src, stream);
+  if (c.rows <= kBalancedMaxRows) {
+    if (c.sel) return run_sched<F, Src, SCHED_SELECT>(c, src, stream);
+    return run_sched<F, Src, SCHED_BALANCED>(c, src, stream);
+  }
+  return run_sched<F, Src, SCHED_ITEMS>(c, src, stream);
 }
 
 template <class Src>
@@ -606,17 +1224,37 @@ hipError_t launch_score(const ScoreCall& c, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+int64_t select_scan_blocks(const ScoreCall& c) {
+  if (c.rows <= 0 || c.rows > kBalancedMaxRows) return 0;
+  if (c.source == SRC_DENSE && prefill_applies(c)) return 0;
+  const bool paged = c.source == SRC_PAGED, sparse = c.source == SRC_SPARSE;
+  switch (c.fmt) {
+    case FMT_BF16:
+      if (paged || sparse) return 0;
+      return sched_blocks<FMT_BF16, DenseSrc, SCHED_SELECT>();
+    case FMT_FP8:
+      return paged ? sched_blocks<FMT_FP8, PagedSrc, SCHED_SELECT>()
+                   : sparse ? sched_blocks<FMT_FP8, SparseSrc, SCHED_SELECT>()
+                            : sched_blocks<FMT_FP8, DenseSrc, SCHED_SELECT>();
+    case FMT_MXFP4:
+      return paged ? sched_blocks<FMT_MXFP4, PagedSrc, SCHED_SELECT>()
+                   : sparse ? sched_blocks<FMT_MXFP4, SparseSrc, SCHED_SELECT>()
+                            : sched_blocks<FMT_MXFP4, DenseSrc, SCHED_SELECT>();
+  }
+  return 0;
+}
+
 // ------------------------------------------------------------------ per-device state
 
 __device__ unsigned g_device_errors;
 
 static std::mutex g_mu;
-static unsigned* g_err_ptr[64];
-static int g_cus[64];
+static unsigned* g_err_ptr[kMaxDevices];
+static int g_cus[kMaxDevices];
 
 unsigned* device_error_word() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_err_ptr[dev]) {
     void* p = nullptr;
@@ -628,7 +1266,7 @@ unsigned* device_error_word() {
 
 int device_cu_count() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_cus[dev]) {
     int n = 0;

@@ -65,10 +65,6 @@ __device__ __forceinline__ int64_t row_len(const TopkCall& a, int r) {
   return n;
 }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 // Appends item[j] for every take[j] of every lane (U entries per lane) to an LDS list
 // with one LDS atomic per wave; entries past cap are dropped (callers size the lists
 // or detect the overflow from the count). Every lane of the wave must call it.
@@ -428,14 +424,14 @@ __device__ void sort_write_e(const TopkCall& a, int r, const Key& key, int cnt, 
   write_sorted<NT, E>(a, r, x);
 }
 
-// Block-wide: sorts the cnt (<= kMaxK) selected keys key(i) and writes row r; xch
-// holds kMaxK keys.
-template <int NT, class Key>
+// Block-wide: sorts the cnt (<= CAP) keys key(i) and writes the first k of them to row
+// r; xch holds CAP keys.
+template <int NT, class Key, int CAP = kMaxK>
 __device__ void sort_and_write(const TopkCall& a, int r, const Key& key, int cnt, uint64_t* xch) {
-  static_assert(NT * 4 >= kMaxK, "sort_and_write: at most four keys per thread");
+  static_assert(NT * 4 >= CAP, "sort_and_write: at most four keys per thread");
   if (cnt <= NT) {
     sort_write_e<NT, 1>(a, r, key, cnt, xch);
-  } else if constexpr (NT * 2 >= kMaxK) {
+  } else if constexpr (NT * 2 >= CAP) {
     sort_write_e<NT, 2>(a, r, key, cnt, xch);
   } else {
     if (cnt <= 2 * NT)
@@ -456,17 +452,16 @@ struct SortShared {
   uint32_t sums[16];
 };
 
-// Block-wide: writes the cnt (<= kMaxK) selected keys key(i) of row r in selection
-// order. The keys are spread over kBuckets buckets linear in the score between the
-// smallest and the largest selected score (a monotone map, so the buckets are in
-// order); an entry's position is the number of entries in higher buckets plus the
-// number of larger keys in its own bucket. counts: kBuckets words of LDS (kMaxK
-// keys), 16-byte aligned; tmp: kMaxK keys of LDS. Neither may overlap what key(i)
-// reads.
-template <int NT, class Key>
+// Block-wide: sorts the cnt (<= CAP) keys key(i) and writes the first k of them to row r
+// in selection order. The keys are spread over kBuckets buckets linear in the score
+// between the smallest and the largest key's score (a monotone map, so the buckets are in
+// order); an entry's position is the number of entries in higher buckets plus the number
+// of larger keys in its own bucket. counts: kBuckets words of LDS, 16-byte aligned; tmp:
+// CAP keys of LDS. Neither may overlap what key(i) reads.
+template <int NT, class Key, int CAP = kMaxK>
 __device__ void bucket_sort_write(const TopkCall& a, int r, const Key& key, int cnt, uint32_t* counts, uint64_t* tmp,
                                   SortShared& ss) {
-  constexpr int E = kMaxK / NT;
+  constexpr int E = CAP / NT;
   constexpr int per = kBuckets / NT;
   constexpr int waves = NT / kWave;
   const int tid = threadIdx.x;
@@ -536,7 +531,7 @@ __device__ void bucket_sort_write(const TopkCall& a, int r, const Key& key, int 
     if (lane_id() == kWave - 1) ss.sums[tid / kWave] = incl;
     __syncthreads();
     if (ss.big) {
-      sort_and_write<NT>(a, r, key, cnt, tmp);
+      sort_and_write<NT, Key, CAP>(a, r, key, cnt, tmp);
       return;
     }
     uint32_t off = incl - sum;
@@ -975,6 +970,164 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(TopkCall a,
     bucket_sort_write<NT>(a, r, key, cnt, (uint32_t*)cand, cand + kBuckets / 2, ss);
   else
     write_list<NT>(a, r, key, cnt);
+}
+
+// ------------------------------------------------------------------ one-pass selection: finish
+//
+// The scan's select mode leaves, for every segment (the part of a row one scan workgroup
+// scored), the segment's survivors as selection keys at surv[first step * 64 ...] and
+// their count at seg_info[first step]. The segments of row r are found again from the
+// balanced split: workgroups w_lo..w_hi cover the row's steps [acc[r], acc[r + 1]),
+// workgroup w holding steps [total w / W, total (w + 1) / W). One workgroup per row
+// gathers the survivors, selects the k largest keys exactly and writes the row.
+
+struct SelFinishArgs {
+  const int64_t* acc;
+  const uint32_t* seg_info;
+  const uint64_t* surv;
+  int64_t waves;
+};
+
+// Survivors up to this count are sorted whole (the first k written) instead of selected.
+constexpr int kFinishSortCap = 4096;
+
+__global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(TopkCall a, SelFinishArgs f) {
+  constexpr int NT = kFinishThreads;
+  constexpr int PER = kSelMaxBlocks / NT;
+  static_assert(kSelMaxBlocks % NT == 0, "segments per thread");
+  static_assert(kMaxK * 2 >= kBuckets && 2 * kFinishSortCap <= kCandCap, "sort scratch in sel and cand");
+  __shared__ __align__(16) uint64_t sel[kMaxK];  // the selected keys, or the sort's bucket counts
+  __shared__ __align__(16) uint64_t cand[kCandCap];  // survivors, then the sort's scratch
+  __shared__ uint32_t soff[kSelMaxBlocks + 1];          // survivors before each segment
+  __shared__ RadixShared sh;
+  __shared__ uint32_t rh[256];
+  __shared__ SortShared ss;
+  __shared__ uint32_t count;
+  __shared__ uint32_t wsum[NT / kWave];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int r = blockIdx.x;
+  const uint64_t total = (uint64_t)f.acc[a.rows];
+  const uint64_t s0 = (uint64_t)f.acc[r], s1 = (uint64_t)f.acc[r + 1];
+  if (s1 <= s0) {
+    write_list<NT>(a, r, [](int) { return 0ull; }, 0);
+    return;
+  }
+  const uint64_t W = (uint64_t)f.waves;
+  const int64_t w_lo = (int64_t)(((s0 + 1) * W - 1) / total);
+  const int64_t w_hi = (int64_t)((s1 * W - 1) / total);  // the wave of step s1 - 1
+  const int nseg = (int)min(w_hi - w_lo + 1, (int64_t)kSelMaxBlocks);
+  auto seg_lo = [&](int i) -> uint64_t { return max(total * (uint64_t)(w_lo + i) / W, s0); };
+  auto seg_hi = [&](int i) -> uint64_t { return min(total * (uint64_t)(w_lo + i + 1) / W, s1); };
+
+  // survivors of each segment (workgroups without steps have none) and their exclusive prefix
+  uint32_t c[PER], t = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid * PER + j;
+    c[j] = 0;
+    if (i < nseg) {
+      const uint64_t lo = seg_lo(i);
+      if (lo < seg_hi(i)) c[j] = f.seg_info[lo] & 0x7FFFFFFFu;
+    }
+    t += c[j];
+  }
+  const uint32_t incl = wave_inclusive_sum(t);
+  if (lane == kWave - 1) wsum[tid / kWave] = incl;
+  __syncthreads();
+  uint32_t off = incl - t, S = 0;
+#pragma unroll
+  for (int wv = 0; wv < NT / kWave; ++wv) {
+    const uint32_t v = wsum[wv];
+    off += wv < tid / kWave ? v : 0u;
+    S += v;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    soff[tid * PER + j] = off;
+    off += c[j];
+  }
+  if (tid == 0) {
+    soff[kSelMaxBlocks] = S;
+    count = 0;
+  }
+  __syncthreads();
+
+  // survivor i of the row: entry i - soff[j] of the segment j with soff[j] <= i < soff[j + 1]
+  auto surv_at = [&](int64_t i) -> uint64_t {
+    int lo = 0, hi = nseg;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (soff[mid] <= (uint32_t)i) lo = mid;
+      else hi = mid;
+    }
+    return f.surv[seg_lo(lo) * kTileTokens + (i - soff[lo])];
+  };
+  int cnt;
+  if (a.sorted && S <= (uint32_t)kFinishSortCap) {
+    // few enough to sort them all and keep the first k: no selection pass
+    constexpr int kPer = kFinishSortCap / NT;
+    uint64_t v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = (uint32_t)(j * NT + tid);
+      v[j] = i < S ? surv_at(i) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = (uint32_t)(j * NT + tid);
+      if (i < S) cand[i] = v[j];
+    }
+    __syncthreads();
+    auto keyc = [&](int i) -> uint64_t { return cand[i]; };
+    bucket_sort_write<NT, decltype(keyc), kFinishSortCap>(a, r, keyc, (int)S, (uint32_t*)sel, cand + kFinishSortCap,
+                                                          ss);
+    return;
+  }
+  if (S <= (uint32_t)kCandCap) {
+    // into LDS, all threads at once (the loads of a thread are independent)
+    constexpr int kPer = kCandCap / NT;
+    uint64_t v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = (uint32_t)(j * NT + tid);
+      v[j] = i < S ? surv_at(i) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = (uint32_t)(j * NT + tid);
+      if (i < S) cand[i] = v[j];
+    }
+    __syncthreads();
+    if (S <= (uint32_t)a.k) {
+      for (uint32_t i = tid; i < S; i += NT) sel[i] = cand[i];
+      cnt = (int)S;
+    } else {
+      auto get = [&](int64_t i) -> uint64_t { return cand[i]; };
+      const uint64_t thr = radix_threshold<NT>(get, S, (uint32_t)a.k, sh, rh);
+      gather_at_least<NT, uint64_t>(get, get, S, thr, sel, &count, (uint32_t)kMaxK);
+      cnt = a.k;
+    }
+  } else {
+    // more survivors than LDS holds (e.g. many equal scores): select from the regions
+    auto get = [&](int64_t i) -> uint64_t { return surv_at(i); };
+    const uint64_t thr = radix_threshold<NT>(get, S, (uint32_t)a.k, sh, rh);
+    gather_at_least<NT, uint64_t>(get, get, S, thr, sel, &count, (uint32_t)kMaxK);
+    cnt = a.k;
+  }
+  __syncthreads();
+  auto key = [&](int i) -> uint64_t { return sel[i]; };
+  if (a.sorted)
+    bucket_sort_write<NT>(a, r, key, cnt, (uint32_t*)cand, cand + kBuckets / 2, ss);
+  else
+    write_list<NT>(a, r, key, cnt);
+}
+
+hipError_t launch_select_finish(const TopkCall& t, const SelectState& s, int64_t blocks, hipStream_t stream) {
+  if (t.rows <= 0) return hipSuccess;
+  SelFinishArgs f{s.acc, s.seg_info, s.surv, blocks};
+  hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)t.rows), dim3(kFinishThreads), 0, stream, t, f);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ host side

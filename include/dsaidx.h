@@ -79,7 +79,10 @@ typedef enum idx_dtype {
 } idx_dtype;
 
 /* idx_topk / idx_select flags */
-#define IDX_TOPK_UNSORTED 1u /* return the selected set in no particular order */
+#define IDX_TOPK_UNSORTED 1u    /* return the selected set in no particular order */
+#define IDX_SELECT_NO_CUTOFF 2u /* idx_select only: skip the sampled cutoff of the one-pass
+                                   selection and finish every scored entry exactly (the
+                                   same result, slower; for checking the exact finish) */
 
 /* ------------------------------------------------------------------ scores */
 

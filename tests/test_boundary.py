@@ -173,16 +173,44 @@ def _problem(**kw):
     return D.idx_problem(**a)
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def _select_layouts(L, rows, width):
+    """Workspace of the two idx_select layouts the header describes: the one-pass selection
+    (1024 workgroups x 2 histogram slots of 2048 + 256 words, a counter per row, rows + 1
+    step offsets, a count per 64-column step, 64 keys of 8 bytes per step, spill score
+    rows) and scores then top-k (score rows, scored lengths, the top-k workspace); ldw =
+    width rounded up to 64."""
+    ldw = (width + 63) // 64 * 64
+    steps = rows * (ldw // 64)
+    one = sum(_r256(b) for b in (1024 * 2 * 2304 * 4, rows * 8, (rows + 1) * 8, steps * 4, steps * 64 * 8,
+                                  rows * ldw * 4))
+    two = _r256(rows * ldw * 4) + _r256(rows * 4) + L.idx_topk_workspace(rows, width, 2048)
+    return one, two
+
+
 def test_select_workspace_sizes(L):
-    # the score matrix (rows padded to 64 columns, 256-byte aligned) plus the top-k workspace
+    # fewer than 8 rows: scores then top-k only
     p = _problem(max_cols=4000)
-    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 4032 * 4
-    p = _problem(mode=D.IDX_MODE_PAGED, page_size=64, block_table=BT, bt_rows=4, bt_ld=2048,
+    _, two = _select_layouts(L, 4, 4000)
+    assert L.idx_select_workspace(C.byref(p), 2048) == two
+    p = _problem(rows=16, max_cols=4000)
+    one, two = _select_layouts(L, 16, 4000)
+    assert L.idx_select_workspace(C.byref(p), 2048) == max(one, two)
+    p = _problem(rows=64, mode=D.IDX_MODE_PAGED, page_size=64, block_table=BT, bt_rows=64, bt_ld=2048,
                  seq_lens=SL)
-    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 131072 * 4 + L.idx_topk_workspace(4, 131072, 2048)
-    p = _problem(mode=D.IDX_MODE_SPARSE_BLOCKS, k_dtype=D.IDX_MXFP4, cand_blocks=CAND, cand_ld=64,
+    one, two = _select_layouts(L, 64, 131072)
+    assert L.idx_select_workspace(C.byref(p), 2048) == max(one, two)
+    p = _problem(rows=64, mode=D.IDX_MODE_SPARSE_BLOCKS, k_dtype=D.IDX_MXFP4, cand_blocks=CAND, cand_ld=64,
                  n_cols=NC, block_size=128)
-    assert L.idx_select_workspace(C.byref(p), 2048) == 4 * 8192 * 4
+    one, two = _select_layouts(L, 64, 8192)
+    assert L.idx_select_workspace(C.byref(p), 2048) == max(one, two)
+    # a prefill chunk (dense fp8, >= 256 rows) takes the tiled kernel and the two-pass layout
+    p = _problem(rows=300, max_cols=5000)
+    _, two = _select_layouts(L, 300, 5000)
+    assert L.idx_select_workspace(C.byref(p), 2048) == two
 
 
 SELECT_CASES = [
@@ -195,6 +223,7 @@ SELECT_CASES = [
     ("out_ld < k", _problem(), dict(old=100), ARG),
     ("dense max_cols zero", _problem(max_cols=0), dict(), ARG),
     ("unknown mode", _problem(mode=7), dict(), ARG),
+    ("unknown flag", _problem(), dict(flags=4), ARG),
     ("paged page 16", _problem(mode=D.IDX_MODE_PAGED, page_size=16, block_table=BT, bt_rows=4,
                                 bt_ld=4, seq_lens=SL), dict(), UNS),
     ("paged table rows", _problem(mode=D.IDX_MODE_PAGED, page_size=64, block_table=BT, bt_rows=2,
