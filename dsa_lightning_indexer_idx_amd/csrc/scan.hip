@@ -517,10 +517,21 @@ __global__ __launch_bounds__(kBlock) void scan_items_kernel(ScanCommon a, Src sr
 // one-pass selection below); a longer range is split evenly between the waves, each
 // scoring its part in LDS-slice segments that are stored as they complete.
 
-constexpr int kBalThreads = 512;
-constexpr int kBalWaves = kBalThreads / kWave;
+// Threads of a balanced workgroup: 8 waves, or 12 for MXFP4 keys, whose steps move half
+// the bytes of fp8 ones and want more waves in flight (their kernels fit the 168 VGPRs
+// that three waves per SIMD leave).
+template <int F>
+constexpr int bal_threads() {
+  return F == FMT_MXFP4 ? 768 : 512;
+}
+constexpr int kBalMaxWaves = 768 / kWave;
 constexpr int kUnit = 2;
-constexpr int kBlockSteps = kBalWaves * kWave;   // 512 steps, 128 KiB of scores
+constexpr int kBlockSteps = 512;   // steps a workgroup keeps in LDS: 128 KiB of scores
+// Steps of a wave's LDS slice when the range does not fit: the slices share the buffer.
+template <int NW>
+constexpr int bal_slice_steps() {
+  return kBlockSteps / NW >= kWave ? kWave : kBlockSteps / NW >= 32 ? 32 : 16;
+}
 constexpr int kMaxParts = kBalancedMaxRows;      // rows one range can meet
 
 // The rows meeting a workgroup's range, in order (built by wave 0).
@@ -662,30 +673,87 @@ __device__ __forceinline__ int64_t sel_block_of(uint64_t s, uint64_t total, int6
   return (int64_t)(((s + 1) * (uint64_t)B - 1) / total);
 }
 
+// One lane's float from the lane (lane ^ 1) or (lane ^ 2): DPP within each group of four.
+template <int X>
+__device__ __forceinline__ float quad_xor(float v) {
+  static_assert(X == 1 || X == 2, "quad xor 1 or 2");
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// Block-wide, groups of 2^GS columns: adds the order key of each group's largest score
+// (fmaxf passes over NaN) to the fine histogram. Consecutive lanes read consecutive
+// float4s, four per thread in flight; a group of 8 or 16 columns spans 2 or 4 neighbouring
+// lanes, whose butterfly leaves its largest score in each of them, so that lane j of a
+// group can count the group of load j: every histogram add then has all lanes busy. n_ent
+// is a multiple of 64, so a group's lanes are all in range or all out.
+template <int GS>
+__device__ __forceinline__ void sel_hist_groups(const float* sc, int64_t n_ent, uint32_t* hf) {
+  constexpr int kU = 4;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int64_t stride = 4 * (int64_t)blockDim.x;
+  auto add = [&](float m) __attribute__((always_inline)) {
+    const uint32_t mk = order_key(m);
+    if (mk) {
+      const uint32_t fb = mk >> 20;
+      atomicAdd(&hf[fb >> 1], 1u << (16 * (fb & 1)));
+    }
+  };
+  for (int64_t b0 = 0; b0 < n_ent; b0 += kU * stride) {
+    float4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = b0 + u * stride + 4 * tid;
+      v[u] = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
+      if (i < n_ent) v[u] = *(const float4*)(sc + i);
+    }
+    if constexpr (GS == 0) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        add(v[u].x);
+        add(v[u].y);
+        add(v[u].z);
+        add(v[u].w);
+      }
+    } else if constexpr (GS == 1) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        add(fmaxf(v[u].x, v[u].y));
+        add(fmaxf(v[u].z, v[u].w));
+      }
+    } else {
+      constexpr int R = 1 << (GS - 2);  // lanes per group
+      float m[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        m[u] = fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w));
+        if constexpr (GS >= 3) m[u] = fmaxf(m[u], quad_xor<1>(m[u]));
+        if constexpr (GS >= 4) m[u] = fmaxf(m[u], quad_xor<2>(m[u]));
+      }
+      const int j = lane & (R - 1);
+#pragma unroll
+      for (int u0 = 0; u0 < kU; u0 += R) {
+        float x = m[u0];
+#pragma unroll
+        for (int q = 1; q < R; ++q) x = j == q ? m[u0 + q] : x;
+        add(x);
+      }
+    }
+  }
+}
+
 // Block-wide: histogram (LDS: hf fine pairs, hc coarse) of the group maxima of the
 // n_ent scores at sc (LDS or global; group i = entries i 2^gs .. (i + 1) 2^gs - 1).
 __device__ __forceinline__ void sel_hist(const float* sc, int64_t n_ent, int gs, uint32_t* hf, uint32_t* hc) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kSelFineBins / 2; i += blockDim.x) hf[i] = 0u;
   lds_barrier();
-  const int64_t ng = n_ent >> gs;
-  for (int64_t i = tid; i < ng; i += blockDim.x) {
-    // the group's largest score (fmaxf passes over NaN), then its order key
-    const float* g = sc + (i << gs);
-    float m = -__builtin_inff();
-    if (gs >= 2) {
-      for (int e = 0; e < (1 << gs); e += 4) {
-        const float4 v = *(const float4*)(g + e);
-        m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-      }
-    } else {
-      for (int e = 0; e < (1 << gs); ++e) m = fmaxf(m, g[e]);
-    }
-    const uint32_t mk = order_key(m);
-    if (mk) {
-      const uint32_t fb = mk >> 20;
-      atomicAdd(&hf[fb >> 1], 1u << (16 * (fb & 1)));
-    }
+  switch (gs) {
+    case 0: sel_hist_groups<0>(sc, n_ent, hf); break;
+    case 1: sel_hist_groups<1>(sc, n_ent, hf); break;
+    case 2: sel_hist_groups<2>(sc, n_ent, hf); break;
+    case 3: sel_hist_groups<3>(sc, n_ent, hf); break;
+    default: sel_hist_groups<4>(sc, n_ent, hf); break;
   }
   lds_barrier();
   for (int c = tid; c < kSelCoarseBins; c += blockDim.x) {
@@ -761,58 +829,64 @@ __device__ __forceinline__ bool sel_wait(const SelectState& st, int r, unsigned 
 }
 
 // Block-wide: the n_ent scores at sc (columns col0 ..) at or above the cut T, as
-// selection keys to out (each wave's in one contiguous run); returns their count. An
-// entry's order key is at least T exactly when its score is at least T's value (the order
-// key is monotone; NaN compares false, -0 == +0); T = 1 keeps every present entry (-inf
-// and NaN excluded).
+// selection keys to out; returns their count. An entry's order key is at least T exactly
+// when its score is at least T's value (the order key is monotone; NaN compares false,
+// -0 == +0); T = 1 keeps every present entry (-inf and NaN excluded). The entries go in
+// chunks of 64 per thread: a thread marks which of its 64 (the float4s at 4 tid + v
+// stride) survive in a 64-bit mask, the counts are scanned over the block (threads in
+// order), and each thread writes its own survivors, reading back only those. n_ent is a
+// multiple of 64.
 __device__ __forceinline__ uint32_t sel_filter(const float* sc, int64_t n_ent, int64_t col0, uint32_t T,
                                                uint64_t* out, uint32_t* wsum) {
+  constexpr int kV = 16;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   const int nw = blockDim.x / kWave;
-  const int64_t step = 4 * (int64_t)blockDim.x;
+  const int64_t stride = 4 * (int64_t)blockDim.x;
   const float t = T <= 1u ? -__FLT_MAX__ : key_value(T);
-  auto vals = [&](int64_t i) __attribute__((always_inline)) -> float4 {
-    float4 v = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
-    if (i < n_ent) v = *(const float4*)(sc + i);
-    return v;
-  };
-  uint32_t mine = 0;
-  for (int64_t i = 4 * tid; i < n_ent; i += step) {
-    const float4 v = vals(i);
-    mine += (v.x >= t ? 1u : 0u) + (v.y >= t ? 1u : 0u) + (v.z >= t ? 1u : 0u) + (v.w >= t ? 1u : 0u);
-  }
-  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(mine), kWave - 1);
-  lds_barrier();  // wsum may still be read by the previous call
-  if (lane == 0) wsum[wv] = wtot;
-  lds_barrier();
-  uint32_t base = 0, tot = 0;
-  for (int w = 0; w < nw; ++w) {
-    const uint32_t v = wsum[w];
-    base += w < wv ? v : 0u;
-    tot += v;
-  }
-  // the wave's survivors in order of (pass, entry of the lane's four, lane)
-  if (wtot) {
-    for (int64_t i0 = 4 * (int64_t)wv * kWave; i0 < n_ent; i0 += step) {
-      const int64_t i = i0 + 4 * lane;
-      const float4 v = vals(i);
-      const float e[4] = {v.x, v.y, v.z, v.w};
+  uint32_t done = 0;  // survivors of the earlier chunks
+  for (int64_t c0 = 0; c0 < n_ent; c0 += kV * stride) {
+    uint64_t mask = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool take = e[j] >= t;
-        const uint64_t m = __ballot(take);
-        if (take) out[base + lanes_below(m)] = ((uint64_t)order_key(e[j]) << 32) | (uint32_t)(~(uint32_t)(col0 + i + j));
-        base += (uint32_t)__popcll(m);
+    for (int v = 0; v < kV; ++v) {
+      const int64_t i = c0 + v * stride + 4 * tid;
+      if (i < n_ent) {
+        const float4 x = *(const float4*)(sc + i);
+        mask |= (x.x >= t ? 1ull : 0ull) << (4 * v);
+        mask |= (x.y >= t ? 2ull : 0ull) << (4 * v);
+        mask |= (x.z >= t ? 4ull : 0ull) << (4 * v);
+        mask |= (x.w >= t ? 8ull : 0ull) << (4 * v);
       }
     }
+    const uint32_t mine = (uint32_t)__popcll(mask);
+    const uint32_t incl = wave_inclusive_sum(mine);
+    lds_barrier();  // wsum may still be read by the previous chunk or call
+    if (lane == kWave - 1) wsum[wv] = incl;
+    lds_barrier();
+    uint32_t before = incl - mine, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+      const uint32_t v = wsum[w];
+      before += w < wv ? v : 0u;
+      tot += v;
+    }
+    uint64_t* o = out + done + before;
+    while (mask) {
+      const int bit = (int)__builtin_ctzll(mask);
+      mask &= mask - 1;
+      const int64_t i = c0 + (bit >> 2) * stride + 4 * tid + (bit & 3);
+      *o++ = ((uint64_t)order_key(sc[i]) << 32) | (uint32_t)(~(uint32_t)(col0 + i));
+    }
+    done += tot;
   }
-  return tot;
+  return done;
 }
 
 // ------------------------------------------------------------------ balanced kernel
 
 template <int F, class Src, bool SELECT>
-__global__ __launch_bounds__(kBalThreads) void scan_bal_kernel(ScanCommon a, Src src, SelectState st) {
+__global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a, Src src, SelectState st) {
+  constexpr int kBalThreads = bal_threads<F>();
+  constexpr int kBalWaves = kBalThreads / kWave;
+  constexpr int kSlice = bal_slice_steps<kBalWaves>();
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wib = tid / kWave;
@@ -933,12 +1007,12 @@ __global__ __launch_bounds__(kBalThreads) void scan_bal_kernel(ScanCommon a, Src
   } else {
     // too long for LDS: each wave an equal part of the range, in stored slice segments
     const uint64_t wbeg = beg + (end - beg) * wib / kBalWaves, wend = beg + (end - beg) * (wib + 1) / kBalWaves;
-    float* sl = buf + wib * kWave * kTileTokens;
+    float* sl = buf + wib * kSlice * kTileTokens;
     for (int p = 0; p < np; ++p) {
       const uint64_t ps = beg + P.off[p], pe = ps + P.len[p];
       const uint64_t lo = max(ps, wbeg), hi = min(pe, wend);
-      for (uint64_t s0 = lo; s0 < hi; s0 += kWave) {
-        const int n = (int)min((uint64_t)kWave, hi - s0);
+      for (uint64_t s0 = lo; s0 < hi; s0 += kSlice) {
+        const int n = (int)min((uint64_t)kSlice, hi - s0);
         scan_segment<F>(a, src, P.r[p], (int64_t)(s0 - ps) + P.rs0[p], n, sl);
       }
     }
@@ -1117,9 +1191,9 @@ static const void* scan_fn() {
   else return (const void*)scan_bal_kernel<F, Src, KIND == SCHED_SELECT>;
 }
 
-template <int KIND>
+template <int F, int KIND>
 constexpr int sched_threads() {
-  return KIND == SCHED_ITEMS ? kBlock : kBalThreads;
+  return KIND == SCHED_ITEMS ? kBlock : bal_threads<F>();
 }
 
 template <int F, class Src, int KIND>
@@ -1131,7 +1205,7 @@ static int resident_blocks_per_cu() {
   std::lock_guard<std::mutex> lock(mu);
   if (!cache[dev]) {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, scan_fn<F, Src, KIND>(), sched_threads<KIND>(), 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, scan_fn<F, Src, KIND>(), sched_threads<F, KIND>(), 0) !=
             hipSuccess ||
         b <= 0)
       b = 1;
@@ -1148,7 +1222,7 @@ static int64_t sched_blocks() {
 template <int F, class Src, int KIND>
 static hipError_t run_sched(const ScoreCall& c, const Src& src, hipStream_t stream) {
   int64_t blocks = sched_blocks<F, Src, KIND>();
-  const int64_t waves_total = blocks * (sched_threads<KIND>() / kWave);
+  const int64_t waves_total = blocks * (sched_threads<F, KIND>() / kWave);
   const int64_t tiles_per_row = (c.ld + kTileTokens - 1) / kTileTokens;
   const int64_t tiles = tiles_per_row * c.rows;
   int64_t ct = tiles / (2 * waves_total);
@@ -1176,11 +1250,11 @@ static hipError_t run_sched(const ScoreCall& c, const Src& src, hipStream_t stre
     hipLaunchKernelGGL((scan_items_kernel<F, Src>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a, src);
   } else if constexpr (KIND == SCHED_SELECT) {
     a.logits = c.sel->spill;
-    hipLaunchKernelGGL((scan_bal_kernel<F, Src, true>), dim3((unsigned)blocks), dim3(kBalThreads), 0, stream, a, src,
-                       *c.sel);
+    hipLaunchKernelGGL((scan_bal_kernel<F, Src, true>), dim3((unsigned)blocks), dim3(bal_threads<F>()), 0, stream, a,
+                       src, *c.sel);
   } else {
-    hipLaunchKernelGGL((scan_bal_kernel<F, Src, false>), dim3((unsigned)blocks), dim3(kBalThreads), 0, stream, a,
-                       src, SelectState{});
+    hipLaunchKernelGGL((scan_bal_kernel<F, Src, false>), dim3((unsigned)blocks), dim3(bal_threads<F>()), 0, stream,
+                       a, src, SelectState{});
   }
   return hipGetLastError();
 }
