@@ -23,6 +23,7 @@ IDX_TOPK_UNSORTED = 1
 IDX_SELECT_NO_CUTOFF = 2
 IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK, IDX_DEVERR_SLOT = 1, 2, 4, 8
 IDX_HEADS, IDX_DIM, IDX_MAX_K = 64, 128, 2048
+IDX_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
 
@@ -31,7 +32,7 @@ EXPORTS = ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_to
            "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
            "idx_last_error", "idx_version", "idx_device_errors", "idx_kcache_write", "idx_read_probe",
            "idx_candidate_blocks", "idx_candidate_blocks_workspace", "idx_sparse_attn_paged",
-           "idx_sparse_attn_workspace")
+           "idx_sparse_attn_workspace", "idx_select_noalloc")
 
 
 class IdxError(RuntimeError):
@@ -83,6 +84,7 @@ def lib() -> C.CDLL:
         L.idx_topk_workspace.argtypes = [I, I64, I]
         L.idx_topk_workspace.restype = SZ
         L.idx_select.argtypes = [C.POINTER(idx_problem), I, P, P, I64, U32, P, SZ, P]
+        L.idx_select_noalloc.argtypes = [C.POINTER(idx_problem), I, P, P, I64, U32, P]
         L.idx_select_workspace.argtypes = [C.POINTER(idx_problem), I]
         L.idx_select_workspace.restype = SZ
         L.idx_status_string.argtypes = [I]
@@ -466,6 +468,21 @@ def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = 
                             out_idx.shape[1],
                             (0 if sorted else IDX_TOPK_UNSORTED) | (0 if cutoff else IDX_SELECT_NO_CUTOFF),
                             _ptr(workspace), wsb, _stream(stream)))
+    return out_idx, out_val
+
+
+def idx_select_noalloc(problem: Problem, k: int, *, sorted: bool = True, out_idx, out_val=None,
+                       cutoff: bool = True, stream=None):
+    """idx_select on the library's static device scratch (C: idx_select_noalloc): the C call
+    allocates nothing; the caller passes the outputs. Returns (out_idx, out_val)."""
+    import torch
+    rows = problem.rows
+    _rows_out(out_idx, "out_idx", rows, torch.int32, k)
+    if out_val is not None and (_rows_out(out_val, "out_val", rows, torch.float32, k) != out_idx.shape[1]):
+        raise ValueError("out_val must have the shape of out_idx")
+    _check(lib().idx_select_noalloc(C.byref(problem.st), k, _ptr(out_idx), _ptr(out_val), out_idx.shape[1],
+                                    (0 if sorted else IDX_TOPK_UNSORTED) | (0 if cutoff else IDX_SELECT_NO_CUTOFF),
+                                    _stream(stream)))
     return out_idx, out_val
 
 

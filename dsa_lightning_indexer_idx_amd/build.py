@@ -18,7 +18,7 @@ INCLUDE = ROOT / "include"
 LIB = PKG / "libdsaidx.so"
 OBJ = PKG / "_build"
 
-SOURCES = ["api.cpp", "scan.hip", "prefill.hip", "topk.hip", "cand.hip", "attn.hip", "kcache.hip", "probe.hip"]
+SOURCES = ["api.cpp", "scan.hip", "prefill.hip", "topk.hip", "cand.hip", "attn.hip", "kcache.hip", "probe.hip", "noalloc.hip"]
 
 # Device code never uses packed-fp32 instructions (the flag is a device-target
 # feature; the host pass only warns that it does not know it). MFMA results stay in

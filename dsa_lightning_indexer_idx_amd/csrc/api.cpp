@@ -3,6 +3,7 @@
 // argument has passed.
 #include "dsaidx.h"
 #include "launch.h"
+#include "api_internal.h"
 
 #include <cmath>
 
@@ -250,6 +251,115 @@ constexpr int64_t kSelectWaitTicks = 200000;
 
 }  // namespace
 
+namespace dsaidx {
+
+idx_status api_fail(idx_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+idx_status select_call(const char* fn, const idx_problem* p, int k, int32_t* out_idx, float* out_val,
+                       int64_t out_ld, uint32_t flags, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  REQUIRE(p, IDX_ERR_ARG, "%s: problem is null", fn);
+  REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
+  REQUIRE((flags & ~(IDX_TOPK_UNSORTED | IDX_SELECT_NO_CUTOFF)) == 0, IDX_ERR_ARG, "%s: unknown flags 0x%x", fn,
+          flags);
+  REQUIRE(p->rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, p->rows);
+  const int64_t width = select_width(p);
+  ScoreCall c;
+  {
+    // validate the problem with a stand-in output so the score checks run
+    idx_status s = check_problem(fn, p, &c, (const float*)p->w, 1, false);
+    if (s != IDX_OK) return s;
+  }
+  if (p->rows == 0) return ok();
+  REQUIRE(width >= 1 && width <= kMaxCols, IDX_ERR_ARG,
+          "%s: score width %lld out of range (dense problems need max_cols >= 1)", fn, (long long)width);
+  REQUIRE(out_idx && out_ld >= k, IDX_ERR_ARG, "%s: out_idx must be non-null and out_ld >= k", fn);
+  REQUIRE(aligned(out_idx, 4) && (!out_val || aligned(out_val, 4)), IDX_ERR_ARG,
+          "%s: outputs must be 4-byte aligned", fn);
+  if (p->mode == IDX_MODE_PAGED)
+    REQUIRE(p->bt_rows >= 1 && (p->row_req || p->bt_rows >= p->rows), IDX_ERR_ARG,
+            "%s: bt_rows = %lld too small", fn, (long long)p->bt_rows);
+  const size_t need = idx_select_workspace(p, k);
+  REQUIRE(workspace && workspace_bytes >= need, IDX_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+  REQUIRE(aligned(workspace, 256), IDX_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
+
+  const int64_t ldw = round_up(width, 64);
+  uint8_t* ws = (uint8_t*)workspace;
+  c.ld = ldw;
+  c.bt_rows = p->bt_rows;
+  c.err = device_error_word();
+  c.skip_tail = 1;  // the top-k below reads each row only up to its scored length
+
+  TopkCall t{};
+  t.ld = ldw;
+  t.n_cols = width;
+  t.rows = p->rows;
+  t.k = k;
+  t.out_idx = out_idx;
+  t.out_val = out_val;
+  t.out_ld = out_ld;
+  t.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
+  if (p->mode == IDX_MODE_SPARSE_BLOCKS) {
+    t.cand = p->cand_blocks;
+    t.cand_ld = p->cand_ld;
+    t.block = p->block_size;
+  }
+
+  const int64_t blocks = select_one_pass_shape(p) ? select_scan_blocks(c) : 0;
+  if (blocks >= 1 && blocks <= kSelMaxBlocks) {
+    const SelectLayout L = select_layout(p);
+    SelectState st{};
+    st.slots = (uint32_t*)(ws + L.slots);
+    st.arrive = (unsigned long long*)(ws + L.arrive);
+    st.acc = (int64_t*)(ws + L.acc);
+    st.seg_info = (uint32_t*)(ws + L.seg_info);
+    st.surv = (uint64_t*)(ws + L.surv);
+    st.spill = (float*)(ws + L.spill);
+    st.k = k;
+    st.gshift = select_group_shift(ldw, k);
+    st.wait_ticks = (flags & IDX_SELECT_NO_CUTOFF) ? 0 : kSelectWaitTicks;
+    c.logits = st.spill;
+    c.sel = &st;
+    log_once("idx_select: one pass (rows %d, width %lld, k %d, groups of %d, %lld scan workgroups)", p->rows,
+             (long long)width, k, 1 << st.gshift, (long long)blocks);
+    hipError_t e = launch_score(c, stream);
+    if (e != hipSuccess) return launched(fn, e);
+    return launched(fn, launch_select_finish(t, st, blocks, stream));
+  }
+
+  // scores to the workspace, then the top-k over each row's scored length
+  float* scores = (float*)ws;
+  int32_t* lens = (int32_t*)(ws + select_scores_bytes(p));
+  uint8_t* topk_ws = ws + select_scores_bytes(p) + select_lens_bytes(p);
+  c.logits = scores;
+  c.lens_out = lens;
+  // the scan kernels clear the top-k's histogram and counters on their way
+  const bool prefill = prefill_applies(c);
+  if (!prefill) {
+    c.zero = (uint32_t*)topk_ws;
+    c.zero_words = (int64_t)(topk_zeroed_bytes(p->rows, width) / 4);
+  }
+  log_once("idx_select: %s then top-k (rows %d, width %lld, k %d)", prefill ? "prefill tiles" : "scan", p->rows,
+           (long long)width, k);
+  hipError_t e = launch_score(c, stream);
+  if (e != hipSuccess) return launched(fn, e);
+  t.logits = scores;
+  t.lens = lens;
+  t.ws_zeroed = c.zero && c.zero_words > 0;
+  return launched(fn, launch_topk(t, topk_ws, stream));
+}
+
+}  // namespace dsaidx
+
 extern "C" {
 
 idx_status idx_logits(const void* q, int q_dtype, const float* w, const void* k, const void* k_scale,
@@ -388,97 +498,8 @@ size_t idx_select_workspace(const idx_problem* p, int k) {
 
 idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_val, int64_t out_ld,
                       uint32_t flags, void* workspace, size_t workspace_bytes, idx_stream_t stream) {
-  const char* fn = "idx_select";
-  REQUIRE(p, IDX_ERR_ARG, "%s: problem is null", fn);
-  REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
-  REQUIRE((flags & ~(IDX_TOPK_UNSORTED | IDX_SELECT_NO_CUTOFF)) == 0, IDX_ERR_ARG, "%s: unknown flags 0x%x", fn,
-          flags);
-  REQUIRE(p->rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, p->rows);
-  const int64_t width = select_width(p);
-  ScoreCall c;
-  {
-    // validate the problem with a stand-in output so the score checks run
-    idx_status s = check_problem(fn, p, &c, (const float*)p->w, 1, false);
-    if (s != IDX_OK) return s;
-  }
-  if (p->rows == 0) return ok();
-  REQUIRE(width >= 1 && width <= kMaxCols, IDX_ERR_ARG,
-          "%s: score width %lld out of range (dense problems need max_cols >= 1)", fn, (long long)width);
-  REQUIRE(out_idx && out_ld >= k, IDX_ERR_ARG, "%s: out_idx must be non-null and out_ld >= k", fn);
-  REQUIRE(aligned(out_idx, 4) && (!out_val || aligned(out_val, 4)), IDX_ERR_ARG,
-          "%s: outputs must be 4-byte aligned", fn);
-  if (p->mode == IDX_MODE_PAGED)
-    REQUIRE(p->bt_rows >= 1 && (p->row_req || p->bt_rows >= p->rows), IDX_ERR_ARG,
-            "%s: bt_rows = %lld too small", fn, (long long)p->bt_rows);
-  const size_t need = idx_select_workspace(p, k);
-  REQUIRE(workspace && workspace_bytes >= need, IDX_ERR_WORKSPACE,
-          "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
-  REQUIRE(aligned(workspace, 256), IDX_ERR_ARG, "%s: workspace must be 256-byte aligned", fn);
-
-  const int64_t ldw = round_up(width, 64);
-  uint8_t* ws = (uint8_t*)workspace;
-  c.ld = ldw;
-  c.bt_rows = p->bt_rows;
-  c.err = device_error_word();
-  c.skip_tail = 1;  // the top-k below reads each row only up to its scored length
-
-  TopkCall t{};
-  t.ld = ldw;
-  t.n_cols = width;
-  t.rows = p->rows;
-  t.k = k;
-  t.out_idx = out_idx;
-  t.out_val = out_val;
-  t.out_ld = out_ld;
-  t.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
-  if (p->mode == IDX_MODE_SPARSE_BLOCKS) {
-    t.cand = p->cand_blocks;
-    t.cand_ld = p->cand_ld;
-    t.block = p->block_size;
-  }
-
-  const int64_t blocks = select_one_pass_shape(p) ? select_scan_blocks(c) : 0;
-  if (blocks >= 1 && blocks <= kSelMaxBlocks) {
-    const SelectLayout L = select_layout(p);
-    SelectState st{};
-    st.slots = (uint32_t*)(ws + L.slots);
-    st.arrive = (unsigned long long*)(ws + L.arrive);
-    st.acc = (int64_t*)(ws + L.acc);
-    st.seg_info = (uint32_t*)(ws + L.seg_info);
-    st.surv = (uint64_t*)(ws + L.surv);
-    st.spill = (float*)(ws + L.spill);
-    st.k = k;
-    st.gshift = select_group_shift(ldw, k);
-    st.wait_ticks = (flags & IDX_SELECT_NO_CUTOFF) ? 0 : kSelectWaitTicks;
-    c.logits = st.spill;
-    c.sel = &st;
-    log_once("idx_select: one pass (rows %d, width %lld, k %d, groups of %d, %lld scan workgroups)", p->rows,
-             (long long)width, k, 1 << st.gshift, (long long)blocks);
-    hipError_t e = launch_score(c, (hipStream_t)stream);
-    if (e != hipSuccess) return launched(fn, e);
-    return launched(fn, launch_select_finish(t, st, blocks, (hipStream_t)stream));
-  }
-
-  // scores to the workspace, then the top-k over each row's scored length
-  float* scores = (float*)ws;
-  int32_t* lens = (int32_t*)(ws + select_scores_bytes(p));
-  uint8_t* topk_ws = ws + select_scores_bytes(p) + select_lens_bytes(p);
-  c.logits = scores;
-  c.lens_out = lens;
-  // the scan kernels clear the top-k's histogram and counters on their way
-  const bool prefill = prefill_applies(c);
-  if (!prefill) {
-    c.zero = (uint32_t*)topk_ws;
-    c.zero_words = (int64_t)(topk_zeroed_bytes(p->rows, width) / 4);
-  }
-  log_once("idx_select: %s then top-k (rows %d, width %lld, k %d)", prefill ? "prefill tiles" : "scan", p->rows,
-           (long long)width, k);
-  hipError_t e = launch_score(c, (hipStream_t)stream);
-  if (e != hipSuccess) return launched(fn, e);
-  t.logits = scores;
-  t.lens = lens;
-  t.ws_zeroed = c.zero && c.zero_words > 0;
-  return launched(fn, launch_topk(t, topk_ws, (hipStream_t)stream));
+  return select_call("idx_select", p, k, out_idx, out_val, out_ld, flags, workspace, workspace_bytes,
+                     (hipStream_t)stream);
 }
 
 const char* idx_status_string(idx_status s) {

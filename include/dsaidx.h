@@ -294,6 +294,24 @@ idx_status idx_select(const idx_problem* p, int k, int32_t* out_idx, float* out_
 
 size_t idx_select_workspace(const idx_problem* p, int k);
 
+/*
+ * idx_select_noalloc: idx_select without a workspace argument and without any device
+ * allocation, for callers that cannot allocate (code under stream capture, serving
+ * loops, hosts that forbid it). The workspace is a static device array of
+ * IDX_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on until the
+ * process ends; its address is looked up on the device's first call. Same arguments,
+ * results and flags as idx_select. Returns IDX_ERR_WORKSPACE (launching nothing) when
+ * idx_select_workspace(p, k) exceeds IDX_NOALLOC_SCRATCH_BYTES, and IDX_ERR_HIP if the
+ * scratch address cannot be found. Nothing in the scratch needs clearing between calls
+ * (the selection's counters are read relative to their value at the start of each call,
+ * and the top-k clears its own histogram with a kernel). All calls on one device share the
+ * one array: calls that may overlap on a device (different streams, or host threads
+ * without ordering) race on it and must be serialised by the caller.
+ */
+#define IDX_NOALLOC_SCRATCH_BYTES (128u << 20)
+idx_status idx_select_noalloc(const idx_problem* p, int k, int32_t* out_idx, float* out_val,
+                              int64_t out_ld, uint32_t flags, idx_stream_t stream);
+
 /* ------------------------------------------------------------------ misc */
 
 /* Static text for a status code. */
