@@ -8,7 +8,8 @@ Inputs are generated once (seeded) and resident in HBM before timing.
 
 Prints one JSON line: tokens scored per second (value), top-k rows per second, the
 roofline of the dominant kernel (the key-cache scan, timed alone with HIP events on its
-stream), and the CPU oracle timed on a bounded sample of the same workload.
+stream), and the CPU oracle timed on the host's cores (1 thread and all of them, median of
+three) over every workload, the 128K paged decode whole as the headline baseline.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -46,14 +47,22 @@ def scan_source_hash() -> str:
 
 def scan_bytes(case) -> int:
     """Algorithmic HBM bytes of one paged scan launch: per valid token its 128-byte fp8 key,
-    4-byte scale and 4-byte score; per page one 4-byte block-table entry; per row q (8 KiB),
-    w (256 B) and the -inf fill of the unscored tail of its score row."""
+    4-byte scale and 4-byte score; per page one 4-byte block-table entry; per row q (8 KiB)
+    and w (256 B). The -inf the scan also writes past each row's length is not the
+    method's work (scan_fill_bytes)."""
     import numpy as np
     L = case.seq_lens.astype(np.int64)
     pages = (L + case.page_size - 1) // case.page_size
+    return int(L.sum() * (128 + 4 + 4) + pages.sum() * 4 + case.rows * (64 * 128 + 64 * 4))
+
+
+def scan_fill_bytes(case) -> int:
+    """Bytes of -inf the paged scan writes past each row's length (to the width of the
+    block table)."""
+    import numpy as np
+    L = case.seq_lens.astype(np.int64)
     width = case.block_table.shape[1] * case.page_size
-    return int(L.sum() * (128 + 4 + 4) + pages.sum() * 4 + case.rows * (64 * 128 + 64 * 4)
-               + (width - L).sum() * 4)
+    return int((width - L).sum() * 4)
 
 
 def step_bytes(case, k: int) -> int:
@@ -181,27 +190,102 @@ def time_each(fn, n: int, warmup: int, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def cpu_baseline(case, k: int, budget_s: float = 15.0):
-    """The oracle (scores + top-k) on whole rows of the same workload. The oracle spreads
-    rows over its OpenMP threads, so each batch holds one row per thread; batches run
-    until about ``budget_s`` seconds have been spent (at least one batch)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _keys_scored(case) -> int:
+    """Keys one select over the case scores: each row's valid range (dense), valid length
+    (paged) or candidate columns (sparse blocks)."""
+    import numpy as np
+    kind = type(case).__name__
+    if kind == "Paged":
+        return int(case.seq_lens.astype(np.int64).sum())
+    if kind == "Sparse":
+        return int(case.n_cols.astype(np.int64).sum())
+    return int((case.row_ke.astype(np.int64) - case.row_ks).sum())
+
+
+def cpu_oracle_legs(k: int = 2048, runs: int = 3):
+    """The CPU oracle (scores + exact top-k, fp64, rows spread over OpenMP threads) timed on
+    this host: with 1 thread and with the process's thread count (OMP_NUM_THREADS, else
+    nproc), median of ``runs`` wall times per leg. The nproc legs cover the tiny dense, the
+    batched decode, the 128K paged decode and the two-level workloads whole and the prefill
+    chunk on every 8th query row (rows 0 and 4095 included); the 1-thread legs take a few
+    rows of each (named in the result). Also the top-k alone over the oracle's 128K scores
+    at k = 2048, 1024, 512. Runs before anything touches the GPU. Returns (headline
+    cpu_baseline, the full report)."""
+    import ctypes
+    import statistics
+    import numpy as np
     import oracle
+    import synth
     oracle.build(force=False)
-    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-    batch = max(1, min(threads, case.rows))
-    done, tokens, spent = 0, 0, 0.0
-    while done < case.rows and spent < budget_s:
-        rows = list(range(done, min(done + batch, case.rows)))
-        sub = oracle.subset_rows(case, rows)
-        t0 = time.perf_counter()
-        oracle.select_case(sub, k=k)
-        spent += time.perf_counter() - t0
-        done += len(rows)
-        tokens += int(sub.seq_lens.sum())
-    return {"value": tokens / spent, "unit": "tokens/s", "cores": batch, "kind": "oracle",
-            "sample": f"rows 0..{done - 1} of {case.rows} ({tokens} keys), scores + top-k "
-                      f"k={k}, {spent:.1f} s wall, one row per OpenMP thread",
-            "rows_per_s": done / spent}
+    gomp = ctypes.CDLL("libgomp.so.1")  # the OpenMP runtime the oracle library runs on
+    n_threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+
+    def timed(fn):
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    prefill_rows = list(range(0, 4096, 8)) + [4095]
+    workloads = [  # name, case, rows of the 1-thread leg, rows of the nproc leg (None: all)
+        ("tiny_dense_bf16_4096_k256", synth.tiny_dense(), None, None, 256),
+        ("batched_decode_32x32768", synth.batched_decode(), [0, 1, 2, 3], None, k),
+        ("paged_decode_128k", synth.paged_decode(poison=False), [0, 1], None, k),
+        ("prefill_4096x8192_every8th", synth.prefill_chunk(), list(range(0, 4096, 256)), prefill_rows, k),
+        ("two_level_64x8192_mxfp4", synth.sparse_blocks(), list(range(8)), None, k),
+    ]
+    report = {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "threads": n_threads, "runs": runs,
+              "timing": "median wall time of the runs, time.perf_counter around oracle.select_case",
+              "legs": {}}
+    headline = None
+    for name, case, rows1, rows_n, kk in workloads:
+        leg = {}
+        for threads, rows in ((1, rows1), (n_threads, rows_n)):
+            sub = case if rows is None else oracle.subset_rows(case, rows)
+            nrows = case.rows if rows is None else len(rows)
+            keys = _keys_scored(sub)
+            gomp.omp_set_num_threads(threads)
+            t = timed(lambda: oracle.select_case(sub, k=kk))
+            leg[f"threads_{threads}"] = {"tokens_per_s": keys / t, "rows_per_s": nrows / t, "s": t,
+                                         "rows": "all" if rows is None else (
+                                             f"{nrows} rows" if len(rows) > 8 else str(rows)),
+                                         "keys": keys}
+            log(f"cpu oracle {name} {threads} thread(s): {keys / t / 1e6:.2f} M keys/s, "
+                f"{nrows / t:.1f} rows/s ({t:.2f} s)")
+        report["legs"][name] = leg
+        if name == "paged_decode_128k":
+            hl = leg[f"threads_{n_threads}"]
+            headline = {"value": hl["tokens_per_s"], "unit": "tokens/s", "cores": n_threads, "kind": "oracle",
+                        "sample": f"all {case.rows} rows of the 128K paged decode ({hl['keys']} keys), "
+                                  f"scores + top-k k={k}, median of {runs} runs, {n_threads} OpenMP threads",
+                        "rows_per_s": hl["rows_per_s"]}
+            # the top-k alone over the oracle's own scores of the whole workload
+            gomp.omp_set_num_threads(n_threads)
+            _, _, lg = oracle.select_case(case, k=k, with_logits=True)
+            lens = case.seq_lens.astype(np.int32)
+            topk = {}
+            for threads in (1, n_threads):
+                gomp.omp_set_num_threads(threads)
+                for kt in (2048, 1024, 512):
+                    t = timed(lambda: oracle.topk(lg, kt, lens=lens))
+                    topk[f"k{kt}_threads_{threads}"] = {"rows_per_s": case.rows / t, "s": t}
+            report["topk_alone_paged_128k"] = topk
+            log(f"cpu oracle top-k alone (64 x 128K): {topk[f'k2048_threads_{n_threads}']['rows_per_s']:.0f} rows/s")
+            del lg
+    gomp.omp_set_num_threads(n_threads)
+    return headline, report
 
 
 FP8_PEAK = 5.0e15  # MI355X dense fp8 MFMA, FLOP/s
@@ -446,6 +530,12 @@ def main() -> int:
         return 2
 
     import numpy as np
+
+    # the CPU oracle first, while nothing has touched the GPU
+    cpu, cpu_report = (None, None)
+    if args.only == "all" and not args.no_cpu:
+        cpu, cpu_report = cpu_oracle_legs(2048)
+
     import torch
 
     import dsa_lightning_indexer_idx_amd as D
@@ -526,16 +616,17 @@ def main() -> int:
 
     res = {}
     if args.only in ("all", "select"):
-        ms, wall_ms = time_loop(select(2048), args.steps, args.warmup, stream)
+        # the call repeated for 0.5 s first: the clocks settle only under the step's own load
+        ms, wall_ms = time_loop(select(2048), args.steps, args.warmup, stream, warm_s=0.5)
         res["select"] = (ms, wall_ms)
         log(f"idx_select k=2048: {ms:.3f} ms/step (wall {wall_ms:.3f})")
         if args.only == "all":
             for k in (1024, 512):
-                kk, _ = time_loop(select(k), max(5, args.steps // 2), 2, stream)
+                kk, _ = time_loop(select(k), max(5, args.steps // 2), 2, stream, warm_s=0.3)
                 res[f"select_k{k}"] = kk
                 log(f"idx_select k={k}: {kk:.3f} ms/step")
     if args.only in ("all", "scan"):
-        ms_scan, _ = time_loop(scan, args.steps, args.warmup, stream)
+        ms_scan, _ = time_loop(scan, args.steps, args.warmup, stream, warm_s=0.3 if args.only == "all" else 0.0)
         res["scan"] = ms_scan
         log(f"scan kernel alone: {ms_scan:.3f} ms/launch")
     if args.only != "all":
@@ -561,7 +652,6 @@ def main() -> int:
     sb = scan_bytes(case)
     achieved = sb / (res["scan"] * 1e-3)
     step_b = step_bytes(case, 2048)
-    cpu = None if args.no_cpu else cpu_baseline(case, 2048)
     out = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -590,7 +680,8 @@ def main() -> int:
                   "ms_per_step_k1024": res["select_k1024"], "ms_per_step_k512": res["select_k512"],
                   "tokens_per_s_k1024": tokens / (res["select_k1024"] * 1e-3),
                   "tokens_per_s_k512": tokens / (res["select_k512"] * 1e-3),
-                  "wall_ms_per_step": res["select"][1], "scan_source_sha": scan_source_hash()},
+                  "wall_ms_per_step": res["select"][1], "scan_source_sha": scan_source_hash(),
+                  "scan_fill_bytes": scan_fill_bytes(case), "cpu_oracle": cpu_report},
     }
     print(json.dumps(out), flush=True)
     return 0

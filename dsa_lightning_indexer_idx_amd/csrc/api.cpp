@@ -90,8 +90,9 @@ idx_status check_common(const char* fn, const void* q, int q_dtype, const float*
   if (rows == 0) return IDX_OK;
   REQUIRE(q && w && k && logits, IDX_ERR_ARG, "%s: q, w, k and logits must be non-null", fn);
   REQUIRE(*fmt == FMT_BF16 || k_scale, IDX_ERR_ARG, "%s: k_scale is required for fp8 and mxfp4 keys", fn);
-  REQUIRE(aligned(q, 16) && aligned(k, 16), IDX_ERR_ARG, "%s: q and k must be 16-byte aligned", fn);
-  REQUIRE(aligned(w, 4) && aligned(logits, 4), IDX_ERR_ARG, "%s: w and logits must be 4-byte aligned", fn);
+  REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(w, 16), IDX_ERR_ARG,
+          "%s: q, k and w must be 16-byte aligned (w is read four weights at a time)", fn);
+  REQUIRE(aligned(logits, 4), IDX_ERR_ARG, "%s: logits must be 4-byte aligned", fn);
   REQUIRE(*fmt != FMT_FP8 || aligned(k_scale, 4), IDX_ERR_ARG, "%s: fp8 k_scale must be 4-byte aligned", fn);
   REQUIRE(ld >= 1 && ld <= kMaxCols, IDX_ERR_ARG, "%s: ld = %lld out of range [1, 2^31)", fn, (long long)ld);
   return IDX_OK;

@@ -69,6 +69,14 @@ struct AttnArgs {
   unsigned* err;
 };
 
+// The entry a position without a valid cache entry reads: zeros, so that its zero
+// softmax weight times its values is 0 (a cache slot could hold Inf or NaN).
+__device__ const uint16_t g_attn_zero_entry[kAttnD] = {};
+
+__device__ __forceinline__ const uint16_t* entry_or_zero(const uint16_t* kv, int64_t e) {
+  return e >= 0 ? kv + e * kAttnD : g_attn_zero_entry;
+}
+
 __device__ __forceinline__ float dpp_row_max(float v) {
   // butterfly over the 16 lanes of a row: quad xor 1, xor 2, half-row mirror, row mirror
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
@@ -155,8 +163,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_partial_kernel(AttnArgs a)
       const int c = tid + u * NT;
       if (c < kChunks) {
         const int64_t e = ent[t * kAttnT + c / (kAttnD / 8)];
-        const int64_t row = e >= 0 ? e : 0;
-        pre[u] = *(const v4i*)(a.kv + row * kAttnD + 8 * (c % (kAttnD / 8)));
+        pre[u] = *(const v4i*)(entry_or_zero(a.kv, e) + 8 * (c % (kAttnD / 8)));
       }
     }
   };
@@ -341,8 +348,8 @@ __global__ __launch_bounds__(kWave, 1) void attn_partial_1w_kernel(AttnArgs a) {
   // that write LDS at the wave-uniform base + 16 l for lane l). Wave w moves dims 0..511
   // of tokens w, w + NW, ... (one 1 KiB load each) and dims 512..575 of 8 tokens per load
   // (lane l: token 8q + l / 8, chunk (l % 8) ^ (token % 8), so the 16 rows a score read
-  // touches spread over the banks). Positions without a valid entry read entry 0, which
-  // always exists: their weights are exactly 0, and its values are finite.
+  // touches spread over the banks). Positions without a valid entry read a zero entry:
+  // their weights are exactly 0, and 0 times its values is 0 whatever the cache holds.
   // (the entry rows are read ahead of the loads, up to 8 tokens at a time: the loads
   // are ordered with LDS accesses, so a read between two of them costs a round trip)
   auto dma = [&](int t, int bs) {
@@ -359,14 +366,14 @@ __global__ __launch_bounds__(kWave, 1) void attn_partial_1w_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const int j = wave + (c + u) * NW;
-        lds_load16(a.kv + (ev[u] >= 0 ? ev[u] : 0) * kAttnD + 8 * lane, mbase + 2 * j * kKPitch);
+        lds_load16(entry_or_zero(a.kv, ev[u]) + 8 * lane, mbase + 2 * j * kKPitch);
       }
     }
 #pragma unroll
     for (int v = 0; v < 4 / NW; ++v) {
       const int q = wave + v * NW;
       const int j = 8 * q + (lane >> 3);
-      lds_load16(a.kv + (tv[v] >= 0 ? tv[v] : 0) * kAttnD + kAttnDV + 8 * ((lane & 7) ^ (j & 7)), tbase + 1024 * q);
+      lds_load16(entry_or_zero(a.kv, tv[v]) + kAttnDV + 8 * ((lane & 7) ^ (j & 7)), tbase + 1024 * q);
     }
   };
   // value operand of dims 16n .. 16n + 15: lane (g, c16) gets tokens 8g .. 8g + 7 of dim
@@ -582,10 +589,9 @@ static hipError_t launch_partial_1w(dim3 grid, size_t ent_bytes, hipStream_t str
 
 template <int NW>
 static hipError_t launch_partial(dim3 grid, size_t ent_bytes, hipStream_t stream, const AttnArgs& a) {
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute((const void*)attn_partial_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  static PerDeviceOnce once;
+  const hipError_t attr = once.run([] {
+    return hipFuncSetAttribute((const void*)attn_partial_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                2048 * (int)sizeof(int64_t));
   });
   if (attr != hipSuccess) return attr;

@@ -349,10 +349,9 @@ hipError_t launch_candidate_blocks(const CandCall& c, void* workspace, hipStream
       hipLaunchKernelGGL(cand_select_wave_kernel<0>, grid, dim3(kWaveSelectThreads), 0, stream, a);
     return hipGetLastError();
   }
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute((const void*)cand_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+  static PerDeviceOnce once;
+  const hipError_t attr = once.run([] {
+    return hipFuncSetAttribute((const void*)cand_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                kCandMaxBlocks * (int)sizeof(uint32_t));
   });
   if (attr != hipSuccess) return attr;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace dsaidx {
 
 enum SourceKind { SRC_DENSE = 1, SRC_PAGED = 2, SRC_SPARSE = 3 };
@@ -12,6 +14,25 @@ enum SourceKind { SRC_DENSE = 1, SRC_PAGED = 2, SRC_SPARSE = 3 };
 // device ids below this.
 constexpr int kMaxDevices = 64;
 enum KeyFmt { FMT_BF16 = 1, FMT_FP8 = 2, FMT_MXFP4 = 3 };
+
+// A host-side set-up step run once per device (the current one when first needed), e.g. a
+// kernel attribute; its result is kept per device. Thread-safe.
+struct PerDeviceOnce {
+  std::mutex mu;
+  bool done[kMaxDevices] = {};
+  hipError_t res[kMaxDevices] = {};
+  template <class F>
+  hipError_t run(F&& f) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done[dev]) {
+      res[dev] = f();
+      done[dev] = true;
+    }
+    return res[dev];
+  }
+};
 
 // idx_select's one-pass selection for rows that read their own keys (the balanced scan).
 // A scan workgroup keeps the scores of its step range in LDS and builds, per row it

@@ -153,7 +153,7 @@ struct SparseSrc {
   }
   __device__ StepDesc step_desc(const Row& R, int64_t pos0, int64_t cb, unsigned* err) const {
     if (pos0 >= R.ncols) return {0, 0};
-    if (cb < 0) {
+    if (cb < 0 || cb * block >= R.len) {  // no token of the block lies in the row's range
       flag_error(err, kErrBlock);
       return {0, 0};
     }

@@ -1152,10 +1152,9 @@ size_t topk_zeroed_bytes(int rows, int64_t n_cols) {
 template <bool V4, int NT>
 static hipError_t launch_short(const TopkCall& c, hipStream_t stream) {
   constexpr int kMaxRow = NT == kWideThreads ? kWideRow : kShortRow;
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute((const void*)topk_short_kernel<V4, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  static PerDeviceOnce once;
+  const hipError_t attr = once.run([] {
+    return hipFuncSetAttribute((const void*)topk_short_kernel<V4, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                kMaxRow * (int)sizeof(uint32_t));
   });
   if (attr != hipSuccess) return attr;

@@ -45,8 +45,9 @@
  *                    scales of the vLLM sparse_indexer page.
  *  - Scores are fp32. Positions a row does not score are written as -inf.
  *  - Leading dimensions (ld, bt_ld, cand_ld, out_ld) count elements.
- *  - Pointers to code arrays (q, k, k_pages) must be 16-byte aligned and
- *    every float / int32 array 4-byte aligned (IDX_ERR_ARG otherwise).
+ *  - Pointers to code arrays (q, k, k_pages) and the head weights w must be
+ *    16-byte aligned and every other float / int32 array 4-byte aligned
+ *    (IDX_ERR_ARG otherwise).
  */
 #ifndef DSAIDX_H
 #define DSAIDX_H
@@ -330,7 +331,9 @@ int idx_version(void);
  */
 #define IDX_DEVERR_RANGE 1u  /* row_ks/row_ke/seq_lens/n_cols outside the buffers */
 #define IDX_DEVERR_PAGE 2u   /* block-table entry outside [0, n_pages) */
-#define IDX_DEVERR_BLOCK 4u  /* candidate block outside the row's key range */
+#define IDX_DEVERR_BLOCK 4u  /* candidate block id < 0, or with no token in the row's
+                                key range (id * block_size >= row_ke - row_ks); its
+                                columns are scored -inf */
 #define IDX_DEVERR_SLOT 8u   /* key-cache slot at or past n_slots (idx_kcache_write) */
 int idx_device_errors(idx_stream_t stream);
 

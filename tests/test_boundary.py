@@ -114,6 +114,7 @@ CASES = [
     ("dense misaligned q", _dense, dict(q=Q + 8), ARG),
     ("dense misaligned k", _dense, dict(k=K + 4), ARG),
     ("dense misaligned w", _dense, dict(w=W + 2), ARG),
+    ("dense w only 4-byte aligned", _dense, dict(w=W + 4), ARG),
     ("dense misaligned out", _dense, dict(out=OUT + 1), ARG),
     ("dense misaligned scale", _dense, dict(sc=S + 2), ARG),
     ("dense misaligned ranges", _dense, dict(ke=KE + 2), ARG),

@@ -102,6 +102,30 @@ def test_tables_and_empty_rows():
     check(c, 0.01, "identity table, flat scores")
 
 
+@pytest.mark.parametrize("heads", [16, 64, 128])
+def test_padding_ignores_nonfinite_cache_entries(heads):
+    """Padded and out-of-range positions must not read what the cache holds: physical
+    page 0 (flat entry 0) and the spare pages carry bf16 NaN and Inf, none of them is
+    referenced by a valid position, and the rows carry -1 / past-length padding; the
+    output is finite and matches the oracle."""
+    require_gpu()
+    c = make_case(95 + heads, 3, heads, [3000, 700, 130], 512, q_std=2.0, pad=0.4)
+    bt = c["bt"]
+    used = set(int(x) for x in bt.ravel() if x >= 0)
+    spare = [pg for pg in range(c["kv"].shape[0]) if pg not in used]
+    if 0 in used:  # move page 0's content to a spare page so that page 0 is unreferenced
+        s0 = spare[0]
+        c["kv"][s0] = c["kv"][0]
+        bt[bt == 0] = s0
+        spare = [pg for pg in range(c["kv"].shape[0]) if pg not in set(int(x) for x in bt.ravel() if x >= 0)]
+    assert 0 in spare
+    for pg in spare:
+        c["kv"][pg, :, 0::2] = 0x7FC0  # NaN
+        c["kv"][pg, :, 1::2] = 0x7F80  # +Inf
+    out, lse = check(c, 1 / np.sqrt(192), f"nonfinite unreferenced entries, {heads} heads")
+    assert np.all(np.isfinite(out)), "padding leaked a non-finite cache value"
+
+
 @pytest.mark.parametrize("heads", [128, 16])
 def test_graph_replay_matches_eager(heads):
     require_gpu()
