@@ -328,11 +328,12 @@ def other_workloads(D, np, torch, stream, args):
     c4 = synth.prefill_chunk()
     q, w, k, sc, ks, ke = map(dev, (c4.q, c4.w, c4.k, c4.k_scale, c4.row_ks, c4.row_ke))
     lg = torch.empty((c4.rows, c4.max_cols), dtype=torch.float32, device="cuda")
-    ms, _ = time_loop(lambda: D.idx_logits(q, w, k, sc, ks, ke, k_dtype="fp8", out=lg), steps, 3, stream, warm_s=0.2)
+    ms, _ = time_loop(lambda: D.idx_logits(q, w, k, sc, ks, ke, k_dtype="fp8", out=lg, prefill=True), steps, 3,
+                      stream, warm_s=0.2)
     flop = float((c4.row_ke.astype(np.int64) - c4.row_ks).sum()) * 64 * 128 * 2
     out["prefill_logits_ms"] = ms
     out["prefill_mfma_frac"] = flop / (ms * 1e-3) / FP8_PEAK
-    p4 = D.dense_problem(q, w, k, sc, ks, ke, k_dtype="fp8", max_cols=c4.max_cols)
+    p4 = D.dense_problem(q, w, k, sc, ks, ke, k_dtype="fp8", max_cols=c4.max_cols, prefill=True)
     ws4 = torch.empty(D.idx_select_workspace(p4, 2048), dtype=torch.uint8, device="cuda")
     oi4 = torch.empty((c4.rows, 2048), dtype=torch.int32, device="cuda")
     ms, _ = time_loop(lambda: D.idx_select(p4, 2048, values=False, out_idx=oi4, workspace=ws4), steps, 3, stream, warm_s=0.2)
@@ -358,6 +359,25 @@ def other_workloads(D, np, torch, stream, args):
     out["batched_decode_tokens_per_s"] = c2.tokens / (ms * 1e-3)
     log(f"batched decode: select {ms*1e3:.1f} us ({c2.tokens/(ms*1e-3)/1e9:.2f} G keys/s)")
     del base, copies, probs, ws2, oi2
+    # a large batched decode: 256 rows x 32768 fp8 keys each (1.1 GB: no rotation). Dense
+    # rows with their own contexts take the row scan (never the prefill tiles); the select
+    # is compared with the plain scan of the same rows, per key.
+    c7 = synth.batched_decode(seed=7, rows=256)
+    t7 = [dev(a) for a in (c7.q, c7.w, c7.k, c7.k_scale, c7.row_ks, c7.row_ke)]
+    p7 = D.dense_problem(*t7, k_dtype="fp8", max_cols=c7.max_cols)
+    ws7 = torch.empty(D.idx_select_workspace(p7, 2048), dtype=torch.uint8, device="cuda")
+    oi7 = torch.empty((c7.rows, 2048), dtype=torch.int32, device="cuda")
+    lg7 = torch.empty((c7.rows, c7.max_cols), dtype=torch.float32, device="cuda")
+    ms_sel, _ = time_loop(lambda: D.idx_select(p7, 2048, values=False, out_idx=oi7, workspace=ws7), steps, 3, stream,
+                          warm_s=0.2)
+    ms_scan, _ = time_loop(lambda: D.idx_logits(*t7, k_dtype="fp8", out=lg7), steps, 3, stream, warm_s=0.2)
+    out["batched_decode_256x32k_select_ms"] = ms_sel
+    out["batched_decode_256x32k_scan_ms"] = ms_scan
+    out["batched_decode_256x32k_select_tokens_per_s"] = c7.tokens / (ms_sel * 1e-3)
+    out["batched_decode_256x32k_select_vs_scan_rate"] = ms_scan / ms_sel
+    log(f"batched decode 256 x 32K: select {ms_sel*1e3:.1f} us, scan alone {ms_scan*1e3:.1f} us "
+        f"(select at {100*ms_scan/ms_sel:.0f}% of the scan's per-key rate)")
+    del t7, p7, ws7, oi7, lg7
     # two-level candidate blocks: 64 rows x 8192 candidate keys of 131072, MXFP4 (rotate 16
     # copies of the candidate data, as a graph)
     c5 = synth.sparse_blocks()
@@ -588,7 +608,7 @@ def main() -> int:
         dev4 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
         q4, w4, k4, sc4, ks4, ke4 = map(dev4, (c4.q, c4.w, c4.k, c4.k_scale, c4.row_ks, c4.row_ke))
         lg4 = torch.empty((c4.rows, c4.max_cols), dtype=torch.float32, device="cuda")
-        ms, _ = time_loop(lambda: D.idx_logits(q4, w4, k4, sc4, ks4, ke4, k_dtype="fp8", out=lg4), args.steps,
+        ms, _ = time_loop(lambda: D.idx_logits(q4, w4, k4, sc4, ks4, ke4, k_dtype="fp8", out=lg4, prefill=True), args.steps,
                           args.warmup, torch.cuda.current_stream(), warm_s=0.5)
         flop = float((c4.row_ke.astype(np.int64) - c4.row_ks).sum()) * 64 * 128 * 2
         log(f"prefill scores: {ms * 1e3:.1f} us per call ({100 * flop / (ms * 1e-3) / FP8_PEAK:.1f}% fp8 MFMA)")

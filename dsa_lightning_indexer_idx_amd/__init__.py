@@ -18,17 +18,17 @@ _LIB_PATH = Path(__file__).resolve().parent / "libdsaidx.so"
 
 IDX_OK, IDX_ERR_ARG, IDX_ERR_UNSUPPORTED, IDX_ERR_WORKSPACE, IDX_ERR_HIP = 0, 1, 2, 3, 4
 IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
-IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS = 1, 2, 3
+IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS, IDX_MODE_PREFILL = 1, 2, 3, 4
 IDX_TOPK_UNSORTED = 1
 IDX_SELECT_NO_CUTOFF = 2
-IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK, IDX_DEVERR_SLOT = 1, 2, 4, 8
+IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK, IDX_DEVERR_SLOT, IDX_DEVERR_ORDER = 1, 2, 4, 8, 16
 IDX_HEADS, IDX_DIM, IDX_MAX_K = 64, 128, 2048
 IDX_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
 
 # Every symbol include/dsaidx.h declares.
-EXPORTS = ("idx_logits", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
+EXPORTS = ("idx_logits", "idx_logits_prefill", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
            "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
            "idx_last_error", "idx_version", "idx_device_errors", "idx_kcache_write", "idx_read_probe",
            "idx_candidate_blocks", "idx_candidate_blocks_workspace", "idx_sparse_attn_paged",
@@ -78,6 +78,7 @@ def lib() -> C.CDLL:
         L = C.CDLL(str(_LIB_PATH))
         P, I, I64, U32, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_uint32, C.c_size_t
         L.idx_logits.argtypes = [P, I, P, P, P, I, I64, P, P, I, P, I64, P]
+        L.idx_logits_prefill.argtypes = [P, I, P, P, P, I, I64, P, P, I, P, I64, P]
         L.idx_logits_paged.argtypes = [P, I, P, P, P, I, I64, I, P, I64, I64, P, P, I, P, I64, P]
         L.idx_logits_sparse_blocks.argtypes = [P, I, P, P, P, I, I64, P, P, P, I64, P, I, I, P, I64, P]
         L.idx_topk.argtypes = [P, I64, P, I64, I, I, P, P, I64, U32, P, SZ, P]
@@ -199,8 +200,10 @@ def _q_dtype(k_dtype: str) -> int:
 
 
 def idx_logits(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, ld: int | None = None,
-               out=None, stream=None):
-    """Scores of rows over contiguous key ranges (C: idx_logits). Returns fp32 [rows, ld]."""
+               out=None, stream=None, prefill: bool = False):
+    """Scores of rows over contiguous key ranges (C: idx_logits, or idx_logits_prefill when
+    ``prefill``: the rows are one prefill chunk's queries sharing the key array). Returns
+    fp32 [rows, ld]."""
     import torch
     rows = _check_score_inputs(q, w, k, k_scale, k_dtype, k.shape[0])
     _need(row_ks, "row_ks", torch.int32, numel=rows)
@@ -210,9 +213,9 @@ def idx_logits(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, ld: int | None
             raise ValueError("give ld or out")
         out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
     ld = _rows_out(out, "out", rows, torch.float32, 1)
-    _check(lib().idx_logits(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k), _ptr(k_scale),
-                            KDTYPES[k_dtype], k.shape[0], _ptr(row_ks), _ptr(row_ke), rows,
-                            _ptr(out), ld, _stream(stream)))
+    fn = lib().idx_logits_prefill if prefill else lib().idx_logits
+    _check(fn(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k), _ptr(k_scale), KDTYPES[k_dtype], k.shape[0],
+              _ptr(row_ks), _ptr(row_ke), rows, _ptr(out), ld, _stream(stream)))
     return out
 
 
@@ -404,12 +407,15 @@ class Problem:
         return self.st.rows
 
 
-def dense_problem(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, max_cols: int) -> Problem:
+def dense_problem(q, w, k, k_scale, row_ks, row_ke, *, k_dtype: str, max_cols: int,
+                  prefill: bool = False) -> Problem:
+    """idx_logits arguments (IDX_MODE_DENSE), or with ``prefill`` idx_logits_prefill's
+    (IDX_MODE_PREFILL: one prefill chunk's queries sharing the key array)."""
     import torch
     rows = _check_score_inputs(q, w, k, k_scale, k_dtype, k.shape[0])
     _need(row_ks, "row_ks", torch.int32, numel=rows)
     _need(row_ke, "row_ke", torch.int32, numel=rows)
-    st = idx_problem(mode=IDX_MODE_DENSE, rows=q.shape[0], q=q.data_ptr(),
+    st = idx_problem(mode=IDX_MODE_PREFILL if prefill else IDX_MODE_DENSE, rows=q.shape[0], q=q.data_ptr(),
                      q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
                      k=k.data_ptr(), k_scale=None if k_scale is None else k_scale.data_ptr(),
                      n_keys=k.shape[0], row_ks=row_ks.data_ptr(), row_ke=row_ke.data_ptr(),

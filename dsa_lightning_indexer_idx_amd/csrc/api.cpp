@@ -127,8 +127,9 @@ idx_status check_problem(const char* fn, const idx_problem* p, ScoreCall* c, con
   c->n_keys = p->n_keys;
   c->logits = (float*)logits;
   c->ld = ld;
-  if (p->mode == IDX_MODE_DENSE) {
+  if (p->mode == IDX_MODE_DENSE || p->mode == IDX_MODE_PREFILL) {
     c->source = SRC_DENSE;
+    c->shared_keys = p->mode == IDX_MODE_PREFILL ? 1 : 0;
     if (p->rows == 0) return IDX_OK;
     REQUIRE(p->n_keys >= 0, IDX_ERR_ARG, "%s: n_keys is negative", fn);
     REQUIRE(p->row_ks && p->row_ke, IDX_ERR_ARG, "%s: row_ks and row_ke must be non-null", fn);
@@ -178,7 +179,8 @@ idx_status check_problem(const char* fn, const idx_problem* p, ScoreCall* c, con
 // Width of the score matrix idx_select builds for a problem.
 int64_t select_width(const idx_problem* p) {
   switch (p->mode) {
-    case IDX_MODE_DENSE: return p->max_cols;
+    case IDX_MODE_DENSE:
+    case IDX_MODE_PREFILL: return p->max_cols;
     case IDX_MODE_PAGED: return p->bt_ld * p->page_size;
     case IDX_MODE_SPARSE_BLOCKS: return p->cand_ld * p->block_size;
   }
@@ -231,7 +233,7 @@ constexpr int kSelMinRows = 8;
 
 bool select_one_pass_shape(const idx_problem* p) {
   if (p->rows < kSelMinRows || p->rows > kBalancedMaxRows) return false;
-  if (p->mode == IDX_MODE_DENSE && p->q_dtype == IDX_FP8_E4M3 && p->k_dtype == IDX_FP8_E4M3 &&
+  if (p->mode == IDX_MODE_PREFILL && p->q_dtype == IDX_FP8_E4M3 && p->k_dtype == IDX_FP8_E4M3 &&
       p->rows >= kPrefillMinRows)
     return false;  // a prefill chunk: the tiled prefill kernel, then the top-k
   return true;
@@ -349,8 +351,8 @@ idx_status select_call(const char* fn, const idx_problem* p, int k, int32_t* out
     c.zero = (uint32_t*)topk_ws;
     c.zero_words = (int64_t)(topk_zeroed_bytes(p->rows, width) / 4);
   }
-  log_once("idx_select: %s then top-k (rows %d, width %lld, k %d)", prefill ? "prefill tiles" : "scan", p->rows,
-           (long long)width, k);
+  log_once("idx_select: %s then top-k, %s (rows %d, width %lld, k %d)", prefill ? "prefill tiles" : "scan",
+           topk_path(p->rows, width), p->rows, (long long)width, k);
   hipError_t e = launch_score(c, stream);
   if (e != hipSuccess) return launched(fn, e);
   t.logits = scores;
@@ -383,7 +385,36 @@ idx_status idx_logits(const void* q, int q_dtype, const float* w, const void* k,
   if (s != IDX_OK) return s;
   if (rows == 0) return ok();
   c.err = device_error_word();
+  log_once("idx_logits: %s (rows %d, ld %lld)",
+           prefill_applies(c) ? "tiled prefill kernel" : rows <= kBalancedMaxRows ? "balanced scan" : "row-item scan",
+           rows, (long long)ld);
   return launched("idx_logits", launch_score(c, (hipStream_t)stream));
+}
+
+idx_status idx_logits_prefill(const void* q, int q_dtype, const float* w, const void* k, const void* k_scale,
+                              int k_dtype, int64_t n_keys, const int32_t* row_ks, const int32_t* row_ke,
+                              int rows, float* logits, int64_t ld, idx_stream_t stream) {
+  idx_problem p{};
+  p.mode = IDX_MODE_PREFILL;
+  p.rows = rows;
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_dtype = k_dtype;
+  p.w = w;
+  p.k = k;
+  p.k_scale = k_scale;
+  p.n_keys = n_keys;
+  p.row_ks = row_ks;
+  p.row_ke = row_ke;
+  ScoreCall c;
+  idx_status s = check_problem("idx_logits_prefill", &p, &c, logits, ld, true);
+  if (s != IDX_OK) return s;
+  if (rows == 0) return ok();
+  c.err = device_error_word();
+  log_once("idx_logits_prefill: %s (rows %d, ld %lld)",
+           prefill_applies(c) ? "tiled prefill kernel" : rows <= kBalancedMaxRows ? "balanced scan" : "row-item scan",
+           rows, (long long)ld);
+  return launched("idx_logits_prefill", launch_score(c, (hipStream_t)stream));
 }
 
 idx_status idx_logits_paged(const void* q, int q_dtype, const float* w, const void* k_pages,
@@ -415,6 +446,8 @@ idx_status idx_logits_paged(const void* q, int q_dtype, const float* w, const vo
           "idx_logits_paged: bt_rows = %lld too small", (long long)bt_rows);
   c.bt_rows = bt_rows;
   c.err = device_error_word();
+  log_once("idx_logits_paged: %s (rows %d, page %d)", rows <= kBalancedMaxRows ? "balanced scan" : "row-item scan",
+           rows, page_size);
   return launched("idx_logits_paged", launch_score(c, (hipStream_t)stream));
 }
 
@@ -448,6 +481,8 @@ idx_status idx_logits_sparse_blocks(const void* q, int q_dtype, const float* w, 
           "idx_logits_sparse_blocks: ld = %lld < cand_ld * block_size = %lld", (long long)ld,
           (long long)(cand_ld * block_size));
   c.err = device_error_word();
+  log_once("idx_logits_sparse_blocks: %s (rows %d, block %d)",
+           rows <= kBalancedMaxRows ? "balanced scan" : "row-item scan", rows, block_size);
   return launched("idx_logits_sparse_blocks", launch_score(c, (hipStream_t)stream));
 }
 
@@ -484,6 +519,7 @@ idx_status idx_topk(const float* logits, int64_t ld, const int32_t* lens, int64_
   c.out_val = out_val;
   c.out_ld = out_ld;
   c.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
+  log_once("idx_topk: %s (rows %d, n_cols %lld, k %d)", topk_path(rows, n_cols), rows, (long long)n_cols, k);
   return launched(fn, launch_topk(c, workspace, (hipStream_t)stream));
 }
 

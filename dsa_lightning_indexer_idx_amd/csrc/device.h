@@ -24,6 +24,7 @@ constexpr unsigned kErrRange = 1u;
 constexpr unsigned kErrPage = 2u;
 constexpr unsigned kErrBlock = 4u;
 constexpr unsigned kErrSlot = 8u;
+constexpr unsigned kErrOrder = 16u;
 
 __device__ __forceinline__ void flag_error(unsigned* err, unsigned bits) {
   if (err) atomicOr(err, bits);

@@ -93,6 +93,8 @@ struct ScoreCall {
   int64_t zero_words;     // histogram and counters)
   const SelectState* sel; // optional: the one-pass selection (balanced scan only)
   int32_t* lens_out;      // optional: each row's scored length (columns a top-k may read)
+  int shared_keys;        // dense: 1 when the rows are one prefill chunk's queries over a
+                          // shared key array (the tiled kernel may take them)
 };
 
 // One top-k call.
@@ -126,8 +128,9 @@ int64_t select_scan_blocks(const ScoreCall& c);
 // survivors and writes the row.
 hipError_t launch_select_finish(const TopkCall& t, const SelectState& s, int64_t blocks, hipStream_t stream);
 
-// Dense fp8 calls with at least this many rows are taken as prefill chunks (rows that
-// share their keys) and run the tiled prefill kernel; fewer rows run the decode scan.
+// Dense fp8 calls the caller marks as a prefill chunk (shared_keys) with at least this
+// many rows run the tiled prefill kernel; fewer rows (too few query tiles to fill the
+// chip) and unmarked dense calls run the decode scan.
 constexpr int kPrefillMinRows = 256;
 bool prefill_applies(const ScoreCall& c);
 hipError_t launch_prefill(const ScoreCall& c, hipStream_t stream);
@@ -135,6 +138,8 @@ size_t topk_workspace_bytes(int rows, int64_t n_cols);
 // Leading bytes of the top-k workspace that must be zero when the top-k starts.
 size_t topk_zeroed_bytes(int rows, int64_t n_cols);
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
+// The top-k path launch_topk takes for rows of n_cols columns (for dispatch logging).
+const char* topk_path(int rows, int64_t n_cols);
 
 // One key-cache write (new bf16 keys quantised into the cache at their slots).
 struct KcacheCall {

@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kPThreads, DSAIDX_PREFILL_WAVES_PER_SIMD) void pref
 }
 
 bool prefill_applies(const ScoreCall& c) {
-  return c.source == SRC_DENSE && c.fmt == FMT_FP8 && c.rows >= kPrefillMinRows;
+  return c.source == SRC_DENSE && c.shared_keys && c.fmt == FMT_FP8 && c.rows >= kPrefillMinRows;
 }
 
 hipError_t launch_prefill(const ScoreCall& c, hipStream_t stream) {

@@ -157,6 +157,9 @@ struct SparseSrc {
       flag_error(err, kErrBlock);
       return {0, 0};
     }
+    // a row's candidate blocks must be strictly increasing (the column order then is the
+    // token order, which the selection's ties follow)
+    if (pos0 % block == 0 && pos0 >= block && R.cand_row[pos0 / block - 1] >= cb) flag_error(err, kErrOrder);
     const int64_t tok0 = cb * block + pos0 % block;
     const int64_t v = min(min(R.ncols - pos0, R.len - tok0), (int64_t)kTileTokens);
     return {R.base + (v > 0 ? tok0 : 0), (int32_t)v};

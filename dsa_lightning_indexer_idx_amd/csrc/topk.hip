@@ -1170,6 +1170,12 @@ static void launch_long(const TopkCall& c, const LongWs& ws, int64_t seg, int64_
   hipLaunchKernelGGL(topk_filter_kernel<V4>, grid, dim3(kSegThreads), 0, stream, c, ws, seg, (int)segs);
 }
 
+const char* topk_path(int rows, int64_t n_cols) {
+  if (n_cols <= kShortRow) return "short rows (one workgroup per row, row in LDS)";
+  if (n_cols <= kWideRow && rows <= device_cu_count()) return "wide rows (one workgroup per row, row in LDS)";
+  return "long rows (histogram, filter, finish over row segments)";
+}
+
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   if (c.rows <= 0) return hipSuccess;
   // rows start on 16-byte boundaries: whole groups of four are read with one load

@@ -100,11 +100,28 @@ typedef enum idx_dtype {
  * keys 0..p). Needs 0 <= row_ks <= row_ke <= n_keys and row_ke - row_ks <= ld
  * (device values; clamped, see above).
  * q_dtype must be IDX_BF16 with k_dtype IDX_BF16, else IDX_FP8_E4M3.
+ * The rows are scanned one by one (each key range read once per row), whatever
+ * their number: right for decode rows with their own contexts. A prefill chunk,
+ * whose queries share one key range, should call idx_logits_prefill.
  */
 idx_status idx_logits(const void* q, int q_dtype, const float* w, const void* k,
                       const void* k_scale, int k_dtype, int64_t n_keys,
                       const int32_t* row_ks, const int32_t* row_ke, int rows, float* logits,
                       int64_t ld, idx_stream_t stream);
+
+/*
+ * idx_logits_prefill: idx_logits for the queries of one prefill chunk, which share
+ * their key array (the fp8_mqa_logits step of the vLLM sparse_indexer page, per-query
+ * cu_seqlen_ks/ke over one K). Same arguments and results as idx_logits. fp8 calls of
+ * at least 256 rows run the tiled MFMA kernel, which reads each key tile once for a
+ * block of queries and the union of their ranges; fewer rows, or bf16 / MXFP4 keys, run
+ * the row scan. Rows with disjoint ranges are still scored correctly, only slower than
+ * with idx_logits (each query block walks the union of its rows' ranges).
+ */
+idx_status idx_logits_prefill(const void* q, int q_dtype, const float* w, const void* k,
+                              const void* k_scale, int k_dtype, int64_t n_keys,
+                              const int32_t* row_ks, const int32_t* row_ke, int rows, float* logits,
+                              int64_t ld, idx_stream_t stream);
 
 /*
  * idx_logits_paged: rows that score a paged key cache.
@@ -247,7 +264,8 @@ size_t idx_sparse_attn_workspace(int rows, int heads, int k);
 typedef enum idx_mode {
     IDX_MODE_DENSE = 1,        /* idx_logits arguments */
     IDX_MODE_PAGED = 2,        /* idx_logits_paged arguments */
-    IDX_MODE_SPARSE_BLOCKS = 3 /* idx_logits_sparse_blocks arguments */
+    IDX_MODE_SPARSE_BLOCKS = 3, /* idx_logits_sparse_blocks arguments */
+    IDX_MODE_PREFILL = 4        /* idx_logits_prefill arguments (idx_logits's) */
 } idx_mode;
 
 /* One scoring problem: the arguments of the matching idx_logits* call. Fields a
@@ -335,6 +353,9 @@ int idx_version(void);
                                 key range (id * block_size >= row_ke - row_ks); its
                                 columns are scored -inf */
 #define IDX_DEVERR_SLOT 8u   /* key-cache slot at or past n_slots (idx_kcache_write) */
+#define IDX_DEVERR_ORDER 16u /* a row's candidate blocks not strictly increasing: the
+                                columns are still scored as given, but equal scores then
+                                no longer break ties by token position */
 int idx_device_errors(idx_stream_t stream);
 
 /* ------------------------------------------------------------------ key-cache writer */

@@ -50,6 +50,8 @@ class Uploaded:
         self.case = case
         kind = type(case).__name__
         self.kind = kind
+        # prefill chunks (and cases that ask to be run as one) go through the prefill entry
+        self.prefill = kind == "Dense" and (case.name == "prefill_chunk" or bool(case.meta.get("as_prefill")))
         self.q, self.w = dev(case.q), dev(case.w)
         if kind == "Paged":
             self.k, self.sc = dev(case.k_pages), dev(case.k_scale_pages)
@@ -65,7 +67,7 @@ class Uploaded:
         c = self.case
         if self.kind == "Dense":
             return D.idx_logits(self.q, self.w, self.k, self.sc, self.ks, self.ke, k_dtype=c.k_dtype,
-                                ld=ld or c.max_cols)
+                                ld=ld or c.max_cols, prefill=self.prefill)
         if self.kind == "Paged":
             return D.idx_logits_paged(self.q, self.w, self.k, self.sc, self.bt, self.sl,
                                       k_dtype=c.k_dtype, row_req=self.rr, ld=ld)
@@ -77,7 +79,7 @@ class Uploaded:
         c = self.case
         if self.kind == "Dense":
             return D.dense_problem(self.q, self.w, self.k, self.sc, self.ks, self.ke,
-                                   k_dtype=c.k_dtype, max_cols=c.max_cols)
+                                   k_dtype=c.k_dtype, max_cols=c.max_cols, prefill=self.prefill)
         if self.kind == "Paged":
             return D.paged_problem(self.q, self.w, self.k, self.sc, self.bt, self.sl,
                                    k_dtype=c.k_dtype, row_req=self.rr)
@@ -87,6 +89,27 @@ class Uploaded:
     def select(self, k=None, sorted=True):
         k = self.case.topk if k is None else k
         return D.idx_select(self.problem(), k, sorted=sorted)
+
+
+# (check, workload, detail) -> (max |err|, max err/tol, rows checked): printed as a parity
+# summary at the end of the run (tests/conftest.py)
+PARITY = {}
+
+
+def record(check: str, workload: str, detail: str, max_err: float, max_ratio: float, rows: str) -> None:
+    PARITY[(check, workload, detail)] = (max_err, max_ratio, rows)
+
+
+def score_error_stats(gpu, ref):
+    """(max |gpu - ref|, max |gpu - ref| / tol) over the finite reference scores."""
+    gpu = np.asarray(gpu)
+    ref = np.asarray(ref)
+    ri = np.isneginf(ref)
+    g, r = gpu[~ri].astype(np.float64), ref[~ri].astype(np.float64)
+    if not g.size:
+        return 0.0, 0.0
+    err = np.abs(g - r)
+    return float(err.max()), float((err / (ATOL + RTOL * np.abs(r))).max())
 
 
 def assert_scores_close(gpu, ref, what=""):
@@ -112,6 +135,7 @@ def assert_selection_matches(gpu_idx, ref_idx, ref_scores_of, kth_ref, what=""):
     scores within twice the tolerance of the oracle's k-th value.
     ``ref_scores_of(r, idx_array)`` returns the oracle scores of the given positions."""
     total, inter = 0, 0
+    worst = 0.0  # largest |score - k-th| / limit over the disagreements
     for r in range(ref_idx.shape[0]):
         a = set(int(x) for x in gpu_idx[r] if x >= 0)
         b = set(int(x) for x in ref_idx[r] if x >= 0)
@@ -123,7 +147,9 @@ def assert_selection_matches(gpu_idx, ref_idx, ref_scores_of, kth_ref, what=""):
             v = ref_scores_of(r, diff).astype(np.float64)
             kth = float(kth_ref[r])
             lim = 2 * (ATOL + RTOL * abs(kth))
+            worst = max(worst, float((np.abs(v - kth) / lim).max()))
             assert np.all(np.abs(v - kth) <= lim), (
                 f"{what}: row {r}: disagreement far from the cut (k-th {kth}, got {v[:5]})")
     assert total == 0 or inter / total >= 0.999, f"{what}: overlap {inter}/{total}"
+    assert_selection_matches.worst = worst
     return inter, total

@@ -208,10 +208,17 @@ def test_select_workspace_sizes(L):
                  n_cols=NC, block_size=128)
     one, two = _select_layouts(L, 64, 8192)
     assert L.idx_select_workspace(C.byref(p), 2048) == max(one, two)
-    # a prefill chunk (dense fp8, >= 256 rows) takes the tiled kernel and the two-pass layout
-    p = _problem(rows=300, max_cols=5000)
-    _, two = _select_layouts(L, 300, 5000)
+    # a prefill chunk (IDX_MODE_PREFILL, fp8, >= 256 rows) takes the tiled kernel and the
+    # two-pass layout; the same rows as dense decode rows can take the one-pass selection
+    p = _problem(rows=300, max_cols=5000, mode=D.IDX_MODE_PREFILL)
+    one, two = _select_layouts(L, 300, 5000)
     assert L.idx_select_workspace(C.byref(p), 2048) == two
+    p = _problem(rows=300, max_cols=5000)
+    assert L.idx_select_workspace(C.byref(p), 2048) == max(one, two)
+    # a small prefill chunk (fewer than 256 rows) runs the scan like dense rows
+    p = _problem(rows=100, max_cols=5000, mode=D.IDX_MODE_PREFILL)
+    one, two = _select_layouts(L, 100, 5000)
+    assert L.idx_select_workspace(C.byref(p), 2048) == max(one, two)
 
 
 SELECT_CASES = [

@@ -6,7 +6,7 @@ import pytest
 
 import oracle as O
 import synth
-from gpu_util import Uploaded, assert_scores_close, host, require_gpu, say
+from gpu_util import record, score_error_stats, Uploaded, assert_scores_close, host, require_gpu, say
 from full_cases import full_case
 
 pytestmark = pytest.mark.gpu
@@ -22,6 +22,11 @@ def _ref_logits(case, ld=None):
                               case.k_dtype, case.block_table, case.seq_lens, case.row_req, ld=ld)
     return O.logits_sparse(case.q, case.q_dtype, case.w, case.k, case.k_scale, case.k_dtype,
                            case.row_ks, case.row_ke, case.cand, case.n_cols, case.block, ld=ld)
+
+
+def _as_prefill(case):
+    case.meta["as_prefill"] = True
+    return case
 
 
 SMALL = {
@@ -42,9 +47,13 @@ SMALL = {
     "sparse_fp8_ragged": lambda: synth.sparse_blocks(seed=109, rows=4, ctx=3000, n_blocks=5,
                                                      kdtype="fp8", ragged=True),
     "prefill_q300_prior700": lambda: synth.prefill_chunk(seed=110, q_tokens=300, prior=700),
-    # 300 rows take the tiled prefill kernel even though their ranges are disjoint and ragged
+    # 300 decode rows with disjoint ragged ranges: the row scan
     "dense_many_rows_disjoint": lambda: synth.batched_decode(seed=116, rows=300, n=700, ragged=True,
                                                              gap=9),
+    # the same rows handed over as a prefill chunk: the tiled kernel walks the union of each
+    # query block's ranges (slow, still exact)
+    "dense_many_rows_disjoint_as_prefill": lambda: _as_prefill(synth.batched_decode(seed=116, rows=300, n=700,
+                                                                                    ragged=True, gap=9)),
     "prefill_q1030_prior64": lambda: synth.prefill_chunk(seed=117, q_tokens=1030, prior=64),
     # no prior context: the first query blocks see fewer keys than one 64-key tile, and the
     # 260-key array ends in a 4-key tile (tile loads clamped to the last key)
@@ -61,6 +70,36 @@ def test_scores_match_oracle(name):
     r = _ref_logits(case, ld=g.shape[1])
     err = assert_scores_close(g, r, name)
     say(f"[scores] {name}: max |err| = {err:.3g}")
+
+
+@pytest.mark.parametrize("name", ["tiny_dense_bf16_n4096", "dense_bf16_ragged"])
+def test_bf16_scores_within_the_fp32_rounding_bound(name):
+    """bf16 keys: every product q_d k_d is exact in fp32, so a score can only be off by the
+    fp32 rounding of its two sums, 128 products per head and 64 weighted heads: at most
+    about 2^-24 (128 A + 65 A) with A = sum_j |w_j| sum_d |q_jd k_d| (standard bound for
+    recursive summation, either order). The test allows 2^-24 * 256 A, far tighter than
+    the 1e-2 absolute tolerance on scores that spread over about 0.06 here."""
+    require_gpu()
+    case = SMALL[name]()
+    g = host(Uploaded(case).logits())
+    r = _ref_logits(case, ld=g.shape[1])
+    q = np.abs(O.decode_bf16(case.q).astype(np.float64)).reshape(case.rows, 64, 128)
+    k = np.abs(O.decode_bf16(case.k).astype(np.float64)).reshape(-1, 128)
+    w = np.abs(case.w.astype(np.float64)).reshape(case.rows, 64)
+    worst = 0.0
+    for row in range(case.rows):
+        s0, s1 = int(case.row_ks[row]), int(case.row_ke[row])
+        A = w[row] @ (q[row] @ k[s0:s1].T)  # [s1 - s0]
+        tol = 2.0 ** -24 * 256 * A
+        err = np.abs(g[row, :s1 - s0].astype(np.float64) - r[row, :s1 - s0])
+        worst = max(worst, float((err / tol).max()))
+        assert np.all(err <= tol), f"{name}: row {row}: {(err > tol).sum()} scores past the fp32 bound"
+    err, ratio = score_error_stats(g, r)
+    record("scores", "tiny dense bf16" if name.startswith("tiny") else "dense bf16 ragged", "",
+           err, ratio, f"{case.rows}/{case.rows}")
+    record("bf16", "tiny dense bf16" if name.startswith("tiny") else "dense bf16 ragged", "fp32 bound ",
+           err, worst, f"{case.rows}/{case.rows}")
+    say(f"[scores] {name}: max err / fp32 rounding bound = {worst:.3f}")
 
 
 def test_paged_identity_table_equals_contiguous_bitwise():
@@ -124,19 +163,53 @@ def test_bad_device_metadata_is_clamped_and_reported():
     assert D.idx_device_errors() == 0
 
 
-FULL_SAMPLES = {2: [0, 17, 31], 3: [0, 40, 63], 4: [0, 1, 2047, 4095], 5: [0, 31, 63], 6: [0, 22, 63]}
+def test_candidate_block_checks_are_reported():
+    """Candidate lists as the two-level path hands them over (ascending, unique, inside the
+    row) raise no device error; a repeated block or a descending pair sets
+    IDX_DEVERR_ORDER, a block past the row's range IDX_DEVERR_BLOCK (its columns scored
+    -inf, like the oracle), and the other rows still match the oracle."""
+    require_gpu()
+    import dsa_lightning_indexer_idx_amd as D
+    case = synth.sparse_blocks(seed=119, rows=4, ctx=4096, n_blocks=6, kdtype="fp8", poison_noncand=False)
+    D.idx_device_errors()
+    host(Uploaded(case).logits())
+    assert D.idx_device_errors() == 0, "well-formed candidate lists"
+    for what, edit, bit in (("repeated", lambda c: c.__setitem__((1, 3), c[1, 2]), D.IDX_DEVERR_ORDER),
+                            ("descending", lambda c: c.__setitem__((1, slice(2, 4)), c[1, 2:4][::-1].copy()),
+                             D.IDX_DEVERR_ORDER),
+                            ("past the row", lambda c: c.__setitem__((1, 5), 4096 // case.block + 3),
+                             D.IDX_DEVERR_BLOCK)):
+        bad = synth.sparse_blocks(seed=119, rows=4, ctx=4096, n_blocks=6, kdtype="fp8", poison_noncand=False)
+        bad.cand = bad.cand.copy()
+        edit(bad.cand)
+        g = host(Uploaded(bad).logits())
+        assert D.idx_device_errors() & bit, what
+        r = _ref_logits(bad, ld=g.shape[1])
+        assert_scores_close(g, r, f"candidate lists, {what}")
+
+
+WORKLOAD_NAMES = {2: "batched decode 32x32K fp8", 3: "paged decode 128K fp8", 4: "prefill 4096x8192 fp8",
+                  5: "two-level 64x8192 mxfp4", 6: "paged decode 128K mxfp4"}
+
+
+def full_rows(cfg, rows):
+    """Every row of the workload, or every 8th row (rows 0 and 4095 included) of the prefill
+    chunk."""
+    return list(range(0, rows, 8)) + [rows - 1] if cfg == 4 else list(range(rows))
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
-def test_full_size_sampled_rows(cfg):
+def test_full_size_every_row(cfg):
     """The workloads at their stated sizes, in the launch shape the benchmark uses; the oracle
-    checks a sample of rows."""
+    checks every row (every 8th of the prefill chunk, with the first and last)."""
     require_gpu()
     case, up = full_case(cfg)
     say(f"[scores] full workload {cfg}: rows={case.rows} tokens={case.tokens}")
     g = host(up.logits())
-    rows = FULL_SAMPLES[cfg]
-    sub = O.subset_rows(case, rows)
+    rows = full_rows(cfg, case.rows)
+    sub = case if len(rows) == case.rows else O.subset_rows(case, rows)
     r = _ref_logits(sub, ld=g.shape[1])
-    err = assert_scores_close(g[rows], r, f"workload {cfg}")
-    say(f"[scores] full workload {cfg}: sampled rows {rows} max |err| = {err:.3g}")
+    assert_scores_close(g[rows], r, f"workload {cfg}")
+    err, ratio = score_error_stats(g[rows], r)
+    record("scores", WORKLOAD_NAMES[cfg], "", err, ratio, f"{len(rows)}/{case.rows}")
+    say(f"[scores] full workload {cfg}: {len(rows)} rows, max |err| = {err:.3g}, max err/tol = {ratio:.3f}")

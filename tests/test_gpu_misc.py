@@ -59,3 +59,30 @@ def test_binding_rejects_wrong_sizes_before_any_launch():
     with pytest.raises(ValueError, match="indices must have"):
         D.idx_sparse_attn_paged(qa, kv, bt, sl, ix[:1], 0.1)
     torch.cuda.synchronize()
+
+
+def test_dispatch_log_lines():
+    """IDX_LOG=1: each distinct dispatch decision is printed once to stderr (checked in a
+    child process, since the setting is read once per process)."""
+    require_gpu()
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})\n"
+        "import synth, torch\n"
+        "from gpu_util import Uploaded\n"
+        "up = Uploaded(synth.paged_decode(seed=401, rows=12, min_len=1000, max_len=9000))\n"
+        "for _ in range(3): up.select(512)\n"
+        "up = Uploaded(synth.paged_decode(seed=402, rows=2, min_len=1000, max_len=9000))\n"
+        "up.select(512); up.logits()\n"
+        "torch.cuda.synchronize()\n"
+    ).format(root=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+             tests=os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, IDX_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[dsaidx]")]
+    assert sum("idx_select: one pass" in l for l in lines) == 1, lines
+    assert any("idx_select: scan then top-k" in l for l in lines), lines
+    assert any(l.startswith("[dsaidx] idx_logits_paged: balanced scan") for l in lines), lines

@@ -8,7 +8,7 @@ import dsa_lightning_indexer_idx_amd as D
 import oracle as O
 import synth
 from full_cases import full_case
-from gpu_util import Uploaded, assert_selection_matches, dev, host, require_gpu, say
+from gpu_util import record, Uploaded, assert_selection_matches, dev, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -107,26 +107,71 @@ def test_unsorted_select_same_set():
         assert sorted(a[r].tolist()) == sorted(b[r].tolist())
 
 
-FULL = {2: [0, 31], 3: [0, 63], 4: [0, 4095], 5: [0, 63], 6: [0, 63]}
+WORKLOAD_NAMES = {2: "batched decode 32x32K fp8", 3: "paged decode 128K fp8", 4: "prefill 4096x8192 fp8",
+                  5: "two-level 64x8192 mxfp4", 6: "paged decode 128K mxfp4"}
+
+
+def _oracle_select(case, ks):
+    """The oracle's selection at each k from one computation of its scores: {k: (idx, val)}
+    (idx: key positions as idx_select returns them) and the scores."""
+    _, _, lg = O.select_case(case, k=max(ks), with_logits=True)
+    kind = type(case).__name__
+    if kind == "Paged":
+        lens = case.seq_lens
+    elif kind == "Sparse":
+        lens = case.n_cols
+    else:
+        lens = case.row_ke.astype(np.int64) - case.row_ks
+    lens = np.clip(lens, 0, lg.shape[1]).astype(np.int32)
+    out = {}
+    for k in ks:
+        idx, val = O.topk(lg, k, lens=lens)
+        if kind == "Sparse":
+            idx = O.columns_to_tokens(idx, case.cand, case.block)
+        out[k] = (idx, val)
+    return out, lg
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_full_size_select(cfg):
-    """The workloads at full size through idx_select (the benchmark's call); the oracle
-    checks sampled rows end to end, and every row is checked against idx_topk."""
+    """The workloads at full size through idx_select (the benchmark's call): every row
+    equals idx_topk over idx_logits* bit for bit, and the oracle checks every row end to
+    end (every 8th row of the prefill chunk, with the first and last)."""
     require_gpu()
     case, up = full_case(cfg)
     ks = [2048, 1024, 512] if cfg == 3 else [case.topk]
+    rows = list(range(0, case.rows, 8)) + [case.rows - 1] if cfg == 4 else list(range(case.rows))
+    sub = case if len(rows) == case.rows else O.subset_rows(case, rows)
+    say(f"[select] full workload {cfg}: oracle over {len(rows)} rows")
+    ref, r_lg = _oracle_select(sub, ks)
     for k in ks:
         say(f"[select] full workload {cfg} k={k}")
         s_idx, _ = _self_consistent(up, k)
-        rows = FULL[cfg]
-        sub = O.subset_rows(case, rows)
-        r_idx, r_val, r_lg = O.select_case(sub, k=k, with_logits=True)
+        r_idx, r_val = ref[k]
         kth = np.array([r_val[i][max(0, int((r_idx[i] >= 0).sum()) - 1)] for i in range(len(rows))])
         inter, total = assert_selection_matches(s_idx[rows], r_idx, _ref_scores_fn(sub, r_lg), kth,
                                                 f"workload {cfg} k={k}")
-        say(f"[select] full workload {cfg} k={k}: sampled overlap {inter}/{total}")
+        worst = assert_selection_matches.worst
+        record("select", WORKLOAD_NAMES[cfg], f"k={k} ovl {inter / max(total, 1):.5f}", 0.0, worst,
+               f"{len(rows)}/{case.rows}")
+        say(f"[select] full workload {cfg} k={k}: overlap {inter}/{total}, worst disagreement {worst:.3f} of limit")
+
+
+def test_batched_decode_256_rows():
+    """256 decode rows of 32768 fp8 keys each (rows with their own contexts, as many as a
+    prefill chunk has tiles of): idx_select takes the row scan and the one-pass selection,
+    equals idx_topk over idx_logits bit for bit and matches the oracle on every row."""
+    require_gpu()
+    case = synth.batched_decode(seed=7, rows=256)
+    up = Uploaded(case)
+    say("[select] batched decode 256 x 32768")
+    s_idx, _ = _self_consistent(up, 2048)
+    ref, r_lg = _oracle_select(case, [2048])
+    r_idx, r_val = ref[2048]
+    kth = np.array([r_val[i][max(0, int((r_idx[i] >= 0).sum()) - 1)] for i in range(case.rows)])
+    inter, total = assert_selection_matches(s_idx, r_idx, _ref_scores_fn(case, r_lg), kth, "batched 256 x 32K")
+    record("select", "batched decode 256x32K fp8", f"k=2048 ovl {inter / max(total, 1):.5f}", 0.0,
+           assert_selection_matches.worst, f"{case.rows}/{case.rows}")
 
 
 def test_long_rows_adversarial():
