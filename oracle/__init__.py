@@ -57,6 +57,8 @@ def _load(path) -> C.CDLL:
     L.ref_logits_paged.argtypes = [P, I, P, P, P, I, I, P, I64, P, P, I, I, I, P, I64]
     L.ref_logits_sparse.restype = None
     L.ref_logits_sparse.argtypes = [P, I, P, P, P, I, P, P, P, I64, P, I, I, I, I, P, I64]
+    L.ref_logits_paged_sparse.restype = None
+    L.ref_logits_paged_sparse.argtypes = [P, I, P, P, P, I, I, P, I64, P, P, P, I64, P, I, I, I, I, P, I64]
     L.ref_topk.restype = None
     L.ref_topk.argtypes = [P, I64, P, I64, I, I, P, P, I64]
     L.ref_encode_fp8_e4m3fn.argtypes = [C.c_float]
@@ -179,6 +181,25 @@ def logits_sparse(q, q_dtype, w, k, k_scale, k_dtype, row_ks, row_ke, cand, n_co
     return out
 
 
+def logits_paged_sparse(q, q_dtype, w, k_pages, k_scale_pages, k_dtype, block_table, seq_lens, cand, n_cols,
+                        block, row_req=None, ld=None) -> np.ndarray:
+    """fp32 [rows, ld] over candidate columns of paged rows: column c is the row's logical
+    token cand[c//block]*block + c%block, read through the row's page table."""
+    q, w, kp, sp = _c(q), _c(w, np.float32), _c(k_pages), _c(k_scale_pages)
+    bt, sl = _c(block_table, np.int32), _c(seq_lens, np.int32)
+    rr = _c(row_req, np.int32)
+    cand, n_cols = _c(cand, np.int32), _c(n_cols, np.int32)
+    rows, heads, dim = _shape_q(q)
+    page = kp.shape[1]
+    if ld is None:
+        ld = cand.shape[1] * block
+    out = np.empty((rows, ld), np.float32)
+    lib().ref_logits_paged_sparse(_p(q), DTYPES[q_dtype], _p(w), _p(kp), _p(sp), DTYPES[k_dtype], page,
+                                  _p(bt), bt.shape[1], _p(sl), _p(rr), _p(cand), cand.shape[1], _p(n_cols),
+                                  block, rows, heads, dim, _p(out), ld)
+    return out
+
+
 # ------------------------------------------------------------------ selection
 
 
@@ -239,6 +260,12 @@ def select_case(case, k=None, with_logits=False):
                            case.row_ks, case.row_ke, case.cand, case.n_cols, case.block)
         cidx, val = topk(lg, k)
         idx = columns_to_tokens(cidx, case.cand, case.block)
+    elif kind == "PagedSparse":
+        lg = logits_paged_sparse(case.q, case.q_dtype, case.w, case.k_pages, case.k_scale_pages, case.k_dtype,
+                                 case.block_table, case.seq_lens, case.cand, case.n_cols, case.block,
+                                 row_req=case.row_req)
+        cidx, val = topk(lg, k)
+        idx = columns_to_tokens(cidx, case.cand, case.block)
     else:
         raise TypeError(kind)
     return (idx, val, lg) if with_logits else (idx, val)
@@ -255,10 +282,10 @@ def subset_rows(case, rows):
     if kind in ("Dense", "Sparse"):
         c.row_ks = case.row_ks[rows]
         c.row_ke = case.row_ke[rows]
-    if kind == "Sparse":
+    if kind in ("Sparse", "PagedSparse"):
         c.cand = case.cand[rows]
         c.n_cols = case.n_cols[rows]
-    if kind == "Paged":
+    if kind in ("Paged", "PagedSparse"):
         c.seq_lens = case.seq_lens[rows]
         if case.row_req is None:
             c.row_req = rows.astype(np.int32)

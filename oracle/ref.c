@@ -23,10 +23,11 @@
  *    group-32 scales (OCP Microscaling v1.0), bf16; an fp8 key is its code times
  *    the token's fp32 scale, which the llama.cpp thread describes as a
  *    quantisation scale (a multiplier at dequantisation).
- *  - The three ways a row names its keys: a contiguous range [ks, ke) (vLLM
+ *  - The ways a row names its keys: a contiguous range [ks, ke) (vLLM
  *    sparse_indexer page: row_ks / row_ke), a block table of fixed-size pages
- *    (same page: block_table, row_indices), and candidate blocks with a valid
- *    sparse-column count (same page: sparse_indices, end).
+ *    (same page: block_table, row_indices), candidate blocks with a valid
+ *    sparse-column count (same page: sparse_indices, end), and candidate blocks of
+ *    a paged row (sparse_indices with a per-row block_table).
  *
  * Parallelism: rows are independent (every query is one row in the varlen
  * decode layout), so rows are spread over OpenMP threads. Nothing is blocked,
@@ -239,6 +240,46 @@ void ref_logits_sparse(const void* q, int q_dtype, const float* w, const uint8_t
             }
             int64_t s = row_ks[r] + tok;
             decode_key(k + s * kb, (const uint8_t*)k_scale + s * sb, k_dtype, dim, kd);
+            logits[r * ld + c] = index_score(qd, w + (int64_t)r * heads, heads, dim, kd);
+        }
+        free(qd);
+        free(kd);
+    }
+}
+
+/* Candidate blocks over a paged cache (the two-level decode layout of the vLLM
+ * sparse_indexer page: a decode row carries a per-row page table next to its
+ * sparse_indices, and the indexer cache's page is a multiple of the sparse block).
+ * Column c names the row's logical token cand[r][c / block] * block + c % block; it
+ * is scored when c < n_cols[r] and the token is < seq_lens[r], reading the key at
+ * page block_table[req][token / page_size], slot token % page_size, with req =
+ * row_req[r] (or r). Every other column of [0, ld) is -inf. */
+void ref_logits_paged_sparse(const void* q, int q_dtype, const float* w, const uint8_t* k_pages,
+                             const void* k_scale_pages, int k_dtype, int page_size,
+                             const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
+                             const int32_t* row_req, const int32_t* cand, int64_t cand_ld,
+                             const int32_t* n_cols, int block, int rows, int heads, int dim,
+                             float* logits, int64_t ld)
+{
+    int kb = key_bytes(k_dtype, dim);
+    int64_t sb = scale_bytes(k_dtype, dim);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < rows; r++) {
+        double* qd = malloc(sizeof(double) * (size_t)heads * dim);
+        double* kd = malloc(sizeof(double) * (size_t)dim);
+        decode_query(q, q_dtype, r, heads, dim, qd);
+        int64_t req = row_req ? row_req[r] : r;
+        for (int64_t c = 0; c < ld; c++) {
+            int64_t b = c / block;
+            int64_t tok = b < cand_ld ? (int64_t)cand[r * cand_ld + b] * block + c % block : -1;
+            if (c >= n_cols[r] || b >= cand_ld || tok < 0 || tok >= seq_lens[r]) {
+                logits[r * ld + c] = -INFINITY;
+                continue;
+            }
+            int64_t page = block_table[req * bt_ld + tok / page_size];
+            int64_t slot = page * page_size + tok % page_size;
+            decode_key(k_pages + slot * kb, (const uint8_t*)k_scale_pages + slot * sb, k_dtype,
+                       dim, kd);
             logits[r * ld + c] = index_score(qd, w + (int64_t)r * heads, heads, dim, kd);
         }
         free(qd);

@@ -392,6 +392,84 @@ def sparse_blocks(seed: int = 5, rows: int = 64, ctx: int = 131072, n_blocks: in
 
 
 @dataclass
+class PagedSparse:
+    """Two-level rows over a paged cache: column c names the row's logical token
+    cand[r][c // block] * block + c % block, which lives in page
+    block_table[req][token // page], slot token % page (req = row_req[r] or r)."""
+    name: str
+    q: np.ndarray
+    q_dtype: str
+    w: np.ndarray
+    k_pages: np.ndarray
+    k_scale_pages: np.ndarray
+    k_dtype: str
+    page_size: int
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    row_req: np.ndarray | None
+    cand: np.ndarray
+    n_cols: np.ndarray
+    block: int
+    topk: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def max_cols(self) -> int:
+        return int(self.cand.shape[1] * self.block)
+
+    @property
+    def tokens(self) -> int:
+        return int(self.n_cols.sum())
+
+
+def page_sparse(sp: Sparse, page: int = 64, seed: int = 0, permute: bool = True, row_req: bool = False,
+                spare_pages: int = 8) -> PagedSparse:
+    """The candidate-block case ``sp`` with each row's context moved into pages: row r's
+    tokens [row_ks, row_ks + ctx) fill its ctx / page pages, taken from a pool that is a
+    random permutation (``permute``) with ``spare_pages`` poisoned pages besides; the table
+    maps logical page p of request req(r) to its physical page; ``row_req`` shuffles the
+    rows' requests. The scores of every column equal those of ``sp`` (same key bytes)."""
+    g = np.random.default_rng([seed, 77])
+    ctx = int(sp.meta["ctx"])
+    assert ctx % page == 0 and page % 64 == 0
+    rows, npg = sp.rows, ctx // page
+    P = rows * npg + spare_pages
+    phys = (g.permutation(P) if permute else np.arange(P)).astype(np.int32)
+    kb = sp.k.shape[1]
+    if sp.k_dtype == "fp8":
+        kp = np.full((P, page, kb), FP8_NAN, np.uint8)
+        scp = np.full((P, page), np.nan, np.float32)
+    else:
+        kp = np.zeros((P, page, kb), np.uint8)
+        scp = np.full((P, page) + sp.k_scale.shape[1:], UE8M0_NAN, np.uint8)
+    used = phys[:rows * npg]
+    kp[used] = sp.k[:rows * ctx].reshape(rows * npg, page, kb)
+    scp[used] = sp.k_scale[:rows * ctx].reshape((rows * npg, page) + sp.k_scale.shape[1:])
+    reqs = (g.permutation(rows) if row_req else np.arange(rows)).astype(np.int32)
+    bt = np.full((rows, npg), -1, np.int32)
+    for i in range(rows):
+        bt[reqs[i]] = used[i * npg:(i + 1) * npg]
+    lens = (sp.row_ke - sp.row_ks).astype(np.int32)
+    return PagedSparse("paged_sparse_blocks", sp.q, sp.q_dtype, sp.w, kp, scp, sp.k_dtype, page, bt, lens,
+                       reqs if row_req else None, sp.cand, sp.n_cols, sp.block, sp.topk,
+                       {**sp.meta, "page": page, "permute": permute})
+
+
+def paged_sparse_blocks(seed: int = 5, rows: int = 64, ctx: int = 131072, n_blocks: int = 64, block: int = 128,
+                        page: int = 64, topk: int = 2048, kdtype: str = "mxfp4", ragged: bool = False,
+                        row_req: bool = False, poison_noncand: bool = True) -> PagedSparse:
+    """The two-level workload over a paged cache: sparse_blocks(...) paged with 64-token
+    pages from a permuted pool."""
+    sp = sparse_blocks(seed=seed, rows=rows, ctx=ctx, n_blocks=n_blocks, block=block, topk=topk, kdtype=kdtype,
+                       ragged=ragged, poison_noncand=poison_noncand)
+    return page_sparse(sp, page=page, seed=seed, row_req=row_req)
+
+
+@dataclass
 class Scores:
     """A candidate-source layer's score matrix (fp32 [rows, ld]) with row lengths."""
     name: str
@@ -455,7 +533,7 @@ def paged_decode_mxfp4(seed: int = 6):
 
 
 def full_size(idx: int):
-    """The five workloads at their stated sizes, by number 1..5, and 6: workload 3 with
-    MXFP4 keys."""
+    """The five workloads at their stated sizes, by number 1..5; 6: workload 3 with MXFP4
+    keys; 7: workload 5 over a paged cache (64-token pages, permuted pool)."""
     return {1: tiny_dense, 2: batched_decode, 3: paged_decode, 4: prefill_chunk,
-            5: sparse_blocks, 6: paged_decode_mxfp4}[idx]()
+            5: sparse_blocks, 6: paged_decode_mxfp4, 7: paged_sparse_blocks}[idx]()

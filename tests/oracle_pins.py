@@ -540,6 +540,53 @@ def pin_sparse_columns():
                 assert lg[r, c] == -np.inf, f"row {r} col {c} should be masked"
 
 
+def pin_paged_sparse_equals_contiguous_sparse():
+    """Candidate blocks read through a page table score exactly like the same candidate
+    blocks of a contiguous row (same key bytes), for an identity and a permuted page pool,
+    with and without a row -> request map, fp8 and MXFP4, ragged lengths and column
+    counts (the last candidate block partly past the row)."""
+    for kd, seed in (("fp8", 81), ("mxfp4", 82)):
+        sp = synth.sparse_blocks(seed=seed, rows=4, ctx=2048, n_blocks=5, block=128, topk=50, kdtype=kd,
+                                 ragged=True, poison_noncand=False)
+        ref = O.logits_sparse(sp.q, "fp8", sp.w, sp.k, sp.k_scale, kd, sp.row_ks, sp.row_ke, sp.cand, sp.n_cols,
+                              sp.block)
+        for permute, row_req in ((False, False), (True, False), (True, True)):
+            ps = synth.page_sparse(sp, page=64, seed=seed, permute=permute, row_req=row_req)
+            got = O.logits_paged_sparse(ps.q, "fp8", ps.w, ps.k_pages, ps.k_scale_pages, kd, ps.block_table,
+                                        ps.seq_lens, ps.cand, ps.n_cols, ps.block, row_req=ps.row_req)
+            assert np.array_equal(got, ref), f"{kd} permute={permute} row_req={row_req}: paged-sparse != sparse"
+        # 128-token pages (two candidate blocks... one block per page)
+        ps = synth.page_sparse(sp, page=128, seed=seed, row_req=True)
+        got = O.logits_paged_sparse(ps.q, "fp8", ps.w, ps.k_pages, ps.k_scale_pages, kd, ps.block_table,
+                                    ps.seq_lens, ps.cand, ps.n_cols, ps.block, row_req=ps.row_req)
+        assert np.array_equal(got, ref), f"{kd}: 128-token pages"
+
+
+def pin_paged_sparse_equals_paged_dense_masked():
+    """Each scored candidate column equals the paged dense score of its token; every other
+    column is -inf; and selecting over the candidate columns picks exactly what the paged
+    dense route picks once non-candidate tokens are masked."""
+    sp = synth.sparse_blocks(seed=83, rows=3, ctx=1024, n_blocks=4, block=128, topk=40, kdtype="fp8",
+                             ragged=True, poison_noncand=False)
+    ps = synth.page_sparse(sp, page=64, seed=83, row_req=True)
+    lg = O.logits_paged_sparse(ps.q, "fp8", ps.w, ps.k_pages, ps.k_scale_pages, "fp8", ps.block_table,
+                               ps.seq_lens, ps.cand, ps.n_cols, ps.block, row_req=ps.row_req)
+    full = O.logits_paged(ps.q, "fp8", ps.w, ps.k_pages, ps.k_scale_pages, "fp8", ps.block_table, ps.seq_lens,
+                          row_req=ps.row_req, ld=1024)
+    mask = np.zeros_like(full, dtype=bool)
+    for r in range(ps.rows):
+        for c in range(lg.shape[1]):
+            tok = int(ps.cand[r, c // 128]) * 128 + c % 128
+            if c < ps.n_cols[r] and tok < ps.seq_lens[r]:
+                assert lg[r, c] == full[r, tok], f"row {r} col {c}"
+                mask[r, tok] = True
+            else:
+                assert lg[r, c] == -np.inf, f"row {r} col {c} should be masked"
+    idx, val = O.select_case(ps, k=40)
+    d_idx, d_val = O.topk(np.where(mask, full, -np.inf).astype(np.float32), 40)
+    assert np.array_equal(idx, d_idx) and np.array_equal(val, d_val), "paged-sparse != paged dense-masked"
+
+
 # ----------------------------------------------------------------------------- key-cache writer
 
 

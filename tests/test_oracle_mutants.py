@@ -59,6 +59,15 @@ MUTANTS = {
     "cand_absent_counted": ("if (!(v > -INFINITY)) /* -inf or NaN */", "if (isnan(v))"),
     "cand_lens_ignored": ("int64_t n = lens ? lens[r] : ncols;\n        if (n < 0)", "int64_t n = ncols;\n        if (n < 0)"),
     "writer_padding_slot": ("if (s < 0)\n            continue;", "if (s < 0)\n            s = 0;"),
+    "paged_sparse_token": ("(int64_t)cand[r * cand_ld + b] * block + c % block : -1;\n            if (c >= n_cols[r] || b >= cand_ld || tok < 0 || tok >= seq_lens[r])",
+                           "(int64_t)cand[r * cand_ld + b] * block + (c + 1) % block : -1;\n            if (c >= n_cols[r] || b >= cand_ld || tok < 0 || tok >= seq_lens[r])"),
+    "paged_sparse_len": ("tok < 0 || tok >= seq_lens[r])", "tok < 0 || tok > seq_lens[r])"),
+    "paged_sparse_page_by_column": ("int64_t page = block_table[req * bt_ld + tok / page_size];",
+                                    "int64_t page = block_table[req * bt_ld + c / page_size];"),
+    "paged_sparse_slot": ("int64_t slot = page * page_size + tok % page_size;",
+                          "int64_t slot = page * page_size + (tok + 1) % page_size;"),
+    "paged_sparse_req": ("int64_t req = row_req ? row_req[r] : r;\n        for (int64_t c = 0; c < ld; c++) {\n            int64_t b = c / block;",
+                         "int64_t req = r;\n        for (int64_t c = 0; c < ld; c++) {\n            int64_t b = c / block;"),
 }
 
 
