@@ -403,6 +403,40 @@ def other_workloads(D, np, torch, stream, args):
     out["two_level_tokens_per_s"] = c5.tokens / (ms * 1e-3)
     log(f"two-level: select {ms*1e3:.1f} us per call ({c5.tokens/(ms*1e-3)/1e9:.2f} G keys/s, graph of {len(probs)})")
     del base, copies, probs, ws5, oi5, g
+    # the same two-level workload with each row's context in a paged cache (64-token pages
+    # from a permuted pool; the 128-token candidate blocks go as pairs of 64-token sparse
+    # blocks, the page being a multiple of the sparse block): candidate blocks read
+    # through the block table (rotate 8 copies, as a graph)
+    c7 = synth.paged_sparse_blocks()
+    base = [dev(a) for a in (c7.q, c7.w, c7.k_pages, c7.k_scale_pages, c7.block_table, c7.seq_lens, c7.cand,
+                             c7.n_cols)]
+    copies = [base] + [[t.clone() for t in base] for _ in range(7)]
+    probs = [D.paged_sparse_problem(*cp, k_dtype="mxfp4", block_size=c7.block) for cp in copies]
+    ws7 = torch.empty(D.idx_select_workspace(probs[0], 2048), dtype=torch.uint8, device="cuda")
+    oi7 = torch.empty((c7.rows, 2048), dtype=torch.int32, device="cuda")
+    for p in probs:
+        D.idx_select(p, 2048, values=False, out_idx=oi7, workspace=ws7)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        g.capture_begin()
+        for p in probs:
+            D.idx_select(p, 2048, values=False, out_idx=oi7, workspace=ws7)
+        g.capture_end()
+    torch.cuda.synchronize()
+    ms, _ = time_loop(g.replay, steps, 2, stream, warm_s=0.2)
+    ms /= len(probs)
+    # bytes: each candidate token's 64 code bytes and 4 scale bytes, one table entry per
+    # 64-token tile, the candidate ids, q and w, the 2048 indices out
+    tok = int(c7.n_cols.astype(np.int64).sum())
+    b7 = tok * 68 + (tok // 64) * 4 + c7.cand.size * 4 + c7.rows * (64 * 128 + 64 * 4 + 2048 * 4)
+    out["two_level_paged_select_ms"] = ms
+    out["two_level_paged_tokens_per_s"] = tok / (ms * 1e-3)
+    out["two_level_paged_hbm_frac"] = b7 / (ms * 1e-3) / HBM_PEAK
+    log(f"two-level, paged cache: select {ms*1e3:.1f} us per call ({tok/(ms*1e-3)/1e9:.2f} G keys/s, "
+        f"{100*out['two_level_paged_hbm_frac']:.1f}% of 8 TB/s, graph of {len(probs)})")
+    del base, copies, probs, ws7, oi7, g
     # the 128K paged decode workload with MXFP4 keys (64 B codes + 4 UE8M0 bytes per token)
     c6 = synth.paged_decode_mxfp4()
     q6, w6, kp6, sp6, bt6, sl6 = map(dev, (c6.q, c6.w, c6.k_pages, c6.k_scale_pages, c6.block_table, c6.seq_lens))

@@ -18,7 +18,7 @@ _LIB_PATH = Path(__file__).resolve().parent / "libdsaidx.so"
 
 IDX_OK, IDX_ERR_ARG, IDX_ERR_UNSUPPORTED, IDX_ERR_WORKSPACE, IDX_ERR_HIP = 0, 1, 2, 3, 4
 IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
-IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS, IDX_MODE_PREFILL = 1, 2, 3, 4
+IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS, IDX_MODE_PREFILL, IDX_MODE_PAGED_SPARSE_BLOCKS = 1, 2, 3, 4, 5
 IDX_TOPK_UNSORTED = 1
 IDX_SELECT_NO_CUTOFF = 2
 IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK, IDX_DEVERR_SLOT, IDX_DEVERR_ORDER = 1, 2, 4, 8, 16
@@ -28,7 +28,7 @@ IDX_NOALLOC_SCRATCH_BYTES = 128 << 20
 KDTYPES = {"bf16": IDX_BF16, "fp8": IDX_FP8_E4M3, "mxfp4": IDX_MXFP4}
 
 # Every symbol include/dsaidx.h declares.
-EXPORTS = ("idx_logits", "idx_logits_prefill", "idx_logits_paged", "idx_logits_sparse_blocks", "idx_topk",
+EXPORTS = ("idx_logits", "idx_logits_prefill", "idx_logits_paged", "idx_logits_paged_sparse_blocks", "idx_logits_sparse_blocks", "idx_topk",
            "idx_topk_workspace", "idx_select", "idx_select_workspace", "idx_status_string",
            "idx_last_error", "idx_version", "idx_device_errors", "idx_kcache_write", "idx_read_probe",
            "idx_candidate_blocks", "idx_candidate_blocks_workspace", "idx_sparse_attn_paged",
@@ -81,6 +81,8 @@ def lib() -> C.CDLL:
         L.idx_logits_prefill.argtypes = [P, I, P, P, P, I, I64, P, P, I, P, I64, P]
         L.idx_logits_paged.argtypes = [P, I, P, P, P, I, I64, I, P, I64, I64, P, P, I, P, I64, P]
         L.idx_logits_sparse_blocks.argtypes = [P, I, P, P, P, I, I64, P, P, P, I64, P, I, I, P, I64, P]
+        L.idx_logits_paged_sparse_blocks.argtypes = [P, I, P, P, P, I, I64, I, P, I64, I64, P, P, P, I64, P, I,
+                                                     I, P, I64, P]
         L.idx_topk.argtypes = [P, I64, P, I64, I, I, P, P, I64, U32, P, SZ, P]
         L.idx_topk_workspace.argtypes = [I, I64, I]
         L.idx_topk_workspace.restype = SZ
@@ -284,6 +286,39 @@ def idx_logits_sparse_blocks(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_co
     return out
 
 
+def _check_paged_sparse_inputs(q, w, k_pages, k_scale_pages, block_table, seq_lens, row_req, cand_blocks, n_cols,
+                               k_dtype):
+    """Paged candidate-block score inputs; returns (rows, page_size, bt_rows, bt_ld, cand_ld)."""
+    import torch
+    rows, page, bt_rows, bt_ld = _check_paged_inputs(q, w, k_pages, k_scale_pages, block_table, seq_lens,
+                                                     row_req, k_dtype)
+    _need(cand_blocks, "cand_blocks", torch.int32)
+    if cand_blocks.dim() != 2 or cand_blocks.shape[0] != rows:
+        raise ValueError(f"cand_blocks must be [{rows}, cand_ld]")
+    _need(n_cols, "n_cols", torch.int32, numel=rows)
+    return rows, page, bt_rows, bt_ld, cand_blocks.shape[1]
+
+
+def idx_logits_paged_sparse_blocks(q, w, k_pages, k_scale_pages, block_table, seq_lens, cand_blocks, n_cols, *,
+                                   k_dtype: str, block_size: int = 128, row_req=None, ld: int | None = None,
+                                   out=None, stream=None):
+    """Scores of two-level decode rows over their candidate blocks in a paged cache
+    (C: idx_logits_paged_sparse_blocks)."""
+    import torch
+    rows, page, bt_rows, bt_ld, cand_ld = _check_paged_sparse_inputs(q, w, k_pages, k_scale_pages, block_table,
+                                                                     seq_lens, row_req, cand_blocks, n_cols, k_dtype)
+    if out is None:
+        ld = cand_ld * block_size if ld is None else ld
+        out = torch.empty((rows, ld), dtype=torch.float32, device=q.device)
+    _rows_out(out, "out", rows, torch.float32, 1)
+    _check(lib().idx_logits_paged_sparse_blocks(_ptr(q), _q_dtype(k_dtype), _ptr(w), _ptr(k_pages),
+                                                _ptr(k_scale_pages), KDTYPES[k_dtype], k_pages.shape[0], page,
+                                                _ptr(block_table), bt_rows, bt_ld, _ptr(seq_lens), _ptr(row_req),
+                                                _ptr(cand_blocks), cand_ld, _ptr(n_cols), block_size, rows,
+                                                _ptr(out), out.shape[1], _stream(stream)))
+    return out
+
+
 # ----------------------------------------------------------------------------- selection
 
 
@@ -446,6 +481,22 @@ def sparse_problem(q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols, *, k_d
                      cand_blocks=cand_blocks.data_ptr(), cand_ld=cand_blocks.shape[1],
                      n_cols=n_cols.data_ptr(), block_size=block_size)
     return Problem(st, (q, w, k, k_scale, row_ks, row_ke, cand_blocks, n_cols))
+
+
+def paged_sparse_problem(q, w, k_pages, k_scale_pages, block_table, seq_lens, cand_blocks, n_cols, *,
+                         k_dtype: str, block_size: int = 128, row_req=None) -> Problem:
+    _check_paged_sparse_inputs(q, w, k_pages, k_scale_pages, block_table, seq_lens, row_req, cand_blocks, n_cols,
+                               k_dtype)
+    st = idx_problem(mode=IDX_MODE_PAGED_SPARSE_BLOCKS, rows=q.shape[0], q=q.data_ptr(),
+                     q_dtype=_q_dtype(k_dtype), k_dtype=KDTYPES[k_dtype], w=w.data_ptr(),
+                     k=k_pages.data_ptr(), k_scale=k_scale_pages.data_ptr(),
+                     n_keys=k_pages.shape[0], page_size=k_pages.shape[1],
+                     block_table=block_table.data_ptr(), bt_rows=block_table.shape[0],
+                     bt_ld=block_table.shape[1], seq_lens=seq_lens.data_ptr(),
+                     row_req=None if row_req is None else row_req.data_ptr(),
+                     cand_blocks=cand_blocks.data_ptr(), cand_ld=cand_blocks.shape[1],
+                     n_cols=n_cols.data_ptr(), block_size=block_size)
+    return Problem(st, (q, w, k_pages, k_scale_pages, block_table, seq_lens, row_req, cand_blocks, n_cols))
 
 
 def idx_select_workspace(problem: Problem, k: int) -> int:

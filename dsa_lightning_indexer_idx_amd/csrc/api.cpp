@@ -173,6 +173,34 @@ idx_status check_problem(const char* fn, const idx_problem* p, ScoreCall* c, con
     c->block = p->block_size;
     return check_ints(fn, {p->row_ks, p->row_ke, p->cand_blocks, p->n_cols});
   }
+  if (p->mode == IDX_MODE_PAGED_SPARSE_BLOCKS) {
+    c->source = SRC_PAGED_SPARSE;
+    REQUIRE(fmt != FMT_BF16, IDX_ERR_UNSUPPORTED, "%s: paged candidate-block keys must be fp8 or mxfp4", fn);
+    REQUIRE(p->page_size >= 64 && p->page_size % 64 == 0, IDX_ERR_UNSUPPORTED,
+            "%s: page_size = %d must be a positive multiple of 64", fn, p->page_size);
+    REQUIRE(p->block_size >= 64 && p->block_size % 64 == 0, IDX_ERR_UNSUPPORTED,
+            "%s: block_size = %d must be a positive multiple of 64", fn, p->block_size);
+    REQUIRE(p->page_size % p->block_size == 0, IDX_ERR_UNSUPPORTED,
+            "%s: page_size = %d must be a multiple of block_size = %d", fn, p->page_size, p->block_size);
+    if (p->rows == 0) return IDX_OK;
+    REQUIRE(p->n_keys >= 1, IDX_ERR_ARG, "%s: n_pages must be >= 1", fn);
+    REQUIRE(p->block_table && p->seq_lens && p->cand_blocks && p->n_cols, IDX_ERR_ARG,
+            "%s: block_table, seq_lens, cand_blocks and n_cols must be non-null", fn);
+    REQUIRE(p->bt_ld >= 1 && p->bt_ld <= kMaxCols / p->page_size, IDX_ERR_ARG,
+            "%s: bt_ld = %lld out of range", fn, (long long)p->bt_ld);
+    REQUIRE(p->cand_ld >= 1 && p->cand_ld <= kMaxCols / p->block_size, IDX_ERR_ARG,
+            "%s: cand_ld = %lld out of range", fn, (long long)p->cand_ld);
+    c->page_size = p->page_size;
+    c->block_table = p->block_table;
+    c->bt_ld = p->bt_ld;
+    c->seq_lens = p->seq_lens;
+    c->row_req = p->row_req;
+    c->cand = p->cand_blocks;
+    c->cand_ld = p->cand_ld;
+    c->n_cols = p->n_cols;
+    c->block = p->block_size;
+    return check_ints(fn, {p->block_table, p->seq_lens, p->row_req, p->cand_blocks, p->n_cols});
+  }
   return fail(IDX_ERR_ARG, "%s: unknown mode %d", fn, p->mode);
 }
 
@@ -182,7 +210,8 @@ int64_t select_width(const idx_problem* p) {
     case IDX_MODE_DENSE:
     case IDX_MODE_PREFILL: return p->max_cols;
     case IDX_MODE_PAGED: return p->bt_ld * p->page_size;
-    case IDX_MODE_SPARSE_BLOCKS: return p->cand_ld * p->block_size;
+    case IDX_MODE_SPARSE_BLOCKS:
+    case IDX_MODE_PAGED_SPARSE_BLOCKS: return p->cand_ld * p->block_size;
   }
   return 0;
 }
@@ -287,7 +316,7 @@ idx_status select_call(const char* fn, const idx_problem* p, int k, int32_t* out
   REQUIRE(out_idx && out_ld >= k, IDX_ERR_ARG, "%s: out_idx must be non-null and out_ld >= k", fn);
   REQUIRE(aligned(out_idx, 4) && (!out_val || aligned(out_val, 4)), IDX_ERR_ARG,
           "%s: outputs must be 4-byte aligned", fn);
-  if (p->mode == IDX_MODE_PAGED)
+  if (p->mode == IDX_MODE_PAGED || p->mode == IDX_MODE_PAGED_SPARSE_BLOCKS)
     REQUIRE(p->bt_rows >= 1 && (p->row_req || p->bt_rows >= p->rows), IDX_ERR_ARG,
             "%s: bt_rows = %lld too small", fn, (long long)p->bt_rows);
   const size_t need = idx_select_workspace(p, k);
@@ -311,7 +340,7 @@ idx_status select_call(const char* fn, const idx_problem* p, int k, int32_t* out
   t.out_val = out_val;
   t.out_ld = out_ld;
   t.sorted = (flags & IDX_TOPK_UNSORTED) ? 0 : 1;
-  if (p->mode == IDX_MODE_SPARSE_BLOCKS) {
+  if (p->mode == IDX_MODE_SPARSE_BLOCKS || p->mode == IDX_MODE_PAGED_SPARSE_BLOCKS) {
     t.cand = p->cand_blocks;
     t.cand_ld = p->cand_ld;
     t.block = p->block_size;
@@ -484,6 +513,49 @@ idx_status idx_logits_sparse_blocks(const void* q, int q_dtype, const float* w, 
   log_once("idx_logits_sparse_blocks: %s (rows %d, block %d)",
            rows <= kBalancedMaxRows ? "balanced scan" : "row-item scan", rows, block_size);
   return launched("idx_logits_sparse_blocks", launch_score(c, (hipStream_t)stream));
+}
+
+idx_status idx_logits_paged_sparse_blocks(const void* q, int q_dtype, const float* w, const void* k_pages,
+                                          const void* k_scale_pages, int k_dtype, int64_t n_pages, int page_size,
+                                          const int32_t* block_table, int64_t bt_rows, int64_t bt_ld,
+                                          const int32_t* seq_lens, const int32_t* row_req,
+                                          const int32_t* cand_blocks, int64_t cand_ld, const int32_t* n_cols,
+                                          int block_size, int rows, float* logits, int64_t ld,
+                                          idx_stream_t stream) {
+  const char* fn = "idx_logits_paged_sparse_blocks";
+  idx_problem p{};
+  p.mode = IDX_MODE_PAGED_SPARSE_BLOCKS;
+  p.rows = rows;
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_dtype = k_dtype;
+  p.w = w;
+  p.k = k_pages;
+  p.k_scale = k_scale_pages;
+  p.n_keys = n_pages;
+  p.page_size = page_size;
+  p.block_table = block_table;
+  p.bt_rows = bt_rows;
+  p.bt_ld = bt_ld;
+  p.seq_lens = seq_lens;
+  p.row_req = row_req;
+  p.cand_blocks = cand_blocks;
+  p.cand_ld = cand_ld;
+  p.n_cols = n_cols;
+  p.block_size = block_size;
+  ScoreCall c;
+  idx_status s = check_problem(fn, &p, &c, logits, ld, true);
+  if (s != IDX_OK) return s;
+  if (rows == 0) return ok();
+  REQUIRE(bt_rows >= 1 && (row_req || bt_rows >= rows), IDX_ERR_ARG, "%s: bt_rows = %lld too small", fn,
+          (long long)bt_rows);
+  REQUIRE(ld >= cand_ld * block_size, IDX_ERR_ARG, "%s: ld = %lld < cand_ld * block_size = %lld", fn,
+          (long long)ld, (long long)(cand_ld * block_size));
+  c.bt_rows = bt_rows;
+  c.err = device_error_word();
+  log_once("%s: %s (rows %d, page %d, block %d)", fn, rows <= kBalancedMaxRows ? "balanced scan" : "row-item scan",
+           rows, page_size, block_size);
+  return launched(fn, launch_score(c, (hipStream_t)stream));
 }
 
 size_t idx_topk_workspace(int rows, int64_t n_cols, int) { return topk_workspace_bytes(rows, n_cols); }

@@ -8,7 +8,7 @@
 
 namespace dsaidx {
 
-enum SourceKind { SRC_DENSE = 1, SRC_PAGED = 2, SRC_SPARSE = 3 };
+enum SourceKind { SRC_DENSE = 1, SRC_PAGED = 2, SRC_SPARSE = 3, SRC_PAGED_SPARSE = 4 };
 
 // Per-device state (error word, CU count, occupancy, kernel attributes) is kept for
 // device ids below this.
@@ -80,7 +80,7 @@ struct ScoreCall {
   int64_t bt_ld;
   const int32_t* seq_lens;
   const int32_t* row_req;
-  const int32_t* cand;    // sparse
+  const int32_t* cand;    // sparse and paged sparse
   int64_t cand_ld;
   const int32_t* n_cols;
   int block;

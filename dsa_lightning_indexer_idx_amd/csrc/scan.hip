@@ -166,6 +166,65 @@ struct SparseSrc {
   }
 };
 
+// Candidate blocks of a paged row (the two-level decode layout): column c names the row's
+// logical token cand[r][c / block] * block + c % block, which lives in page
+// block_table[req][token / page], slot token % page; columns at or past n_cols[r] are not
+// scored. Blocks and pages are multiples of 64 tokens, so a step's 64 tokens lie in one
+// block and one page.
+struct PagedSparseSrc {
+  const int32_t* bt;
+  int64_t bt_rows, bt_ld;
+  const int32_t* seq_lens;
+  const int32_t* row_req;
+  int64_t n_pages;
+  int page;
+  const int32_t* cand;
+  int64_t cand_ld;
+  const int32_t* n_cols;
+  int block;
+  struct Row {
+    const int32_t* bt_row;
+    int64_t len;
+    const int32_t* cand_row;
+    int64_t ncols;
+  };
+  __device__ Row row(int r, int64_t ld, unsigned* err, bool report) const {
+    int64_t req = row_req ? (int64_t)row_req[r] : (int64_t)r;
+    int64_t req2 = min(max(req, (int64_t)0), bt_rows - 1);
+    int64_t L = seq_lens[r];
+    int64_t L2 = min(max(L, (int64_t)0), bt_ld * page);
+    int64_t nc = n_cols[r];
+    int64_t nc2 = min(max(nc, (int64_t)0), min(cand_ld * block, ld));
+    if (report && (req2 != req || L2 != L || nc2 != nc)) flag_error(err, kErrRange);
+    if (L2 == 0) nc2 = 0;  // no keys: nothing to score
+    return {bt + req2 * bt_ld, L2, cand + (int64_t)r * cand_ld, nc2};
+  }
+  __device__ int64_t bound(const Row& R) const { return R.ncols; }
+  __device__ int64_t step_raw(const Row& R, int64_t pos0) const {
+    return pos0 < R.ncols ? (int64_t)R.cand_row[pos0 / block] : 0;
+  }
+  __device__ StepDesc step(const Row& R, int64_t pos0, unsigned* err) const {
+    return step_desc(R, pos0, step_raw(R, pos0), err);
+  }
+  __device__ StepDesc step_desc(const Row& R, int64_t pos0, int64_t cb, unsigned* err) const {
+    if (pos0 >= R.ncols) return {0, 0};
+    if (cb < 0 || cb * block >= R.len) {  // no token of the block lies in the row
+      flag_error(err, kErrBlock);
+      return {0, 0};
+    }
+    if (pos0 % block == 0 && pos0 >= block && R.cand_row[pos0 / block - 1] >= cb) flag_error(err, kErrOrder);
+    const int64_t tok0 = cb * block + pos0 % block;
+    const int64_t v = min(min(R.ncols - pos0, R.len - tok0), (int64_t)kTileTokens);
+    if (v <= 0) return {0, 0};
+    int64_t pg = R.bt_row[tok0 / page];
+    if (pg < 0 || pg >= n_pages) {
+      flag_error(err, kErrPage);
+      pg = min(max(pg, (int64_t)0), n_pages - 1);
+    }
+    return {pg * page + tok0 % page, (int32_t)v};
+  }
+};
+
 // ------------------------------------------------------------------ per-format operands
 
 template <int F>
@@ -1297,6 +1356,11 @@ hipError_t launch_score(const ScoreCall& c, hipStream_t stream) {
       SparseSrc s{c.row_ks, c.row_ke, c.n_keys, c.cand, c.cand_ld, c.n_cols, c.block};
       return run_fmt(c, s, stream);
     }
+    case SRC_PAGED_SPARSE: {
+      PagedSparseSrc s{c.block_table, c.bt_rows, c.bt_ld, c.seq_lens, c.row_req, c.n_keys, c.page_size,
+                       c.cand, c.cand_ld, c.n_cols, c.block};
+      return run_fmt(c, s, stream);
+    }
   }
   return hipErrorInvalidValue;
 }
@@ -1304,19 +1368,23 @@ hipError_t launch_score(const ScoreCall& c, hipStream_t stream) {
 int64_t select_scan_blocks(const ScoreCall& c) {
   if (c.rows <= 0 || c.rows > kBalancedMaxRows) return 0;
   if (c.source == SRC_DENSE && prefill_applies(c)) return 0;
-  const bool paged = c.source == SRC_PAGED, sparse = c.source == SRC_SPARSE;
   switch (c.fmt) {
     case FMT_BF16:
-      if (paged || sparse) return 0;
-      return sched_blocks<FMT_BF16, DenseSrc, SCHED_SELECT>();
+      return c.source == SRC_DENSE ? sched_blocks<FMT_BF16, DenseSrc, SCHED_SELECT>() : 0;
     case FMT_FP8:
-      return paged ? sched_blocks<FMT_FP8, PagedSrc, SCHED_SELECT>()
-                   : sparse ? sched_blocks<FMT_FP8, SparseSrc, SCHED_SELECT>()
-                            : sched_blocks<FMT_FP8, DenseSrc, SCHED_SELECT>();
+      switch (c.source) {
+        case SRC_PAGED: return sched_blocks<FMT_FP8, PagedSrc, SCHED_SELECT>();
+        case SRC_SPARSE: return sched_blocks<FMT_FP8, SparseSrc, SCHED_SELECT>();
+        case SRC_PAGED_SPARSE: return sched_blocks<FMT_FP8, PagedSparseSrc, SCHED_SELECT>();
+        default: return sched_blocks<FMT_FP8, DenseSrc, SCHED_SELECT>();
+      }
     case FMT_MXFP4:
-      return paged ? sched_blocks<FMT_MXFP4, PagedSrc, SCHED_SELECT>()
-                   : sparse ? sched_blocks<FMT_MXFP4, SparseSrc, SCHED_SELECT>()
-                            : sched_blocks<FMT_MXFP4, DenseSrc, SCHED_SELECT>();
+      switch (c.source) {
+        case SRC_PAGED: return sched_blocks<FMT_MXFP4, PagedSrc, SCHED_SELECT>();
+        case SRC_SPARSE: return sched_blocks<FMT_MXFP4, SparseSrc, SCHED_SELECT>();
+        case SRC_PAGED_SPARSE: return sched_blocks<FMT_MXFP4, PagedSparseSrc, SCHED_SELECT>();
+        default: return sched_blocks<FMT_MXFP4, DenseSrc, SCHED_SELECT>();
+      }
   }
   return 0;
 }

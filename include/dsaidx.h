@@ -171,6 +171,35 @@ idx_status idx_logits_sparse_blocks(const void* q, int q_dtype, const float* w, 
                                     const int32_t* n_cols, int block_size, int rows,
                                     float* logits, int64_t ld, idx_stream_t stream);
 
+/*
+ * idx_logits_paged_sparse_blocks: two-level decode rows whose context lives in a
+ * paged cache (the fp8_fp4_paged_sparse_mqa_logits step named by the vLLM
+ * sparse_indexer page: decode rows carry a per-row block_table next to their
+ * sparse_indices, and the indexer cache's page must be a multiple of the sparse
+ * block).
+ *
+ * Row r's context is the paged cache of idx_logits_paged (request req = row_req[r],
+ * or r when row_req is NULL; logical token s in page block_table[req * bt_ld +
+ * s / page_size], slot s % page_size; seq_lens[r] tokens). It is handed
+ * cand_blocks[r * cand_ld + b], ascending unique block ids of block_size tokens, and
+ * n_cols[r], its valid sparse-column count. Sparse column c = b * block_size + i names
+ * the logical token tok = cand_blocks[r][b] * block_size + i:
+ *     logits[r][c] = I(r, tok)   if c < n_cols[r] and tok < seq_lens[r]
+ *     logits[r][c] = -inf        otherwise, for c in [0, ld).
+ * page_size and block_size: positive multiples of 64 with page_size a multiple of
+ * block_size (IDX_ERR_UNSUPPORTED otherwise); ld >= cand_ld * block_size; bt_rows as
+ * for idx_logits_paged. k_dtype IDX_FP8_E4M3 or IDX_MXFP4 with q_dtype IDX_FP8_E4M3.
+ * Bad device values (page ids, block ids, lengths, requests) are clamped and flagged
+ * like the other score calls'.
+ */
+idx_status idx_logits_paged_sparse_blocks(const void* q, int q_dtype, const float* w, const void* k_pages,
+                                          const void* k_scale_pages, int k_dtype, int64_t n_pages, int page_size,
+                                          const int32_t* block_table, int64_t bt_rows, int64_t bt_ld,
+                                          const int32_t* seq_lens, const int32_t* row_req,
+                                          const int32_t* cand_blocks, int64_t cand_ld, const int32_t* n_cols,
+                                          int block_size, int rows, float* logits, int64_t ld,
+                                          idx_stream_t stream);
+
 /* ------------------------------------------------------------------ top-k */
 
 /*
@@ -265,7 +294,8 @@ typedef enum idx_mode {
     IDX_MODE_DENSE = 1,        /* idx_logits arguments */
     IDX_MODE_PAGED = 2,        /* idx_logits_paged arguments */
     IDX_MODE_SPARSE_BLOCKS = 3, /* idx_logits_sparse_blocks arguments */
-    IDX_MODE_PREFILL = 4        /* idx_logits_prefill arguments (idx_logits's) */
+    IDX_MODE_PREFILL = 4,       /* idx_logits_prefill arguments (idx_logits's) */
+    IDX_MODE_PAGED_SPARSE_BLOCKS = 5 /* idx_logits_paged_sparse_blocks arguments */
 } idx_mode;
 
 /* One scoring problem: the arguments of the matching idx_logits* call. Fields a
@@ -300,10 +330,10 @@ typedef struct idx_problem {
  *
  * Returns in out_idx[r * out_ld + i] the i-th selected KEY POSITION of row r:
  * relative to row_ks (dense), the logical position (paged), or the token
- * position relative to row_ks named by the selected sparse column (sparse
- * blocks: column -> token through cand_blocks, the col_indices step of the
- * sparse_indexer page). The result equals idx_logits* followed by idx_topk
- * (and, for sparse blocks, the column -> token map) bit for bit. out_val
+ * position named by the selected sparse column (sparse blocks: relative to row_ks;
+ * paged sparse blocks: the logical position; column -> token through cand_blocks,
+ * the col_indices step of the sparse_indexer page). The result equals idx_logits*
+ * followed by idx_topk (and, for sparse blocks, the column -> token map) bit for bit. out_val
  * (optional) receives the scores. workspace of at least
  * idx_select_workspace(p, k) bytes, 256-byte aligned.
  */

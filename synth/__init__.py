@@ -432,10 +432,21 @@ def page_sparse(sp: Sparse, page: int = 64, seed: int = 0, permute: bool = True,
     tokens [row_ks, row_ks + ctx) fill its ctx / page pages, taken from a pool that is a
     random permutation (``permute``) with ``spare_pages`` poisoned pages besides; the table
     maps logical page p of request req(r) to its physical page; ``row_req`` shuffles the
-    rows' requests. The scores of every column equal those of ``sp`` (same key bytes)."""
+    rows' requests. The page must be a multiple of the kernel's sparse block: candidate
+    blocks longer than a page are handed over split into page-sized sparse blocks (each
+    candidate block b becomes blocks b*f .. b*f + f - 1, f = block / page), which name the
+    same tokens column for column. The scores of every column equal those of ``sp`` (same
+    key bytes)."""
     g = np.random.default_rng([seed, 77])
     ctx = int(sp.meta["ctx"])
     assert ctx % page == 0 and page % 64 == 0
+    if page % sp.block:
+        assert sp.block % page == 0
+        f = sp.block // page
+        cand = (sp.cand.astype(np.int64)[:, :, None] * f + np.arange(f)[None, None, :]).reshape(sp.rows, -1)
+        cand, block = cand.astype(np.int32), page
+    else:
+        cand, block = sp.cand, sp.block
     rows, npg = sp.rows, ctx // page
     P = rows * npg + spare_pages
     phys = (g.permutation(P) if permute else np.arange(P)).astype(np.int32)
@@ -455,15 +466,16 @@ def page_sparse(sp: Sparse, page: int = 64, seed: int = 0, permute: bool = True,
         bt[reqs[i]] = used[i * npg:(i + 1) * npg]
     lens = (sp.row_ke - sp.row_ks).astype(np.int32)
     return PagedSparse("paged_sparse_blocks", sp.q, sp.q_dtype, sp.w, kp, scp, sp.k_dtype, page, bt, lens,
-                       reqs if row_req else None, sp.cand, sp.n_cols, sp.block, sp.topk,
-                       {**sp.meta, "page": page, "permute": permute})
+                       reqs if row_req else None, cand, sp.n_cols, block, sp.topk,
+                       {**sp.meta, "page": page, "permute": permute, "candidate_block": sp.block})
 
 
 def paged_sparse_blocks(seed: int = 5, rows: int = 64, ctx: int = 131072, n_blocks: int = 64, block: int = 128,
                         page: int = 64, topk: int = 2048, kdtype: str = "mxfp4", ragged: bool = False,
                         row_req: bool = False, poison_noncand: bool = True) -> PagedSparse:
     """The two-level workload over a paged cache: sparse_blocks(...) paged with 64-token
-    pages from a permuted pool."""
+    pages from a permuted pool (128-token candidate blocks handed over as pairs of 64-token
+    sparse blocks)."""
     sp = sparse_blocks(seed=seed, rows=rows, ctx=ctx, n_blocks=n_blocks, block=block, topk=topk, kdtype=kdtype,
                        ragged=ragged, poison_noncand=poison_noncand)
     return page_sparse(sp, page=page, seed=seed, row_req=row_req)

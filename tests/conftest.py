@@ -32,8 +32,8 @@ def pytest_terminal_summary(terminalreporter):
     tr.write_sep("-", "parity against the oracle (max |err|, max err/tol; tol = 1e-2 + 1e-3 |ref|)")
     for (check, workload, detail), (err, ratio, rows) in sorted(PARITY.items()):
         if check == "select":  # index overlap; disagreements' distance to the k-th score / the tie-gap limit
-            tr.write_line(f"[parity] {check:8s} {workload:28s} rows {rows:>10s}  {detail}  "
+            tr.write_line(f"[parity] {check:8s} {workload:30s} rows {rows:>10s}  {detail}  "
                           f"worst disagreement {ratio:.3f} of the tie-gap limit")
         else:
-            tr.write_line(f"[parity] {check:8s} {workload:28s} rows {rows:>10s}  {detail}"
+            tr.write_line(f"[parity] {check:8s} {workload:30s} rows {rows:>10s}  {detail}"
                           f"max|err| {err:.3e}  max err/tol {ratio:.3f}")

@@ -53,10 +53,12 @@ class Uploaded:
         # prefill chunks (and cases that ask to be run as one) go through the prefill entry
         self.prefill = kind == "Dense" and (case.name == "prefill_chunk" or bool(case.meta.get("as_prefill")))
         self.q, self.w = dev(case.q), dev(case.w)
-        if kind == "Paged":
+        if kind in ("Paged", "PagedSparse"):
             self.k, self.sc = dev(case.k_pages), dev(case.k_scale_pages)
             self.bt, self.sl = dev(case.block_table), dev(case.seq_lens)
             self.rr = dev(case.row_req)
+            if kind == "PagedSparse":
+                self.cand, self.nc = dev(case.cand), dev(case.n_cols)
         else:
             self.k, self.sc = dev(case.k), dev(case.k_scale)
             self.ks, self.ke = dev(case.row_ks), dev(case.row_ke)
@@ -71,6 +73,10 @@ class Uploaded:
         if self.kind == "Paged":
             return D.idx_logits_paged(self.q, self.w, self.k, self.sc, self.bt, self.sl,
                                       k_dtype=c.k_dtype, row_req=self.rr, ld=ld)
+        if self.kind == "PagedSparse":
+            return D.idx_logits_paged_sparse_blocks(self.q, self.w, self.k, self.sc, self.bt, self.sl, self.cand,
+                                                    self.nc, k_dtype=c.k_dtype, block_size=c.block,
+                                                    row_req=self.rr, ld=ld)
         return D.idx_logits_sparse_blocks(self.q, self.w, self.k, self.sc, self.ks, self.ke,
                                           self.cand, self.nc, k_dtype=c.k_dtype,
                                           block_size=c.block, ld=ld)
@@ -83,6 +89,9 @@ class Uploaded:
         if self.kind == "Paged":
             return D.paged_problem(self.q, self.w, self.k, self.sc, self.bt, self.sl,
                                    k_dtype=c.k_dtype, row_req=self.rr)
+        if self.kind == "PagedSparse":
+            return D.paged_sparse_problem(self.q, self.w, self.k, self.sc, self.bt, self.sl, self.cand, self.nc,
+                                          k_dtype=c.k_dtype, block_size=c.block, row_req=self.rr)
         return D.sparse_problem(self.q, self.w, self.k, self.sc, self.ks, self.ke, self.cand,
                                 self.nc, k_dtype=c.k_dtype, block_size=c.block)
 

@@ -555,8 +555,9 @@ def pin_paged_sparse_equals_contiguous_sparse():
             got = O.logits_paged_sparse(ps.q, "fp8", ps.w, ps.k_pages, ps.k_scale_pages, kd, ps.block_table,
                                         ps.seq_lens, ps.cand, ps.n_cols, ps.block, row_req=ps.row_req)
             assert np.array_equal(got, ref), f"{kd} permute={permute} row_req={row_req}: paged-sparse != sparse"
-        # 128-token pages (two candidate blocks... one block per page)
+        # 128-token pages hold whole candidate blocks (no split)
         ps = synth.page_sparse(sp, page=128, seed=seed, row_req=True)
+        assert ps.block == 128
         got = O.logits_paged_sparse(ps.q, "fp8", ps.w, ps.k_pages, ps.k_scale_pages, kd, ps.block_table,
                                     ps.seq_lens, ps.cand, ps.n_cols, ps.block, row_req=ps.row_req)
         assert np.array_equal(got, ref), f"{kd}: 128-token pages"
@@ -574,9 +575,10 @@ def pin_paged_sparse_equals_paged_dense_masked():
     full = O.logits_paged(ps.q, "fp8", ps.w, ps.k_pages, ps.k_scale_pages, "fp8", ps.block_table, ps.seq_lens,
                           row_req=ps.row_req, ld=1024)
     mask = np.zeros_like(full, dtype=bool)
+    assert ps.block == 64  # 128-token candidate blocks split over 64-token pages
     for r in range(ps.rows):
         for c in range(lg.shape[1]):
-            tok = int(ps.cand[r, c // 128]) * 128 + c % 128
+            tok = int(ps.cand[r, c // ps.block]) * ps.block + c % ps.block
             if c < ps.n_cols[r] and tok < ps.seq_lens[r]:
                 assert lg[r, c] == full[r, tok], f"row {r} col {c}"
                 mask[r, tok] = True

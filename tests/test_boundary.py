@@ -91,6 +91,16 @@ def _sparse(L, **kw):
                                       a["rows"], a["out"], a["ld"], None)
 
 
+def _paged_sparse(L, **kw):
+    a = dict(q=Q, qd=D.IDX_FP8_E4M3, w=W, k=K, sc=S, kd=D.IDX_MXFP4, npages=100, page=128, bt=BT,
+             bt_rows=4, bt_ld=16, sl=SL, rr=None, cand=CAND, cand_ld=4, nc=NC, block=128, rows=4, out=OUT, ld=512)
+    a.update(kw)
+    return L.idx_logits_paged_sparse_blocks(a["q"], a["qd"], a["w"], a["k"], a["sc"], a["kd"], a["npages"],
+                                            a["page"], a["bt"], a["bt_rows"], a["bt_ld"], a["sl"], a["rr"],
+                                            a["cand"], a["cand_ld"], a["nc"], a["block"], a["rows"], a["out"],
+                                            a["ld"], None)
+
+
 def _topk(L, **kw):
     a = dict(lg=OUT, ld=1024, lens=None, ncols=1024, rows=4, k=256, oi=Q, ov=None, old=256,
              flags=0, ws=None, wsb=0)
@@ -139,6 +149,19 @@ CASES = [
     ("sparse null n_cols", _sparse, dict(nc=None), ARG),
     ("sparse cand_ld zero", _sparse, dict(cand_ld=0), ARG),
     ("sparse cand_ld wrapping", _sparse, dict(cand_ld=1 << 57, ld=1 << 40), ARG),
+    ("paged sparse page not a multiple of the block", _paged_sparse, dict(page=192), UNS),
+    ("paged sparse page smaller than the block", _paged_sparse, dict(page=64), UNS),
+    ("paged sparse page 96", _paged_sparse, dict(page=96, block=64), UNS),
+    ("paged sparse block 100", _paged_sparse, dict(block=100), UNS),
+    ("paged sparse bf16", _paged_sparse, dict(qd=D.IDX_BF16, kd=D.IDX_BF16), UNS),
+    ("paged sparse ld too small", _paged_sparse, dict(ld=511), ARG),
+    ("paged sparse null table", _paged_sparse, dict(bt=None), ARG),
+    ("paged sparse null cand", _paged_sparse, dict(cand=None), ARG),
+    ("paged sparse null n_cols", _paged_sparse, dict(nc=None), ARG),
+    ("paged sparse no pages", _paged_sparse, dict(npages=0), ARG),
+    ("paged sparse too few table rows", _paged_sparse, dict(bt_rows=3), ARG),
+    ("paged sparse misaligned cand", _paged_sparse, dict(cand=CAND + 2), ARG),
+    ("paged sparse cand_ld zero", _paged_sparse, dict(cand_ld=0), ARG),
     ("topk k zero", _topk, dict(k=0), UNS),
     ("topk k too large", _topk, dict(k=2049, old=4096), UNS),
     ("topk out_ld < k", _topk, dict(old=255), ARG),
@@ -161,7 +184,14 @@ def test_host_rejects(L, name, fn, kw, status):
     assert L.idx_last_error(), "a failed call must set idx_last_error"
 
 
-@pytest.mark.parametrize("fn", [_dense, _paged, _sparse, _topk])
+def test_paged_sparse_accepts_pages_that_are_block_multiples(L):
+    """page_size a multiple of block_size passes the host checks (the call is only checked
+    here: zero rows)."""
+    for page, block in ((64, 64), (128, 64), (128, 128), (256, 128), (512, 256)):
+        assert _paged_sparse(L, page=page, block=block, rows=0) == D.IDX_OK
+
+
+@pytest.mark.parametrize("fn", [_dense, _paged, _sparse, _paged_sparse, _topk])
 def test_zero_rows_is_noop(L, fn):
     assert fn(L, rows=0) == D.IDX_OK
     assert L.idx_last_error() == b""

@@ -20,6 +20,10 @@ def _ref_logits(case, ld=None):
     if kind == "Paged":
         return O.logits_paged(case.q, case.q_dtype, case.w, case.k_pages, case.k_scale_pages,
                               case.k_dtype, case.block_table, case.seq_lens, case.row_req, ld=ld)
+    if kind == "PagedSparse":
+        return O.logits_paged_sparse(case.q, case.q_dtype, case.w, case.k_pages, case.k_scale_pages, case.k_dtype,
+                                     case.block_table, case.seq_lens, case.cand, case.n_cols, case.block,
+                                     row_req=case.row_req, ld=ld)
     return O.logits_sparse(case.q, case.q_dtype, case.w, case.k, case.k_scale, case.k_dtype,
                            case.row_ks, case.row_ke, case.cand, case.n_cols, case.block, ld=ld)
 
@@ -46,6 +50,12 @@ SMALL = {
                                                        ragged=True),
     "sparse_fp8_ragged": lambda: synth.sparse_blocks(seed=109, rows=4, ctx=3000, n_blocks=5,
                                                      kdtype="fp8", ragged=True),
+    "paged_sparse_fp8_rowreq": lambda: synth.paged_sparse_blocks(seed=120, rows=5, ctx=4096, n_blocks=7,
+                                                                 kdtype="fp8", ragged=True, row_req=True),
+    "paged_sparse_mxfp4_page128": lambda: synth.page_sparse(
+        synth.sparse_blocks(seed=121, rows=4, ctx=4096, n_blocks=6, ragged=True), page=128, seed=121),
+    "paged_sparse_mxfp4_block64": lambda: synth.paged_sparse_blocks(seed=122, rows=3, ctx=2048, n_blocks=9,
+                                                                    block=64, ragged=True),
     "prefill_q300_prior700": lambda: synth.prefill_chunk(seed=110, q_tokens=300, prior=700),
     # 300 decode rows with disjoint ragged ranges: the row scan
     "dense_many_rows_disjoint": lambda: synth.batched_decode(seed=116, rows=300, n=700, ragged=True,
@@ -120,6 +130,19 @@ def test_paged_identity_table_equals_contiguous_bitwise():
     assert np.array_equal(gd, gp)
 
 
+@pytest.mark.parametrize("kd", ["fp8", "mxfp4"])
+def test_paged_sparse_equals_sparse_bitwise(kd):
+    """Candidate blocks read through a permuted page table (with a row -> request map)
+    give exactly the scores of the same blocks of contiguous rows: same kernel arithmetic,
+    different addressing."""
+    require_gpu()
+    sp = synth.sparse_blocks(seed=123, rows=6, ctx=8192, n_blocks=11, kdtype=kd, ragged=True)
+    ps = synth.page_sparse(sp, page=64, seed=123, row_req=True)
+    a = host(Uploaded(sp).logits())
+    b = host(Uploaded(ps).logits())
+    assert np.array_equal(a, b)
+
+
 def test_ld_not_multiple_of_tile_and_empty_rows():
     require_gpu()
     case = synth.batched_decode(seed=112, rows=4, n=900, ragged=False)
@@ -189,7 +212,7 @@ def test_candidate_block_checks_are_reported():
 
 
 WORKLOAD_NAMES = {2: "batched decode 32x32K fp8", 3: "paged decode 128K fp8", 4: "prefill 4096x8192 fp8",
-                  5: "two-level 64x8192 mxfp4", 6: "paged decode 128K mxfp4"}
+                  5: "two-level 64x8192 mxfp4", 6: "paged decode 128K mxfp4", 7: "two-level paged 64x8192 mxfp4"}
 
 
 def full_rows(cfg, rows):
@@ -198,7 +221,7 @@ def full_rows(cfg, rows):
     return list(range(0, rows, 8)) + [rows - 1] if cfg == 4 else list(range(rows))
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6, 7])
 def test_full_size_every_row(cfg):
     """The workloads at their stated sizes, in the launch shape the benchmark uses; the oracle
     checks every row (every 8th of the prefill chunk, with the first and last)."""

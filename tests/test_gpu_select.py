@@ -25,6 +25,9 @@ SMALL = {
     "sparse_fp8": lambda: synth.sparse_blocks(seed=136, rows=3, ctx=8192, n_blocks=20,
                                               kdtype="fp8"),
     "prefill": lambda: synth.prefill_chunk(seed=137, q_tokens=96, prior=3000),
+    "paged_sparse_mxfp4": lambda: synth.paged_sparse_blocks(seed=138, rows=5, ctx=16384, n_blocks=24, ragged=True,
+                                                            row_req=True),
+    "paged_sparse_fp8": lambda: synth.paged_sparse_blocks(seed=139, rows=3, ctx=8192, n_blocks=20, kdtype="fp8"),
 }
 
 
@@ -41,7 +44,7 @@ def _self_consistent(up, k):
         lens = up.nc
     t_idx, t_val = D.idx_topk(lg, k, lens=lens.contiguous(), n_cols=lg.shape[1])
     t_idx, t_val = host(t_idx), host(t_val)
-    if up.kind == "Sparse":
+    if up.kind in ("Sparse", "PagedSparse"):
         t_idx = O.columns_to_tokens(t_idx, case.cand, case.block)
     s_idx, s_val = host(s_idx), host(s_val)
     assert np.array_equal(s_idx, t_idx), "select != topk(logits)"
@@ -50,7 +53,7 @@ def _self_consistent(up, k):
 
 
 def _ref_scores_fn(case, ref_lg):
-    if type(case).__name__ != "Sparse":
+    if type(case).__name__ not in ("Sparse", "PagedSparse"):
         return lambda r, idx: ref_lg[r][idx]
     # sparse: selected values are tokens; find their columns
     def f(r, toks):
@@ -108,7 +111,7 @@ def test_unsorted_select_same_set():
 
 
 WORKLOAD_NAMES = {2: "batched decode 32x32K fp8", 3: "paged decode 128K fp8", 4: "prefill 4096x8192 fp8",
-                  5: "two-level 64x8192 mxfp4", 6: "paged decode 128K mxfp4"}
+                  5: "two-level 64x8192 mxfp4", 6: "paged decode 128K mxfp4", 7: "two-level paged 64x8192 mxfp4"}
 
 
 def _oracle_select(case, ks):
@@ -118,7 +121,7 @@ def _oracle_select(case, ks):
     kind = type(case).__name__
     if kind == "Paged":
         lens = case.seq_lens
-    elif kind == "Sparse":
+    elif kind in ("Sparse", "PagedSparse"):
         lens = case.n_cols
     else:
         lens = case.row_ke.astype(np.int64) - case.row_ks
@@ -126,13 +129,13 @@ def _oracle_select(case, ks):
     out = {}
     for k in ks:
         idx, val = O.topk(lg, k, lens=lens)
-        if kind == "Sparse":
+        if kind in ("Sparse", "PagedSparse"):
             idx = O.columns_to_tokens(idx, case.cand, case.block)
         out[k] = (idx, val)
     return out, lg
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6, 7])
 def test_full_size_select(cfg):
     """The workloads at full size through idx_select (the benchmark's call): every row
     equals idx_topk over idx_logits* bit for bit, and the oracle checks every row end to

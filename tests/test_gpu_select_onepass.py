@@ -28,7 +28,7 @@ def _reference(up, k, sorted=True):
         lens = up.nc
     t_idx, t_val = D.idx_topk(lg, k, lens=lens.contiguous(), n_cols=lg.shape[1], sorted=sorted)
     t_idx, t_val = host(t_idx), host(t_val)
-    if up.kind == "Sparse":
+    if up.kind in ("Sparse", "PagedSparse"):
         t_idx = O.columns_to_tokens(t_idx, up.case.cand, up.case.block)
     return t_idx, t_val
 
@@ -46,6 +46,9 @@ CASES = {
     "dense_bf16": lambda: synth.tiny_dense(seed=204, n=5000, rows=8, topk=300),
     "sparse_mxfp4": lambda: synth.sparse_blocks(seed=205, rows=10, ctx=16384, n_blocks=24, ragged=True),
     "sparse_fp8": lambda: synth.sparse_blocks(seed=206, rows=8, ctx=8192, n_blocks=12, kdtype="fp8"),
+    "paged_sparse_mxfp4": lambda: synth.paged_sparse_blocks(seed=216, rows=12, ctx=16384, n_blocks=20, ragged=True,
+                                                            row_req=True),
+    "paged_sparse_fp8": lambda: synth.paged_sparse_blocks(seed=217, rows=9, ctx=8192, n_blocks=14, kdtype="fp8"),
     # fewer steps than workgroups: most workgroups hold one step or none
     "paged_fp8_tiny_rows": lambda: synth.paged_decode(seed=214, rows=8, min_len=1, max_len=1200),
     # rows ragged far past the 64-step slice and around the workgroup ranges
