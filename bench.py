@@ -356,6 +356,11 @@ def other_workloads(D, np, torch, stream, args):
         it[0] += 1
     ms, _ = time_loop(sel2, 4 * steps, 4, stream, warm_s=0.2)
     out["batched_decode_select_ms"] = ms
+
+    def sel2_one():
+        D.idx_select(probs[it[0] % 4], 2048, values=False, out_idx=oi2, workspace=ws2, one_pass=True)
+        it[0] += 1
+    out["batched_decode_select_one_pass_ms"], _ = time_loop(sel2_one, 4 * steps, 4, stream, warm_s=0.2)
     out["batched_decode_tokens_per_s"] = c2.tokens / (ms * 1e-3)
     log(f"batched decode: select {ms*1e3:.1f} us ({c2.tokens/(ms*1e-3)/1e9:.2f} G keys/s)")
     del base, copies, probs, ws2, oi2
@@ -371,11 +376,15 @@ def other_workloads(D, np, torch, stream, args):
     ms_sel, _ = time_loop(lambda: D.idx_select(p7, 2048, values=False, out_idx=oi7, workspace=ws7), steps, 3, stream,
                           warm_s=0.2)
     ms_scan, _ = time_loop(lambda: D.idx_logits(*t7, k_dtype="fp8", out=lg7), steps, 3, stream, warm_s=0.2)
+    ms_one, _ = time_loop(lambda: D.idx_select(p7, 2048, values=False, out_idx=oi7, workspace=ws7, one_pass=True),
+                          steps, 3, stream, warm_s=0.2)
+    out["batched_decode_256x32k_select_one_pass_ms"] = ms_one
     out["batched_decode_256x32k_select_ms"] = ms_sel
     out["batched_decode_256x32k_scan_ms"] = ms_scan
     out["batched_decode_256x32k_select_tokens_per_s"] = c7.tokens / (ms_sel * 1e-3)
     out["batched_decode_256x32k_select_vs_scan_rate"] = ms_scan / ms_sel
-    log(f"batched decode 256 x 32K: select {ms_sel*1e3:.1f} us, scan alone {ms_scan*1e3:.1f} us "
+    log(f"batched decode 256 x 32K: select {ms_sel*1e3:.1f} us (forced one pass {ms_one*1e3:.1f}), "
+        f"scan alone {ms_scan*1e3:.1f} us "
         f"(select at {100*ms_scan/ms_sel:.0f}% of the scan's per-key rate)")
     del t7, p7, ws7, oi7, lg7
     # two-level candidate blocks: 64 rows x 8192 candidate keys of 131072, MXFP4 (rotate 16

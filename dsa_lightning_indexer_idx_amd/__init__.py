@@ -21,6 +21,7 @@ IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
 IDX_MODE_DENSE, IDX_MODE_PAGED, IDX_MODE_SPARSE_BLOCKS, IDX_MODE_PREFILL, IDX_MODE_PAGED_SPARSE_BLOCKS = 1, 2, 3, 4, 5
 IDX_TOPK_UNSORTED = 1
 IDX_SELECT_NO_CUTOFF = 2
+IDX_SELECT_ONE_PASS = 4
 IDX_DEVERR_RANGE, IDX_DEVERR_PAGE, IDX_DEVERR_BLOCK, IDX_DEVERR_SLOT, IDX_DEVERR_ORDER = 1, 2, 4, 8, 16
 IDX_HEADS, IDX_DIM, IDX_MAX_K = 64, 128, 2048
 IDX_NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -504,9 +505,11 @@ def idx_select_workspace(problem: Problem, k: int) -> int:
 
 
 def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = True,
-               out_idx=None, out_val=None, workspace=None, cutoff: bool = True, stream=None):
+               out_idx=None, out_val=None, workspace=None, cutoff: bool = True, one_pass: bool = False,
+               stream=None):
     """Scores + exact top-k in one call (C: idx_select). Returns (idx, val or None).
-    cutoff=False sets IDX_SELECT_NO_CUTOFF (every scored entry goes to the exact finish)."""
+    cutoff=False sets IDX_SELECT_NO_CUTOFF (every scored entry goes to the exact finish);
+    one_pass=True sets IDX_SELECT_ONE_PASS (the one-pass selection wherever it can run)."""
     import torch
     dev = problem._keep[0].device
     rows = problem.rows
@@ -523,7 +526,8 @@ def idx_select(problem: Problem, k: int, *, sorted: bool = True, values: bool = 
     wsb = _workspace_bytes(workspace)
     _check(lib().idx_select(C.byref(problem.st), k, _ptr(out_idx), _ptr(out_val),
                             out_idx.shape[1],
-                            (0 if sorted else IDX_TOPK_UNSORTED) | (0 if cutoff else IDX_SELECT_NO_CUTOFF),
+                            (0 if sorted else IDX_TOPK_UNSORTED) | (0 if cutoff else IDX_SELECT_NO_CUTOFF)
+                            | (IDX_SELECT_ONE_PASS if one_pass else 0),
                             _ptr(workspace), wsb, _stream(stream)))
     return out_idx, out_val
 

@@ -254,18 +254,29 @@ size_t select_scores_bytes(const idx_problem* p) {
 
 size_t select_lens_bytes(const idx_problem* p) { return (size_t)round_up((int64_t)p->rows * 4, 256); }
 
-// Whether the problem can take the one-pass selection (the balanced scan of rows that read
+// Whether the problem takes the one-pass selection (the balanced scan of rows that read
 // their own keys); the launch must also fit the finish's segment table (checked per call).
 // Fewer rows than this take scores then top-k: each row would span more than
-// kSelMaxSpan of the CUs' workgroups, too many to exchange histograms between.
+// kSelMaxSpan of the CUs' workgroups, too many to exchange histograms between. Rows of
+// up to kTopkShortRow columns also take scores then top-k: their one-workgroup-per-row
+// top-k costs less than the one-pass epilogue and finish (two-level 64 x 8192: 31
+// against 37 us). Wider rows take the one pass: batched decode 32 x 32768 50 against
+// 50 us, 256 x 32768 185 against 197 us, the 128K paged decode 158 against 172 us.
 constexpr int kSelMinRows = 8;
 
-bool select_one_pass_shape(const idx_problem* p) {
+// The shapes the one-pass selection can run at all (the workspace covers both layouts).
+bool select_one_pass_possible(const idx_problem* p) {
   if (p->rows < kSelMinRows || p->rows > kBalancedMaxRows) return false;
   if (p->mode == IDX_MODE_PREFILL && p->q_dtype == IDX_FP8_E4M3 && p->k_dtype == IDX_FP8_E4M3 &&
       p->rows >= kPrefillMinRows)
     return false;  // a prefill chunk: the tiled prefill kernel, then the top-k
   return true;
+}
+
+// The shapes that take it by default (IDX_SELECT_ONE_PASS: every possible one).
+bool select_one_pass_shape(const idx_problem* p, uint32_t flags) {
+  if (!select_one_pass_possible(p)) return false;
+  return (flags & IDX_SELECT_ONE_PASS) || select_width(p) > kTopkShortRow;
 }
 
 // Group size of the one-pass cutoff: 16 columns, halved while a row of the call's width
@@ -300,8 +311,8 @@ idx_status select_call(const char* fn, const idx_problem* p, int k, int32_t* out
                        hipStream_t stream) {
   REQUIRE(p, IDX_ERR_ARG, "%s: problem is null", fn);
   REQUIRE(k >= 1 && k <= IDX_MAX_K, IDX_ERR_UNSUPPORTED, "%s: k = %d outside [1, %d]", fn, k, IDX_MAX_K);
-  REQUIRE((flags & ~(IDX_TOPK_UNSORTED | IDX_SELECT_NO_CUTOFF)) == 0, IDX_ERR_ARG, "%s: unknown flags 0x%x", fn,
-          flags);
+  REQUIRE((flags & ~(IDX_TOPK_UNSORTED | IDX_SELECT_NO_CUTOFF | IDX_SELECT_ONE_PASS)) == 0, IDX_ERR_ARG,
+          "%s: unknown flags 0x%x", fn, flags);
   REQUIRE(p->rows >= 0, IDX_ERR_ARG, "%s: rows = %d is negative", fn, p->rows);
   const int64_t width = select_width(p);
   ScoreCall c;
@@ -346,7 +357,7 @@ idx_status select_call(const char* fn, const idx_problem* p, int k, int32_t* out
     t.block = p->block_size;
   }
 
-  const int64_t blocks = select_one_pass_shape(p) ? select_scan_blocks(c) : 0;
+  const int64_t blocks = select_one_pass_shape(p, flags) ? select_scan_blocks(c) : 0;
   if (blocks >= 1 && blocks <= kSelMaxBlocks) {
     const SelectLayout L = select_layout(p);
     SelectState st{};
@@ -601,7 +612,7 @@ size_t idx_select_workspace(const idx_problem* p, int k) {
   int64_t width = select_width(p);
   if (width <= 0) return 0;
   const size_t two_pass = select_scores_bytes(p) + select_lens_bytes(p) + topk_workspace_bytes(p->rows, width);
-  if (!select_one_pass_shape(p)) return two_pass;
+  if (!select_one_pass_possible(p)) return two_pass;
   return std::max(two_pass, select_layout(p).total);
 }
 

@@ -140,6 +140,8 @@ size_t topk_zeroed_bytes(int rows, int64_t n_cols);
 hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
 // The top-k path launch_topk takes for rows of n_cols columns (for dispatch logging).
 const char* topk_path(int rows, int64_t n_cols);
+// Rows up to this width take the short-row top-k: one workgroup per row, the row in LDS.
+constexpr int kTopkShortRow = 16384;
 
 // One key-cache write (new bf16 keys quantised into the cache at their slots).
 struct KcacheCall {

@@ -84,6 +84,11 @@ typedef enum idx_dtype {
 #define IDX_SELECT_NO_CUTOFF 2u /* idx_select only: skip the sampled cutoff of the one-pass
                                    selection and finish every scored entry exactly (the
                                    same result, slower; for checking the exact finish) */
+#define IDX_SELECT_ONE_PASS 4u  /* idx_select only: take the one-pass selection (scores kept
+                                   in the scan, cut there, exact finish) for every shape
+                                   that allows it (8..512 rows of a decode source), not only
+                                   for rows long enough to need the long-row top-k; the same
+                                   result (a testing aid and a tuning knob) */
 
 /* ------------------------------------------------------------------ scores */
 

@@ -261,7 +261,7 @@ SELECT_CASES = [
     ("out_ld < k", _problem(), dict(old=100), ARG),
     ("dense max_cols zero", _problem(max_cols=0), dict(), ARG),
     ("unknown mode", _problem(mode=7), dict(), ARG),
-    ("unknown flag", _problem(), dict(flags=4), ARG),
+    ("unknown flag", _problem(), dict(flags=8), ARG),
     ("paged page 16", _problem(mode=D.IDX_MODE_PAGED, page_size=16, block_table=BT, bt_rows=4,
                                 bt_ld=4, seq_lens=SL), dict(), UNS),
     ("paged table rows", _problem(mode=D.IDX_MODE_PAGED, page_size=64, block_table=BT, bt_rows=2,

@@ -72,7 +72,7 @@ def test_dispatch_log_lines():
         "import sys; sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})\n"
         "import synth, torch\n"
         "from gpu_util import Uploaded\n"
-        "up = Uploaded(synth.paged_decode(seed=401, rows=12, min_len=1000, max_len=9000))\n"
+        "up = Uploaded(synth.paged_decode(seed=401, rows=12, min_len=20000, max_len=40000))\n"
         "for _ in range(3): up.select(512)\n"
         "up = Uploaded(synth.paged_decode(seed=402, rows=2, min_len=1000, max_len=9000))\n"
         "up.select(512); up.logits()\n"

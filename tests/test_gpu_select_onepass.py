@@ -1,6 +1,7 @@
 """GPU idx_select through the one-pass selection (rows that read their own keys: the scan
 adds each group's largest score to its row's histogram, cuts at the k-th largest group
-maximum and writes the entries above the cut for an exact finish). Every result must equal
+maximum and writes the entries above the cut for an exact finish), forced with
+IDX_SELECT_ONE_PASS for the shorter rows the default sends to scores-then-top-k. Every result must equal
 idx_topk over idx_logits* bit for bit, with the cutoff and without it, whatever the
 workspace held before, on rows the cutoff cannot shrink (equal scores, rows shorter than k)
 and on rows with empty or clamped ranges; the scores-then-top-k path (prefill chunks, more
@@ -34,6 +35,9 @@ def _reference(up, k, sorted=True):
 
 
 def _select(up, k, **kw):
+    """idx_select through the one-pass selection (forced for rows the default would send
+    to scores-then-top-k), unless the caller says otherwise."""
+    kw.setdefault("one_pass", True)
     idx, val = D.idx_select(up.problem(), k, **kw)
     return host(idx), host(val)
 
@@ -84,7 +88,7 @@ def test_garbage_workspace_and_back_to_back_calls():
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for up, k in ((a, 2048), (b, 1024), (a, 700), (b, 2048), (a, 2048)):
         r_idx, r_val = _reference(up, k)
-        s_idx, s_val = D.idx_select(up.problem(), k, workspace=ws)
+        s_idx, s_val = D.idx_select(up.problem(), k, workspace=ws, one_pass=True)
         assert np.array_equal(host(s_idx), r_idx) and np.array_equal(host(s_val), r_val)
 
 
