@@ -86,7 +86,7 @@ def stored_traffic():
 
 
 COPY_BYTES = 512 << 20
-SCAN_KERNEL = "scan_kernel<2, dsaidx::PagedSrc, true>"
+SCAN_KERNEL = "scan_bal_kernel<2, dsaidx::PagedSrc, false>"
 
 
 def summarize_counters(fetch_dir: str, write_dir: str) -> int:
@@ -689,7 +689,7 @@ def main() -> int:
                 res[f"select_k{k}"] = kk
                 log(f"idx_select k={k}: {kk:.3f} ms/step")
     if args.only in ("all", "scan"):
-        ms_scan, _ = time_loop(scan, args.steps, args.warmup, stream, warm_s=0.3 if args.only == "all" else 0.0)
+        ms_scan, _ = time_loop(scan, args.steps, args.warmup, stream, warm_s=0.3)
         res["scan"] = ms_scan
         log(f"scan kernel alone: {ms_scan:.3f} ms/launch")
     if args.only != "all":
@@ -735,7 +735,7 @@ def main() -> int:
         "step_hbm_frac": step_b / (ms * 1e-3) / HBM_PEAK,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": stored_traffic(),
-                     "kernel": "scan_kernel<fp8, paged>", "ms_per_launch": res["scan"],
+                     "kernel": "scan_bal_kernel<fp8, paged> (idx_logits_paged)", "ms_per_launch": res["scan"],
                      "bytes_per_launch": sb,
                      "frac_of_read_probe": achieved / 1e9 / extra["read_probe_gbps"]},
         "cpu_baseline": cpu,
