@@ -220,13 +220,13 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // idx_select workspace. Two layouts, the larger one sized:
 //  - one-pass selection (rows that read their own keys, kSelMinRows..kBalancedMaxRows rows):
-//    the histogram slots, arrival counters, row step offsets, per-segment counts and
-//    survivor regions of SelectState, then the spill score rows [rows, ldw];
+//    the histogram slots, arrival counters, row step offsets, segment records and survivor
+//    regions of SelectState, then the spill score rows [rows, ldw];
 //  - scores then top-k (prefill chunks, more rows): the score matrix [rows, ldw], the
 //    rows' scored lengths, then the top-k workspace.
 // Every region starts on a 256-byte boundary; ldw = width rounded up to 64 columns.
 struct SelectLayout {
-  size_t slots, arrive, acc, seg_info, surv, spill, total;
+  size_t slots, arrive, acc, seg, surv, spill, total;
 };
 
 SelectLayout select_layout(const idx_problem* p) {
@@ -241,7 +241,7 @@ SelectLayout select_layout(const idx_problem* p) {
   L.slots = take((int64_t)kSelMaxBlocks * 2 * kSelSlotWords * 4);
   L.arrive = take(R * 8);
   L.acc = take((R + 1) * 8);
-  L.seg_info = take(steps * 4);
+  L.seg = take(steps * 16);
   L.surv = take(steps * 64 * 8);
   L.spill = take(R * ldw * 4);
   L.total = o;
@@ -364,12 +364,13 @@ idx_status select_call(const char* fn, const idx_problem* p, int k, int32_t* out
     st.slots = (uint32_t*)(ws + L.slots);
     st.arrive = (unsigned long long*)(ws + L.arrive);
     st.acc = (int64_t*)(ws + L.acc);
-    st.seg_info = (uint32_t*)(ws + L.seg_info);
+    st.seg = (uint4*)(ws + L.seg);
     st.surv = (uint64_t*)(ws + L.surv);
     st.spill = (float*)(ws + L.spill);
     st.k = k;
     st.gshift = select_group_shift(ldw, k);
-    st.wait_ticks = (flags & IDX_SELECT_NO_CUTOFF) ? 0 : kSelectWaitTicks;
+    st.cutoff = (flags & IDX_SELECT_NO_CUTOFF) ? 0 : 1;
+    st.wait_ticks = kSelectWaitTicks;
     c.logits = st.spill;
     c.sel = &st;
     log_once("idx_select: one pass (rows %d, width %lld, k %d, groups of %d, %lld scan workgroups)", p->rows,

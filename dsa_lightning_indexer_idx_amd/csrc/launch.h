@@ -48,18 +48,21 @@ constexpr int kSelCoarseBins = 256;   // and of its top 8 bits (16 fine bins eac
 constexpr int kSelSlotWords = kSelFineBins / 2 + kSelCoarseBins;  // 16-bit fine counts in pairs, coarse
 constexpr int kSelMaxBlocks = 1024;   // workgroups of a one-pass scan launch
 constexpr int kSelMaxSpan = 32;       // workgroups a row may span and still be cut
+constexpr uint32_t kSegNoCut = 0x80000000u;  // segment record: every entry was kept
 struct SelectState {
   uint32_t* slots;               // [kSelMaxBlocks, 2, kSelSlotWords]: histogram of a workgroup's
                                  // first (0) and last (1) row when shared with other workgroups
   unsigned long long* arrive;    // [rows] workgroups done with the row (counts up, never cleared)
   int64_t* acc;                  // [rows + 1] first step of each row in the call's step order
-  uint32_t* seg_info;            // [steps] at a segment's first step: survivors | (1 << 31) when
-                                 // the segment kept every entry (no cutoff)
+  uint4* seg;                    // [steps] at a segment's first step: x = survivors, | kSegNoCut
+                                 // when the segment kept every entry; y = its cut (the order key
+                                 // every survivor reaches); z = the largest survivor's order key
   uint64_t* surv;                // [steps, 64] survivor keys from the segment's first step on
   float* spill;                  // [rows, ld] scores of ranges that do not fit in LDS
   int k;
   int gshift;                    // group size 2^gshift columns, 0..4
-  int64_t wait_ticks;            // limit of a row wait (100 MHz clock); 0: no cutoff
+  int cutoff;                    // 0: every scored entry survives
+  int64_t wait_ticks;            // limit of a row wait (100 MHz clock)
 };
 
 // One scoring call, validated by the C-ABI layer.

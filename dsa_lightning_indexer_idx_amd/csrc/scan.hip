@@ -714,7 +714,8 @@ __device__ __forceinline__ void bal_stream(const ScanCommon& a, const StepTab& T
 //   * the cut is the lower edge of the fine bin holding the k-th largest group maximum,
 //     so at least k groups, hence k entries, reach it; the part's entries at or above it
 //     go, as selection keys, to the workgroup's region at the part's first step * 64,
-//     their count to seg_info at the part's first step.
+//     the part's record (their count, the cut, the largest of them) to seg at the part's
+//     first step.
 // Slots and counters are shared by all XCDs, so they are written and read with device-
 // scope atomic operations only. A wait that runs past wait_ticks, or a row spanning more
 // than kSelMaxSpan workgroups, keeps every entry of the part: correct in every case, only
@@ -890,8 +891,20 @@ __device__ __forceinline__ bool sel_wait(const SelectState& st, int r, unsigned 
   }
 }
 
+// Wave-wide maximum (lanes without a source in a DPP row shift contribute 0).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(a, b), max(c, d));
+}
+
 // Block-wide: the n_ent scores at sc (columns col0 ..) at or above the cut T, as
-// selection keys to out; returns their count. An entry's order key is at least T exactly
+// selection keys to out; returns their count, and to thread 0 in *kmax the largest order
+// key among them (0 if none). An entry's order key is at least T exactly
 // when its score is at least T's value (the order key is monotone; NaN compares false,
 // -0 == +0); T = 1 keeps every present entry (-inf and NaN excluded). The entries go in
 // chunks of 64 per thread: a thread marks which of its 64 (the float4s at 4 tid + v
@@ -899,13 +912,14 @@ __device__ __forceinline__ bool sel_wait(const SelectState& st, int r, unsigned 
 // order), and each thread writes its own survivors, reading back only those. n_ent is a
 // multiple of 64.
 __device__ __forceinline__ uint32_t sel_filter(const float* sc, int64_t n_ent, int64_t col0, uint32_t T,
-                                               uint64_t* out, uint32_t* wsum) {
+                                               uint64_t* out, uint32_t* wsum, uint32_t* wmax, uint32_t* kmax) {
   constexpr int kV = 16;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   const int nw = blockDim.x / kWave;
   const int64_t stride = 4 * (int64_t)blockDim.x;
   const float t = T <= 1u ? -__FLT_MAX__ : key_value(T);
   uint32_t done = 0;  // survivors of the earlier chunks
+  uint32_t mx = 0;    // this thread's largest survivor key
   for (int64_t c0 = 0; c0 < n_ent; c0 += kV * stride) {
     uint64_t mask = 0;
 #pragma unroll
@@ -935,9 +949,19 @@ __device__ __forceinline__ uint32_t sel_filter(const float* sc, int64_t n_ent, i
       const int bit = (int)__builtin_ctzll(mask);
       mask &= mask - 1;
       const int64_t i = c0 + (bit >> 2) * stride + 4 * tid + (bit & 3);
-      *o++ = ((uint64_t)order_key(sc[i]) << 32) | (uint32_t)(~(uint32_t)(col0 + i));
+      const uint32_t ok = order_key(sc[i]);
+      mx = max(mx, ok);
+      *o++ = ((uint64_t)ok << 32) | (uint32_t)(~(uint32_t)(col0 + i));
     }
     done += tot;
+  }
+  const uint32_t wm = wave_max_u32(mx);
+  if (lane == 0) wmax[wv] = wm;
+  lds_barrier();
+  if (tid == 0) {
+    uint32_t m = 0;
+    for (int w = 0; w < nw; ++w) m = max(m, wmax[w]);
+    *kmax = m;
   }
   return done;
 }
@@ -961,8 +985,8 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
   __shared__ uint32_t ctr;
   __shared__ unsigned long long sbase[2];
   __shared__ uint32_t hc[SELECT ? kSelCoarseBins : 1];
-  __shared__ uint32_t wsum[kBalWaves];
-  __shared__ uint32_t s_T, s_ok, s_above, s_f16[16];
+  __shared__ uint32_t wsum[kBalWaves], wmax[kBalWaves];
+  __shared__ uint32_t s_T, s_ok, s_above, s_f16[16], s_kmax;
   __shared__ int s_cbin;
   if (!SELECT && a.zero) {
     const int64_t per = (a.zero_words + nwaves - 1) / nwaves;
@@ -1106,7 +1130,7 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
       if (np == 0 || (which == 1 && np == 1)) break;
       int64_t b_lo, b_hi;
       const int64_t nb = span(p, b_lo, b_hi);
-      if (nb <= 1 || nb > kSelMaxSpan) continue;
+      if (nb <= 1 || nb > kSelMaxSpan || !st.cutoff) continue;
       with_scores(p, [&](const float* sc) { sel_hist(sc, (int64_t)P.len[p] * kTileTokens, st.gshift, hf, hc); });
       uint32_t* slot = st.slots + (b * 2 + which) * (int64_t)kSelSlotWords;
       for (int i = tid; i < kSelFineBins / 2; i += kBalThreads) atomic_st(slot + i, hf[i]);
@@ -1121,7 +1145,12 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
       int64_t b_lo, b_hi;
       const int64_t nb = span(p, b_lo, b_hi);
       const int64_t n_ent = (int64_t)P.len[p] * kTileTokens;
-      if (nb == 1) {
+      if (nb == 1 && !st.cutoff) {
+        if (tid == 0) {
+          s_T = 1u;
+          s_ok = 0u;
+        }
+      } else if (nb == 1) {
         // the whole row is here
         with_scores(p, [&](const float* sc) { sel_hist(sc, n_ent, st.gshift, hf, hc); });
         if (wib == 0) {
@@ -1143,8 +1172,8 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
             s_ok = 1;
           }
         }
-      } else if (nb <= kSelMaxSpan && (p == 0 || p == np - 1)) {
-        if (tid == 0) s_ok = st.wait_ticks > 0 && sel_wait(st, r, sbase[p == 0 ? 0 : 1], nb);
+      } else if (nb <= kSelMaxSpan && st.cutoff) {
+        if (tid == 0) s_ok = sel_wait(st, r, sbase[p == 0 ? 0 : 1], nb);
         // the row's slots: slot 1 of a workgroup where the row starts inside the range (it is
         // that range's last row), slot 0 where it covers the range's start
         const uint64_t acc_r = row_first(p);
@@ -1212,19 +1241,17 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
                                         : 1u;
           if (lane == 0) s_T = T2;
         }
-      } else {
-        if (tid == 0) {
-          s_T = 1u;  // spans too many workgroups: every entry survives
-          s_ok = 0;
-        }
+      } else if (tid == 0) {
+        s_T = 1u;  // no cutoff, or too many workgroups: every entry survives
+        s_ok = 0u;
       }
       lds_barrier();
       uint32_t cnt = 0;
       with_scores(p, [&](const float* sc) {
         cnt = sel_filter(sc, n_ent, (int64_t)P.rs0[p] * kTileTokens, s_T,
-                         st.surv + (int64_t)(beg + P.off[p]) * kTileTokens, wsum);
+                         st.surv + (int64_t)(beg + P.off[p]) * kTileTokens, wsum, wmax, &s_kmax);
       });
-      if (tid == 0) st.seg_info[beg + P.off[p]] = cnt | (s_ok ? 0u : 0x80000000u);
+      if (tid == 0) st.seg[beg + P.off[p]] = make_uint4(cnt | (s_ok ? 0u : kSegNoCut), s_T, s_kmax, 0u);
       lds_barrier();
     }
   } else if (!a.skip_tail) {

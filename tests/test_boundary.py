@@ -211,12 +211,12 @@ def _r256(x):
 def _select_layouts(L, rows, width):
     """Workspace of the two idx_select layouts the header describes: the one-pass selection
     (1024 workgroups x 2 histogram slots of 2048 + 256 words, a counter per row, rows + 1
-    step offsets, a count per 64-column step, 64 keys of 8 bytes per step, spill score
-    rows) and scores then top-k (score rows, scored lengths, the top-k workspace); ldw =
-    width rounded up to 64."""
+    step offsets, a 16-byte segment record per 64-column step, 64 keys of 8 bytes per step,
+    spill score rows) and scores then top-k (score rows, scored lengths, the top-k
+    workspace); ldw = width rounded up to 64."""
     ldw = (width + 63) // 64 * 64
     steps = rows * (ldw // 64)
-    one = sum(_r256(b) for b in (1024 * 2 * 2304 * 4, rows * 8, (rows + 1) * 8, steps * 4, steps * 64 * 8,
+    one = sum(_r256(b) for b in (1024 * 2 * 2304 * 4, rows * 8, (rows + 1) * 8, steps * 16, steps * 64 * 8,
                                   rows * ldw * 4))
     two = _r256(rows * ldw * 4) + _r256(rows * 4) + L.idx_topk_workspace(rows, width, 2048)
     return one, two
