@@ -190,8 +190,11 @@ __global__ __launch_bounds__(NT) void topk_short_kernel(TopkCall a) {
     const uint32_t c = sel[i];
     return sel_key(vkeys[c], c);
   };
+  // the sort's bounds from the histogram: every selected key lies in bins cut .. top
+  uint32_t lo_key = 0u, hi_key = 0u;
+  if (cut >= 0) bin_bounds(cut, ci.top, lo_key, hi_key);
   if (a.sorted)
-    bucket_sort_write<NT>(a, r, key, (int)keff, u.hist, (uint64_t*)dyn, ss);
+    bucket_sort_write<NT>(a, r, key, (int)keff, u.hist, (uint64_t*)dyn, ss, lo_key, hi_key);
   else
     write_list<NT>(a, r, key, (int)keff);
 }

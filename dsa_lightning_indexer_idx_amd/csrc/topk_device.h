@@ -192,6 +192,7 @@ __device__ void gather_at_least(const Get& get, const Item& item, int64_t n, uin
 
 struct CutInfo {
   int bin;          // bin of the k-th largest entry; -1: at most k entries, all selected
+  int top;          // highest bin holding an entry (-1: none)
   uint32_t above;   // entries in higher bins
   uint32_t count;   // entries in the cut bin
   uint32_t total;   // present entries
@@ -228,10 +229,21 @@ __device__ void find_cut(const uint32_t* h, int k, CutInfo& ci) {
   const uint32_t excl = incl - c;
   if (tid == 0) {
     ci.total = total;
+    if (total == 0u) ci.top = -1;
     if (total <= (uint32_t)k) {
       ci.bin = -1;
       ci.above = total;
       ci.count = 0;
+    }
+  }
+  if (excl == 0u && c != 0u) {  // the thread holding the highest entries
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      if (!found && hb[j] != 0u) {
+        ci.top = kHistBins - 1 - per * tid - j;
+        found = true;
+      }
     }
   }
   if (total > (uint32_t)k && excl < (uint32_t)k && (uint32_t)k <= incl) {
@@ -249,6 +261,14 @@ __device__ void find_cut(const uint32_t* h, int k, CutInfo& ci) {
     }
   }
   __syncthreads();
+}
+
+// Order-key bounds of the entries in bins lo_bin .. hi_bin (for bucket_sort_write): the
+// lower edge of lo_bin (at least 1) and the upper edge of hi_bin, no higher than +inf's key.
+__device__ __forceinline__ void bin_bounds(int lo_bin, int hi_bin, uint32_t& lo_key, uint32_t& hi_key) {
+  lo_key = max((uint32_t)lo_bin << kBinShift, 1u);
+  const uint64_t hi = (((uint64_t)hi_bin + 1) << kBinShift) - 1;
+  hi_key = (uint32_t)min(hi, (uint64_t)0xFF800000u);
 }
 
 // ------------------------------------------------------------------ sorting
