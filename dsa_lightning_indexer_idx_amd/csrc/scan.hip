@@ -19,6 +19,7 @@
 // read once per call, so their loads are non-temporal.
 #include "device.h"
 #include "launch.h"
+#include "topk_device.h"
 
 #include <mutex>
 
@@ -636,9 +637,11 @@ __device__ __forceinline__ void build_steps(const ScanCommon& a, const Src& src,
 
 // Scores the n steps of the range into buf (LDS, step i's 64 scores at buf + 64 i), taking
 // units of kUnit consecutive steps from *ctr until none is left. A wave keeps the next unit
-// taken one unit ahead and issues the loads of its next step across unit boundaries.
+// taken one unit ahead and issues the loads of its next step across unit boundaries. With
+// gmax, also the largest score of each 16 columns (step i's four at gmax + 4 i).
 template <int F>
-__device__ __forceinline__ void bal_stream(const ScanCommon& a, const StepTab& T, int n, uint32_t* ctr, float* buf) {
+__device__ __forceinline__ void bal_stream(const ScanCommon& a, const StepTab& T, int n, uint32_t* ctr, float* buf,
+                                           float* gmax) {
   const int lane = lane_id();
   const float NEG_INF = -__builtin_inff();
   const int nunits = (n + kUnit - 1) / kUnit;
@@ -683,7 +686,18 @@ __device__ __forceinline__ void bal_stream(const ScanCommon& a, const StepTab& T
     vn = sn >= 0 ? T.vlim[sn] : 0;
     if (vn > 0) load_step<F>(kn, scn, a, T.kidx0[sn], vn, lane);
     const float v = vc > 0 ? score_step<F>(kc, scc, qo, wr) : NEG_INF;
-    buf[sc * kTileTokens + lane] = lane < vc ? v : NEG_INF;
+    const float vs = lane < vc ? v : NEG_INF;
+    buf[sc * kTileTokens + lane] = vs;
+    if (gmax) {
+      // the 16-lane row's maximum lands in its last lane (a lane without a source keeps
+      // its own value)
+      float m = vs;
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x111, 0xF, 0xF, false)));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x112, 0xF, 0xF, false)));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x114, 0xF, 0xF, false)));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x118, 0xF, 0xF, false)));
+      if ((lane & 15) == 15) gmax[sc * 4 + (lane >> 4)] = m;
+    }
     if (sn < 0) return false;
     sc = sn;
     const int rn = T.row[sn];
@@ -807,16 +821,28 @@ __device__ __forceinline__ void sel_hist_groups(const float* sc, int64_t n_ent, 
 
 // Block-wide: histogram (LDS: hf fine pairs, hc coarse) of the group maxima of the
 // n_ent scores at sc (LDS or global; group i = entries i 2^gs .. (i + 1) 2^gs - 1).
-__device__ __forceinline__ void sel_hist(const float* sc, int64_t n_ent, int gs, uint32_t* hf, uint32_t* hc) {
+__device__ __forceinline__ void sel_hist(const float* sc, int64_t n_ent, int gs, uint32_t* hf, uint32_t* hc,
+                                         const float* gm = nullptr) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kSelFineBins / 2; i += blockDim.x) hf[i] = 0u;
   lds_barrier();
-  switch (gs) {
-    case 0: sel_hist_groups<0>(sc, n_ent, hf); break;
-    case 1: sel_hist_groups<1>(sc, n_ent, hf); break;
-    case 2: sel_hist_groups<2>(sc, n_ent, hf); break;
-    case 3: sel_hist_groups<3>(sc, n_ent, hf); break;
-    default: sel_hist_groups<4>(sc, n_ent, hf); break;
+  if (gm && gs == 4) {
+    // groups of 16 columns: their maxima were kept while scoring (gm, LDS)
+    for (int64_t i = tid; i < n_ent / 16; i += blockDim.x) {
+      const uint32_t mk = order_key(gm[i]);
+      if (mk) {
+        const uint32_t fb = mk >> 20;
+        atomicAdd(&hf[fb >> 1], 1u << (16 * (fb & 1)));
+      }
+    }
+  } else {
+    switch (gs) {
+      case 0: sel_hist_groups<0>(sc, n_ent, hf); break;
+      case 1: sel_hist_groups<1>(sc, n_ent, hf); break;
+      case 2: sel_hist_groups<2>(sc, n_ent, hf); break;
+      case 3: sel_hist_groups<3>(sc, n_ent, hf); break;
+      default: sel_hist_groups<4>(sc, n_ent, hf); break;
+    }
   }
   lds_barrier();
   for (int c = tid; c < kSelCoarseBins; c += blockDim.x) {
@@ -900,6 +926,78 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
   const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
   return max(max(a, b), max(c, d));
+}
+
+// Block-wide, as sel_filter for scores kept in LDS with their 16-column maxima gm: only the
+// groups whose maximum reaches the cut are read. Those groups are listed first (list: LDS
+// of n_ent / 16 entries, *lcount an LDS word), then their float4s are taken kI per thread,
+// marked in a mask, counted over the block and written by each thread, as in sel_filter.
+__device__ __forceinline__ uint32_t sel_filter_groups(const float* sc, const float* gm, int64_t n_ent, int64_t col0,
+                                                      uint32_t T, uint64_t* out, uint16_t* list, uint32_t* lcount,
+                                                      uint32_t* wsum, uint32_t* wmax, uint32_t* kmax) {
+  constexpr int kI = 8;  // float4s per thread per pass
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  const int nw = blockDim.x / kWave;
+  const int nt = blockDim.x;
+  const float t = T <= 1u ? -__FLT_MAX__ : key_value(T);
+  const int ng = (int)(n_ent / 16);
+  if (tid == 0) *lcount = 0u;
+  lds_barrier();
+  for (int g0 = 0; g0 < ng; g0 += nt) {
+    const int g = g0 + tid;
+    const bool take[1] = {g < ng && gm[g] >= t};
+    const uint16_t item[1] = {(uint16_t)g};
+    wave_append<1>(take, item, list, lcount, (uint32_t)ng);
+  }
+  lds_barrier();
+  const int nq = 4 * (int)*lcount;  // float4s of the listed groups
+  uint32_t done = 0;  // survivors of the earlier passes
+  uint32_t mx = 0;    // this thread's largest survivor key
+  for (int q0 = 0; q0 < nq; q0 += kI * nt) {
+    uint32_t mask = 0;
+#pragma unroll
+    for (int v = 0; v < kI; ++v) {
+      const int q = q0 + v * nt + tid;
+      if (q < nq) {
+        const float4 x = *(const float4*)(sc + 16 * list[q >> 2] + 4 * (q & 3));
+        mask |= (x.x >= t ? 1u : 0u) << (4 * v);
+        mask |= (x.y >= t ? 2u : 0u) << (4 * v);
+        mask |= (x.z >= t ? 4u : 0u) << (4 * v);
+        mask |= (x.w >= t ? 8u : 0u) << (4 * v);
+      }
+    }
+    const uint32_t mine = (uint32_t)__popc(mask);
+    const uint32_t incl = wave_inclusive_sum(mine);
+    lds_barrier();  // wsum may still be read by the previous pass
+    if (lane == kWave - 1) wsum[wv] = incl;
+    lds_barrier();
+    uint32_t before = incl - mine, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+      const uint32_t v = wsum[w];
+      before += w < wv ? v : 0u;
+      tot += v;
+    }
+    uint64_t* o = out + done + before;
+    while (mask) {
+      const int bit = (int)__builtin_ctz(mask);
+      mask &= mask - 1;
+      const int q = q0 + (bit >> 2) * nt + tid;
+      const int64_t i = 16 * (int64_t)list[q >> 2] + 4 * (q & 3) + (bit & 3);
+      const uint32_t ok = order_key(sc[i]);
+      mx = max(mx, ok);
+      *o++ = ((uint64_t)ok << 32) | (uint32_t)(~(uint32_t)(col0 + i));
+    }
+    done += tot;
+  }
+  const uint32_t wm = wave_max_u32(mx);
+  if (lane == 0) wmax[wv] = wm;
+  lds_barrier();
+  if (tid == 0) {
+    uint32_t m = 0;
+    for (int w = 0; w < nw; ++w) m = max(m, wmax[w]);
+    *kmax = m;
+  }
+  return done;
 }
 
 // Block-wide: the n_ent scores at sc (columns col0 ..) at or above the cut T, as
@@ -986,6 +1084,8 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
   __shared__ unsigned long long sbase[2];
   __shared__ uint32_t hc[SELECT ? kSelCoarseBins : 1];
   __shared__ uint32_t wsum[kBalWaves], wmax[kBalWaves];
+  __shared__ float gmax[SELECT ? kBlockSteps * 4 : 1];  // idx_select: each 16 columns' largest score
+  __shared__ uint32_t s_lcount;
   __shared__ uint32_t s_T, s_ok, s_above, s_f16[16], s_kmax;
   __shared__ int s_cbin;
   if (!SELECT && a.zero) {
@@ -1067,7 +1167,10 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
   if (resident) {
     build_steps(a, src, P, (int)(end - beg), T);
     __syncthreads();
-    bal_stream<F>(a, T, (int)(end - beg), &ctr, buf);
+    // idx_select with groups of 16 columns keeps their maxima while scoring: the histogram
+    // then reads those, and the filter reads only the groups that reach the cut (with
+    // smaller groups the cut passes most 16-column groups and this does not pay)
+    bal_stream<F>(a, T, (int)(end - beg), &ctr, buf, SELECT && st.gshift == 4 ? gmax : nullptr);
     __syncthreads();
     if constexpr (!SELECT) {
       // the range's scores to their rows, four per thread per store
@@ -1107,6 +1210,7 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
   if constexpr (SELECT) {
     static_assert(sizeof(StepTab) >= kSelFineBins * 2, "the fine histogram reuses the step table");
     uint32_t* hf = (uint32_t*)&T;
+    const bool use_gmax = resident && st.gshift == 4;  // the maxima of 16 columns were kept
     __syncthreads();
     // f(scores of part p): in LDS, or in the spill rows. Two calls, so that each inlined
     // copy reads through a pointer of known memory (a pointer that may be either takes
@@ -1131,7 +1235,9 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
       int64_t b_lo, b_hi;
       const int64_t nb = span(p, b_lo, b_hi);
       if (nb <= 1 || nb > kSelMaxSpan || !st.cutoff) continue;
-      with_scores(p, [&](const float* sc) { sel_hist(sc, (int64_t)P.len[p] * kTileTokens, st.gshift, hf, hc); });
+      with_scores(p, [&](const float* sc) {
+        sel_hist(sc, (int64_t)P.len[p] * kTileTokens, st.gshift, hf, hc, use_gmax ? gmax + 4 * P.off[p] : nullptr);
+      });
       uint32_t* slot = st.slots + (b * 2 + which) * (int64_t)kSelSlotWords;
       for (int i = tid; i < kSelFineBins / 2; i += kBalThreads) atomic_st(slot + i, hf[i]);
       for (int i = tid; i < kSelCoarseBins; i += kBalThreads) atomic_st(slot + kSelFineBins / 2 + i, hc[i]);
@@ -1152,7 +1258,9 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
         }
       } else if (nb == 1) {
         // the whole row is here
-        with_scores(p, [&](const float* sc) { sel_hist(sc, n_ent, st.gshift, hf, hc); });
+        with_scores(p, [&](const float* sc) {
+          sel_hist(sc, n_ent, st.gshift, hf, hc, use_gmax ? gmax + 4 * P.off[p] : nullptr);
+        });
         if (wib == 0) {
           int cbin;
           uint32_t above, T2 = 1u;
@@ -1246,11 +1354,14 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
         s_ok = 0u;
       }
       lds_barrier();
-      uint32_t cnt = 0;
-      with_scores(p, [&](const float* sc) {
-        cnt = sel_filter(sc, n_ent, (int64_t)P.rs0[p] * kTileTokens, s_T,
-                         st.surv + (int64_t)(beg + P.off[p]) * kTileTokens, wsum, wmax, &s_kmax);
-      });
+      uint32_t cnt;
+      const int64_t col0 = (int64_t)P.rs0[p] * kTileTokens;
+      uint64_t* so = st.surv + (int64_t)(beg + P.off[p]) * kTileTokens;
+      if (use_gmax)  // the group list reuses the step table's space (the cut is done with it)
+        cnt = sel_filter_groups(buf + P.off[p] * kTileTokens, gmax + 4 * P.off[p], n_ent, col0, s_T, so,
+                                (uint16_t*)&T, &s_lcount, wsum, wmax, &s_kmax);
+      else
+        with_scores(p, [&](const float* sc) { cnt = sel_filter(sc, n_ent, col0, s_T, so, wsum, wmax, &s_kmax); });
       if (tid == 0) st.seg[beg + P.off[p]] = make_uint4(cnt | (s_ok ? 0u : kSegNoCut), s_T, s_kmax, 0u);
       lds_barrier();
     }
