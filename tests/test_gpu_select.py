@@ -198,3 +198,26 @@ def test_long_rows_adversarial():
         kth = np.array([r_val[i][max(0, int((r_idx[i] >= 0).sum()) - 1)] for i in range(len(rows))])
         assert_selection_matches(s_idx[rows], r_idx, _ref_scores_fn(sub, r_lg), kth, f"long rows k={k}")
         assert np.array_equal(s_idx[1], np.arange(k, dtype=np.int32)), "equal scores: the first k"
+
+
+@pytest.mark.parametrize("shape", ["uniform", "ragged"])
+def test_select_spilled_ranges(shape):
+    """More steps than a workgroup keeps in LDS (about 600 per workgroup): the one-pass
+    selection reads the spilled scores for its histogram and its filter, rows span two to
+    several workgroups and share their histograms; every row equals idx_topk over
+    idx_logits bit for bit and the oracle confirms sampled rows."""
+    require_gpu()
+    if shape == "uniform":
+        case = synth.batched_decode(seed=151, rows=160, n=65536)
+    else:
+        case = synth.batched_decode(seed=152, rows=200, n=98304, ragged=True)
+    up = Uploaded(case)
+    lens = case.row_ke - case.row_ks
+    rows = sorted({0, 1, case.rows // 2, case.rows - 1, int(np.argmax(lens)), int(np.argmin(lens))})
+    sub = O.subset_rows(case, rows)
+    for k in (2048, 512):
+        say(f"[select] spilled ranges {shape} k={k}")
+        s_idx, _ = _self_consistent(up, k)
+        r_idx, r_val, r_lg = O.select_case(sub, k=k, with_logits=True)
+        kth = np.array([r_val[i][max(0, int((r_idx[i] >= 0).sum()) - 1)] for i in range(len(rows))])
+        assert_selection_matches(s_idx[rows], r_idx, _ref_scores_fn(sub, r_lg), kth, f"spilled {shape} k={k}")
