@@ -40,9 +40,10 @@ struct PerDeviceOnce {
 // k-th largest group maximum of a row is a value that at least k entries reach, so the
 // entries at or above it (the survivors) hold the row's top k. A row inside one workgroup
 // is cut at once; the two rows a workgroup may share with its neighbours (its first and
-// last) are cut once every workgroup of the row has published its histogram. Each
-// workgroup writes its survivors to its own region; a finish kernel selects exactly
-// among them.
+// last) are cut once every workgroup of the row has published its histogram; a shared
+// part may first be filtered at a lower speculative cut of its own while the row's cut is
+// summed up (and again at the row's cut when that comes out lower). Each workgroup
+// writes its survivors to its own region; a finish kernel selects exactly among them.
 constexpr int kSelFineBins = 4096;    // histogram of the top 12 bits of the order key
 constexpr int kSelCoarseBins = 256;   // and of its top 8 bits (16 fine bins each)
 constexpr int kSelSlotWords = kSelFineBins / 2 + kSelCoarseBins;  // 16-bit fine counts in pairs, coarse
@@ -56,7 +57,9 @@ struct SelectState {
   int64_t* acc;                  // [rows + 1] first step of each row in the call's step order
   uint4* seg;                    // [steps] at a segment's first step: x = survivors, | kSegNoCut
                                  // when the segment kept every entry; y = its cut (the order key
-                                 // every survivor reaches); z = the largest survivor's order key
+                                 // every survivor reaches); z = the largest survivor's order key;
+                                 // w = the row's cut as this segment found it (1: none), which
+                                 // every entry of the row's top k reaches
   uint64_t* surv;                // [steps, 64] survivor keys from the segment's first step on
   float* spill;                  // [rows, ld] scores of ranges that do not fit in LDS
   int k;

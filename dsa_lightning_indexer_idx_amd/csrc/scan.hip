@@ -588,7 +588,7 @@ constexpr int bal_threads() {
   return F == FMT_MXFP4 ? 768 : 512;
 }
 constexpr int kBalMaxWaves = 768 / kWave;
-constexpr int kUnit = 2;
+constexpr int kUnit = 1;
 constexpr int kBlockSteps = 512;   // steps a workgroup keeps in LDS: 128 KiB of scores
 // Steps of a wave's LDS slice when the range does not fit: the slices share the buffer.
 template <int NW>
@@ -596,6 +596,7 @@ constexpr int bal_slice_steps() {
   return kBlockSteps / NW >= kWave ? kWave : kBlockSteps / NW >= 32 ? 32 : 16;
 }
 constexpr int kMaxParts = kBalancedMaxRows;      // rows one range can meet
+constexpr int kSpecSteps = 128;                  // idx_select: parts filtered at a speculative cut
 
 // The rows meeting a workgroup's range, in order (built by wave 0).
 struct BlockParts {
@@ -723,13 +724,16 @@ __device__ __forceinline__ void bal_stream(const ScanCommon& a, const StepTab& T
 //   * a row inside the workgroup's range is cut at once from that histogram;
 //   * a row shared with other workgroups (only the range's first and last can be) is
 //     cut once each of the row's workgroups has published its histogram to its slot and
-//     counted itself in the row's arrival counter: the histograms of the row's slots are
-//     added up, coarse bins first;
+//     counted itself in the row's arrival counter: one wave per shared row adds up the
+//     histograms of the row's slots, coarse bins first, while the other waves filter the
+//     part at a speculative cut taken from its own histogram (almost surely at or below
+//     the row's cut, checked once that is known; a part filtered too high, or without a
+//     speculative cut, is filtered at the row's cut after);
 //   * the cut is the lower edge of the fine bin holding the k-th largest group maximum,
 //     so at least k groups, hence k entries, reach it; the part's entries at or above it
-//     go, as selection keys, to the workgroup's region at the part's first step * 64,
-//     the part's record (their count, the cut, the largest of them) to seg at the part's
-//     first step.
+//     go, as selection keys (in any order), to the workgroup's region at the part's
+//     first step * 64, the part's record (their count, the cut they reach, the largest of
+//     them, the row's cut) to seg at the part's first step.
 // Slots and counters are shared by all XCDs, so they are written and read with device-
 // scope atomic operations only. A wait that runs past wait_ticks, or a row spanning more
 // than kSelMaxSpan workgroups, keeps every entry of the part: correct in every case, only
@@ -1064,6 +1068,134 @@ __device__ __forceinline__ uint32_t sel_filter(const float* sc, int64_t n_ent, i
   return done;
 }
 
+// One wave: the cut of row r (as sel_cut over the sum of the slots of workgroups b_lo ..
+// b_lo + nbb - 1, those with steps) once the row's counter has moved nb past base
+// (bounded wait). 1 when the wait runs out or the row has fewer than k groups. Lane j
+// finds slot j's address once (slot_of(bb) = 0: no steps); then two rounds of loads: the
+// coarse bins of every slot (lane l: bins 255 - 4l .. 252 - 4l, eight slots in flight),
+// then the 16 fine bins of the coarse bin holding the k-th largest (lane l: bin l % 16 of
+// slots l / 16, l / 16 + 4, ...).
+template <class SlotOf>
+__device__ __forceinline__ uint32_t sel_row_cut_wave(const SelectState& st, int r, unsigned long long base, int64_t nb,
+                                                     int64_t b_lo, int nbb, const SlotOf& slot_of) {
+  const int lane = lane_id();
+  // lane j: slot j's address (slots past 64 are found as they come)
+  const uint64_t mp0 = lane < nbb ? (uint64_t)slot_of(b_lo + lane) : 0ull;
+  int ok = 0;
+  if (lane == 0) ok = sel_wait(st, r, base, nb) ? 1 : 0;
+  if (!__builtin_amdgcn_readlane(ok, 0)) return 1u;
+  auto slot_at = [&](uint64_t mp, int j, bool uniform) -> const uint32_t* {
+    if (uniform)
+      return (const uint32_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(mp >> 32), j) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mp, j));
+    return (const uint32_t*)(((uint64_t)(uint32_t)__shfl((int)(mp >> 32), j) << 32) | (uint32_t)__shfl((int)(uint32_t)mp, j));
+  };
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  for (int s0 = 0; s0 < nbb; s0 += kWave) {
+    const uint64_t mp = s0 == 0 ? mp0 : (s0 + lane < nbb ? (uint64_t)slot_of(b_lo + s0 + lane) : 0ull);
+    const int ns = min(kWave, nbb - s0);
+    constexpr int kS = 8;
+    for (int j0 = 0; j0 < ns; j0 += kS) {
+      uint32_t v[kS][4];
+#pragma unroll
+      for (int u = 0; u < kS; ++u) {
+        const uint32_t* sp = slot_at(mp, min(j0 + u, ns - 1), true);
+        const bool in = j0 + u < ns && sp != nullptr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[u][q] = in ? atomic_ld(sp + kSelFineBins / 2 + kSelCoarseBins - 1 - 4 * lane - q) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kS; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] += v[u][q];
+    }
+  }
+  int cbin;
+  uint32_t above;
+  if (!sel_cut_coarse((uint32_t)st.k,
+                      [&](uint32_t (&cc)[4]) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) cc[q] = c[q];
+                      },
+                      cbin, above))
+    return 1u;
+  const int fb = cbin * 16 + (lane & 15);
+  uint32_t f = 0;
+  for (int s0 = 0; s0 < nbb; s0 += kWave) {
+    const uint64_t mp = s0 == 0 ? mp0 : (s0 + lane < nbb ? (uint64_t)slot_of(b_lo + s0 + lane) : 0ull);
+    const int ns = min(kWave, nbb - s0);
+    // lane l: slots l / 16 + 4 i of this group of 64, 16 loads in flight
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 4 * i + (lane >> 4);
+      const uint32_t* sp = slot_at(mp, min(j, ns - 1), false);
+      v[i] = j < ns && sp != nullptr ? atomic_ld(sp + (fb >> 1)) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f += (v[i] >> (16 * (fb & 1))) & 0xFFFFu;
+  }
+  f += (uint32_t)__shfl_xor((int)f, 16);
+  f += (uint32_t)__shfl_xor((int)f, 32);
+  const uint32_t fr = (uint32_t)__shfl((int)f, 15 - (lane & 15));  // bin 15 - lane % 16
+  return sel_cut_fine((uint32_t)st.k, cbin, above, [&](int) { return fr; });
+}
+
+// Waves w .. w + nwv - 1 of the block (no block barrier): the n_ent scores at sc (columns
+// col0 ..) at or above the cut T (T <= 1: every present entry, as sel_filter), as
+// selection keys appended at out in any order (each wave takes its room from the LDS
+// counter *cnt), their largest order key max'd into *kmx. With gm (each 16 columns'
+// largest score, LDS) a lane takes a group of 16 and reads it only when its maximum
+// reaches the cut; without, two float4s 64 apart.
+template <bool GROUPS>
+__device__ __forceinline__ void sel_filter_waves(const float* sc, const float* gm, int64_t n_ent, int64_t col0,
+                                                 uint32_t T, uint64_t* out, uint32_t* cnt, uint32_t* kmx, int w,
+                                                 int nwv) {
+  constexpr int V = GROUPS ? 4 : 2;  // float4s of a lane's unit
+  const int lane = lane_id();
+  const float t = T <= 1u ? -__FLT_MAX__ : key_value(T);
+  const int nu = (int)(n_ent / (4 * V));  // units
+  uint32_t mx = 0;
+  for (int u0 = w * kWave; u0 < nu; u0 += nwv * kWave) {
+    const int u = u0 + lane;
+    // entry j of the lane's unit: GROUPS: 16 u + j; else float4 (u0 V + lane + 64 (j / 4)), item j % 4
+    auto at = [&](int j) -> int64_t {
+      return GROUPS ? 16 * (int64_t)u + j : 4 * ((int64_t)u0 * V + lane + kWave * (j >> 2)) + (j & 3);
+    };
+    uint32_t m = 0;
+    if (GROUPS ? u < nu && gm[u] >= t : true) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if (!GROUPS && u0 * V + lane + kWave * v >= V * nu) continue;
+        const float4 x = *(const float4*)(sc + at(4 * v));
+        m |= (x.x >= t ? 1u : 0u) << (4 * v);
+        m |= (x.y >= t ? 2u : 0u) << (4 * v);
+        m |= (x.z >= t ? 4u : 0u) << (4 * v);
+        m |= (x.w >= t ? 8u : 0u) << (4 * v);
+      }
+    }
+    const uint32_t c = (uint32_t)__popc(m);
+    const uint32_t incl = wave_inclusive_sum(c);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    if (tot == 0) continue;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(cnt, tot);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+    uint64_t* o = out + base + incl - c;
+    while (m) {
+      const int j = (int)__builtin_ctz(m);
+      m &= m - 1;
+      const int64_t i = at(j);
+      const uint32_t ok = order_key(sc[i]);
+      mx = max(mx, ok);
+      *o++ = ((uint64_t)ok << 32) | (uint32_t)(~(uint32_t)(col0 + i));
+    }
+  }
+  const uint32_t wm = wave_max_u32(mx);
+  if (lane == 0 && wm) atomicMax(kmx, wm);
+}
+
 // ------------------------------------------------------------------ balanced kernel
 
 template <int F, class Src, bool SELECT>
@@ -1086,8 +1218,9 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
   __shared__ uint32_t wsum[kBalWaves], wmax[kBalWaves];
   __shared__ float gmax[SELECT ? kBlockSteps * 4 : 1];  // idx_select: each 16 columns' largest score
   __shared__ uint32_t s_lcount;
-  __shared__ uint32_t s_T, s_ok, s_above, s_f16[16], s_kmax;
-  __shared__ int s_cbin;
+  __shared__ uint32_t s_T, s_ok, s_kmax;
+  __shared__ int s_sp[2];                                            // idx_select: the shared parts
+  __shared__ uint32_t s_spec[2], s_T2[2], s_cnt2[2], s_kmax2[2];   // and their speculative cuts
   if (!SELECT && a.zero) {
     const int64_t per = (a.zero_words + nwaves - 1) / nwaves;
     const int64_t z1 = min(a.zero_words, (wave + 1) * per);
@@ -1211,6 +1344,10 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
     static_assert(sizeof(StepTab) >= kSelFineBins * 2, "the fine histogram reuses the step table");
     uint32_t* hf = (uint32_t*)&T;
     const bool use_gmax = resident && st.gshift == 4;  // the maxima of 16 columns were kept
+    if (tid < 2) {
+      s_sp[tid] = -1;
+      s_spec[tid] = 0u;
+    }
     __syncthreads();
     // f(scores of part p): in LDS, or in the spill rows. Two calls, so that each inlined
     // copy reads through a pointer of known memory (a pointer that may be either takes
@@ -1228,26 +1365,89 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
       b_hi = sel_block_of(acc_r + P.rlen[p] - 1, total, B);
       return total >= (uint64_t)B ? b_hi - b_lo + 1 : (int64_t)P.rlen[p];
     };
-    // publish the histograms of the shared first and last rows, then count this workgroup
-    for (int which = 0; which < 2; ++which) {
+    auto bbeg = [&](int64_t bb) -> uint64_t { return total * (uint64_t)bb / (uint64_t)B; };
+    auto has_steps = [&](int64_t bb) -> bool { return bbeg(bb + 1) > bbeg(bb); };
+    // the slot holding part p's row of workgroup bb: slot 1 of a workgroup where the row
+    // starts inside the range (it is that range's last row), slot 0 where it covers the
+    // range's start
+    auto slot_of = [&](int p, int64_t bb) -> const uint32_t* {
+      return st.slots + (bb * 2 + (row_first(p) > bbeg(bb) ? 1 : 0)) * (int64_t)kSelSlotWords;
+    };
+    auto surv_of = [&](int p) -> uint64_t* { return st.surv + (int64_t)(beg + P.off[p]) * kTileTokens; };
+    // publish the histograms of the shared first and last rows (one store drain for both),
+    // then count this workgroup in their arrival counters. A part held in LDS also gets a
+    // speculative cut: the lower edge of the fine bin of its own m-th largest group
+    // maximum. The row's cut is the lower edge of the fine bin holding the row's k-th
+    // largest, so fewer than k of the row's groups lie in higher bins, about share * k of
+    // them in this part; m = share * k + 4 sqrt(share * k) + 8 puts the speculative cut
+    // at or below the row's cut but for a deviation of four standard deviations (then the
+    // part is filtered again). None (0) for a part of fewer than kSpecSteps steps, whose
+    // filter after the cut is short, or when m passes 3/4 of the part's groups (too many
+    // survivors): those parts are filtered at the row's cut once it is known
+    // which of the first and last parts are shared (and published)
+    auto shared_part = [&](int which) -> int {
       const int p = which == 0 ? 0 : np - 1;
-      if (np == 0 || (which == 1 && np == 1)) break;
+      if (np == 0 || (which == 1 && np == 1)) return -1;
       int64_t b_lo, b_hi;
       const int64_t nb = span(p, b_lo, b_hi);
-      if (nb <= 1 || nb > kSelMaxSpan || !st.cutoff) continue;
+      return nb <= 1 || nb > kSelMaxSpan || !st.cutoff ? -1 : p;
+    };
+    const int sp0 = shared_part(0), sp1 = shared_part(1);
+    // wave 0: the speculative cut of shared part `which` from the histogram in hf / hc
+    auto spec_cut = [&](int which) {
+      const int p = which == 0 ? sp0 : sp1;
+      if (!resident || wib != 0) return;
+      const int64_t n_ent = (int64_t)P.len[p] * kTileTokens;
+      const uint64_t groups = (uint64_t)n_ent >> st.gshift;
+      const uint64_t row_groups = ((uint64_t)P.rlen[p] * kTileTokens) >> st.gshift;
+      const float share = (float)st.k * (float)groups / (float)row_groups;
+      const uint64_t m = (uint64_t)(share + 4.f * __builtin_sqrtf(share)) + 8;
+      uint32_t ts = 0u;
+      int cbin;
+      uint32_t above;
+      if (P.len[p] >= kSpecSteps && 4 * m < 3 * groups &&
+          sel_cut_coarse(
+              (uint32_t)m,
+              [&](uint32_t (&c)[4]) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) c[q] = hc[kSelCoarseBins - 1 - 4 * lane - q];
+              },
+              cbin, above))
+        ts = sel_cut_fine((uint32_t)m, cbin, above, [&](int q) {
+          const int f = cbin * 16 + q;
+          return (hf[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
+        });
+      if (lane == 0) s_spec[which] = ts > 1u ? ts : 0u;
+    };
+    // the speculative cut of the first part is taken before the last part's histogram
+    // replaces it; that of the last published part after the counters are moved
+    for (int which = 0; which < 2; ++which) {
+      const int p = which == 0 ? sp0 : sp1;
+      if (p < 0) continue;
+      const int64_t n_ent = (int64_t)P.len[p] * kTileTokens;
       with_scores(p, [&](const float* sc) {
-        sel_hist(sc, (int64_t)P.len[p] * kTileTokens, st.gshift, hf, hc, use_gmax ? gmax + 4 * P.off[p] : nullptr);
+        sel_hist(sc, n_ent, st.gshift, hf, hc, use_gmax ? gmax + 4 * P.off[p] : nullptr);
       });
       uint32_t* slot = st.slots + (b * 2 + which) * (int64_t)kSelSlotWords;
       for (int i = tid; i < kSelFineBins / 2; i += kBalThreads) atomic_st(slot + i, hf[i]);
       for (int i = tid; i < kSelCoarseBins; i += kBalThreads) atomic_st(slot + kSelFineBins / 2 + i, hc[i]);
-      __builtin_amdgcn_s_waitcnt(0);  // the slot is written before the workgroup counts itself
-      __syncthreads();
-      if (tid == 0)
-        (void)__hip_atomic_fetch_add(st.arrive + P.r[p], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) s_sp[which] = p;
+      if (which == 0 && sp1 >= 0) {
+        spec_cut(0);
+        lds_barrier();  // the stores and the speculative cut have read hf and hc
+      }
     }
+    if (sp0 >= 0 || sp1 >= 0) {
+      __builtin_amdgcn_s_waitcnt(0);  // the slots are written before the workgroup counts itself
+      __syncthreads();
+      if (tid < 2 && s_sp[tid] >= 0)
+        (void)__hip_atomic_fetch_add(st.arrive + P.r[s_sp[tid]], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      spec_cut(sp1 >= 0 ? 1 : 0);
+      lds_barrier();
+    }
+    // the parts not shared with other workgroups, one after the other
     for (int p = 0; p < np; ++p) {
-      const int r = P.r[p];
+      if (p == s_sp[0] || p == s_sp[1]) continue;
       int64_t b_lo, b_hi;
       const int64_t nb = span(p, b_lo, b_hi);
       const int64_t n_ent = (int64_t)P.len[p] * kTileTokens;
@@ -1280,75 +1480,6 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
             s_ok = 1;
           }
         }
-      } else if (nb <= kSelMaxSpan && st.cutoff) {
-        if (tid == 0) s_ok = sel_wait(st, r, sbase[p == 0 ? 0 : 1], nb);
-        // the row's slots: slot 1 of a workgroup where the row starts inside the range (it is
-        // that range's last row), slot 0 where it covers the range's start
-        const uint64_t acc_r = row_first(p);
-        auto bbeg = [&](int64_t bb) -> uint64_t { return total * (uint64_t)bb / (uint64_t)B; };
-        auto slot_of = [&](int64_t bb) -> const uint32_t* {
-          return st.slots + (bb * 2 + (acc_r > bbeg(bb) ? 1 : 0)) * (int64_t)kSelSlotWords;
-        };
-        const int nbb = (int)(b_hi - b_lo + 1);  // the workgroups b_lo..b_hi, some maybe without steps
-        for (int i = tid; i < kSelCoarseBins; i += kBalThreads) hc[i] = 0u;
-        if (tid < 16) s_f16[tid] = 0u;
-        __syncthreads();
-        if (s_ok) {
-          // coarse bins summed over the slots, all loads of a thread issued together
-          constexpr int kU = 8;
-          for (int base = 0; base < nbb * kSelCoarseBins; base += kU * kBalThreads) {
-            uint32_t v[kU];
-            int bin[kU];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-              const int i = base + u * kBalThreads + tid;
-              v[u] = 0u;
-              bin[u] = i % kSelCoarseBins;
-              const int64_t bb = b_lo + i / kSelCoarseBins;
-              if (i < nbb * kSelCoarseBins && bbeg(bb + 1) > bbeg(bb))
-                v[u] = atomic_ld(slot_of(bb) + kSelFineBins / 2 + bin[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < kU; ++u)
-              if (v[u]) atomicAdd(&hc[bin[u]], v[u]);
-          }
-        }
-        lds_barrier();
-        if (wib == 0) {
-          int cbin = -1;
-          uint32_t above = 0;
-          const bool cut = s_ok && sel_cut_coarse(
-                                       (uint32_t)st.k,
-                                       [&](uint32_t (&c)[4]) {
-#pragma unroll
-                                         for (int j = 0; j < 4; ++j) c[j] = hc[kSelCoarseBins - 1 - 4 * lane - j];
-                                       },
-                                       cbin, above);
-          if (lane == 0) {
-            s_cbin = cut ? cbin : -1;
-            s_above = above;
-          }
-        }
-        lds_barrier();
-        const int cbin = s_cbin;
-        if (cbin >= 0) {
-          // the 16 fine bins of the coarse bin, summed over the slots: one load per thread
-          for (int i = tid; i < 16 * nbb; i += kBalThreads) {
-            const int64_t bb = b_lo + i / 16;
-            const int f = cbin * 16 + i % 16;
-            if (bbeg(bb + 1) > bbeg(bb)) {
-              const uint32_t w = atomic_ld(slot_of(bb) + (f >> 1));
-              const uint32_t v = (w >> (16 * (f & 1))) & 0xFFFFu;
-              if (v) atomicAdd(&s_f16[i % 16], v);
-            }
-          }
-        }
-        lds_barrier();
-        if (tid < kWave) {
-          const uint32_t T2 = cbin >= 0 ? sel_cut_fine((uint32_t)st.k, cbin, s_above, [&](int j) { return s_f16[j]; })
-                                        : 1u;
-          if (lane == 0) s_T = T2;
-        }
       } else if (tid == 0) {
         s_T = 1u;  // no cutoff, or too many workgroups: every entry survives
         s_ok = 0u;
@@ -1356,14 +1487,77 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
       lds_barrier();
       uint32_t cnt;
       const int64_t col0 = (int64_t)P.rs0[p] * kTileTokens;
-      uint64_t* so = st.surv + (int64_t)(beg + P.off[p]) * kTileTokens;
+      uint64_t* so = surv_of(p);
       if (use_gmax)  // the group list reuses the step table's space (the cut is done with it)
         cnt = sel_filter_groups(buf + P.off[p] * kTileTokens, gmax + 4 * P.off[p], n_ent, col0, s_T, so,
                                 (uint16_t*)&T, &s_lcount, wsum, wmax, &s_kmax);
       else
         with_scores(p, [&](const float* sc) { cnt = sel_filter(sc, n_ent, col0, s_T, so, wsum, wmax, &s_kmax); });
-      if (tid == 0) st.seg[beg + P.off[p]] = make_uint4(cnt | (s_ok ? 0u : kSegNoCut), s_T, s_kmax, 0u);
+      if (tid == 0) st.seg[beg + P.off[p]] = make_uint4(cnt | (s_ok ? 0u : kSegNoCut), s_T, s_kmax, s_T);
       lds_barrier();
+    }
+    // the shared parts: waves 0 and 1 cut the first and the last part's row from the slots
+    // while the other waves filter the parts that have a speculative cut at it; a part
+    // without one, or whose row cut comes out below it, is filtered at the row cut after
+    if (s_sp[0] >= 0 || s_sp[1] >= 0) {
+      if (tid < 2) {
+        s_cnt2[tid] = 0u;
+        s_kmax2[tid] = 0u;
+        s_T2[tid] = 1u;
+      }
+      lds_barrier();
+      if (wib < 2) {
+        const int which = wib;
+        if (s_sp[which] >= 0) {
+          const int p = s_sp[which];
+          int64_t b_lo, b_hi;
+          const int64_t nb = span(p, b_lo, b_hi);
+          const uint32_t tr =
+              sel_row_cut_wave(st, P.r[p], sbase[which], nb, b_lo, (int)(b_hi - b_lo + 1),
+                               [&](int64_t bb) { return has_steps(bb) ? slot_of(p, bb) : (const uint32_t*)nullptr; });
+          if (lane == 0) s_T2[which] = tr;
+        }
+      } else {
+        for (int which = 0; which < 2; ++which) {
+          if (!s_spec[which]) continue;
+          const int p = s_sp[which];
+          const int64_t n_ent = (int64_t)P.len[p] * kTileTokens, col0 = (int64_t)P.rs0[p] * kTileTokens;
+          if (use_gmax)
+            sel_filter_waves<true>(buf + P.off[p] * kTileTokens, gmax + 4 * P.off[p], n_ent, col0, s_spec[which],
+                                   surv_of(p), &s_cnt2[which], &s_kmax2[which], wib - 2, kBalWaves - 2);
+          else
+            sel_filter_waves<false>(buf + P.off[p] * kTileTokens, nullptr, n_ent, col0, s_spec[which], surv_of(p),
+                                    &s_cnt2[which], &s_kmax2[which], wib - 2, kBalWaves - 2);
+        }
+      }
+      lds_barrier();
+      // the parts without a speculative cut, or whose row cut came out below it, at the
+      // row cut by all waves
+      auto refilter = [&](int which) { return s_sp[which] >= 0 && (!s_spec[which] || s_T2[which] < s_spec[which]); };
+      if (tid < 2 && refilter(tid)) {
+        s_cnt2[tid] = 0u;
+        s_kmax2[tid] = 0u;
+      }
+      lds_barrier();
+      for (int which = 0; which < 2; ++which) {
+        if (!refilter(which)) continue;
+        const int p = s_sp[which];
+        const int64_t n_ent = (int64_t)P.len[p] * kTileTokens, col0 = (int64_t)P.rs0[p] * kTileTokens;
+        if (use_gmax)
+          sel_filter_waves<true>(buf + P.off[p] * kTileTokens, gmax + 4 * P.off[p], n_ent, col0, s_T2[which],
+                                 surv_of(p), &s_cnt2[which], &s_kmax2[which], wib, kBalWaves);
+        else
+          with_scores(p, [&](const float* sc) {
+            sel_filter_waves<false>(sc, nullptr, n_ent, col0, s_T2[which], surv_of(p), &s_cnt2[which],
+                                    &s_kmax2[which], wib, kBalWaves);
+          });
+      }
+      lds_barrier();
+      if (tid < 2 && s_sp[tid] >= 0) {
+        const uint32_t tr = s_T2[tid];
+        st.seg[beg + P.off[s_sp[tid]]] =
+            make_uint4(s_cnt2[tid] | (tr > 1u ? 0u : kSegNoCut), refilter(tid) ? tr : s_spec[tid], s_kmax2[tid], tr);
+      }
     }
   } else if (!a.skip_tail) {
     // -inf past each row's scored steps, in 4096-column pieces spread over all waves

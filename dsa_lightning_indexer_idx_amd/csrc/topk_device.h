@@ -627,7 +627,7 @@ struct alignas(16) FinishLds {
   RadixShared sh;
   SortShared ss;
   uint32_t count;
-  uint32_t wsum[NT / kWave], wlo[NT / kWave], whi[NT / kWave];
+  uint32_t wsum[NT / kWave], wlo[NT / kWave], whi[NT / kWave], wcut[NT / kWave];
 };
 
 // Block-wide: row r from the exact top k of the S keys in L.cand (lo_key / hi_key: order
@@ -664,8 +664,10 @@ __device__ __forceinline__ void finish_cand(const TopkCall& a, int r, int S, uin
 }
 
 // Block-wide: row r (steps [s0, s1) of total, s0 < s1, over the W workgroups of the
-// scan) from its segments' survivors. The bounds of the final sort come from the segment
-// records: the lowest cut (when every segment had one) and the largest survivor.
+// scan) from its segments' survivors. A segment may hold survivors below the row's cut
+// (it was filtered at a lower cut of its own): those are dropped as the survivors come
+// into LDS. The bounds of the final sort come from the segment records: the row's cut,
+// or else the lowest cut (when every segment had one), and the largest survivor.
 template <int NT>
 __device__ __forceinline__ void finish_survivors(const TopkCall& a, int r, uint64_t total, uint64_t s0, uint64_t s1,
                                                  uint64_t W, const uint4* seg, const uint64_t* surv,
@@ -682,7 +684,7 @@ __device__ __forceinline__ void finish_survivors(const TopkCall& a, int r, uint6
   // segment i: steps [max(total (w_lo + i) / W, s0), min(total (w_lo + i + 1) / W, s1))
   // (workgroups without steps have none); its survivors and their exclusive prefix; the
   // lowest cut (0: a segment kept every entry) and the largest survivor
-  uint32_t c[PER], t = 0, lo = ~0u, hi = 0u;
+  uint32_t c[PER], t = 0, lo = ~0u, hi = 0u, cut = 0u;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = tid * PER + j;
@@ -693,6 +695,7 @@ __device__ __forceinline__ void finish_survivors(const TopkCall& a, int r, uint6
       if (sl < min(total * (uint64_t)(w_lo + i + 1) / W, s1)) {
         const uint4 g = seg[sl];
         c[j] = g.x & ~kSegNoCut;
+        cut = max(cut, g.w);
         if (c[j]) {
           lo = min(lo, (g.x & kSegNoCut) ? 0u : g.y);
           hi = max(hi, g.z);
@@ -706,11 +709,13 @@ __device__ __forceinline__ void finish_survivors(const TopkCall& a, int r, uint6
   for (int lb = 0; lb < 6; ++lb) {
     lo = min(lo, xor_lane(lo, lb));
     hi = max(hi, xor_lane(hi, lb));
+    cut = max(cut, xor_lane(cut, lb));
   }
   if (lane == kWave - 1) L.wsum[wv] = incl;
   if (lane == 0) {
     L.wlo[wv] = lo;
     L.whi[wv] = hi;
+    L.wcut[wv] = cut;
   }
   __syncthreads();
   uint32_t off = incl - t, S = 0;
@@ -721,6 +726,7 @@ __device__ __forceinline__ void finish_survivors(const TopkCall& a, int r, uint6
     S += v;
     lo = min(lo, L.wlo[w]);
     hi = max(hi, L.whi[w]);
+    cut = max(cut, L.wcut[w]);
   }
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -749,14 +755,38 @@ __device__ __forceinline__ void finish_survivors(const TopkCall& a, int r, uint6
       const int64_t i = (int64_t)j * NT + tid;
       v[j] = i < (int64_t)S ? surv_at(i) : 0ull;
     }
+    int S2 = (int)S;
+    if (cut > 1u && lo < cut) {
+      // those at or above the row's cut, packed in thread order
+      uint32_t keep = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int64_t i = (int64_t)j * NT + tid;
-      if (i < (int64_t)S) L.cand[i] = v[j];
+      for (int j = 0; j < kPer; ++j) keep |= (v[j] != 0ull && (uint32_t)(v[j] >> 32) >= cut ? 1u : 0u) << j;
+      const uint32_t mine = (uint32_t)__popc(keep);
+      const uint32_t inc = wave_inclusive_sum(mine);
+      if (lane == kWave - 1) L.wsum[wv] = inc;
+      __syncthreads();
+      uint32_t at = inc - mine, all = 0;
+#pragma unroll
+      for (int w = 0; w < NT / kWave; ++w) {
+        const uint32_t n = L.wsum[w];
+        at += w < wv ? n : 0u;
+        all += n;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if ((keep >> j) & 1u) L.cand[at++] = v[j];
+      S2 = (int)all;
+      lo = cut;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int64_t i = (int64_t)j * NT + tid;
+        if (i < (int64_t)S) L.cand[i] = v[j];
+      }
     }
     __syncthreads();
     const bool bounded = lo > 1u && lo != ~0u && hi >= lo;  // a cut of 1 is no bound
-    finish_cand<NT>(a, r, (int)S, bounded ? lo : 0u, bounded ? hi : 0u, L);
+    finish_cand<NT>(a, r, S2, bounded ? lo : 0u, bounded ? hi : 0u, L);
     return;
   }
   // more than LDS holds (e.g. many equal scores): select from the survivors in place
