@@ -169,3 +169,35 @@ def test_empty_and_clamped_ranges_two_pass():
     r_idx, _ = _reference(up, 128)
     assert np.all(s_idx[5] == -1)
     assert np.array_equal(s_idx, r_idx)
+
+
+@pytest.mark.parametrize("n, rows", [(131072, 48), (65536, 64)])
+def test_speculative_cut_too_high(n, rows):
+    """Rows whose top k sits in one stretch of keys (scales 8x over the first 30% of the
+    row): the workgroup part holding that stretch takes a speculative cut from its own
+    histogram far above the row's cut and is filtered again at the row's cut, on the
+    16-column maxima path (128K-wide rows, and k = 512) and on the plain filter (64K-wide
+    rows at k = 2048 take groups of 8). A cold stretch (scales / 8 over the second half)
+    gives parts whose speculative cut lies far below. Every row equals idx_topk over
+    idx_logits bit for bit; the oracle confirms the hot and cold rows."""
+    require_gpu()
+    case = synth.batched_decode(seed=221 + rows, rows=rows, n=n)
+    hot, cold = [0, 5, rows - 1], [3]
+    for r in hot:
+        s = int(case.row_ks[r])
+        case.k_scale[s:s + (3 * n) // 10] *= np.float32(8)
+    for r in cold:
+        s = int(case.row_ks[r])
+        case.k_scale[s + n // 2:s + n] /= np.float32(8)
+    up = Uploaded(case)
+    check = sorted(hot + cold)
+    sub = O.subset_rows(case, check)
+    for k in (2048, 512):
+        say(f"[one-pass] speculative cut, {rows} x {n}, k={k}")
+        s_idx, s_val = _select(up, k, one_pass=False)
+        t_idx, t_val = _reference(up, k)
+        assert np.array_equal(s_idx, t_idx), "select != topk(logits)"
+        assert np.array_equal(s_val, t_val)
+        r_idx, r_val, r_lg = O.select_case(sub, k=k, with_logits=True)
+        kth = np.array([r_val[i][max(0, int((r_idx[i] >= 0).sum()) - 1)] for i in range(len(check))])
+        assert_selection_matches(s_idx[check], r_idx, lambda i, idx: r_lg[i][idx], kth, f"speculative {n} k={k}")
