@@ -1071,44 +1071,52 @@ __device__ __forceinline__ uint32_t sel_filter(const float* sc, int64_t n_ent, i
 // One wave: the cut of row r (as sel_cut over the sum of the slots of workgroups b_lo ..
 // b_lo + nbb - 1, those with steps) once the row's counter has moved nb past base
 // (bounded wait). 1 when the wait runs out or the row has fewer than k groups. Lane j
-// finds slot j's address once (slot_of(bb) = 0: no steps); then two rounds of loads: the
-// coarse bins of every slot (lane l: bins 255 - 4l .. 252 - 4l, eight slots in flight),
-// then the 16 fine bins of the coarse bin holding the k-th largest (lane l: bin l % 16 of
-// slots l / 16, l / 16 + 4, ...).
+// finds slot j's index once (slot_of(bb) < 0: no steps). One round of loads takes the
+// coarse bins of every slot (lane l: bins 255 - 4l .. 252 - 4l, eight slots in flight)
+// and the fine bins of the four coarse bins pc - 1 .. pc + 2 around a predicted one (lane
+// l: fine word l % 32 of them, of every other slot); when the coarse bin holding the k-th
+// largest is not among them (or pc < 1), a second round takes its 16 fine bins.
 template <class SlotOf>
 __device__ __forceinline__ uint32_t sel_row_cut_wave(const SelectState& st, int r, unsigned long long base, int64_t nb,
-                                                     int64_t b_lo, int nbb, const SlotOf& slot_of) {
+                                                     int64_t b_lo, int nbb, const SlotOf& slot_of, int pc) {
   const int lane = lane_id();
-  // lane j: slot j's address (slots past 64 are found as they come)
-  const uint64_t mp0 = lane < nbb ? (uint64_t)slot_of(b_lo + lane) : 0ull;
+  const int si0 = lane < nbb ? slot_of(b_lo + lane) : -1;
   int ok = 0;
   if (lane == 0) ok = sel_wait(st, r, base, nb) ? 1 : 0;
   if (!__builtin_amdgcn_readlane(ok, 0)) return 1u;
-  auto slot_at = [&](uint64_t mp, int j, bool uniform) -> const uint32_t* {
-    if (uniform)
-      return (const uint32_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(mp >> 32), j) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mp, j));
-    return (const uint32_t*)(((uint64_t)(uint32_t)__shfl((int)(mp >> 32), j) << 32) | (uint32_t)__shfl((int)(uint32_t)mp, j));
-  };
+  // word w of the slot of index x (none: x < 0)
+  auto word = [&](int x, int w) -> uint32_t { return x >= 0 ? atomic_ld(st.slots + (int64_t)x * kSelSlotWords + w) : 0u; };
   uint32_t c[4] = {0u, 0u, 0u, 0u};
+  const int pw0 = 8 * (pc - 1);  // first fine word of the predicted coarse bins
+  const bool pred = pc >= 1 && pc + 2 < kSelCoarseBins;
+  uint32_t plo = 0, phi = 0;     // fine word pw0 + lane % 32 (its two counts) over slots lane / 32, + 2, ...
   for (int s0 = 0; s0 < nbb; s0 += kWave) {
-    const uint64_t mp = s0 == 0 ? mp0 : (s0 + lane < nbb ? (uint64_t)slot_of(b_lo + s0 + lane) : 0ull);
+    const int si = s0 == 0 ? si0 : (s0 + lane < nbb ? slot_of(b_lo + s0 + lane) : -1);
     const int ns = min(kWave, nbb - s0);
     constexpr int kS = 8;
     for (int j0 = 0; j0 < ns; j0 += kS) {
-      uint32_t v[kS][4];
+      uint32_t v[kS][4], fw[kS / 2];
 #pragma unroll
       for (int u = 0; u < kS; ++u) {
-        const uint32_t* sp = slot_at(mp, min(j0 + u, ns - 1), true);
-        const bool in = j0 + u < ns && sp != nullptr;
+        const int x = j0 + u < ns ? __builtin_amdgcn_readlane(si, j0 + u) : -1;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[u][q] = in ? atomic_ld(sp + kSelFineBins / 2 + kSelCoarseBins - 1 - 4 * lane - q) : 0u;
+        for (int q = 0; q < 4; ++q) v[u][q] = word(x, kSelFineBins / 2 + kSelCoarseBins - 1 - 4 * lane - q);
+      }
+#pragma unroll
+      for (int u = 0; u < kS / 2; ++u) {
+        const int j = j0 + 2 * u + (lane >> 5);
+        const int x = __shfl(si, min(j, ns - 1));
+        fw[u] = word(pred && j < ns ? x : -1, pw0 + (lane & 31));
       }
 #pragma unroll
       for (int u = 0; u < kS; ++u)
 #pragma unroll
         for (int q = 0; q < 4; ++q) c[q] += v[u][q];
+#pragma unroll
+      for (int u = 0; u < kS / 2; ++u) {
+        plo += fw[u] & 0xFFFFu;
+        phi += fw[u] >> 16;
+      }
     }
   }
   int cbin;
@@ -1120,18 +1128,28 @@ __device__ __forceinline__ uint32_t sel_row_cut_wave(const SelectState& st, int 
                       },
                       cbin, above))
     return 1u;
+  plo += (uint32_t)__shfl_xor((int)plo, 32);
+  phi += (uint32_t)__shfl_xor((int)phi, 32);
+  if (pred && cbin >= pc - 1 && cbin <= pc + 2) {
+    // fine bin j of cbin: half j % 2 of word 8 (cbin - pc + 1) + j / 2
+    const int j = 15 - (lane & 15);  // this lane's bin
+    const int src = 8 * (cbin - pc + 1) + (j >> 1);
+    const uint32_t lo = (uint32_t)__shfl((int)plo, src), hi = (uint32_t)__shfl((int)phi, src);
+    const uint32_t fr = (j & 1) ? hi : lo;
+    return sel_cut_fine((uint32_t)st.k, cbin, above, [&](int) { return fr; });
+  }
   const int fb = cbin * 16 + (lane & 15);
   uint32_t f = 0;
   for (int s0 = 0; s0 < nbb; s0 += kWave) {
-    const uint64_t mp = s0 == 0 ? mp0 : (s0 + lane < nbb ? (uint64_t)slot_of(b_lo + s0 + lane) : 0ull);
+    const int si = s0 == 0 ? si0 : (s0 + lane < nbb ? slot_of(b_lo + s0 + lane) : -1);
     const int ns = min(kWave, nbb - s0);
     // lane l: slots l / 16 + 4 i of this group of 64, 16 loads in flight
     uint32_t v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = 4 * i + (lane >> 4);
-      const uint32_t* sp = slot_at(mp, min(j, ns - 1), false);
-      v[i] = j < ns && sp != nullptr ? atomic_ld(sp + (fb >> 1)) : 0u;
+      const int x = __shfl(si, min(j, ns - 1));
+      v[i] = word(j < ns ? x : -1, fb >> 1);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) f += (v[i] >> (16 * (fb & 1))) & 0xFFFFu;
@@ -1221,6 +1239,7 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
   __shared__ uint32_t s_T, s_ok, s_kmax;
   __shared__ int s_sp[2];                                            // idx_select: the shared parts
   __shared__ uint32_t s_spec[2], s_T2[2], s_cnt2[2], s_kmax2[2];   // and their speculative cuts
+  __shared__ int s_pc[2];                                           // and predicted coarse bins
   if (!SELECT && a.zero) {
     const int64_t per = (a.zero_words + nwaves - 1) / nwaves;
     const int64_t z1 = min(a.zero_words, (wave + 1) * per);
@@ -1347,6 +1366,7 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
     if (tid < 2) {
       s_sp[tid] = -1;
       s_spec[tid] = 0u;
+      s_pc[tid] = -1;
     }
     __syncthreads();
     // f(scores of part p): in LDS, or in the spill rows. Two calls, so that each inlined
@@ -1367,12 +1387,6 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
     };
     auto bbeg = [&](int64_t bb) -> uint64_t { return total * (uint64_t)bb / (uint64_t)B; };
     auto has_steps = [&](int64_t bb) -> bool { return bbeg(bb + 1) > bbeg(bb); };
-    // the slot holding part p's row of workgroup bb: slot 1 of a workgroup where the row
-    // starts inside the range (it is that range's last row), slot 0 where it covers the
-    // range's start
-    auto slot_of = [&](int p, int64_t bb) -> const uint32_t* {
-      return st.slots + (bb * 2 + (row_first(p) > bbeg(bb) ? 1 : 0)) * (int64_t)kSelSlotWords;
-    };
     auto surv_of = [&](int p) -> uint64_t* { return st.surv + (int64_t)(beg + P.off[p]) * kTileTokens; };
     // publish the histograms of the shared first and last rows (one store drain for both),
     // then count this workgroup in their arrival counters. A part held in LDS also gets a
@@ -1393,47 +1407,56 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
       return nb <= 1 || nb > kSelMaxSpan || !st.cutoff ? -1 : p;
     };
     const int sp0 = shared_part(0), sp1 = shared_part(1);
-    // wave 0: the speculative cut of shared part `which` from the histogram in hf / hc
-    auto spec_cut = [&](int which) {
+    // wave w, from the histogram of shared part `which` in f / c: the coarse bin of its own
+    // share of the row's k-th largest group maximum (the row's cut is most likely in it or
+    // next to it), and the speculative cut
+    auto spec_cut = [&](int which, int w, const uint32_t* f, const uint32_t* c) {
       const int p = which == 0 ? sp0 : sp1;
-      if (!resident || wib != 0) return;
+      if (wib != w) return;
       const int64_t n_ent = (int64_t)P.len[p] * kTileTokens;
       const uint64_t groups = (uint64_t)n_ent >> st.gshift;
       const uint64_t row_groups = ((uint64_t)P.rlen[p] * kTileTokens) >> st.gshift;
       const float share = (float)st.k * (float)groups / (float)row_groups;
-      const uint64_t m = (uint64_t)(share + 4.f * __builtin_sqrtf(share)) + 8;
-      uint32_t ts = 0u;
+      auto coarse4 = [&](uint32_t (&cc)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cc[q] = c[kSelCoarseBins - 1 - 4 * lane - q];
+      };
       int cbin;
       uint32_t above;
-      if (P.len[p] >= kSpecSteps && 4 * m < 3 * groups &&
-          sel_cut_coarse(
-              (uint32_t)m,
-              [&](uint32_t (&c)[4]) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) c[q] = hc[kSelCoarseBins - 1 - 4 * lane - q];
-              },
-              cbin, above))
+      const bool pc = sel_cut_coarse((uint32_t)max(share + 0.5f, 1.f), coarse4, cbin, above);
+      if (lane == 0) s_pc[which] = pc ? cbin : -1;
+      const uint64_t m = (uint64_t)(share + 4.f * __builtin_sqrtf(share)) + 8;
+      uint32_t ts = 0u;
+      if (resident && P.len[p] >= kSpecSteps && 4 * m < 3 * groups && sel_cut_coarse((uint32_t)m, coarse4, cbin, above))
         ts = sel_cut_fine((uint32_t)m, cbin, above, [&](int q) {
-          const int f = cbin * 16 + q;
-          return (hf[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
+          const int fb = cbin * 16 + q;
+          return (f[fb >> 1] >> (16 * (fb & 1))) & 0xFFFFu;
         });
       if (lane == 0) s_spec[which] = ts > 1u ? ts : 0u;
     };
-    // the speculative cut of the first part is taken before the last part's histogram
-    // replaces it; that of the last published part after the counters are moved
+    // the last part's histogram goes past the range's scores in buf when they leave room
+    // (both histograms then stand until the speculative cuts are taken after the arrival
+    // counters move); else it replaces the first part's, whose speculative cut is taken
+    // before
+    const bool room = resident && (end - beg) * kTileTokens + kSelFineBins / 2 + kSelCoarseBins <=
+                                      (uint64_t)kBlockSteps * kTileTokens;
+    uint32_t* hf1 = room ? (uint32_t*)(buf + (end - beg) * kTileTokens) : hf;
+    uint32_t* hc1 = room ? hf1 + kSelFineBins / 2 : hc;
     for (int which = 0; which < 2; ++which) {
       const int p = which == 0 ? sp0 : sp1;
       if (p < 0) continue;
+      uint32_t* f = which == 0 ? hf : hf1;
+      uint32_t* c = which == 0 ? hc : hc1;
       const int64_t n_ent = (int64_t)P.len[p] * kTileTokens;
       with_scores(p, [&](const float* sc) {
-        sel_hist(sc, n_ent, st.gshift, hf, hc, use_gmax ? gmax + 4 * P.off[p] : nullptr);
+        sel_hist(sc, n_ent, st.gshift, f, c, use_gmax ? gmax + 4 * P.off[p] : nullptr);
       });
       uint32_t* slot = st.slots + (b * 2 + which) * (int64_t)kSelSlotWords;
-      for (int i = tid; i < kSelFineBins / 2; i += kBalThreads) atomic_st(slot + i, hf[i]);
-      for (int i = tid; i < kSelCoarseBins; i += kBalThreads) atomic_st(slot + kSelFineBins / 2 + i, hc[i]);
+      for (int i = tid; i < kSelFineBins / 2; i += kBalThreads) atomic_st(slot + i, f[i]);
+      for (int i = tid; i < kSelCoarseBins; i += kBalThreads) atomic_st(slot + kSelFineBins / 2 + i, c[i]);
       if (tid == 0) s_sp[which] = p;
-      if (which == 0 && sp1 >= 0) {
-        spec_cut(0);
+      if (which == 0 && sp1 >= 0 && !room) {
+        spec_cut(0, 0, hf, hc);
         lds_barrier();  // the stores and the speculative cut have read hf and hc
       }
     }
@@ -1442,7 +1465,12 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
       __syncthreads();
       if (tid < 2 && s_sp[tid] >= 0)
         (void)__hip_atomic_fetch_add(st.arrive + P.r[s_sp[tid]], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      spec_cut(sp1 >= 0 ? 1 : 0);
+      if (sp1 < 0) spec_cut(0, 0, hf, hc);
+      else if (room && sp0 >= 0) {
+        spec_cut(0, 0, hf, hc);
+        spec_cut(1, 1, hf1, hc1);
+      } else
+        spec_cut(1, 0, hf1, hc1);
       lds_barrier();
     }
     // the parts not shared with other workgroups, one after the other
@@ -1514,7 +1542,13 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
           const int64_t nb = span(p, b_lo, b_hi);
           const uint32_t tr =
               sel_row_cut_wave(st, P.r[p], sbase[which], nb, b_lo, (int)(b_hi - b_lo + 1),
-                               [&](int64_t bb) { return has_steps(bb) ? slot_of(p, bb) : (const uint32_t*)nullptr; });
+                               // the slot of part p's row in workgroup bb: slot 1 of a workgroup
+                               // where the row starts inside the range (that range's last
+                               // row), slot 0 where it covers the range's start
+                               [&](int64_t bb) -> int {
+                                 return has_steps(bb) ? (int)(bb * 2 + (row_first(p) > bbeg(bb) ? 1 : 0)) : -1;
+                               },
+                               s_pc[which]);
           if (lane == 0) s_T2[which] = tr;
         }
       } else {
