@@ -486,8 +486,8 @@ static void launch_long(const TopkCall& c, const LongWs& ws, int64_t seg, int64_
 }
 
 const char* topk_path(int rows, int64_t n_cols) {
+  if (n_cols <= kWideRow && rows <= device_cu_count()) return "wide rows (one 1024-thread workgroup per row, row in LDS)";
   if (n_cols <= kShortRow) return "short rows (one workgroup per row, row in LDS)";
-  if (n_cols <= kWideRow && rows <= device_cu_count()) return "wide rows (one workgroup per row, row in LDS)";
   return "long rows (histogram, filter, finish over row segments)";
 }
 
@@ -495,12 +495,14 @@ hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   if (c.rows <= 0) return hipSuccess;
   // rows start on 16-byte boundaries: whole groups of four are read with one load
   const bool v4 = ((uintptr_t)c.logits % 16 == 0) && (c.ld % 4 == 0);
-  if (c.n_cols <= kShortRow)
-    return v4 ? launch_short<true, kShortThreads>(c, stream) : launch_short<false, kShortThreads>(c, stream);
-  // a few rows of up to kWideRow: one pass over each row, all rows at once, beats the
-  // long-row path's four kernels (its workspace, sized for the long path, goes unused)
+  // no more rows than compute units, up to kWideRow columns: one 1024-thread workgroup
+  // per row, all rows at once (for longer rows this beats the long-row path's four
+  // kernels, whose workspace, sized for it, goes unused; for short ones it beats 512
+  // threads: two-level 64 x 8192, 27.7 against 28.5 us per call)
   if (c.n_cols <= kWideRow && c.rows <= device_cu_count())
     return v4 ? launch_short<true, kWideThreads>(c, stream) : launch_short<false, kWideThreads>(c, stream);
+  if (c.n_cols <= kShortRow)
+    return v4 ? launch_short<true, kShortThreads>(c, stream) : launch_short<false, kShortThreads>(c, stream);
   const int64_t R = c.rows;
   uint8_t* p = (uint8_t*)workspace;
   LongWs ws;
