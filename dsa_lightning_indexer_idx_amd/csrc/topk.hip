@@ -199,6 +199,232 @@ __global__ __launch_bounds__(NT) void topk_short_kernel(TopkCall a) {
     write_list<NT>(a, r, key, (int)keff);
 }
 
+// ------------------------------------------------------------------ short rows, one pass
+
+// Rows of up to NT * PER entries, each thread's PER of them held in registers: the
+// row's buckets, linear in the score between its smallest and largest entry (a
+// monotone map), both pick the k-th largest entry and order the winners. Every entry
+// counts itself into its bucket; an exclusive scan of the counts from the highest
+// bucket down gives each bucket's first position and the cut bucket, the one holding
+// the k-th largest entry. Every entry in the cut bucket or above takes a position of its
+// bucket in LDS, and its place in the row is its bucket's first position plus the
+// number of larger keys in the same bucket; places past k are not written. A bucket at or above the cut holding more than kBucketCap
+// entries (clustered scores) sends the row to an exact radix threshold over the row
+// instead, then the bucket sort of the winners (itself bitonic when a bucket is full).
+template <bool V4, int NT, int PER>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void topk_lin_kernel(TopkCall a) {
+  static_assert(PER % 4 == 0 && kBuckets % (4 * NT) == 0, "four entries per load, four counts per read");
+  constexpr int kTmp = kMaxK + kBucketCap;    // keys at or above the cut bucket
+  constexpr int per = kBuckets / NT;          // buckets a thread scans
+  constexpr int waves = NT / kWave;
+  // bucket counts (then first positions) and the keys at or above the cut bucket; for a
+  // row the buckets cannot sort, the row's value keys
+  __shared__ __align__(16) union {
+    struct {
+      uint32_t cnt[kBuckets];
+      uint64_t tmp[kTmp];
+    } b;
+    uint32_t vk[NT * PER];
+  } u;
+  static_assert(sizeof(u.vk) <= sizeof(u.b) && kTmp >= kMaxK, "the row's keys fit the bucket space");
+  uint32_t* cnt = u.b.cnt;
+  uint64_t* tmp = u.b.tmp;
+  __shared__ uint16_t sel[kMaxK];                    // exact path: the winners' columns
+  __shared__ uint32_t rh[256];
+  __shared__ RadixShared sh;
+  __shared__ uint32_t wmx[waves], wmn[waves], wsum[waves];
+  __shared__ uint32_t s_cut, s_fill, s_big, n_sel;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
+  const int r = blockIdx.x;
+  const int64_t n = row_len(a, r);
+  const float* row = a.logits + (int64_t)r * a.ld;
+
+  // entry e of this thread: column 4 (e / 4 * NT + tid) + e % 4
+  uint32_t key[PER];
+#pragma unroll
+  for (int g = 0; g < PER / 4; ++g) {
+    const float4 v = load4<V4, true>(row, ((int64_t)g * NT + tid) * 4, n);
+    key[4 * g] = order_key(v.x);
+    key[4 * g + 1] = order_key(v.y);
+    key[4 * g + 2] = order_key(v.z);
+    key[4 * g + 3] = order_key(v.w);
+  }
+  for (int i = tid; i < kBuckets / 4; i += NT) ((uint4*)cnt)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) {
+    s_big = 0u;
+    n_sel = 0u;
+  }
+  // the smallest and largest present key
+  uint32_t mx = 0u, mn = ~0u;  // the smallest key less one (absent keys wrap to the top)
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    mx = max(mx, key[e]);
+    mn = min(mn, key[e] - 1u);
+  }
+#pragma unroll
+  for (int lb = 0; lb < 6; ++lb) {
+    mx = max(mx, xor_lane(mx, lb));
+    mn = min(mn, xor_lane(mn, lb));
+  }
+  if (lane == 0) {
+    wmx[wv] = mx;
+    wmn[wv] = mn;
+  }
+  __syncthreads();
+  uint32_t lo_key = ~0u, hi_key = 0u;
+#pragma unroll
+  for (int w = 0; w < waves; ++w) {
+    lo_key = min(lo_key, wmn[w]);
+    hi_key = max(hi_key, wmx[w]);
+  }
+  ++lo_key;
+  int32_t* oi = a.out_idx + (int64_t)r * a.out_ld;
+  float* ov = a.out_val ? a.out_val + (int64_t)r * a.out_ld : nullptr;
+  if (hi_key == 0u) {  // nothing present
+    for (int i = tid; i < a.k; i += NT) {
+      oi[i] = -1;
+      if (ov) ov[i] = -__builtin_inff();
+    }
+    return;
+  }
+  // bucket of a key, highest first: (v - lo) * scale, clamped (NaN, only from 0 * inf,
+  // goes to the lowest); an absent key gets kBuckets, past every bucket
+  const float lo = key_value(lo_key);
+  const float d = key_value(hi_key) - lo;
+  const float scale = (d > 0.f && d <= 3.0e38f) ? (float)(kBuckets - 0.01) / d : 0.f;
+  auto bucket = [&](uint32_t k) -> uint32_t {
+    const float f = (key_value(k) - lo) * scale;
+    const int b = f >= 1.f ? min((int)f, kBuckets - 1) : 0;
+    return k ? (uint32_t)(kBuckets - 1 - b) : (uint32_t)kBuckets;
+  };
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const uint32_t b = bucket(key[e]);
+    if (b < (uint32_t)kBuckets) atomicAdd(&cnt[b], 1u);
+  }
+  __syncthreads();
+
+  // exclusive scan of the counts (thread t: buckets per t ..), the cut bucket, and
+  // whether a bucket at or above it is too full
+  uint32_t c[per], sum = 0u;
+#pragma unroll
+  for (int j = 0; j < per; j += 4) {
+    const uint4 q = ((const uint4*)cnt)[per / 4 * tid + j / 4];
+    c[j] = q.x;
+    c[j + 1] = q.y;
+    c[j + 2] = q.z;
+    c[j + 3] = q.w;
+  }
+#pragma unroll
+  for (int j = 0; j < per; ++j) sum += c[j];
+  const uint32_t incl = wave_inclusive_sum(sum);
+  if (lane == kWave - 1) wsum[wv] = incl;
+  __syncthreads();
+  uint32_t off = incl - sum, total = 0u;
+#pragma unroll
+  for (int w = 0; w < waves; ++w) {
+    off += w < wv ? wsum[w] : 0u;
+    total += wsum[w];
+  }
+  const uint32_t keff = min((uint32_t)a.k, total);
+  {
+    uint32_t o = off, jc = ~0u, fc = 0u;
+    bool big = false;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      big |= o < keff && c[j] > (uint32_t)kBucketCap;
+      const bool here = o < keff && keff <= o + c[j];
+      jc = here ? (uint32_t)j : jc;
+      fc = here ? o + c[j] : fc;
+      o += c[j];
+    }
+    if (jc != ~0u) {
+      s_cut = (uint32_t)per * tid + jc;
+      s_fill = fc;
+    }
+    if (big) s_big = 1u;
+  }
+#pragma unroll
+  for (int j = 0; j < per; j += 4) {
+    uint4 q;
+    q.x = off;
+    q.y = q.x + c[j];
+    q.z = q.y + c[j + 1];
+    q.w = q.z + c[j + 2];
+    off = q.w + c[j + 3];
+    ((uint4*)cnt)[per / 4 * tid + j / 4] = q;
+  }
+  __syncthreads();
+  const uint32_t cut = s_cut, fill = s_fill;
+  const int32_t* cand_row = a.cand ? a.cand + (int64_t)r * a.cand_ld : nullptr;
+
+  if (!s_big) {
+    // the entries at or above the cut bucket to their bucket's positions (each bucket's
+    // first position counts up to the next bucket's); the buckets are computed again
+    // rather than kept from the count (the empty asm hides that they are the same)
+    int t4 = 4 * tid;
+    asm volatile("" : "+v"(t4));  // nor the columns kept from the start
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      asm volatile("" : "+v"(key[e]));
+      const uint32_t b = bucket(key[e]);
+      if (b <= cut) {
+        const int64_t col = (int64_t)(e / 4) * NT * 4 + t4 + (e & 3);
+        tmp[atomicAdd(&cnt[b], 1u)] = sel_key(key[e], col);
+      }
+    }
+    __syncthreads();
+    // each one's place: its bucket's first position (the end of the bucket above) plus
+    // the larger keys of its bucket
+    for (uint32_t i = tid; i < fill; i += NT) {
+      const uint64_t x = tmp[i];
+      const uint32_t b = bucket((uint32_t)(x >> 32));
+      const uint32_t st = b > 0 ? cnt[b - 1] : 0u;
+      const uint32_t len = cnt[b] - st;
+      uint32_t pos = st;
+      for (uint32_t j = 0; j < len; j += 4) {
+        uint64_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = tmp[st + min(j + q, len - 1)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pos += (j + q < len) & (v[q] > x);
+      }
+      if (pos < keff) {
+        oi[pos] = out_index(a, cand_row, key_col(x));
+        if (ov) ov[pos] = key_value((uint32_t)(x >> 32));
+      }
+    }
+    for (int i = (int)keff + tid; i < a.k; i += NT) {
+      oi[i] = -1;
+      if (ov) ov[i] = -__builtin_inff();
+    }
+    return;
+  }
+
+  // a full bucket: the row's value keys to LDS, the exact threshold by radix passes over
+  // them, then the columns at or above it, bitonic-sorted (the sort's exchange space
+  // overlaps the keys, which it reads before its first barrier)
+  for (int g = 0; g < PER / 4; ++g) {
+    const float4 v = load4<V4, false>(row, ((int64_t)g * NT + tid) * 4, n);
+    ((uint4*)u.vk)[g * NT + tid] = make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
+  }
+  __syncthreads();
+  auto get = [&](int64_t i) -> uint64_t {
+    const uint32_t v = u.vk[i];
+    return v ? sel_key(v, i) : 0ull;
+  };
+  const uint64_t thr = keff == total ? 1ull : radix_threshold<NT>(get, n, keff, sh, rh);
+  gather_at_least<NT, uint16_t>(get, [&](int64_t i) { return (uint16_t)i; }, n, thr, sel, &n_sel,
+                                (uint32_t)kMaxK);
+  auto keyf = [&](int i) -> uint64_t { return get(sel[i]); };
+  if (a.sorted)
+    sort_and_write<NT>(a, r, keyf, (int)keff, tmp);
+  else
+    write_list<NT>(a, r, keyf, (int)keff);
+}
+
 // ------------------------------------------------------------------ long rows
 
 struct LongWs {
@@ -485,7 +711,22 @@ static void launch_long(const TopkCall& c, const LongWs& ws, int64_t seg, int64_
   hipLaunchKernelGGL(topk_filter_kernel<V4>, grid, dim3(kSegThreads), 0, stream, c, ws, seg, (int)segs);
 }
 
+// Rows of up to kLinRow entries take the one-pass bucket kernel: 1024 threads per row
+// when the rows fit the compute units at once, else 512 (four workgroups per CU).
+constexpr int kLinRow = 8192;
+
+template <bool V4>
+static void launch_lin(const TopkCall& c, hipStream_t stream) {
+  if (c.rows <= device_cu_count())
+    hipLaunchKernelGGL((topk_lin_kernel<V4, 1024, kLinRow / 1024>), dim3((unsigned)c.rows), dim3(1024), 0, stream, c);
+  else
+    hipLaunchKernelGGL((topk_lin_kernel<V4, 512, kLinRow / 512>), dim3((unsigned)c.rows), dim3(512), 0, stream, c);
+}
+
 const char* topk_path(int rows, int64_t n_cols) {
+  if (n_cols <= kLinRow)
+    return rows <= device_cu_count() ? "short rows, one pass (one 1024-thread workgroup per row, linear buckets)"
+                                     : "short rows, one pass (one 512-thread workgroup per row, linear buckets)";
   if (n_cols <= kWideRow && rows <= device_cu_count()) return "wide rows (one 1024-thread workgroup per row, row in LDS)";
   if (n_cols <= kShortRow) return "short rows (one workgroup per row, row in LDS)";
   return "long rows (histogram, filter, finish over row segments)";
@@ -495,6 +736,13 @@ hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   if (c.rows <= 0) return hipSuccess;
   // rows start on 16-byte boundaries: whole groups of four are read with one load
   const bool v4 = ((uintptr_t)c.logits % 16 == 0) && (c.ld % 4 == 0);
+  if (c.n_cols <= kLinRow) {
+    if (v4)
+      launch_lin<true>(c, stream);
+    else
+      launch_lin<false>(c, stream);
+    return hipGetLastError();
+  }
   // no more rows than compute units, up to kWideRow columns: one 1024-thread workgroup
   // per row, all rows at once (for longer rows this beats the long-row path's four
   // kernels, whose workspace, sized for it, goes unused; for short ones it beats 512

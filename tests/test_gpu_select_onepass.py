@@ -171,15 +171,17 @@ def test_empty_and_clamped_ranges_two_pass():
     assert np.array_equal(s_idx, r_idx)
 
 
-@pytest.mark.parametrize("n, rows", [(131072, 48), (65536, 64)])
+@pytest.mark.parametrize("n, rows", [(131072, 48), (65536, 64), (131072, 63)])
 def test_speculative_cut_too_high(n, rows):
     """Rows whose top k sits in one stretch of keys (scales 8x over the first 30% of the
     row): the workgroup part holding that stretch takes a speculative cut from its own
     histogram far above the row's cut and is filtered again at the row's cut, on the
     16-column maxima path (128K-wide rows, and k = 512) and on the plain filter (64K-wide
     rows at k = 2048 take groups of 8). A cold stretch (scales / 8 over the second half)
-    gives parts whose speculative cut lies far below. Every row equals idx_topk over
-    idx_logits bit for bit; the oracle confirms the hot and cold rows."""
+    gives parts whose speculative cut lies far below. With 63 rows of 128K each range of
+    a 256-CU device holds 504 of the 512 steps LDS keeps: no room past the scores for the
+    last part's histogram, which then takes the first part's place. Every row equals
+    idx_topk over idx_logits bit for bit; the oracle confirms the hot and cold rows."""
     require_gpu()
     case = synth.batched_decode(seed=221 + rows, rows=rows, n=n)
     hot, cold = [0, 5, rows - 1], [3]

@@ -54,6 +54,31 @@ def test_adversarial_rows(k):
         _check(lg, k, lens=lens, what=f"adversarial+lens n={n} k={k}")
 
 
+@pytest.mark.parametrize("k", [7, 2048])
+def test_adversarial_rows_many(k):
+    """More rows than compute units (512 threads per row on the one-pass bucket path): the
+    adversarial rows repeated, plus rows whose buckets cannot order them (one outlier
+    squeezes the rest into a few buckets, a cluster of near-equal scores at the cut), each
+    row against the oracle, sorted and unsorted."""
+    require_gpu()
+    for n in (5, 2049, 8192):
+        base = adversarial_rows(n, seed=3 * n + k)
+        rng = np.random.default_rng(n + k)
+        outlier = rng.standard_normal(n).astype(np.float32)
+        outlier[n // 3] = 1e30
+        cluster = rng.standard_normal(n).astype(np.float32)
+        cluster[: n // 2] = np.float32(1.0) + rng.integers(0, 3, n // 2).astype(np.float32) * np.float32(2 ** -20)
+        lg = np.concatenate([np.tile(base, (26, 1)), outlier[None], cluster[None]])
+        lens = rng.integers(0, n + 1, lg.shape[0]).astype(np.int32)
+        _check(lg, k, what=f"many rows n={n} k={k}")
+        _check(lg, k, lens=lens, what=f"many rows+lens n={n} k={k}")
+        r_idx, _ = O.topk(lg, k)
+        g_idx, _ = D.idx_topk(dev(lg), k, sorted=False)
+        g_idx = host(g_idx)
+        for r in range(lg.shape[0]):
+            assert sorted(g_idx[r].tolist()) == sorted(r_idx[r].tolist()), f"unsorted n={n} k={k} row {r}"
+
+
 SMALL = {
     "tiny_dense": lambda: synth.tiny_dense(),
     "dense_fp8": lambda: synth.batched_decode(seed=121, rows=4, n=5000, ragged=True),
