@@ -575,11 +575,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "scan", "select", "copy", "attn", "attn16", "prefill"], default="all",
+    ap.add_argument("--only", choices=["all", "scan", "select", "copy", "attn", "attn16", "prefill", "prefill_select",
+                                          "two_level"], default="all",
                     help="run one timed loop only (for profiler runs); copy: a plain 512 MiB "
                          "device-to-device copy, the counters' calibration; attn: the sparse "
                          "attention workload (attn16: with 16 of its heads); prefill: the prefill "
-                         "chunk's score kernel")
+                         "chunk's score kernel; prefill_select: its idx_select (scores, then "
+                         "top-k); two_level: the two-level candidate workload's idx_select")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) over "
@@ -655,6 +657,28 @@ def main() -> int:
                           args.warmup, torch.cuda.current_stream(), warm_s=0.5)
         flop = float((c4.row_ke.astype(np.int64) - c4.row_ks).sum()) * 64 * 128 * 2
         log(f"prefill scores: {ms * 1e3:.1f} us per call ({100 * flop / (ms * 1e-3) / FP8_PEAK:.1f}% fp8 MFMA)")
+        return 0
+    if args.only == "prefill_select":
+        c4 = synth.prefill_chunk()
+        dev4 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        p4 = D.dense_problem(*map(dev4, (c4.q, c4.w, c4.k, c4.k_scale, c4.row_ks, c4.row_ke)), k_dtype="fp8",
+                             max_cols=c4.max_cols, prefill=True)
+        ws4 = torch.empty(D.idx_select_workspace(p4, 2048), dtype=torch.uint8, device="cuda")
+        oi4 = torch.empty((c4.rows, 2048), dtype=torch.int32, device="cuda")
+        ms, _ = time_loop(lambda: D.idx_select(p4, 2048, values=False, out_idx=oi4, workspace=ws4), args.steps,
+                          args.warmup, torch.cuda.current_stream(), warm_s=0.5)
+        log(f"prefill select: {ms * 1e3:.1f} us per call")
+        return 0
+    if args.only == "two_level":
+        c5 = synth.sparse_blocks()
+        dev5 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        p5 = D.sparse_problem(*map(dev5, (c5.q, c5.w, c5.k, c5.k_scale, c5.row_ks, c5.row_ke, c5.cand, c5.n_cols)),
+                              k_dtype="mxfp4", block_size=128)
+        ws5 = torch.empty(D.idx_select_workspace(p5, 2048), dtype=torch.uint8, device="cuda")
+        oi5 = torch.empty((c5.rows, 2048), dtype=torch.int32, device="cuda")
+        ms, _ = time_loop(lambda: D.idx_select(p5, 2048, values=False, out_idx=oi5, workspace=ws5), args.steps,
+                          args.warmup, torch.cuda.current_stream(), warm_s=0.5)
+        log(f"two-level select: {ms * 1e3:.1f} us per call")
         return 0
     log("generating the 128K paged decode workload")
     case = synth.paged_decode(poison=False)
