@@ -260,9 +260,13 @@ size_t select_lens_bytes(const idx_problem* p) { return (size_t)round_up((int64_
 // kSelMaxSpan of the CUs' workgroups, too many to exchange histograms between. Rows of
 // up to kTopkShortRow columns also take scores then top-k: their one-workgroup-per-row
 // top-k costs less than the one-pass epilogue and finish (two-level 64 x 8192: 31
-// against 37 us). Wider rows take the one pass: batched decode 32 x 32768 50 against
-// 50 us, 256 x 32768 185 against 197 us, the 128K paged decode 158 against 172 us.
+// against 37 us), and so do rows of up to kTopkWideRow columns when there are at most
+// kSelTwoPassRows of them (batched decode R x 32768, scores then top-k against one
+// pass: R = 16 31.9 / 35.8 us, 32 42.6 / 43.8, 64 64.1 / 62.5, 128 106.4 / 104.3).
+// Wider rows take the one pass: 256 x 32768 180 against 185 us, the 128K paged decode
+// 153 against 172 us.
 constexpr int kSelMinRows = 8;
+constexpr int kSelTwoPassRows = 32;
 
 // The shapes the one-pass selection can run at all (the workspace covers both layouts).
 bool select_one_pass_possible(const idx_problem* p) {
@@ -276,7 +280,8 @@ bool select_one_pass_possible(const idx_problem* p) {
 // The shapes that take it by default (IDX_SELECT_ONE_PASS: every possible one).
 bool select_one_pass_shape(const idx_problem* p, uint32_t flags) {
   if (!select_one_pass_possible(p)) return false;
-  return (flags & IDX_SELECT_ONE_PASS) || select_width(p) > kTopkShortRow;
+  const int64_t w = select_width(p);
+  return (flags & IDX_SELECT_ONE_PASS) || (w > kTopkShortRow && !(w <= kTopkWideRow && p->rows <= kSelTwoPassRows));
 }
 
 // Group size of the one-pass cutoff: 16 columns, halved while a row of the call's width

@@ -148,6 +148,8 @@ hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream);
 const char* topk_path(int rows, int64_t n_cols);
 // Rows up to this width take the short-row top-k: one workgroup per row, the row in LDS.
 constexpr int kTopkShortRow = 16384;
+// Rows up to this width take the one-pass bucket top-k when they fit the compute units.
+constexpr int kTopkWideRow = 32768;
 
 // One key-cache write (new bf16 keys quantised into the cache at their slots).
 struct KcacheCall {

@@ -212,21 +212,23 @@ __global__ __launch_bounds__(NT) void topk_short_kernel(TopkCall a) {
 // entries (clustered scores) sends the row to an exact radix threshold over the row
 // instead, then the bucket sort of the winners (itself bitonic when a bucket is full).
 template <bool V4, int NT, int PER>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void topk_lin_kernel(TopkCall a) {
+__global__ __launch_bounds__(NT, PER <= 16 ? 8 : 4) void topk_lin_kernel(TopkCall a) {
   static_assert(PER % 4 == 0 && kBuckets % (4 * NT) == 0, "four entries per load, four counts per read");
   constexpr int kTmp = kMaxK + kBucketCap;    // keys at or above the cut bucket
   constexpr int per = kBuckets / NT;          // buckets a thread scans
   constexpr int waves = NT / kWave;
   // bucket counts (then first positions) and the keys at or above the cut bucket; for a
-  // row the buckets cannot sort, the row's value keys
+  // row the buckets cannot sort, the row's value keys (rows of up to 8192 entries; longer
+  // ones are read again from memory)
+  constexpr bool kKeysInLds = NT * PER <= 8192;
   __shared__ __align__(16) union {
     struct {
       uint32_t cnt[kBuckets];
       uint64_t tmp[kTmp];
     } b;
-    uint32_t vk[NT * PER];
+    uint32_t vk[kKeysInLds ? NT * PER : 1];
   } u;
-  static_assert(sizeof(u.vk) <= sizeof(u.b) && kTmp >= kMaxK, "the row's keys fit the bucket space");
+  static_assert(sizeof(u.vk) <= sizeof(u.b) && kTmp >= kMaxK && NT * PER <= 65536, "the row's keys fit the bucket space");
   uint32_t* cnt = u.b.cnt;
   uint64_t* tmp = u.b.tmp;
   __shared__ uint16_t sel[kMaxK];                    // exact path: the winners' columns
@@ -406,13 +408,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
   // a full bucket: the row's value keys to LDS, the exact threshold by radix passes over
   // them, then the columns at or above it, bitonic-sorted (the sort's exchange space
   // overlaps the keys, which it reads before its first barrier)
-  for (int g = 0; g < PER / 4; ++g) {
-    const float4 v = load4<V4, false>(row, ((int64_t)g * NT + tid) * 4, n);
-    ((uint4*)u.vk)[g * NT + tid] = make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
+  if constexpr (kKeysInLds) {
+    for (int g = 0; g < PER / 4; ++g) {
+      const float4 v = load4<V4, false>(row, ((int64_t)g * NT + tid) * 4, n);
+      ((uint4*)u.vk)[g * NT + tid] = make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
+    }
+    __syncthreads();
   }
-  __syncthreads();
   auto get = [&](int64_t i) -> uint64_t {
-    const uint32_t v = u.vk[i];
+    const uint32_t v = kKeysInLds ? u.vk[i] : order_key(row[i]);
     return v ? sel_key(v, i) : 0ull;
   };
   const uint64_t thr = keff == total ? 1ull : radix_threshold<NT>(get, n, keff, sh, rh);
@@ -683,7 +687,7 @@ size_t topk_workspace_bytes(int rows, int64_t n_cols) {
 }
 
 size_t topk_zeroed_bytes(int rows, int64_t n_cols) {
-  if (rows <= 0 || n_cols <= kShortRow) return 0;
+  if (rows <= 0 || n_cols <= kShortRow || (n_cols <= kWideRow && rows <= device_cu_count())) return 0;
   const int64_t R = rows;
   return (size_t)(round_up(R * kHistBins * 4, 256) + round_up(R * 2 * 4, 256));
 }
@@ -712,22 +716,29 @@ static void launch_long(const TopkCall& c, const LongWs& ws, int64_t seg, int64_
 }
 
 // Rows of up to kLinRow entries take the one-pass bucket kernel: 1024 threads per row
-// when the rows fit the compute units at once, else 512 (four workgroups per CU).
+// when the rows fit the compute units at once, else 512 (four workgroups per CU); rows
+// up to kWideRow entries too when they fit the compute units (1024 threads, 16 or 32
+// entries each).
 constexpr int kLinRow = 8192;
 
 template <bool V4>
 static void launch_lin(const TopkCall& c, hipStream_t stream) {
-  if (c.rows <= device_cu_count())
-    hipLaunchKernelGGL((topk_lin_kernel<V4, 1024, kLinRow / 1024>), dim3((unsigned)c.rows), dim3(1024), 0, stream, c);
-  else
+  if (c.rows > device_cu_count())
     hipLaunchKernelGGL((topk_lin_kernel<V4, 512, kLinRow / 512>), dim3((unsigned)c.rows), dim3(512), 0, stream, c);
+  else if (c.n_cols <= kLinRow)
+    hipLaunchKernelGGL((topk_lin_kernel<V4, 1024, kLinRow / 1024>), dim3((unsigned)c.rows), dim3(1024), 0, stream, c);
+  else if (c.n_cols <= 2 * kLinRow)
+    hipLaunchKernelGGL((topk_lin_kernel<V4, 1024, 2 * kLinRow / 1024>), dim3((unsigned)c.rows), dim3(1024), 0, stream,
+                       c);
+  else
+    hipLaunchKernelGGL((topk_lin_kernel<V4, 1024, kWideRow / 1024>), dim3((unsigned)c.rows), dim3(1024), 0, stream, c);
 }
 
 const char* topk_path(int rows, int64_t n_cols) {
-  if (n_cols <= kLinRow)
-    return rows <= device_cu_count() ? "short rows, one pass (one 1024-thread workgroup per row, linear buckets)"
-                                     : "short rows, one pass (one 512-thread workgroup per row, linear buckets)";
-  if (n_cols <= kWideRow && rows <= device_cu_count()) return "wide rows (one 1024-thread workgroup per row, row in LDS)";
+  if (n_cols <= kLinRow && rows > device_cu_count())
+    return "short rows, one pass (one 512-thread workgroup per row, linear buckets)";
+  if (n_cols <= kWideRow && rows <= device_cu_count())
+    return "rows within the compute units, one pass (one 1024-thread workgroup per row, linear buckets)";
   if (n_cols <= kShortRow) return "short rows (one workgroup per row, row in LDS)";
   return "long rows (histogram, filter, finish over row segments)";
 }
@@ -736,19 +747,16 @@ hipError_t launch_topk(const TopkCall& c, void* workspace, hipStream_t stream) {
   if (c.rows <= 0) return hipSuccess;
   // rows start on 16-byte boundaries: whole groups of four are read with one load
   const bool v4 = ((uintptr_t)c.logits % 16 == 0) && (c.ld % 4 == 0);
-  if (c.n_cols <= kLinRow) {
+  // no more rows than compute units, up to kWideRow columns: one 1024-thread workgroup
+  // per row, all rows at once (for longer rows this beats the long-row path's four
+  // kernels, whose workspace, sized for it, goes unused)
+  if (c.n_cols <= kLinRow || (c.n_cols <= kWideRow && c.rows <= device_cu_count())) {
     if (v4)
       launch_lin<true>(c, stream);
     else
       launch_lin<false>(c, stream);
     return hipGetLastError();
   }
-  // no more rows than compute units, up to kWideRow columns: one 1024-thread workgroup
-  // per row, all rows at once (for longer rows this beats the long-row path's four
-  // kernels, whose workspace, sized for it, goes unused; for short ones it beats 512
-  // threads: two-level 64 x 8192, 27.7 against 28.5 us per call)
-  if (c.n_cols <= kWideRow && c.rows <= device_cu_count())
-    return v4 ? launch_short<true, kWideThreads>(c, stream) : launch_short<false, kWideThreads>(c, stream);
   if (c.n_cols <= kShortRow)
     return v4 ? launch_short<true, kShortThreads>(c, stream) : launch_short<false, kShortThreads>(c, stream);
   const int64_t R = c.rows;

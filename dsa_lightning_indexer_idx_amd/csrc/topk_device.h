@@ -12,7 +12,7 @@ namespace dsaidx {
 
 constexpr int kMaxK = 2048;
 constexpr int kShortRow = kTopkShortRow;  // rows up to this width take the one-kernel path
-constexpr int kWideRow = 32768;        // and up to this width too when there are at most as
+constexpr int kWideRow = kTopkWideRow;  // and up to this width too when there are at most as
                                        // many rows as compute units (1024 threads per row)
 constexpr int kHistBits = 12;          // bins of the value histogram
 constexpr int kHistBins = 1 << kHistBits;
