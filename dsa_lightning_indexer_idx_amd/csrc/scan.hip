@@ -1250,9 +1250,20 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
   // lengths and (idx_select) each row's first step
   const bool first = b == 0 && wib == 0;
   uint64_t total = 0;
+  // scores alone: each lane's row steps of every 64-row pass stay in registers for the
+  // parts below (the launch takes at most kBalancedMaxRows rows: kPasses passes; measured
+  // 0.2-0.6 us off the two-level and batched scans, and no gain beyond noise for
+  // idx_select's one pass, which reads them again)
+  constexpr int kPasses = kBalancedMaxRows / kWave;
+  uint32_t nk[kPasses];
   for (int r0 = 0; r0 < a.rows; r0 += kWave) {
     const int r = r0 + lane;
     const uint32_t n = r < a.rows ? (uint32_t)row_steps(a, src, r, first) : 0u;
+    if constexpr (!SELECT) {
+#pragma unroll
+      for (int i = 0; i < kPasses; ++i)
+        if (r0 == i * kWave) nk[i] = n;
+    }
     const uint32_t incl = wave_inclusive_sum(n);
     if (first && r < a.rows) {
       if (a.lens_out) a.lens_out[r] = (int32_t)row_cols(a, src, r);
@@ -1271,7 +1282,14 @@ __global__ __launch_bounds__(bal_threads<F>()) void scan_bal_kernel(ScanCommon a
     int np = 0;
     for (int r0 = 0; r0 < a.rows && acc < end; r0 += kWave) {
       const int r = r0 + lane;
-      const uint32_t n = r < a.rows ? (uint32_t)row_steps(a, src, r, false) : 0u;
+      uint32_t n = 0u;
+      if constexpr (SELECT) {
+        n = r < a.rows ? (uint32_t)row_steps(a, src, r, false) : 0u;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i)
+          if (r0 == i * kWave) n = nk[i];
+      }
       const uint32_t incl = wave_inclusive_sum(n);
       const uint64_t s = acc + incl - n, e = acc + incl;
       const uint64_t lo = max(s, beg), hi = min(e, end);
