@@ -243,11 +243,13 @@ __global__ __launch_bounds__(NT, PER <= 16 ? 8 : 4) void topk_lin_kernel(TopkCal
   const int64_t n = row_len(a, r);
   const float* row = a.logits + (int64_t)r * a.ld;
 
-  // entry e of this thread: column 4 (e / 4 * NT + tid) + e % 4
+  // entry e of this thread: column 4 (e / 4 * NT + tid) + e % 4 (plain loads: the scores
+  // were mostly just written by the score kernel, and non-temporal loads of them measured
+  // 2 us slower on the prefill chunk's 4096 rows)
   uint32_t key[PER];
 #pragma unroll
   for (int g = 0; g < PER / 4; ++g) {
-    const float4 v = load4<V4, true>(row, ((int64_t)g * NT + tid) * 4, n);
+    const float4 v = load4<V4, false>(row, ((int64_t)g * NT + tid) * 4, n);
     key[4 * g] = order_key(v.x);
     key[4 * g + 1] = order_key(v.y);
     key[4 * g + 2] = order_key(v.z);
