@@ -208,9 +208,11 @@ __global__ __launch_bounds__(NT) void topk_short_kernel(TopkCall a) {
 // bucket down gives each bucket's first position and the cut bucket, the one holding
 // the k-th largest entry. Every entry in the cut bucket or above takes a position of its
 // bucket in LDS, and its place in the row is its bucket's first position plus the
-// number of larger keys in the same bucket; places past k are not written. A bucket at or above the cut holding more than kBucketCap
-// entries (clustered scores) sends the row to an exact radix threshold over the row
-// instead, then the bucket sort of the winners (itself bitonic when a bucket is full).
+// number of larger keys in the same bucket; places past k are not written. A bucket at
+// or above the cut holding more than kBucketCap entries (equal or clustered scores, a
+// far outlier) sends the row to an exact path instead: a radix threshold over the row's
+// keys (in LDS, or read again from memory for rows wider than 8192), the columns at or
+// above it, and a bitonic sort of those.
 template <bool V4, int NT, int PER>
 __global__ __launch_bounds__(NT, PER <= 16 ? 8 : 4) void topk_lin_kernel(TopkCall a) {
   static_assert(PER % 4 == 0 && kBuckets % (4 * NT) == 0, "four entries per load, four counts per read");
@@ -228,7 +230,8 @@ __global__ __launch_bounds__(NT, PER <= 16 ? 8 : 4) void topk_lin_kernel(TopkCal
     } b;
     uint32_t vk[kKeysInLds ? NT * PER : 1];
   } u;
-  static_assert(sizeof(u.vk) <= sizeof(u.b) && kTmp >= kMaxK && NT * PER <= 65536, "the row's keys fit the bucket space");
+  static_assert(sizeof(u.vk) <= sizeof(u.b) && kTmp >= kMaxK && NT * PER <= 65536,
+                "the row's keys fit the bucket space; columns fit 16 bits");
   uint32_t* cnt = u.b.cnt;
   uint64_t* tmp = u.b.tmp;
   __shared__ uint16_t sel[kMaxK];                    // exact path: the winners' columns
