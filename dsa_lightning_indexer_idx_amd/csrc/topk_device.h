@@ -628,7 +628,133 @@ struct alignas(16) FinishLds {
   SortShared ss;
   uint32_t count;
   uint32_t wsum[NT / kWave], wlo[NT / kWave], whi[NT / kWave], wcut[NT / kWave];
+  uint64_t ltmp[kMaxK + kBucketCap];  // finish_lin: the keys at or above the cut bucket
+  uint32_t lcut, lfill, lbig;
 };
+
+// Block-wide: row r from the exact top k of the S (<= kCandCap) keys in L.cand, whose
+// order keys lie in [lo_key, hi_key] (lo_key > 0), in one pass as the one-pass short-row
+// kernel does it: counts in kBuckets buckets linear in the score, an exclusive scan from
+// the highest down for each bucket's first position and the cut bucket, the keys at or
+// above it to their buckets' positions, and each key's place from the larger keys of its
+// bucket. false, with nothing written, when a bucket at or above the cut holds more than
+// kBucketCap keys.
+template <int NT>
+__device__ bool finish_lin(const TopkCall& a, int r, int S, uint32_t lo_key, uint32_t hi_key, FinishLds<NT>& L) {
+  constexpr int E = kCandCap / NT;
+  constexpr int per = kBuckets / NT;
+  static_assert(per % 4 == 0 || per == 4, "four counts per read");
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
+  uint32_t* cnt = (uint32_t*)L.sel;  // kBuckets counts, then first positions
+  uint64_t* tmp = L.ltmp;
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = e * NT + tid;
+    x[e] = i < S ? L.cand[i] : 0ull;
+  }
+  for (int i = tid; i < kBuckets / 4; i += NT) ((uint4*)cnt)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) L.lbig = 0u;
+  __syncthreads();
+  const float lo = key_value(lo_key);
+  const float d = key_value(hi_key) - lo;
+  const float scale = (d > 0.f && d <= 3.0e38f) ? (float)(kBuckets - 0.01) / d : 0.f;
+  auto bucket = [&](uint32_t k) -> uint32_t {
+    const float f = (key_value(k) - lo) * scale;
+    const int b = f >= 1.f ? min((int)f, kBuckets - 1) : 0;
+    return (uint32_t)(kBuckets - 1 - b);
+  };
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (x[e]) atomicAdd(&cnt[bucket((uint32_t)(x[e] >> 32))], 1u);
+  __syncthreads();
+  uint32_t c[per], sum = 0u;
+#pragma unroll
+  for (int j = 0; j < per; j += 4) {
+    const uint4 q = ((const uint4*)cnt)[per / 4 * tid + j / 4];
+    c[j] = q.x;
+    c[j + 1] = q.y;
+    c[j + 2] = q.z;
+    c[j + 3] = q.w;
+  }
+#pragma unroll
+  for (int j = 0; j < per; ++j) sum += c[j];
+  const uint32_t incl = wave_inclusive_sum(sum);
+  if (lane == kWave - 1) L.wsum[wv] = incl;
+  __syncthreads();
+  uint32_t off = incl - sum, total = 0u;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    off += w < wv ? L.wsum[w] : 0u;
+    total += L.wsum[w];
+  }
+  const uint32_t keff = min((uint32_t)a.k, total);
+  {
+    uint32_t o = off, jc = ~0u, fc = 0u;
+    bool big = false;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      big |= o < keff && c[j] > (uint32_t)kBucketCap;
+      const bool here = o < keff && keff <= o + c[j];
+      jc = here ? (uint32_t)j : jc;
+      fc = here ? o + c[j] : fc;
+      o += c[j];
+    }
+    if (jc != ~0u) {
+      L.lcut = (uint32_t)per * tid + jc;
+      L.lfill = fc;
+    }
+    if (big) L.lbig = 1u;
+  }
+#pragma unroll
+  for (int j = 0; j < per; j += 4) {
+    uint4 q;
+    q.x = off;
+    q.y = q.x + c[j];
+    q.z = q.y + c[j + 1];
+    q.w = q.z + c[j + 2];
+    off = q.w + c[j + 3];
+    ((uint4*)cnt)[per / 4 * tid + j / 4] = q;
+  }
+  __syncthreads();
+  if (L.lbig || keff == 0u) return false;
+  const uint32_t cut = L.lcut, fill = L.lfill;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (!x[e]) continue;
+    const uint32_t b = bucket((uint32_t)(x[e] >> 32));
+    if (b <= cut) tmp[atomicAdd(&cnt[b], 1u)] = x[e];
+  }
+  __syncthreads();
+  int32_t* oi = a.out_idx + (int64_t)r * a.out_ld;
+  float* ov = a.out_val ? a.out_val + (int64_t)r * a.out_ld : nullptr;
+  const int32_t* cand_row = a.cand ? a.cand + (int64_t)r * a.cand_ld : nullptr;
+  for (uint32_t i = tid; i < fill; i += NT) {
+    const uint64_t y = tmp[i];
+    const uint32_t b = bucket((uint32_t)(y >> 32));
+    const uint32_t st = b > 0 ? cnt[b - 1] : 0u;
+    const uint32_t len = cnt[b] - st;
+    uint32_t pos = st;
+    for (uint32_t j = 0; j < len; j += 4) {
+      uint64_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = tmp[st + min(j + q, len - 1)];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pos += (j + q < len) & (v[q] > y);
+    }
+    if (pos < keff) {
+      oi[pos] = out_index(a, cand_row, key_col(y));
+      if (ov) ov[pos] = key_value((uint32_t)(y >> 32));
+    }
+  }
+  for (int i = (int)keff + tid; i < a.k; i += NT) {
+    oi[i] = -1;
+    if (ov) ov[i] = -__builtin_inff();
+  }
+  return true;
+}
 
 // Block-wide: row r from the exact top k of the S keys in L.cand (lo_key / hi_key: order
 // keys at or below and at or above all of them, 0 if not known).
@@ -644,6 +770,9 @@ __device__ __forceinline__ void finish_cand(const TopkCall& a, int r, int S, uin
                                                           L.ss, lo_key, hi_key);
     return;
   }
+  // more: one pass over linear buckets when the bounds are known and no bucket at or
+  // above the cut is too full, else a radix threshold, then the sort of the k
+  if (a.sorted && lo_key > 0u && S <= kCandCap && finish_lin<NT>(a, r, S, lo_key, hi_key, L)) return;
   if (tid == 0) L.count = 0;
   __syncthreads();
   int cnt;
